@@ -1,0 +1,576 @@
+/*
+ * ring_oracle.c -- plain, single-threaded CPU oracle for the bucketed
+ * data-parallel gradient-synchronisation path.
+ *
+ * TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg are the only callers. The HIP library never
+ * links, loads or calls this file, and the two share no source, header,
+ * table or helper.
+ *
+ * Build (see oracle/__init__.py):
+ *   gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fPIC -shared
+ * so every fp32 operation below is one IEEE-754 binary32 operation with
+ * round-to-nearest-even: no FMA contraction, no reassociation, no flush of
+ * subnormals, division correctly rounded.
+ *
+ * Sources, cited by page title and section:
+ *   [DDP] "PyTorch DDP Deep Dive -- Initialization, Buffer Broadcast, the
+ *         Reducer, and the torch.compile Story"
+ *   [COL] "Collective Ops From Scratch"
+ *   [DP]  "Data parallelism" (zerotofrontier.app, distributed chapter)
+ *
+ * What is computed, and where it comes from:
+ *   orc_bucket_plan     reverse-registration greedy bucketing with a small
+ *                       first bucket ([DDP] Part 1 "What _ddp_init_helper
+ *                       actually does"; [DDP] Part 3, the DDPOptimizer
+ *                       reverse walk; [DP] "Overlapping communication with
+ *                       the backward pass").
+ *   orc_flatten /       copy each parameter's gradient into / out of its slot
+ *   orc_unflatten       of the bucket's flat buffer, optional pre-divide
+ *                       ([DDP] Part 2 "Step 2: backward", item 1, and
+ *                       "Step 3: finalize_backward").
+ *   orc_ring_allreduce  zero-pad to a multiple of p, p-1 reduce-scatter steps,
+ *                       p-1 all-gather steps, trim ([COL] "Ring allreduce in
+ *                       two passes"; [DP] "Ring all-reduce, derived"), with
+ *                       explicit send buffers and a message log.
+ *   orc_reduce_scatter  the first pass alone, pre-rotated so rank r ends with
+ *                       chunk r; n must divide by p ([COL] list of what the
+ *                       implementation provides).
+ *   orc_allgather       p-1 ring rotations of shards ([COL]; [DP] "The
+ *                       collective operations").
+ *   orc_broadcast       doubling (binomial) tree from src ([COL]).
+ *   orc_fold_samples    the per-element value the ring reaches, written as a
+ *                       fold over ranks (derived from the chunk's journey in
+ *                       [DP] "Ring all-reduce, derived"); pinned in tests to
+ *                       the literal simulation.
+ *
+ * Readings where the pages leave a step open (also listed in the design
+ * notes): equal chunks of ceil(n/p) with the padding at the end; averaging is
+ * one correctly rounded fp32 division of the finished sum by (float)p or by
+ * (float)(total tokens); bf16 inputs are widened exactly, folded in fp32 and
+ * rounded once to bf16 with round-to-nearest-even; the "wire" of a bf16 ring
+ * carries fp32 partials.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL (-1)
+#define ORC_ENOTDIVISIBLE (-2)
+#define ORC_ENOMEM (-3)
+
+#define ORC_AVG_NONE 0
+#define ORC_AVG_WORLD 1
+#define ORC_AVG_TOKENS 2
+
+#define ORC_PHASE_REDUCE_SCATTER 0
+#define ORC_PHASE_ALLGATHER 1
+#define ORC_PHASE_BROADCAST 2
+
+/* One logged message: who sent which chunk to whom, in which step. */
+typedef struct {
+  int32_t phase;
+  int32_t step;
+  int32_t src;
+  int32_t dst;
+  int32_t chunk;
+  int32_t reserved;
+  int64_t bytes;
+} orc_msg;
+
+typedef struct {
+  orc_msg *entries;
+  int64_t capacity;
+  int64_t count;
+} msg_log;
+
+static void log_msg(msg_log *log, int32_t phase, int32_t step, int32_t src,
+                    int32_t dst, int32_t chunk, int64_t bytes) {
+  if (log->entries != NULL && log->count < log->capacity) {
+    orc_msg *m = &log->entries[log->count];
+    m->phase = phase;
+    m->step = step;
+    m->src = src;
+    m->dst = dst;
+    m->chunk = chunk;
+    m->reserved = 0;
+    m->bytes = bytes;
+  }
+  log->count += 1;
+}
+
+static int32_t mod_p(int64_t a, int32_t p) {
+  int64_t m = a % p;
+  return (int32_t)(m < 0 ? m + p : m);
+}
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> fp32                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 is the upper half of a binary32, so widening is exact. */
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Round a binary32 to the nearest bf16, ties to the even neighbour.
+ * Written from the definition: keep the upper 16 bits, then look at the 16
+ * discarded bits. Above half way rounds up, below rounds down, exactly half
+ * way rounds to whichever neighbour has a zero last bit. A carry out of the
+ * mantissa moves into the exponent, which is the correct next value
+ * (including overflow to infinity). NaN stays a quiet NaN. */
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint32_t upper = u >> 16;
+  uint32_t lower = u & 0xFFFFu;
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0) {
+    return (uint16_t)(upper | 0x0040u);
+  }
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) {
+    upper += 1;
+  }
+  return (uint16_t)upper;
+}
+
+void orc_f32_to_bf16_array(const float *in, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(in[i]);
+}
+
+void orc_bf16_to_f32_array(const uint16_t *in, float *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_to_f32(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Averaging divisor                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* World averaging divides by the number of ranks ([DP] "Overlapping
+ * communication with the backward pass", last paragraph). Token averaging
+ * sums per-rank token counts across all ranks and divides the summed
+ * gradient once by that total ([DP] "Why averaging gradients is exactly
+ * large-batch training"). The divisor is the binary32 nearest the integer. */
+static int avg_divisor(int32_t mode, int32_t p, const int64_t *tokens,
+                       float *divisor) {
+  if (mode == ORC_AVG_NONE) {
+    *divisor = 1.0f;
+    return ORC_OK;
+  }
+  if (mode == ORC_AVG_WORLD) {
+    *divisor = (float)p;
+    return ORC_OK;
+  }
+  if (mode == ORC_AVG_TOKENS) {
+    if (tokens == NULL) return ORC_EINVAL;
+    int64_t total = 0;
+    for (int32_t r = 0; r < p; ++r) {
+      if (tokens[r] < 0) return ORC_EINVAL;
+      total += tokens[r];
+    }
+    if (total <= 0) return ORC_EINVAL;
+    *divisor = (float)total;
+    return ORC_OK;
+  }
+  return ORC_EINVAL;
+}
+
+int orc_avg_divisor(int32_t mode, int32_t p, const int64_t *tokens,
+                    float *divisor) {
+  if (p < 1) return ORC_EINVAL;
+  return avg_divisor(mode, p, tokens, divisor);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bucket plan                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Walk the parameters from the last registered to the first (the order in
+ * which backward produces their gradients). Before adding a parameter, if
+ * the open bucket holds at least one parameter and its byte size has reached
+ * its cap, close it and open a new one. The cap of the first bucket filled
+ * is min(first_cap, cap); every later bucket's cap is `cap`. A bucket can
+ * therefore overshoot its cap by its last parameter, and no bucket is empty.
+ *
+ * Outputs:
+ *   fill_order[k]     k-th parameter in fill order (bucket 0 first)
+ *   bucket_begin[b]   index into fill_order where bucket b starts;
+ *                     bucket_begin[n_buckets] == n_params
+ *   offset[i]         element offset of parameter i inside its bucket
+ *   bucket_of[i]      bucket that holds parameter i
+ */
+int orc_bucket_plan(const int64_t *numel, int32_t n_params, int32_t elem_bytes,
+                    int64_t cap, int64_t first_cap, int32_t *fill_order,
+                    int32_t *bucket_begin, int64_t *offset, int32_t *bucket_of,
+                    int32_t *n_buckets) {
+  if (n_params < 0 || elem_bytes <= 0 || cap < 0 || first_cap < 0) {
+    return ORC_EINVAL;
+  }
+  for (int32_t i = 0; i < n_params; ++i) {
+    if (numel[i] < 0) return ORC_EINVAL;
+  }
+  int32_t buckets = 0;       /* buckets opened so far */
+  int32_t filled = 0;        /* parameters placed so far */
+  int64_t open_elems = 0;    /* elements in the open bucket */
+  int32_t open_count = 0;    /* parameters in the open bucket */
+  for (int32_t i = n_params - 1; i >= 0; --i) {
+    if (buckets == 0) {
+      buckets = 1;
+      bucket_begin[0] = 0;
+    } else {
+      int64_t limit = cap;
+      if (buckets == 1 && first_cap < cap) limit = first_cap;
+      if (open_count > 0 && open_elems * elem_bytes >= limit) {
+        bucket_begin[buckets] = filled;
+        buckets += 1;
+        open_elems = 0;
+        open_count = 0;
+      }
+    }
+    fill_order[filled] = i;
+    offset[i] = open_elems;
+    bucket_of[i] = buckets - 1;
+    open_elems += numel[i];
+    open_count += 1;
+    filled += 1;
+  }
+  bucket_begin[buckets] = filled;
+  *n_buckets = buckets;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Flatten / unflatten (one rank)                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Copy every gradient of bucket `b` into the flat buffer at its offset. With
+ * divisor != 1 each element is divided on the way in, as the reducer does
+ * when it pre-divides by the world size. dtype 0 = fp32, 1 = bf16 (the
+ * division then happens in fp32 and rounds once to bf16). */
+int orc_flatten(const void *const *grads, const int64_t *numel,
+                const int32_t *fill_order, const int32_t *bucket_begin,
+                const int64_t *offset, int32_t b, int32_t dtype, float divisor,
+                void *flat) {
+  if (dtype != 0 && dtype != 1) return ORC_EINVAL;
+  for (int32_t k = bucket_begin[b]; k < bucket_begin[b + 1]; ++k) {
+    int32_t i = fill_order[k];
+    int64_t n = numel[i];
+    if (dtype == 0) {
+      const float *g = (const float *)grads[i];
+      float *dst = (float *)flat + offset[i];
+      for (int64_t j = 0; j < n; ++j) {
+        dst[j] = (divisor == 1.0f) ? g[j] : g[j] / divisor;
+      }
+    } else {
+      const uint16_t *g = (const uint16_t *)grads[i];
+      uint16_t *dst = (uint16_t *)flat + offset[i];
+      for (int64_t j = 0; j < n; ++j) {
+        dst[j] = (divisor == 1.0f)
+                     ? g[j]
+                     : orc_f32_to_bf16(orc_bf16_to_f32(g[j]) / divisor);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* Copy each slice of the reduced flat buffer back to its gradient. */
+int orc_unflatten(void *const *grads, const int64_t *numel,
+                  const int32_t *fill_order, const int32_t *bucket_begin,
+                  const int64_t *offset, int32_t b, int32_t elem_bytes,
+                  const void *flat) {
+  if (elem_bytes <= 0) return ORC_EINVAL;
+  for (int32_t k = bucket_begin[b]; k < bucket_begin[b + 1]; ++k) {
+    int32_t i = fill_order[k];
+    memcpy(grads[i], (const char *)flat + offset[i] * elem_bytes,
+           (size_t)(numel[i] * elem_bytes));
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The literal ring, on p padded fp32 arrays                                 */
+/* ------------------------------------------------------------------------ */
+
+/* work[r] holds rank r's padded array of p*C floats. Runs at most
+ * `max_steps` of the 2(p-1) ring steps (a negative value runs all of them).
+ * Every step first copies each rank's outgoing chunk into its own send
+ * buffer, then delivers all messages, so within a step no rank reads a value
+ * another rank wrote in that same step.
+ *
+ * Reduce-scatter step k (k = 0..p-2): rank r sends chunk (r - k - shift) mod p
+ * to rank r+1, which adds it into its own copy. With shift = 0 this is the
+ * all-reduce schedule ([COL] "Ring allreduce in two passes"; [DP] "Ring
+ * all-reduce, derived", phase 1) and leaves rank q owning chunk (q+1) mod p.
+ * shift = 1 is the pre-rotated standalone reduce-scatter, leaving rank q
+ * owning chunk q.
+ *
+ * When the reduce-scatter phase is complete, each owner divides its finished
+ * chunk by the divisor (if averaging), so the all-gather hands out averages.
+ *
+ * All-gather step k: rank r sends chunk (r + 1 - k) mod p to rank r+1, which
+ * overwrites its copy ([DP] "Ring all-reduce, derived", phase 2).
+ *
+ * Returns the number of steps executed. */
+static int32_t ring_on_work(float **work, float **send, int32_t p, int64_t C,
+                            int32_t shift, int32_t run_allgather,
+                            int32_t max_steps, int32_t do_divide,
+                            float divisor, int64_t wire_bytes, msg_log *log) {
+  int32_t done = 0;
+  for (int32_t k = 0; k <= p - 2; ++k) {
+    if (max_steps >= 0 && done >= max_steps) return done;
+    for (int32_t r = 0; r < p; ++r) {
+      int32_t j = mod_p((int64_t)r - k - shift, p);
+      memcpy(send[r], work[r] + (int64_t)j * C, (size_t)C * sizeof(float));
+      log_msg(log, ORC_PHASE_REDUCE_SCATTER, k, r, (r + 1) % p, j,
+              C * wire_bytes);
+    }
+    for (int32_t r = 0; r < p; ++r) {
+      int32_t dst = (r + 1) % p;
+      int32_t j = mod_p((int64_t)r - k - shift, p);
+      float *mine = work[dst] + (int64_t)j * C;
+      for (int64_t e = 0; e < C; ++e) mine[e] = mine[e] + send[r][e];
+    }
+    done += 1;
+  }
+  if (do_divide) {
+    for (int32_t q = 0; q < p; ++q) {
+      int32_t j = mod_p((int64_t)q + 1 - shift, p);
+      float *mine = work[q] + (int64_t)j * C;
+      for (int64_t e = 0; e < C; ++e) mine[e] = mine[e] / divisor;
+    }
+  }
+  if (!run_allgather) return done;
+  for (int32_t k = 0; k <= p - 2; ++k) {
+    if (max_steps >= 0 && done >= max_steps) return done;
+    for (int32_t r = 0; r < p; ++r) {
+      int32_t j = mod_p((int64_t)r + 1 - k, p);
+      memcpy(send[r], work[r] + (int64_t)j * C, (size_t)C * sizeof(float));
+      log_msg(log, ORC_PHASE_ALLGATHER, k, r, (r + 1) % p, j, C * wire_bytes);
+    }
+    for (int32_t r = 0; r < p; ++r) {
+      int32_t dst = (r + 1) % p;
+      int32_t j = mod_p((int64_t)r + 1 - k, p);
+      memcpy(work[dst] + (int64_t)j * C, send[r], (size_t)C * sizeof(float));
+    }
+    done += 1;
+  }
+  return done;
+}
+
+static void free_arrays(float **a, int32_t p) {
+  if (a == NULL) return;
+  for (int32_t r = 0; r < p; ++r) free(a[r]);
+  free(a);
+}
+
+static float **alloc_arrays(int32_t p, int64_t len) {
+  float **a = (float **)calloc((size_t)p, sizeof(float *));
+  if (a == NULL) return NULL;
+  for (int32_t r = 0; r < p; ++r) {
+    /* calloc: the padding elements start at +0.0 */
+    a[r] = (float *)calloc((size_t)(len > 0 ? len : 1), sizeof(float));
+    if (a[r] == NULL) {
+      free_arrays(a, p);
+      return NULL;
+    }
+  }
+  return a;
+}
+
+/* Ring all-reduce of p rank arrays of n elements, in place.
+ * dtype 0: bufs are float*; dtype 1: bufs are bf16 (uint16_t*).
+ * avg_mode: ORC_AVG_NONE / ORC_AVG_WORLD / ORC_AVG_TOKENS (tokens[p]).
+ * max_steps < 0 runs the whole schedule; otherwise only the first max_steps
+ * ring steps run (the divide happens once the reduce-scatter phase is done)
+ * and the partial state is written back, trimmed to n.
+ * log/log_capacity may be NULL/0; *n_msgs receives the message count.
+ * Padding: C = ceil(n/p) elements per chunk, zeros at the end, trimmed. */
+int orc_ring_allreduce(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
+                       int32_t avg_mode, const int64_t *tokens,
+                       int32_t max_steps, orc_msg *log, int64_t log_capacity,
+                       int64_t *n_msgs) {
+  if (p < 1 || n < 0 || (dtype != 0 && dtype != 1)) return ORC_EINVAL;
+  float divisor = 1.0f;
+  int rc = avg_divisor(avg_mode, p, tokens, &divisor);
+  if (rc != ORC_OK) return rc;
+  int64_t C = (n + p - 1) / p;
+  int64_t n_pad = C * p;
+  float **work = alloc_arrays(p, n_pad);
+  float **send = alloc_arrays(p, C);
+  if (work == NULL || send == NULL) {
+    free_arrays(work, p);
+    free_arrays(send, p);
+    return ORC_ENOMEM;
+  }
+  for (int32_t r = 0; r < p; ++r) {
+    if (dtype == 0) {
+      memcpy(work[r], bufs[r], (size_t)n * sizeof(float));
+    } else {
+      orc_bf16_to_f32_array((const uint16_t *)bufs[r], work[r], n);
+    }
+  }
+  msg_log lg = {log, log_capacity, 0};
+  /* The wire carries fp32 values for both dtypes. */
+  ring_on_work(work, send, p, C, /*shift=*/0, /*run_allgather=*/1, max_steps,
+               avg_mode != ORC_AVG_NONE, divisor, (int64_t)sizeof(float), &lg);
+  for (int32_t r = 0; r < p; ++r) {
+    if (dtype == 0) {
+      memcpy(bufs[r], work[r], (size_t)n * sizeof(float));
+    } else {
+      orc_f32_to_bf16_array(work[r], (uint16_t *)bufs[r], n);
+    }
+  }
+  if (n_msgs != NULL) *n_msgs = lg.count;
+  free_arrays(work, p);
+  free_arrays(send, p);
+  return ORC_OK;
+}
+
+/* Standalone reduce-scatter: in[r] has n elements (n divisible by p),
+ * out[r] receives the (averaged) sum of chunk r, C = n/p elements. The
+ * schedule is the ring's first pass with the chunk index shifted by one, so
+ * rank r finishes owning chunk r. */
+int orc_reduce_scatter(const void *const *in, void *const *out, int32_t p,
+                       int64_t n, int32_t dtype, int32_t avg_mode,
+                       const int64_t *tokens, orc_msg *log,
+                       int64_t log_capacity, int64_t *n_msgs) {
+  if (p < 1 || n < 0 || (dtype != 0 && dtype != 1)) return ORC_EINVAL;
+  if (n % p != 0) return ORC_ENOTDIVISIBLE;
+  float divisor = 1.0f;
+  int rc = avg_divisor(avg_mode, p, tokens, &divisor);
+  if (rc != ORC_OK) return rc;
+  int64_t C = n / p;
+  float **work = alloc_arrays(p, n);
+  float **send = alloc_arrays(p, C);
+  if (work == NULL || send == NULL) {
+    free_arrays(work, p);
+    free_arrays(send, p);
+    return ORC_ENOMEM;
+  }
+  for (int32_t r = 0; r < p; ++r) {
+    if (dtype == 0) {
+      memcpy(work[r], in[r], (size_t)n * sizeof(float));
+    } else {
+      orc_bf16_to_f32_array((const uint16_t *)in[r], work[r], n);
+    }
+  }
+  msg_log lg = {log, log_capacity, 0};
+  ring_on_work(work, send, p, C, /*shift=*/1, /*run_allgather=*/0, -1,
+               avg_mode != ORC_AVG_NONE, divisor, (int64_t)sizeof(float), &lg);
+  for (int32_t r = 0; r < p; ++r) {
+    const float *mine = work[r] + (int64_t)r * C;
+    if (dtype == 0) {
+      memcpy(out[r], mine, (size_t)C * sizeof(float));
+    } else {
+      orc_f32_to_bf16_array(mine, (uint16_t *)out[r], C);
+    }
+  }
+  if (n_msgs != NULL) *n_msgs = lg.count;
+  free_arrays(work, p);
+  free_arrays(send, p);
+  return ORC_OK;
+}
+
+/* Standalone all-gather: in[r] is rank r's shard of `shard` elements of
+ * elem_bytes each; out[r] receives the rank-ordered concatenation of all
+ * shards (p*shard elements). Schedule: p-1 ring rotations; at step k rank r
+ * forwards the shard of rank (r - k) mod p to rank r+1. */
+int orc_allgather(const void *const *in, void *const *out, int32_t p,
+                  int64_t shard, int32_t elem_bytes, orc_msg *log,
+                  int64_t log_capacity, int64_t *n_msgs) {
+  if (p < 1 || shard < 0 || elem_bytes <= 0) return ORC_EINVAL;
+  size_t sb = (size_t)(shard * elem_bytes);
+  char **have = (char **)calloc((size_t)p, sizeof(char *));
+  char **send = (char **)calloc((size_t)p, sizeof(char *));
+  if (have == NULL || send == NULL) {
+    free(have);
+    free(send);
+    return ORC_ENOMEM;
+  }
+  int fail = 0;
+  for (int32_t r = 0; r < p && !fail; ++r) {
+    have[r] = (char *)calloc((size_t)p * sb + 1, 1);
+    send[r] = (char *)calloc(sb + 1, 1);
+    if (have[r] == NULL || send[r] == NULL) fail = 1;
+  }
+  if (!fail) {
+    msg_log lg = {log, log_capacity, 0};
+    for (int32_t r = 0; r < p; ++r) {
+      memcpy(have[r] + (size_t)r * sb, in[r], sb);
+    }
+    for (int32_t k = 0; k <= p - 2; ++k) {
+      for (int32_t r = 0; r < p; ++r) {
+        int32_t j = mod_p((int64_t)r - k, p);
+        memcpy(send[r], have[r] + (size_t)j * sb, sb);
+        log_msg(&lg, ORC_PHASE_ALLGATHER, k, r, (r + 1) % p, j, (int64_t)sb);
+      }
+      for (int32_t r = 0; r < p; ++r) {
+        int32_t j = mod_p((int64_t)r - k, p);
+        memcpy(have[(r + 1) % p] + (size_t)j * sb, send[r], sb);
+      }
+    }
+    for (int32_t r = 0; r < p; ++r) memcpy(out[r], have[r], (size_t)p * sb);
+    if (n_msgs != NULL) *n_msgs = lg.count;
+  }
+  for (int32_t r = 0; r < p; ++r) {
+    free(have[r]);
+    free(send[r]);
+  }
+  free(have);
+  free(send);
+  return fail ? ORC_ENOMEM : ORC_OK;
+}
+
+/* Broadcast over a doubling tree, in place: bufs[src] is copied to every
+ * rank. With relative rank v = (r - src) mod p, in round j every rank with
+ * v < 2^j that already holds the data sends it to v + 2^j (if that rank
+ * exists). ceil(log2 p) rounds. */
+int orc_broadcast(void *const *bufs, int32_t p, int64_t n, int32_t elem_bytes,
+                  int32_t src, orc_msg *log, int64_t log_capacity,
+                  int64_t *n_msgs) {
+  if (p < 1 || n < 0 || elem_bytes <= 0 || src < 0 || src >= p) {
+    return ORC_EINVAL;
+  }
+  size_t nb = (size_t)(n * elem_bytes);
+  msg_log lg = {log, log_capacity, 0};
+  int32_t round = 0;
+  for (int64_t span = 1; span < p; span *= 2, ++round) {
+    for (int64_t v = 0; v < span; ++v) {
+      int64_t to = v + span;
+      if (to >= p) continue;
+      int32_t s = (int32_t)((v + src) % p);
+      int32_t d = (int32_t)((to + src) % p);
+      memcpy(bufs[d], bufs[s], nb);
+      log_msg(&lg, ORC_PHASE_BROADCAST, round, s, d, 0, (int64_t)nb);
+    }
+  }
+  if (n_msgs != NULL) *n_msgs = lg.count;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The ring's result at single elements                                      */
+/* ------------------------------------------------------------------------ */
+
+/* For each sample s: vals[s*p + r] is rank r's value at that element and
+ * start[s] the rank whose contribution the ring takes first (the element's
+ * chunk index for the all-reduce; chunk + 1 for the pre-rotated
+ * reduce-scatter). Following one chunk around the ring, every hop adds the
+ * next rank's untouched original value, so the finished sum is
+ *   x[start] + x[start+1] + ... + x[start+p-1]   (indices mod p),
+ * accumulated left to right in fp32, then divided once if averaging. */
+void orc_fold_samples(const float *vals, const int64_t *start, int32_t p,
+                      int64_t count, int32_t do_divide, float divisor,
+                      float *out) {
+  for (int64_t s = 0; s < count; ++s) {
+    const float *x = vals + s * p;
+    int32_t c = mod_p(start[s], p);
+    float acc = x[c];
+    for (int32_t t = 1; t < p; ++t) acc = acc + x[(c + t) % p];
+    out[s] = do_divide ? acc / divisor : acc;
+  }
+}

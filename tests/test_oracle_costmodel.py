@@ -1,0 +1,57 @@
+"""Pin the reconstructed cost model to the figures the page prints.
+
+The page's display equations were lost; oracle/costmodel.py rebuilds them
+from the prose, and these checks hold them to every number the page gives
+("Data parallelism": "Ring all-reduce, derived"; "Latency, trees, and
+choosing an algorithm"; "When data parallelism stops scaling").
+"""
+import json
+import os
+
+import pytest
+
+from oracle import costmodel as cm
+from bucketed_gradient_all_ddp_amd import workloads as W
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "cost_model.json")))
+
+
+def _near(x, entry):
+    return abs(x - entry["printed"]) <= entry["unit"] / 2
+
+
+def test_naive_root_allreduce():
+    e = GOLD["naive_allreduce_seconds"]
+    assert _near(cm.naive_allreduce_time(e["M_bytes"], e["p"], e["bandwidth_Bps"]), e)
+
+
+def test_alpha_over_beta():
+    e = GOLD["alpha_over_beta_bytes"]
+    assert _near(e["alpha_s"] * e["bandwidth_Bps"], e)
+
+
+@pytest.mark.parametrize("e", GOLD["ring_crossover_bytes"])
+def test_crossover(e):
+    beta = 1.0 / e["bandwidth_Bps"]
+    m = cm.ring_crossover(e["p"], e["alpha_s"], beta)
+    assert _near(m, e)
+    # at the crossover the two times agree; above it the ring is faster
+    t_r = cm.allreduce_time(m, e["p"], e["alpha_s"], beta, "ring")
+    t_d = cm.allreduce_time(m, e["p"], e["alpha_s"], beta, "rd")
+    assert abs(t_r - t_d) < 1e-12
+    assert cm.allreduce_time(2 * m, e["p"], e["alpha_s"], beta, "ring") < \
+        cm.allreduce_time(2 * m, e["p"], e["alpha_s"], beta, "rd")
+
+
+@pytest.mark.parametrize("e", GOLD["overlap_tokens"])
+def test_overlap_tokens(e):
+    assert _near(cm.overlap_tokens(e["flops"], e["bandwidth_Bps"]), e)
+
+
+def test_bytes_per_rank_and_caps():
+    assert cm.collective_bytes("allreduce", 800, 8) == 1400
+    assert cm.collective_bytes("reduce_scatter", 800, 8) == 700
+    assert 2 * cm.collective_bytes("allgather", 1e6, 64) == cm.collective_bytes("allreduce", 1e6, 64)
+    caps = GOLD["default_caps_bytes"]
+    assert W.BUCKET_CAP_BYTES == caps["bucket_cap"]
+    assert W.FIRST_BUCKET_CAP_BYTES == caps["first_bucket_cap"]
