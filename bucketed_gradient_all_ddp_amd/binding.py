@@ -1,0 +1,317 @@
+"""Python binding of libddpsim.so (include/ddpsim.h), argument marshalling only.
+
+Each function takes torch tensors for device buffers, passes their
+addresses, sizes and the current HIP stream to the C entry point of the same
+name, and turns a non-zero status into DDPError. No arithmetic of the path
+happens here: every step runs in the library's HIP kernels. PyTorch is used
+only for device memory and streams.
+
+The library is loaded on first use; if it has not been built, the call
+raises ImportError rather than falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libddpsim.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+AVG = {"none": 0, "world": 1, "tokens": 2}
+ALGO = {"fused": 0, "ring": 1}
+MAX_RANKS = 64
+
+STATUS = {
+    0: "DDP_OK", 1: "DDP_EINVAL", 2: "DDP_ERANGE", 3: "DDP_EALIGN", 4: "DDP_EALIAS",
+    5: "DDP_ENOTDIVISIBLE", 6: "DDP_ENOTREADY", 7: "DDP_EWORKSPACE", 8: "DDP_EHIP",
+}
+
+EXPORTS = [
+    "ddp_strerror", "ddp_last_error", "ddp_version",
+    "ddp_bucket_plan", "ddp_plan_free", "ddp_plan_num_params", "ddp_plan_num_buckets",
+    "ddp_plan_bucket_numel", "ddp_plan_bucket_size", "ddp_plan_bucket_params",
+    "ddp_plan_param_bucket", "ddp_plan_param_offset", "ddp_plan_device_bytes",
+    "ddp_plan_upload", "ddp_flatten", "ddp_unflatten",
+    "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
+    "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
+]
+
+
+class DDPError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{func}: {self.name}: {detail}")
+
+
+class CommStats(ctypes.Structure):
+    _fields_ = [
+        ("steps", ctypes.c_int64),
+        ("messages", ctypes.c_int64),
+        ("bytes_sent_per_rank", ctypes.c_int64),
+        ("bytes_recv_per_rank", ctypes.c_int64),
+        ("total_bytes", ctypes.c_int64),
+        ("hbm_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libddpsim.so and declare the C signatures (once)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_float, ctypes.c_size_t)
+    st = ctypes.c_int
+    sig = {
+        "ddp_strerror": ([st], ctypes.c_char_p),
+        "ddp_last_error": ([], ctypes.c_char_p),
+        "ddp_version": ([], ctypes.c_char_p),
+        "ddp_bucket_plan": ([vp, i32, i32, i64, i64, ctypes.POINTER(vp)], st),
+        "ddp_plan_free": ([vp], None),
+        "ddp_plan_num_params": ([vp], i32),
+        "ddp_plan_num_buckets": ([vp], i32),
+        "ddp_plan_bucket_numel": ([vp, i32], i64),
+        "ddp_plan_bucket_size": ([vp, i32], i32),
+        "ddp_plan_bucket_params": ([vp, i32, vp], st),
+        "ddp_plan_param_bucket": ([vp, i32], i32),
+        "ddp_plan_param_offset": ([vp, i32], i64),
+        "ddp_plan_device_bytes": ([vp], sz),
+        "ddp_plan_upload": ([vp, vp, sz, vp], st),
+        "ddp_flatten": ([vp, i32, i32, vp, vp, i32, f32, vp], st),
+        "ddp_unflatten": ([vp, i32, i32, vp, vp, i32, vp], st),
+        "ring_allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, vp, sz, vp, vp], st),
+        "ring_allreduce_sim_workspace": ([i32, i64, i32, i32], sz),
+        "ring_allreduce_sim_steps": ([vp, i32, i64, i32, vp, i32, i32, vp], st),
+        "reduce_scatter_sim": ([vp, vp, i32, i64, i32, i32, vp, vp, vp], st),
+        "allgather_sim": ([vp, vp, i32, i64, i32, vp, vp], st),
+        "broadcast_sim": ([vp, i32, i64, i32, i32, vp, vp], st),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        detail = load_library().ddp_last_error().decode(errors="replace")
+        raise DDPError(status, func, detail)
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptrs(tensors: Sequence) -> ctypes.Array:
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def _tokens(tokens, p: int):
+    if tokens is None:
+        return None
+    arr = (ctypes.c_int64 * p)(*[int(t) for t in tokens])
+    if len(tokens) != p:
+        raise ValueError("tokens needs one count per rank")
+    return arr
+
+
+def _numel_all(tensors: Sequence) -> int:
+    n = tensors[0].numel()
+    for t in tensors:
+        if t.numel() != n or t.dtype != tensors[0].dtype or not t.is_contiguous():
+            raise ValueError("rank buffers must be contiguous with equal size and dtype")
+    return n
+
+
+# ---------------------------------------------------------------------------
+# Bucket plan
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owner of a ddp_plan handle (host) and, after upload(), its device table."""
+
+    def __init__(self, handle: int, elem_bytes: int):
+        self._h = ctypes.c_void_p(handle)
+        self.elem_bytes = elem_bytes
+        self._table = None
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value and _lib is not None:
+            _lib.ddp_plan_free(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def num_params(self) -> int:
+        return load_library().ddp_plan_num_params(self._h)
+
+    @property
+    def num_buckets(self) -> int:
+        return load_library().ddp_plan_num_buckets(self._h)
+
+    def bucket_numel(self, b: int) -> int:
+        return load_library().ddp_plan_bucket_numel(self._h, b)
+
+    def bucket_params(self, b: int) -> List[int]:
+        L = load_library()
+        k = L.ddp_plan_bucket_size(self._h, b)
+        if k < 0:
+            raise IndexError(b)
+        out = (ctypes.c_int32 * max(k, 1))()
+        _check(L.ddp_plan_bucket_params(self._h, b, out), "ddp_plan_bucket_params")
+        return list(out[:k])
+
+    def buckets(self) -> List[List[int]]:
+        return [self.bucket_params(b) for b in range(self.num_buckets)]
+
+    def param_bucket(self, i: int) -> int:
+        return load_library().ddp_plan_param_bucket(self._h, i)
+
+    def param_offset(self, i: int) -> int:
+        return load_library().ddp_plan_param_offset(self._h, i)
+
+    def device_bytes(self) -> int:
+        return load_library().ddp_plan_device_bytes(self._h)
+
+    def upload(self, device="cuda", stream=None) -> "Plan":
+        import torch
+
+        nbytes = self.device_bytes()
+        self._table = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _check(load_library().ddp_plan_upload(self._h, self._table.data_ptr(), nbytes,
+                                              _stream(stream)), "ddp_plan_upload")
+        return self
+
+
+def ddp_bucket_plan(numel: Sequence[int], elem_bytes: int = 4,
+                    bucket_cap_bytes: int = 25 * 1024 * 1024,
+                    first_bucket_cap_bytes: int = 1024 * 1024) -> Plan:
+    L = load_library()
+    n = len(numel)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in numel])
+    out = ctypes.c_void_p()
+    _check(L.ddp_bucket_plan(arr, n, elem_bytes, bucket_cap_bytes, first_bucket_cap_bytes,
+                             ctypes.byref(out)), "ddp_bucket_plan")
+    return Plan(out.value, elem_bytes)
+
+
+def grad_pointer_table(grads: Sequence[Sequence], device="cuda"):
+    """Device int64 tensor of p * n_params gradient addresses, rank-major."""
+    import torch
+
+    flat = [g.data_ptr() for rank in grads for g in rank]
+    return torch.tensor(flat, dtype=torch.int64, device=device)
+
+
+def ddp_flatten(plan: Plan, bucket: int, grad_table, bucket_bufs: Sequence,
+                prescale_divisor: float = 1.0, stream=None) -> None:
+    p = len(bucket_bufs)
+    _check(load_library().ddp_flatten(plan.handle, bucket, p, grad_table.data_ptr(),
+                                      _ptrs(bucket_bufs), _dtype_code(bucket_bufs[0]),
+                                      float(prescale_divisor), _stream(stream)),
+           "ddp_flatten")
+
+
+def ddp_unflatten(plan: Plan, bucket: int, bucket_bufs: Sequence, grad_table,
+                  stream=None) -> None:
+    p = len(bucket_bufs)
+    _check(load_library().ddp_unflatten(plan.handle, bucket, p, _ptrs(bucket_bufs),
+                                        grad_table.data_ptr(), _dtype_code(bucket_bufs[0]),
+                                        _stream(stream)), "ddp_unflatten")
+
+
+# ---------------------------------------------------------------------------
+# Collectives
+# ---------------------------------------------------------------------------
+
+def ring_allreduce_sim_workspace(p: int, n: int, dtype: int, algo: str = "fused") -> int:
+    return load_library().ring_allreduce_sim_workspace(p, n, dtype, ALGO[algo])
+
+
+def ring_allreduce_sim(bufs: Sequence, avg: str = "none", tokens=None,
+                       algo: str = "fused", workspace=None, stream=None) -> CommStats:
+    p = len(bufs)
+    n = _numel_all(bufs)
+    st = CommStats()
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().ring_allreduce_sim(
+        _ptrs(bufs), p, n, _dtype_code(bufs[0]), AVG[avg], _tokens(tokens, p),
+        ALGO[algo], ws_ptr, ws_bytes, _stream(stream), ctypes.byref(st)),
+        "ring_allreduce_sim")
+    return st
+
+
+def ring_allreduce_sim_steps(bufs: Sequence, first_step: int, n_steps: int,
+                             avg: str = "none", tokens=None, stream=None) -> None:
+    p = len(bufs)
+    n = _numel_all(bufs)
+    if _dtype_code(bufs[0]) != DTYPE_F32:
+        raise TypeError("ring_allreduce_sim_steps runs on float32 buffers")
+    _check(load_library().ring_allreduce_sim_steps(
+        _ptrs(bufs), p, n, AVG[avg], _tokens(tokens, p), first_step, n_steps,
+        _stream(stream)), "ring_allreduce_sim_steps")
+
+
+def reduce_scatter_sim(inputs: Sequence, outputs: Sequence, avg: str = "none",
+                       tokens=None, stream=None) -> CommStats:
+    p = len(inputs)
+    n = _numel_all(inputs)
+    st = CommStats()
+    _check(load_library().reduce_scatter_sim(
+        _ptrs(inputs), _ptrs(outputs), p, n, _dtype_code(inputs[0]), AVG[avg],
+        _tokens(tokens, p), _stream(stream), ctypes.byref(st)), "reduce_scatter_sim")
+    return st
+
+
+def allgather_sim(inputs: Sequence, outputs: Sequence, stream=None) -> CommStats:
+    p = len(outputs)
+    n = _numel_all(outputs)
+    st = CommStats()
+    _check(load_library().allgather_sim(
+        _ptrs(inputs), _ptrs(outputs), p, n, _dtype_code(outputs[0]), _stream(stream),
+        ctypes.byref(st)), "allgather_sim")
+    return st
+
+
+def broadcast_sim(bufs: Sequence, src: int = 0, stream=None) -> CommStats:
+    p = len(bufs)
+    n = _numel_all(bufs)
+    st = CommStats()
+    _check(load_library().broadcast_sim(
+        _ptrs(bufs), p, n, src, _dtype_code(bufs[0]), _stream(stream), ctypes.byref(st)),
+        "broadcast_sim")
+    return st

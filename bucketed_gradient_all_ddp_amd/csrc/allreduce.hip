@@ -1,0 +1,366 @@
+// allreduce.hip -- ring all-reduce over p simulated ranks in one GPU's HBM.
+//
+// Two algorithms with identical results ("Collective Ops From Scratch",
+// section "Ring allreduce in two passes"; "Data parallelism", section "Ring
+// all-reduce, derived"):
+//
+//   FUSED  fused_allreduce_kernel: every workgroup owns a tile of one chunk c,
+//          reads the tile from all p ranks once (16-byte loads, all of a batch
+//          in flight), folds it in registers in the ring's order (rank c
+//          first), averages, and writes the result to all p ranks. HBM traffic
+//          2 p n bytes-per-element: the minimum for an in-place all-reduce.
+//
+//   RING   ring_step_kernel, launched 2(p-1) times: one launch is one ring
+//          step in which every rank r "sends" one chunk to rank r+1, i.e. the
+//          receiver's chunk is updated from the sender's copy in HBM
+//          (reduce-scatter: add, all-gather: overwrite). Within a step no
+//          rank reads a chunk another rank writes, so a step needs no
+//          synchronisation beyond the launch boundary. The last
+//          reduce-scatter step also averages each owner's finished chunk.
+//          bf16 runs on an fp32 workspace (the partials are fp32).
+//
+// Padding to a multiple of p is virtual: chunks are [c C, (c+1) C) clipped
+// to n, and elements past n are never read or written.
+#include <algorithm>
+
+#include "fold.hpp"
+#include "internal.hpp"
+
+namespace ddpsim {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Kernels
+// ---------------------------------------------------------------------------
+
+template <typename Tr, int VPT, int RB, bool kNT>
+__global__ __launch_bounds__(kThreads) void fused_allreduce_kernel(
+    RankTable bufs, int32_t p, int64_t n, int64_t C, int32_t tiles_per_chunk,
+    Divide div) {
+  constexpr int V = Tr::kVec;
+  const int32_t c = static_cast<int32_t>(blockIdx.x) / tiles_per_chunk;
+  const int32_t t = static_cast<int32_t>(blockIdx.x) - c * tiles_per_chunk;
+  const ChunkSpan k = chunk_span(c, C, n, V);
+  if (k.s >= k.e) return;
+  const int tid = static_cast<int>(threadIdx.x);
+
+  // Up to V-1 unaligned elements on each side of the chunk: tile 0's first
+  // lanes fold them one by one.
+  if (t == 0 && tid < 2 * (V - 1)) {
+    const bool head = tid < V - 1;
+    const int64_t i = head ? k.s + tid : k.tail_begin + (tid - (V - 1));
+    if (i < (head ? k.head_end : k.e)) {
+      const float y = apply_divide(fold_scalar<Tr>(bufs, p, c, i), div);
+      for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
+    }
+  }
+
+  const int64_t nv = (k.ve - k.vs) / V;
+  const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+  if (base >= nv) return;
+  int64_t vi[VPT];
+  bool ok[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int64_t j = base + u * kThreads + tid;
+    ok[u] = j < nv;
+    vi[u] = k.vs / V + j;
+  }
+  float acc[VPT][V];
+  fold_vectors<Tr, VPT, RB>(bufs, p, c, vi, ok, acc);
+  uint4 y[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
+    y[u] = Tr::narrow(acc[u]);
+  }
+  for (int32_t r = 0; r < p; ++r) {
+    void *dst = bufs.ptr[r];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);
+    }
+  }
+}
+
+// One ring step on p fp32 buffers. Sender r = blockIdx.x / tiles_per_chunk
+// sends chunk (r + chunk_shift) mod p to rank r+1.
+//   kReduce  receiver = receiver + sender (then divide, on the last
+//            reduce-scatter step); otherwise receiver = sender.
+template <bool kReduce, int VPT>
+__global__ __launch_bounds__(kThreads) void ring_step_kernel(
+    RankTable bufs, int32_t p, int32_t chunk_shift, int64_t n, int64_t C,
+    int32_t tiles_per_chunk, Divide div) {
+  constexpr int V = 4;
+  const int32_t r = static_cast<int32_t>(blockIdx.x) / tiles_per_chunk;
+  const int32_t t = static_cast<int32_t>(blockIdx.x) - r * tiles_per_chunk;
+  const int32_t dst = r + 1 == p ? 0 : r + 1;
+  const int32_t j = ring_rank(r, chunk_shift, p);
+  const ChunkSpan k = chunk_span(j, C, n, V);
+  if (k.s >= k.e) return;
+  const float *src = static_cast<const float *>(bufs.ptr[r]);
+  float *out = static_cast<float *>(bufs.ptr[dst]);
+  const int tid = static_cast<int>(threadIdx.x);
+
+  if (t == 0 && tid < 2 * (V - 1)) {
+    const bool head = tid < V - 1;
+    const int64_t i = head ? k.s + tid : k.tail_begin + (tid - (V - 1));
+    if (i < (head ? k.head_end : k.e)) {
+      out[i] = kReduce ? apply_divide(out[i] + src[i], div) : src[i];
+    }
+  }
+
+  const int64_t nv = (k.ve - k.vs) / V;
+  const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+  if (base >= nv) return;
+  uint4 a[VPT], b[VPT];
+  int64_t vi[VPT];
+  bool ok[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int64_t jj = base + u * kThreads + tid;
+    ok[u] = jj < nv;
+    vi[u] = k.vs / V + jj;
+    if (ok[u]) {
+      b[u] = load_vec(src, vi[u]);
+      if (kReduce) a[u] = load_vec(out, vi[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    if (!ok[u]) continue;
+    if (kReduce) {
+      float fa[4], fb[4];
+      F32Traits::widen(a[u], fa);
+      F32Traits::widen(b[u], fb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fa[e] = apply_divide(fa[e] + fb[e], div);
+      store_vec<false>(out, vi[u], F32Traits::narrow(fa));
+    } else {
+      store_vec<false>(out, vi[u], b[u]);
+    }
+  }
+}
+
+// bf16 rank buffers <-> fp32 workspace rows (row r at ws + r * stride).
+template <bool kToWorkspace>
+__global__ __launch_bounds__(kThreads) void bf16_workspace_kernel(
+    RankTable bufs, float *ws, int64_t ws_stride, int64_t n,
+    int32_t tiles_per_rank) {
+  constexpr int kElems = 8;  // one 16-byte bf16 vector, two fp32 vectors
+  const int32_t r = static_cast<int32_t>(blockIdx.x) / tiles_per_rank;
+  const int32_t t = static_cast<int32_t>(blockIdx.x) - r * tiles_per_rank;
+  uint16_t *b = static_cast<uint16_t *>(bufs.ptr[r]);
+  float *w = ws + r * ws_stride;
+  const int64_t v = static_cast<int64_t>(t) * kThreads + threadIdx.x;
+  const int64_t i0 = v * kElems;
+  if (i0 >= n) return;
+  if (i0 + kElems <= n) {
+    if (kToWorkspace) {
+      float f[8];
+      BF16Traits::widen(load_vec(b, v), f);
+      store_vec<false>(w, 2 * v, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                            __float_as_uint(f[2]), __float_as_uint(f[3])));
+      store_vec<false>(w, 2 * v + 1, make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]),
+                                                __float_as_uint(f[6]), __float_as_uint(f[7])));
+    } else {
+      float f[8];
+      float lo[4], hi[4];
+      F32Traits::widen(load_vec(w, 2 * v), lo);
+      F32Traits::widen(load_vec(w, 2 * v + 1), hi);
+      for (int e = 0; e < 4; ++e) {
+        f[e] = lo[e];
+        f[e + 4] = hi[e];
+      }
+      store_vec<false>(b, v, BF16Traits::narrow(f));
+    }
+  } else {
+    for (int64_t i = i0; i < n; ++i) {
+      if (kToWorkspace) {
+        w[i] = BF16Traits::load1(b, i);
+      } else {
+        BF16Traits::store1(b, i, w[i]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+constexpr int kFusedVpt = 2;  // 16-byte vectors per thread
+constexpr int kFusedRb = 8;   // rank loads in flight per vector
+constexpr int kStepVpt = 4;
+
+int32_t tiles_for(int64_t C, int vec, int vpt) {
+  const int64_t vectors = C / vec;
+  return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(vectors, int64_t(kThreads) * vpt)));
+}
+
+ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtype,
+                        const Divide &div, hipStream_t stream) {
+  const int64_t C = ceil_div(n, p);
+  const int vec = dtype == DDP_F32 ? 4 : 8;
+  const int32_t tpc = tiles_for(C, vec, kFusedVpt);
+  const int64_t blocks = int64_t(tpc) * p;
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
+  if (dtype == DDP_F32) {
+    fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false>
+        <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, n, C, tpc, div);
+  } else {
+    fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false>
+        <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, n, C, tpc, div);
+  }
+  return check_hip(hipGetLastError(), "fused_allreduce_kernel launch");
+}
+
+// Launch ring steps [first, first + count) on fp32 buffers.
+ddp_status launch_steps(const RankTable &tab, int32_t p, int64_t n, const Divide &div,
+                        int32_t first, int32_t count, hipStream_t stream) {
+  const int64_t C = ceil_div(n, p);
+  const int32_t tpc = tiles_for(C, 4, kStepVpt);
+  const int64_t blocks = int64_t(tpc) * p;
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring step: n too large");
+  const Divide none{kNone, 1.0f, 1.0f};
+  for (int32_t s = first; s < first + count; ++s) {
+    if (s < p - 1) {
+      const int32_t k = s;  // reduce-scatter step k: rank r sends chunk r - k
+      const int32_t shift = ((-k) % p + p) % p;
+      const Divide &d = (k == p - 2) ? div : none;
+      ring_step_kernel<true, kStepVpt>
+          <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, shift, n, C, tpc, d);
+    } else {
+      const int32_t k = s - (p - 1);  // all-gather step k: chunk r + 1 - k
+      const int32_t shift = ((1 - k) % p + p) % p;
+      ring_step_kernel<false, kStepVpt>
+          <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, shift, n, C, tpc, none);
+    }
+    ddp_status st = check_hip(hipGetLastError(), "ring_step_kernel launch");
+    if (st != DDP_OK) return st;
+  }
+  return DDP_OK;
+}
+
+int64_t workspace_stride_elems(int64_t n) {
+  // fp32 rows rounded up to 256 bytes
+  return ceil_div(n * 4, 256) * 256 / 4;
+}
+
+void fill_allreduce_stats(ddp_comm_stats *st, int32_t p, int64_t n, int32_t dtype,
+                          int32_t algo) {
+  if (st == nullptr) return;
+  const int64_t eb = elem_bytes_of(dtype);
+  const int64_t C = n > 0 ? ceil_div(n, p) : 0;
+  st->steps = 2 * int64_t(p - 1);
+  st->messages = 2 * int64_t(p) * (p - 1);
+  st->bytes_sent_per_rank = 2 * int64_t(p - 1) * C * 4;
+  st->bytes_recv_per_rank = st->bytes_sent_per_rank;
+  st->total_bytes = st->messages * C * 4;
+  if (algo == DDP_ALGO_FUSED || p == 1) {
+    st->hbm_bytes = 2 * int64_t(p) * n * eb;
+  } else {
+    int64_t b = 5 * int64_t(p - 1) * n * 4;
+    if (dtype == DDP_BF16) b += 2 * int64_t(p) * n * (2 + 4);
+    st->hbm_bytes = b;
+  }
+}
+
+ddp_status validate_common(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
+                           int32_t avg_mode, const int64_t *tokens, Divide *div,
+                           const char *what) {
+  ddp_status s = check_p(p, what);
+  if (s != DDP_OK) return s;
+  if (n < 0) return fail(DDP_EINVAL, "%s: n=%lld is negative", what, (long long)n);
+  const int eb = elem_bytes_of(dtype);
+  if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  s = make_divide(avg_mode, p, tokens, div);
+  if (s != DDP_OK) return s;
+  return check_rank_buffers(what, bufs, p, n * eb);
+}
+
+}  // namespace
+}  // namespace ddpsim
+
+using namespace ddpsim;
+
+extern "C" size_t ring_allreduce_sim_workspace(int32_t p, int64_t n, int32_t dtype,
+                                               int32_t algo) {
+  if (p < 1 || p > kMaxRanks || n <= 0) return 0;
+  if (algo != DDP_ALGO_RING || dtype != DDP_BF16 || p == 1) return 0;
+  return static_cast<size_t>(p) * workspace_stride_elems(n) * 4;
+}
+
+extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n,
+                                         int32_t dtype, int32_t avg_mode,
+                                         const int64_t *tokens, int32_t algo,
+                                         void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream, ddp_comm_stats *stats) {
+  clear_error();
+  Divide div;
+  ddp_status s = validate_common(bufs, p, n, dtype, avg_mode, tokens, &div,
+                                 "ring_allreduce_sim");
+  if (s != DDP_OK) return s;
+  if (algo != DDP_ALGO_FUSED && algo != DDP_ALGO_RING) {
+    return fail(DDP_EINVAL, "ring_allreduce_sim: unknown algorithm %d", algo);
+  }
+  const size_t need = ring_allreduce_sim_workspace(p, n, dtype, algo);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) {
+      return fail(DDP_EWORKSPACE, "ring_allreduce_sim: needs %zu workspace bytes, got %zu",
+                  need, workspace == nullptr ? size_t(0) : workspace_bytes);
+    }
+    if (reinterpret_cast<uintptr_t>(workspace) % kVecBytes != 0) {
+      return fail(DDP_EALIGN, "ring_allreduce_sim: workspace is not 16-byte aligned");
+    }
+    const int64_t eb = elem_bytes_of(dtype);
+    for (int32_t r = 0; r < p; ++r) {
+      if (ranges_overlap(workspace, int64_t(need), bufs[r], n * eb)) {
+        return fail(DDP_EALIAS, "ring_allreduce_sim: workspace overlaps rank %d", r);
+      }
+    }
+  }
+  fill_allreduce_stats(stats, p, n, dtype, algo);
+  if (n == 0) return DDP_OK;
+  const RankTable tab = make_table(bufs, p);
+  if (algo == DDP_ALGO_FUSED || p == 1) return launch_fused(tab, p, n, dtype, div, stream);
+  if (dtype == DDP_F32) return launch_steps(tab, p, n, div, 0, 2 * (p - 1), stream);
+
+  // bf16 ring: widen into fp32 rows, run the steps there, round back.
+  const int64_t stride = workspace_stride_elems(n);
+  float *ws = static_cast<float *>(workspace);
+  const int32_t tpr = static_cast<int32_t>(ceil_div(ceil_div(n, 8), kThreads));
+  const int64_t blocks = int64_t(tpr) * p;
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
+  bf16_workspace_kernel<true><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+      tab, ws, stride, n, tpr);
+  s = check_hip(hipGetLastError(), "bf16_workspace_kernel launch");
+  if (s != DDP_OK) return s;
+  RankTable rows;
+  for (int32_t r = 0; r < kMaxRanks; ++r) rows.ptr[r] = r < p ? ws + r * stride : nullptr;
+  s = launch_steps(rows, p, n, div, 0, 2 * (p - 1), stream);
+  if (s != DDP_OK) return s;
+  bf16_workspace_kernel<false><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+      tab, ws, stride, n, tpr);
+  return check_hip(hipGetLastError(), "bf16_workspace_kernel launch");
+}
+
+extern "C" ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int64_t n,
+                                               int32_t avg_mode, const int64_t *tokens,
+                                               int32_t first_step, int32_t n_steps,
+                                               hipStream_t stream) {
+  clear_error();
+  Divide div;
+  ddp_status s = validate_common(bufs, p, n, DDP_F32, avg_mode, tokens, &div,
+                                 "ring_allreduce_sim_steps");
+  if (s != DDP_OK) return s;
+  if (p < 2) return fail(DDP_ERANGE, "ring_allreduce_sim_steps: needs p >= 2");
+  const int32_t total = 2 * (p - 1);
+  if (first_step < 0 || n_steps < 0 || first_step > total || n_steps > total - first_step) {
+    return fail(DDP_ERANGE, "ring_allreduce_sim_steps: steps [%d, %d) outside [0, %d)",
+                first_step, first_step + n_steps, total);
+  }
+  if (n == 0 || n_steps == 0) return DDP_OK;
+  return launch_steps(make_table(bufs, p), p, n, div, first_step, n_steps, stream);
+}

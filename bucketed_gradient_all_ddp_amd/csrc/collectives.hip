@@ -1,0 +1,316 @@
+// collectives.hip -- standalone reduce-scatter, all-gather and broadcast over
+// p simulated ranks in one GPU's HBM ("Collective Ops From Scratch", the
+// list of primitives its implementation provides; "Data parallelism",
+// section "The collective operations").
+//
+//   reduce-scatter  out[r] = average of chunk r summed over ranks, folded in
+//                   the ring order of the pre-rotated schedule (rank r+1
+//                   first). One pass: each input read once, each output
+//                   written once.
+//   all-gather      out[r] = in[0] || ... || in[p-1]: every shard is read
+//                   once and written to all p outputs (its owner's slice is
+//                   skipped when the call is in place).
+//   broadcast       the source buffer is read once and written to the other
+//                   p-1 ranks. The doubling tree's rounds exist only in the
+//                   accounting: on one device every copy reads the same
+//                   bytes, so the tree would only add passes.
+#include <algorithm>
+#include <cstring>
+
+#include "fold.hpp"
+#include "internal.hpp"
+
+namespace ddpsim {
+namespace {
+
+constexpr int kRsVpt = 2;
+constexpr int kRsRb = 8;
+constexpr int kCopyVpt = 4;
+
+// Reduce-scatter, C = n/p elements per shard. Workgroups of shard c:
+// blockIdx.x / tiles_per_chunk. kVector: C is a whole number of 16-byte
+// vectors, so input chunk c and output c are both vector aligned.
+template <typename Tr, int VPT, int RB, bool kVector>
+__global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(
+    RankTable in, RankTable out, int32_t p, int64_t C, int32_t tiles_per_chunk,
+    Divide div) {
+  constexpr int V = Tr::kVec;
+  const int32_t c = static_cast<int32_t>(blockIdx.x) / tiles_per_chunk;
+  const int32_t t = static_cast<int32_t>(blockIdx.x) - c * tiles_per_chunk;
+  const int32_t first = c + 1 == p ? 0 : c + 1;
+  void *dst = out.ptr[c];
+  const int tid = static_cast<int>(threadIdx.x);
+  if constexpr (kVector) {
+    const int64_t nv = C / V;
+    const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+    if (base >= nv) return;
+    int64_t vi[VPT];
+    bool ok[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int64_t j = base + u * kThreads + tid;
+      ok[u] = j < nv;
+      vi[u] = static_cast<int64_t>(c) * nv + j;
+    }
+    float acc[VPT][V];
+    fold_vectors<Tr, VPT, RB>(in, p, first, vi, ok, acc);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
+      store_vec<false>(dst, vi[u] - static_cast<int64_t>(c) * nv, Tr::narrow(acc[u]));
+    }
+  } else {
+    // Element-wise path for shards that are not a whole number of vectors.
+    const int64_t per_tile = int64_t(kThreads) * VPT * V;
+    const int64_t lo = static_cast<int64_t>(t) * per_tile;
+    for (int64_t j = lo + tid; j < lo + per_tile && j < C; j += kThreads) {
+      const float y = apply_divide(fold_scalar<Tr>(in, p, first, c * C + j), div);
+      Tr::store1(dst, j, y);
+    }
+  }
+}
+
+// Copy `bytes` from each source s (blockIdx.y) to every destination r at
+// byte offset s * dst_stride, except r == skip[s]. kVector: sources and
+// destination offsets are 16-byte aligned; the last bytes % 16 are copied
+// as 16-bit units (element sizes are 2 or 4 bytes).
+struct SkipTable {
+  int32_t rank[kMaxRanks];
+};
+
+template <int VPT, bool kVector>
+__global__ __launch_bounds__(kThreads) void fanout_copy_kernel(
+    RankTable src, RankTable dst, int32_t p, int64_t bytes, int64_t dst_stride,
+    SkipTable skip) {
+  const int32_t s = static_cast<int32_t>(blockIdx.y);
+  const int32_t no = skip.rank[s];
+  const char *from = static_cast<const char *>(src.ptr[s]);
+  const int64_t off = static_cast<int64_t>(s) * dst_stride;
+  const int tid = static_cast<int>(threadIdx.x);
+  if constexpr (kVector) {
+    const int64_t nv = bytes / 16;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * VPT);
+    uint4 x[VPT];
+    bool ok[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int64_t j = base + u * kThreads + tid;
+      ok[u] = j < nv;
+      if (ok[u]) x[u] = load_vec(from, j);
+    }
+    for (int32_t r = 0; r < p; ++r) {
+      if (r == no) continue;
+      char *to = static_cast<char *>(dst.ptr[r]) + off;
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        if (ok[u]) store_vec<false>(to, base + u * kThreads + tid, x[u]);
+      }
+    }
+    // trailing bytes, by the last workgroup
+    if (blockIdx.x == gridDim.x - 1) {
+      const int64_t tail = bytes - nv * 16;
+      const int64_t units = tail / 2;
+      if (tid < units) {
+        const int64_t b = nv * 16 + 2 * tid;
+        const uint16_t v = *reinterpret_cast<const uint16_t *>(from + b);
+        for (int32_t r = 0; r < p; ++r) {
+          if (r == no) continue;
+          *reinterpret_cast<uint16_t *>(static_cast<char *>(dst.ptr[r]) + off + b) = v;
+        }
+      }
+    }
+  } else {
+    const int64_t units = bytes / 2;
+    const int64_t per_tile = int64_t(kThreads) * VPT * 8;
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * per_tile;
+    for (int64_t j = lo + tid; j < lo + per_tile && j < units; j += kThreads) {
+      const uint16_t v = reinterpret_cast<const uint16_t *>(from)[j];
+      for (int32_t r = 0; r < p; ++r) {
+        if (r == no) continue;
+        *reinterpret_cast<uint16_t *>(static_cast<char *>(dst.ptr[r]) + off + 2 * j) = v;
+      }
+    }
+  }
+}
+
+ddp_status launch_fanout(const RankTable &src, int32_t n_src, const RankTable &dst,
+                         int32_t p, int64_t bytes, int64_t dst_stride,
+                         const SkipTable &skip, hipStream_t stream, const char *what) {
+  if (bytes == 0) return DDP_OK;
+  const bool vec = dst_stride % 16 == 0;
+  const int64_t per_tile = vec ? int64_t(kThreads) * kCopyVpt * 16
+                               : int64_t(kThreads) * kCopyVpt * 16;
+  const int64_t tiles = std::max<int64_t>(1, ceil_div(bytes, per_tile));
+  if (tiles > INT32_MAX) return fail(DDP_EINVAL, "%s: buffer too large", what);
+  const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(n_src));
+  if (vec) {
+    fanout_copy_kernel<kCopyVpt, true><<<grid, dim3(kThreads), 0, stream>>>(
+        src, dst, p, bytes, dst_stride, skip);
+  } else {
+    fanout_copy_kernel<kCopyVpt, false><<<grid, dim3(kThreads), 0, stream>>>(
+        src, dst, p, bytes, dst_stride, skip);
+  }
+  return check_hip(hipGetLastError(), what);
+}
+
+void fill_stats(ddp_comm_stats *st, int64_t steps, int64_t messages, int64_t sent,
+                int64_t recv, int64_t total, int64_t hbm) {
+  if (st == nullptr) return;
+  st->steps = steps;
+  st->messages = messages;
+  st->bytes_sent_per_rank = sent;
+  st->bytes_recv_per_rank = recv;
+  st->total_bytes = total;
+  st->hbm_bytes = hbm;
+}
+
+}  // namespace
+}  // namespace ddpsim
+
+using namespace ddpsim;
+
+extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out,
+                                         int32_t p, int64_t n, int32_t dtype,
+                                         int32_t avg_mode, const int64_t *tokens,
+                                         hipStream_t stream, ddp_comm_stats *stats) {
+  clear_error();
+  const char *what = "reduce_scatter_sim";
+  ddp_status s = check_p(p, what);
+  if (s != DDP_OK) return s;
+  if (n < 0) return fail(DDP_EINVAL, "%s: n is negative", what);
+  const int eb = elem_bytes_of(dtype);
+  if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  if (n % p != 0) {
+    return fail(DDP_ENOTDIVISIBLE, "%s: n=%lld is not divisible by p=%d", what,
+                (long long)n, p);
+  }
+  Divide div;
+  s = make_divide(avg_mode, p, tokens, &div);
+  if (s != DDP_OK) return s;
+  const int64_t C = n / p;
+  s = check_rank_buffers(what, in, p, n * eb);
+  if (s != DDP_OK) return s;
+  s = check_rank_buffers(what, reinterpret_cast<const void *const *>(out), p, C * eb);
+  if (s != DDP_OK) return s;
+  // out[r] may sit exactly on its own chunk of in[r]; nothing else may overlap.
+  for (int32_t r = 0; r < p && C > 0; ++r) {
+    const char *own = static_cast<const char *>(in[r]) + r * C * eb;
+    for (int32_t q = 0; q < p; ++q) {
+      if (!ranges_overlap(out[r], C * eb, in[q], n * eb)) continue;
+      if (q == r && out[r] == own) continue;
+      return fail(DDP_EALIAS, "%s: output of rank %d overlaps input of rank %d", what, r, q);
+    }
+  }
+  fill_stats(stats, p - 1, int64_t(p) * (p - 1), (p - 1) * C * 4, (p - 1) * C * 4,
+             int64_t(p) * (p - 1) * C * 4, (int64_t(p) + 1) * n * eb);
+  if (n == 0) return DDP_OK;
+  const RankTable tin = make_table(in, p);
+  const RankTable tout = make_table(reinterpret_cast<const void *const *>(out), p);
+  const int V = dtype == DDP_F32 ? 4 : 8;
+  const bool vec = C % V == 0;
+  const int64_t per_tile = int64_t(kThreads) * kRsVpt * (vec ? 1 : V);
+  const int64_t units = vec ? C / V : C;
+  const int64_t tpc = std::max<int64_t>(1, ceil_div(units, per_tile));
+  const int64_t blocks = tpc * p;
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "%s: n too large", what);
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  const int32_t tpc32 = static_cast<int32_t>(tpc);
+  if (dtype == DDP_F32) {
+    if (vec) {
+      reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true><<<grid, dim3(kThreads), 0, stream>>>(
+          tin, tout, p, C, tpc32, div);
+    } else {
+      reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false><<<grid, dim3(kThreads), 0, stream>>>(
+          tin, tout, p, C, tpc32, div);
+    }
+  } else {
+    if (vec) {
+      reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true><<<grid, dim3(kThreads), 0, stream>>>(
+          tin, tout, p, C, tpc32, div);
+    } else {
+      reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false><<<grid, dim3(kThreads), 0, stream>>>(
+          tin, tout, p, C, tpc32, div);
+    }
+  }
+  return check_hip(hipGetLastError(), "reduce_scatter_kernel launch");
+}
+
+extern "C" ddp_status allgather_sim(const void *const *in, void *const *out, int32_t p,
+                                    int64_t n, int32_t dtype, hipStream_t stream,
+                                    ddp_comm_stats *stats) {
+  clear_error();
+  const char *what = "allgather_sim";
+  ddp_status s = check_p(p, what);
+  if (s != DDP_OK) return s;
+  if (n < 0) return fail(DDP_EINVAL, "%s: n is negative", what);
+  const int eb = elem_bytes_of(dtype);
+  if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  if (n % p != 0) {
+    return fail(DDP_ENOTDIVISIBLE, "%s: n=%lld is not divisible by p=%d", what,
+                (long long)n, p);
+  }
+  const int64_t C = n / p;
+  s = check_rank_buffers(what, reinterpret_cast<const void *const *>(out), p, n * eb);
+  if (s != DDP_OK) return s;
+  if (in == nullptr) return fail(DDP_EINVAL, "%s: input array is NULL", what);
+  SkipTable skip;
+  for (int32_t r = 0; r < kMaxRanks; ++r) skip.rank[r] = -1;
+  int64_t in_place = 0;
+  for (int32_t j = 0; j < p && C > 0; ++j) {
+    if (in[j] == nullptr) return fail(DDP_EINVAL, "%s: input of rank %d is NULL", what, j);
+    if (reinterpret_cast<uintptr_t>(in[j]) % kVecBytes != 0) {
+      return fail(DDP_EALIGN, "%s: input of rank %d is not 16-byte aligned", what, j);
+    }
+    const char *slot = static_cast<const char *>(out[j]) + j * C * eb;
+    if (in[j] == slot) {
+      skip.rank[j] = j;
+      ++in_place;
+      for (int32_t r = 0; r < p; ++r) {
+        if (r != j && ranges_overlap(in[j], C * eb, out[r], n * eb)) {
+          return fail(DDP_EALIAS, "%s: input of rank %d overlaps output of rank %d", what, j, r);
+        }
+      }
+      continue;
+    }
+    for (int32_t r = 0; r < p; ++r) {
+      if (ranges_overlap(in[j], C * eb, out[r], n * eb)) {
+        return fail(DDP_EALIAS, "%s: input of rank %d overlaps output of rank %d", what, j, r);
+      }
+    }
+  }
+  fill_stats(stats, p - 1, int64_t(p) * (p - 1), (p - 1) * C * eb, (p - 1) * C * eb,
+             int64_t(p) * (p - 1) * C * eb, n * eb + (int64_t(p) * p - in_place) * C * eb);
+  if (n == 0) return DDP_OK;
+  return launch_fanout(make_table(in, p), p, make_table(reinterpret_cast<const void *const *>(out), p),
+                       p, C * eb, C * eb, skip, stream, "allgather fanout_copy_kernel launch");
+}
+
+extern "C" ddp_status broadcast_sim(void *const *bufs, int32_t p, int64_t n, int32_t src,
+                                    int32_t dtype, hipStream_t stream,
+                                    ddp_comm_stats *stats) {
+  clear_error();
+  const char *what = "broadcast_sim";
+  ddp_status s = check_p(p, what);
+  if (s != DDP_OK) return s;
+  if (n < 0) return fail(DDP_EINVAL, "%s: n is negative", what);
+  const int eb = elem_bytes_of(dtype);
+  if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  if (src < 0 || src >= p) return fail(DDP_ERANGE, "%s: src=%d outside [0, %d)", what, src, p);
+  s = check_rank_buffers(what, reinterpret_cast<const void *const *>(bufs), p, n * eb);
+  if (s != DDP_OK) return s;
+  int64_t rounds = 0;
+  while ((int64_t(1) << rounds) < p) ++rounds;
+  fill_stats(stats, rounds, p - 1, rounds * n * eb, p > 1 ? n * eb : 0,
+             int64_t(p - 1) * n * eb, int64_t(p) * n * eb);
+  if (n == 0 || p == 1) return DDP_OK;
+  RankTable from;
+  std::memset(&from, 0, sizeof from);
+  from.ptr[0] = bufs[src];
+  SkipTable skip;
+  for (int32_t r = 0; r < kMaxRanks; ++r) skip.rank[r] = -1;
+  skip.rank[0] = src;
+  return launch_fanout(from, 1, make_table(reinterpret_cast<const void *const *>(bufs), p), p,
+                       n * eb, 0, skip, stream, "broadcast fanout_copy_kernel launch");
+}

@@ -1,0 +1,173 @@
+// flatten.hip -- copy gradients into a bucket's flat buffer and back
+// ("PyTorch DDP Deep Dive", Part 2 "Step 2: backward", the reducer's copy of
+// each gradient into its slice of the bucket, with the optional pre-divide;
+// "Step 3: finalize_backward", the copy back into each .grad).
+//
+// One launch handles one bucket for all p ranks: grid (tiles, p). Each
+// parameter of the bucket is cut into tiles of kFlattenTile elements, and a
+// workgroup finds its parameter by binary search over the tiles' starting
+// indices in the plan's device table (uniform across the workgroup, so the
+// search runs on scalar loads). A tile whose source and destination are both
+// 16-byte aligned moves 16-byte vectors; any other tile moves elements.
+#include <cmath>
+
+#include "internal.hpp"
+
+namespace ddpsim {
+bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
+                      int32_t *count, int32_t *tiles, int64_t *elems,
+                      const void **table, int32_t *n_params, int32_t *elem_bytes,
+                      bool *uploaded);
+
+namespace {
+
+template <typename Tr, bool kToFlat>
+__global__ __launch_bounds__(kThreads) void flatten_kernel(
+    const ParamDesc *__restrict__ desc, int32_t count, int32_t n_params,
+    const void *const *__restrict__ grad_ptrs, RankTable flat, Divide div) {
+  constexpr int V = Tr::kVec;
+  constexpr int kVpt = kFlattenTile / V / kThreads;
+  using E = typename Tr::elem;
+  const int32_t tile = static_cast<int32_t>(blockIdx.x);
+  const int32_t r = static_cast<int32_t>(blockIdx.y);
+  // last descriptor whose first tile is <= this tile
+  int32_t lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (desc[mid].tile_begin <= tile) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  const ParamDesc d = desc[lo];
+  const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile;
+  const int64_t left = d.numel - start;
+  if (left <= 0) return;
+  const int64_t cnt = left < kFlattenTile ? left : kFlattenTile;
+  E *grad = static_cast<E *>(const_cast<void *>(
+                grad_ptrs[static_cast<int64_t>(r) * n_params + d.param])) + start;
+  E *bucket = static_cast<E *>(flat.ptr[r]) + d.bucket_offset + start;
+  const E *src = kToFlat ? grad : bucket;
+  E *dst = kToFlat ? bucket : grad;
+  const bool scale = kToFlat && div.mode != kNone;
+  const int tid = static_cast<int>(threadIdx.x);
+
+  const bool aligned = ((reinterpret_cast<uintptr_t>(src) |
+                         reinterpret_cast<uintptr_t>(dst)) % kVecBytes) == 0;
+  int64_t done = 0;
+  if (aligned) {
+    const int64_t nv = cnt / V;
+    uint4 x[kVpt];
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) {
+      const int64_t v = u * kThreads + tid;
+      if (v < nv) x[u] = load_vec(src, v);
+    }
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) {
+      const int64_t v = u * kThreads + tid;
+      if (v >= nv) continue;
+      if (scale) {
+        float f[V];
+        Tr::widen(x[u], f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = apply_divide(f[e], div);
+        x[u] = Tr::narrow(f);
+      }
+      store_vec<false>(dst, v, x[u]);
+    }
+    done = nv * V;
+  }
+  for (int64_t i = done + tid; i < cnt; i += kThreads) {
+    if (scale) {
+      Tr::store1(dst, i, apply_divide(Tr::load1(src, i), div));
+    } else {
+      dst[i] = src[i];
+    }
+  }
+}
+
+ddp_status run(const ddp_plan *plan, int32_t bucket, int32_t p,
+               const void *const *d_grad_ptrs, const void *const *bucket_bufs,
+               int32_t dtype, float prescale, bool to_flat, hipStream_t stream,
+               const char *what) {
+  clear_error();
+  int32_t first, count, tiles, n_params, eb_plan;
+  int64_t elems;
+  const void *table;
+  bool uploaded;
+  if (plan == nullptr) return fail(DDP_EINVAL, "%s: plan is NULL", what);
+  if (!plan_bucket_info(plan, bucket, &first, &count, &tiles, &elems, &table,
+                        &n_params, &eb_plan, &uploaded)) {
+    return fail(DDP_ERANGE, "%s: bucket %d out of range", what, bucket);
+  }
+  if (!uploaded) return fail(DDP_ENOTREADY, "%s: call ddp_plan_upload first", what);
+  ddp_status s = check_p(p, what);
+  if (s != DDP_OK) return s;
+  const int eb = elem_bytes_of(dtype);
+  if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  if (eb != eb_plan) {
+    return fail(DDP_EINVAL, "%s: dtype has %d-byte elements, the plan %d", what, eb, eb_plan);
+  }
+  if (!(prescale > 0.0f) || prescale > 3.0e38f) {
+    return fail(DDP_EINVAL, "%s: prescale divisor must be finite and > 0", what);
+  }
+  if (tiles > 0 && d_grad_ptrs == nullptr) {
+    return fail(DDP_EINVAL, "%s: gradient pointer table is NULL", what);
+  }
+  s = check_rank_buffers(what, bucket_bufs, p, elems * eb);
+  if (s != DDP_OK) return s;
+  if (tiles == 0) return DDP_OK;
+  Divide div{kNone, 1.0f, 1.0f};
+  if (prescale != 1.0f) {
+    int e = 0;
+    const float m = std::frexp(prescale, &e);
+    if (m == 0.5f && e - 1 <= 126 && e - 1 >= -126) {
+      div = Divide{kScale, prescale, std::ldexp(1.0f, -(e - 1))};
+    } else {
+      div = Divide{kDivide, prescale, 1.0f};
+    }
+  }
+  const ParamDesc *desc = static_cast<const ParamDesc *>(table) + first;
+  const RankTable tab = make_table(bucket_bufs, p);
+  const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(p));
+  if (dtype == DDP_F32) {
+    if (to_flat) {
+      flatten_kernel<F32Traits, true><<<grid, dim3(kThreads), 0, stream>>>(
+          desc, count, n_params, d_grad_ptrs, tab, div);
+    } else {
+      flatten_kernel<F32Traits, false><<<grid, dim3(kThreads), 0, stream>>>(
+          desc, count, n_params, d_grad_ptrs, tab, div);
+    }
+  } else {
+    if (to_flat) {
+      flatten_kernel<BF16Traits, true><<<grid, dim3(kThreads), 0, stream>>>(
+          desc, count, n_params, d_grad_ptrs, tab, div);
+    } else {
+      flatten_kernel<BF16Traits, false><<<grid, dim3(kThreads), 0, stream>>>(
+          desc, count, n_params, d_grad_ptrs, tab, div);
+    }
+  }
+  return check_hip(hipGetLastError(), "flatten_kernel launch");
+}
+
+}  // namespace
+}  // namespace ddpsim
+
+using namespace ddpsim;
+
+extern "C" ddp_status ddp_flatten(const ddp_plan *plan, int32_t bucket, int32_t p,
+                                  const void *const *d_grad_ptrs, void *const *bucket_bufs,
+                                  int32_t dtype, float prescale_divisor,
+                                  hipStream_t stream) {
+  return run(plan, bucket, p, d_grad_ptrs, reinterpret_cast<const void *const *>(bucket_bufs),
+             dtype, prescale_divisor, true, stream, "ddp_flatten");
+}
+
+extern "C" ddp_status ddp_unflatten(const ddp_plan *plan, int32_t bucket, int32_t p,
+                                    const void *const *bucket_bufs, void *const *d_grad_ptrs,
+                                    int32_t dtype, hipStream_t stream) {
+  return run(plan, bucket, p, reinterpret_cast<const void *const *>(d_grad_ptrs), bucket_bufs,
+             dtype, 1.0f, false, stream, "ddp_unflatten");
+}

@@ -1,0 +1,74 @@
+// fold.hpp -- the ring-order fold, shared by the fused all-reduce and the
+// fused reduce-scatter kernels.
+//
+// The ring's reduce-scatter carries chunk c from rank c to rank c+1, c+2,
+// ... and each hop adds that rank's own, still untouched value ("Data
+// parallelism", section "Ring all-reduce, derived"). So the finished sum of
+// any element of chunk c is
+//     x[first] + x[first+1] + ... + x[first+p-1]      (ranks mod p)
+// accumulated left to right in fp32, with first = c for the all-reduce and
+// first = c+1 for the pre-rotated reduce-scatter. The kernels below reproduce
+// that order exactly while keeping every load of a batch in flight at once:
+// loads do not depend on each other, only the additions are ordered.
+//
+// The accumulator starts at -0.0f: -0 + x == x for every x (including +0
+// and -0), so adding all p values to it gives the same bits as starting
+// from x[first].
+#pragma once
+
+#include "internal.hpp"
+
+namespace ddpsim {
+
+// Fold VPT 16-byte vectors (global vector indices vi[u], valid where ok[u])
+// over the p ranks in ring order starting at `first`. RB rank loads are
+// issued before their additions.
+template <typename Tr, int VPT, int RB>
+__device__ __forceinline__ void fold_vectors(const RankTable &in, int32_t p,
+                                             int32_t first,
+                                             const int64_t (&vi)[VPT],
+                                             const bool (&ok)[VPT],
+                                             float (&acc)[VPT][Tr::kVec]) {
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+#pragma unroll
+    for (int e = 0; e < Tr::kVec; ++e) acc[u][e] = -0.0f;
+  }
+  for (int32_t s0 = 0; s0 < p; s0 += RB) {
+    uint4 x[RB][VPT];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const bool live = s0 + j < p;
+      const void *src = in.ptr[live ? ring_rank(first, s0 + j, p) : 0];
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        x[j][u] = (live && ok[u]) ? load_vec(src, vi[u]) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      if (s0 + j < p) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+          float w[Tr::kVec];
+          Tr::widen(x[j][u], w);
+#pragma unroll
+          for (int e = 0; e < Tr::kVec; ++e) acc[u][e] = acc[u][e] + w[e];
+        }
+      }
+    }
+  }
+}
+
+// The same fold for one element.
+template <typename Tr>
+__device__ __forceinline__ float fold_scalar(const RankTable &in, int32_t p,
+                                             int32_t first, int64_t i) {
+  float acc = -0.0f;
+  for (int32_t s = 0; s < p; ++s) {
+    acc = acc + Tr::load1(in.ptr[ring_rank(first, s, p)], i);
+  }
+  return acc;
+}
+
+}  // namespace ddpsim

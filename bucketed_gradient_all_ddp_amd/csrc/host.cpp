@@ -1,0 +1,153 @@
+// host.cpp -- error reporting, argument validation and averaging set-up
+// shared by every entry point of libddpsim.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "internal.hpp"
+
+namespace ddpsim {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+ddp_status fail(ddp_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ddp_status check_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return DDP_OK;
+  return fail(DDP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes_of(int32_t dtype) {
+  if (dtype == DDP_F32) return 4;
+  if (dtype == DDP_BF16) return 2;
+  return 0;
+}
+
+ddp_status check_p(int32_t p, const char *what) {
+  if (p < 1 || p > kMaxRanks) {
+    return fail(DDP_ERANGE, "%s: p=%d outside [1, %d]", what, p, kMaxRanks);
+  }
+  return DDP_OK;
+}
+
+bool ranges_overlap(const void *a, int64_t na, const void *b, int64_t nb) {
+  if (na <= 0 || nb <= 0) return false;
+  auto x = reinterpret_cast<uintptr_t>(a);
+  auto y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
+ddp_status check_rank_buffers(const char *what, const void *const *bufs,
+                              int32_t p, int64_t bytes) {
+  if (bufs == nullptr) return fail(DDP_EINVAL, "%s: pointer array is NULL", what);
+  if (bytes == 0) return DDP_OK;
+  std::vector<std::pair<uintptr_t, int32_t>> order;
+  order.reserve(p);
+  for (int32_t r = 0; r < p; ++r) {
+    if (bufs[r] == nullptr) {
+      return fail(DDP_EINVAL, "%s: buffer of rank %d is NULL", what, r);
+    }
+    auto a = reinterpret_cast<uintptr_t>(bufs[r]);
+    if (a % kVecBytes != 0) {
+      return fail(DDP_EALIGN, "%s: buffer of rank %d is not 16-byte aligned",
+                  what, r);
+    }
+    order.emplace_back(a, r);
+  }
+  std::sort(order.begin(), order.end());
+  for (size_t k = 1; k < order.size(); ++k) {
+    if (order[k].first < order[k - 1].first + static_cast<uintptr_t>(bytes)) {
+      return fail(DDP_EALIAS, "%s: buffers of ranks %d and %d overlap", what,
+                  order[k - 1].second, order[k].second);
+    }
+  }
+  return DDP_OK;
+}
+
+ddp_status make_divide(int32_t avg_mode, int32_t p, const int64_t *tokens,
+                       Divide *out) {
+  double divisor = 1.0;
+  if (avg_mode == DDP_AVG_NONE) {
+    divisor = 1.0;
+  } else if (avg_mode == DDP_AVG_WORLD) {
+    divisor = p;
+  } else if (avg_mode == DDP_AVG_TOKENS) {
+    if (tokens == nullptr) {
+      return fail(DDP_EINVAL, "token averaging needs the per-rank token counts");
+    }
+    int64_t total = 0;
+    for (int32_t r = 0; r < p; ++r) {
+      if (tokens[r] < 0) {
+        return fail(DDP_EINVAL, "token count of rank %d is negative", r);
+      }
+      if (tokens[r] > (INT64_MAX >> 8)) {
+        return fail(DDP_EINVAL, "token count of rank %d is too large", r);
+      }
+      total += tokens[r];
+    }
+    if (total <= 0) return fail(DDP_EINVAL, "total token count must be > 0");
+    // binary32 nearest to the integer total (the conversion rounds to
+    // nearest even); exact up to 2^24.
+    out->divisor = static_cast<float>(total);
+    divisor = out->divisor;
+  } else {
+    return fail(DDP_EINVAL, "unknown averaging mode %d", avg_mode);
+  }
+  const float d = static_cast<float>(divisor);
+  out->divisor = d;
+  out->recip = 1.0f;
+  int e = 0;
+  const float m = std::frexp(d, &e);  // d = m * 2^e, m in [0.5, 1)
+  if (d == 1.0f) {
+    out->mode = kNone;
+  } else if (m == 0.5f && e - 1 <= 126) {
+    out->mode = kScale;  // d = 2^(e-1): its reciprocal is exact
+    out->recip = std::ldexp(1.0f, -(e - 1));
+  } else {
+    out->mode = kDivide;
+  }
+  return DDP_OK;
+}
+
+RankTable make_table(const void *const *bufs, int32_t p) {
+  RankTable t;
+  std::memset(&t, 0, sizeof t);
+  for (int32_t r = 0; r < p; ++r) t.ptr[r] = const_cast<void *>(bufs[r]);
+  return t;
+}
+
+}  // namespace ddpsim
+
+using namespace ddpsim;
+
+extern "C" const char *ddp_strerror(ddp_status s) {
+  switch (s) {
+    case DDP_OK: return "success";
+    case DDP_EINVAL: return "invalid argument";
+    case DDP_ERANGE: return "argument out of range";
+    case DDP_EALIGN: return "buffer not 16-byte aligned";
+    case DDP_EALIAS: return "buffers overlap";
+    case DDP_ENOTDIVISIBLE: return "element count not divisible by the number of ranks";
+    case DDP_ENOTREADY: return "plan has no device table";
+    case DDP_EWORKSPACE: return "workspace missing or too small";
+    case DDP_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char *ddp_last_error(void) { return g_last_error; }
+
+extern "C" const char *ddp_version(void) { return "ddpsim 0.1 (gfx950)"; }

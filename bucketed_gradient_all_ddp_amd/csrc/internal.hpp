@@ -1,0 +1,213 @@
+// internal.hpp -- shared declarations of libddpsim (host and device).
+//
+// Everything here is private to the library; the public surface is
+// include/ddpsim.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ddpsim.h"
+
+namespace ddpsim {
+
+constexpr int kThreads = 256;               // threads per workgroup (4 waves)
+constexpr int kMaxRanks = DDP_MAX_RANKS;
+constexpr int kVecBytes = 16;               // one global_load/store_dwordx4
+
+// Rank buffers travel by value in the kernel arguments (64 x 8 = 512 bytes),
+// so a workgroup reads a rank's base address with one scalar load.
+struct RankTable {
+  void *ptr[kMaxRanks];
+};
+
+// How a kernel applies the average to a finished fp32 sum.
+//   kNone      leave the sum
+//   kScale     multiply by an exact power-of-two reciprocal: x * 2^-k rounds
+//              the same real number as x / 2^k, so the bits are identical
+//   kDivide    one correctly rounded fp32 division
+enum DivideMode : int32_t { kNone = 0, kScale = 1, kDivide = 2 };
+
+struct Divide {
+  int32_t mode;
+  float divisor;
+  float recip;
+};
+
+// One parameter of a bucket plan, as the flatten kernels read it from the
+// plan's device table (32 bytes, fill order, all buckets back to back).
+struct ParamDesc {
+  int64_t bucket_offset;  // element offset of the parameter in its bucket
+  int64_t numel;          // elements of the parameter
+  int32_t param;          // registration index
+  int32_t tile_begin;     // first flatten tile of the parameter in its bucket
+  int64_t reserved;
+};
+static_assert(sizeof(ParamDesc) == 32, "ParamDesc layout");
+
+constexpr int kFlattenTile = 4096;  // elements per flatten workgroup
+
+// ---------------------------------------------------------------------------
+// Host helpers (defined in host.cpp)
+// ---------------------------------------------------------------------------
+
+void clear_error();
+ddp_status fail(ddp_status s, const char *fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+ddp_status check_hip(hipError_t e, const char *what);
+
+// Bytes per element of a ddp_dtype, or 0 if the dtype is unknown.
+int elem_bytes_of(int32_t dtype);
+
+ddp_status check_p(int32_t p, const char *what);
+
+// Null, 16-byte alignment and pairwise overlap of p ranges of `bytes` each.
+ddp_status check_rank_buffers(const char *what, const void *const *bufs,
+                              int32_t p, int64_t bytes);
+
+// True if [a, a+na) and [b, b+nb) share a byte.
+bool ranges_overlap(const void *a, int64_t na, const void *b, int64_t nb);
+
+// Averaging divisor from the mode and the host token counts.
+ddp_status make_divide(int32_t avg_mode, int32_t p, const int64_t *tokens,
+                       Divide *out);
+
+RankTable make_table(const void *const *bufs, int32_t p);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+#if defined(__HIPCC__)
+
+__device__ __forceinline__ float apply_divide(float x, const Divide &d) {
+  if (d.mode == kScale) return x * d.recip;
+  if (d.mode == kDivide) return x / d.divisor;  // correctly rounded (build flag)
+  return x;
+}
+
+// bf16 -> fp32 is exact: the bf16 bits are the upper half of the binary32.
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) {
+  return __uint_as_float(w & 0xFFFF0000u);
+}
+
+// fp32 -> bf16, round to nearest, ties to even. Adding 0x7FFF plus the last
+// kept bit carries into bit 16 exactly when the discarded half exceeds one
+// half, or equals it with an odd kept part. NaN is kept quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element traits: how a 16-byte vector of the storage type widens to fp32
+// lanes and narrows back.
+struct F32Traits {
+  using elem = float;
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static __forceinline__ void widen(const uint4 &v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ uint4 narrow(const float (&f)[4]) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+  __device__ static __forceinline__ float load1(const void *base, int64_t i) {
+    return static_cast<const float *>(base)[i];
+  }
+  __device__ static __forceinline__ void store1(void *base, int64_t i, float v) {
+    static_cast<float *>(base)[i] = v;
+  }
+};
+
+struct BF16Traits {
+  using elem = uint16_t;
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ void widen(const uint4 &v, float (&f)[8]) {
+    f[0] = bf16_lo_to_f32(v.x);
+    f[1] = bf16_hi_to_f32(v.x);
+    f[2] = bf16_lo_to_f32(v.y);
+    f[3] = bf16_hi_to_f32(v.y);
+    f[4] = bf16_lo_to_f32(v.z);
+    f[5] = bf16_hi_to_f32(v.z);
+    f[6] = bf16_lo_to_f32(v.w);
+    f[7] = bf16_hi_to_f32(v.w);
+  }
+  __device__ static __forceinline__ uint4 narrow(const float (&f)[8]) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+  }
+  __device__ static __forceinline__ float load1(const void *base, int64_t i) {
+    return __uint_as_float(
+        static_cast<uint32_t>(static_cast<const uint16_t *>(base)[i]) << 16);
+  }
+  __device__ static __forceinline__ void store1(void *base, int64_t i, float v) {
+    static_cast<uint16_t *>(base)[i] =
+        static_cast<uint16_t>(f32_to_bf16_bits(v));
+  }
+};
+
+__device__ __forceinline__ uint4 load_vec(const void *base, int64_t v) {
+  return static_cast<const uint4 *>(base)[v];
+}
+
+template <bool kNonTemporal>
+__device__ __forceinline__ void store_vec(void *base, int64_t v, uint4 x) {
+  uint4 *p = static_cast<uint4 *>(base) + v;
+  if constexpr (kNonTemporal) {
+    __builtin_nontemporal_store(x.x, &p->x);
+    __builtin_nontemporal_store(x.y, &p->y);
+    __builtin_nontemporal_store(x.z, &p->z);
+    __builtin_nontemporal_store(x.w, &p->w);
+  } else {
+    *p = x;
+  }
+}
+
+// Rank (first + t) mod p without a division; first < p and t < p.
+__device__ __forceinline__ int32_t ring_rank(int32_t first, int32_t t,
+                                             int32_t p) {
+  int32_t r = first + t;
+  return r >= p ? r - p : r;
+}
+
+// The element range of chunk c of an n-element buffer cut into chunks of C,
+// split into a 16-byte aligned vector body and at most kVec-1 scalar
+// elements on each side:
+//   head  [s, head_end)      body  [vs, ve) (vector aligned)
+//   tail  [tail_begin, e)
+struct ChunkSpan {
+  int64_t s, e, head_end, vs, ve, tail_begin;
+};
+
+__device__ __forceinline__ ChunkSpan chunk_span(int64_t c, int64_t C,
+                                                int64_t n, int vec) {
+  ChunkSpan k;
+  k.s = c * C;
+  k.e = k.s + C < n ? k.s + C : n;
+  if (k.e < k.s) k.e = k.s;
+  k.vs = (k.s + vec - 1) / vec * vec;
+  k.ve = k.e / vec * vec;
+  k.head_end = k.vs < k.e ? k.vs : k.e;
+  if (k.ve < k.vs) k.ve = k.vs;           // no aligned body
+  k.tail_begin = k.ve > k.head_end ? k.ve : k.head_end;
+  return k;
+}
+
+#endif  // __HIPCC__
+
+}  // namespace ddpsim

@@ -1,0 +1,196 @@
+// plan.cpp -- bucket assignment ("PyTorch DDP Deep Dive", Part 1 "What
+// _ddp_init_helper actually does" and Part 3's DDPOptimizer reverse walk;
+// "Data parallelism", section "Overlapping communication with the backward
+// pass") and the plan's device descriptor table.
+//
+// Gradients become ready in the reverse of registration order, so the walk
+// starts from the last registered parameter and the first bucket it fills is
+// the one whose all-reduce can start first; that bucket has the small cap.
+// A bucket is closed, before the next parameter would join it, once its
+// bytes have reached its cap.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.hpp"
+
+using namespace ddpsim;
+
+struct ddp_plan {
+  int32_t n_params = 0;
+  int32_t elem_bytes = 0;
+  std::vector<int64_t> numel;                // registration order
+  std::vector<int32_t> bucket_of;            // per parameter
+  std::vector<int64_t> offset;               // per parameter, in elements
+  std::vector<std::vector<int32_t>> members; // per bucket, fill order
+  std::vector<int64_t> bucket_elems;
+  std::vector<int32_t> desc_first;           // first ParamDesc of each bucket
+  std::vector<int32_t> tiles;                // flatten tiles of each bucket
+  std::vector<ParamDesc> desc;
+  void *d_table = nullptr;
+  bool uploaded = false;
+};
+
+namespace ddpsim {
+
+// Accessors used by flatten.hip.
+bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
+                      int32_t *count, int32_t *tiles, int64_t *elems,
+                      const void **table, int32_t *n_params, int32_t *elem_bytes,
+                      bool *uploaded) {
+  if (plan == nullptr || b < 0 || b >= static_cast<int32_t>(plan->members.size())) {
+    return false;
+  }
+  *first = plan->desc_first[b];
+  *count = static_cast<int32_t>(plan->members[b].size());
+  *tiles = plan->tiles[b];
+  *elems = plan->bucket_elems[b];
+  *table = plan->d_table;
+  *n_params = plan->n_params;
+  *elem_bytes = plan->elem_bytes;
+  *uploaded = plan->uploaded;
+  return true;
+}
+
+}  // namespace ddpsim
+
+extern "C" ddp_status ddp_bucket_plan(const int64_t *numel, int32_t n_params,
+                                      int32_t elem_bytes, int64_t bucket_cap_bytes,
+                                      int64_t first_bucket_cap_bytes, ddp_plan **out) {
+  clear_error();
+  if (out == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: out is NULL");
+  *out = nullptr;
+  if (n_params < 0) return fail(DDP_EINVAL, "ddp_bucket_plan: n_params < 0");
+  if (n_params > 0 && numel == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: numel is NULL");
+  if (elem_bytes != 2 && elem_bytes != 4) {
+    return fail(DDP_EINVAL, "ddp_bucket_plan: elem_bytes must be 2 or 4");
+  }
+  if (bucket_cap_bytes < 0 || first_bucket_cap_bytes < 0) {
+    return fail(DDP_EINVAL, "ddp_bucket_plan: caps must be >= 0");
+  }
+  for (int32_t i = 0; i < n_params; ++i) {
+    if (numel[i] < 0) return fail(DDP_EINVAL, "ddp_bucket_plan: numel[%d] < 0", i);
+  }
+  ddp_plan *plan = new (std::nothrow) ddp_plan;
+  if (plan == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: out of host memory");
+  plan->n_params = n_params;
+  plan->elem_bytes = elem_bytes;
+  plan->numel.assign(numel, numel + n_params);
+  plan->bucket_of.assign(n_params, -1);
+  plan->offset.assign(n_params, 0);
+
+  const int64_t small_cap = std::min(first_bucket_cap_bytes, bucket_cap_bytes);
+  int64_t open_bytes = 0;
+  for (int32_t i = n_params - 1; i >= 0; --i) {
+    const bool have_open = !plan->members.empty() && !plan->members.back().empty();
+    const int64_t cap = plan->members.size() <= 1 ? small_cap : bucket_cap_bytes;
+    if (!have_open || open_bytes >= cap) {
+      plan->members.emplace_back();
+      plan->bucket_elems.push_back(0);
+      open_bytes = 0;
+    }
+    const int32_t b = static_cast<int32_t>(plan->members.size()) - 1;
+    plan->bucket_of[i] = b;
+    plan->offset[i] = plan->bucket_elems[b];
+    plan->members[b].push_back(i);
+    plan->bucket_elems[b] += numel[i];
+    open_bytes += numel[i] * elem_bytes;
+  }
+
+  // Device descriptors, bucket after bucket, each parameter cut into
+  // flatten tiles of kFlattenTile elements.
+  for (size_t b = 0; b < plan->members.size(); ++b) {
+    plan->desc_first.push_back(static_cast<int32_t>(plan->desc.size()));
+    int64_t tiles = 0;
+    for (int32_t i : plan->members[b]) {
+      ParamDesc d;
+      std::memset(&d, 0, sizeof d);
+      d.bucket_offset = plan->offset[i];
+      d.numel = numel[i];
+      d.param = i;
+      d.tile_begin = static_cast<int32_t>(tiles);
+      tiles += ceil_div(numel[i], kFlattenTile);
+      plan->desc.push_back(d);
+    }
+    if (tiles > INT32_MAX) {
+      delete plan;
+      return fail(DDP_EINVAL, "ddp_bucket_plan: bucket %zu is too large", b);
+    }
+    plan->tiles.push_back(static_cast<int32_t>(tiles));
+  }
+  *out = plan;
+  return DDP_OK;
+}
+
+extern "C" void ddp_plan_free(ddp_plan *plan) { delete plan; }
+
+extern "C" int32_t ddp_plan_num_params(const ddp_plan *plan) {
+  return plan ? plan->n_params : -1;
+}
+
+extern "C" int32_t ddp_plan_num_buckets(const ddp_plan *plan) {
+  return plan ? static_cast<int32_t>(plan->members.size()) : -1;
+}
+
+extern "C" int64_t ddp_plan_bucket_numel(const ddp_plan *plan, int32_t b) {
+  if (plan == nullptr || b < 0 || b >= static_cast<int32_t>(plan->members.size())) return -1;
+  return plan->bucket_elems[b];
+}
+
+extern "C" int32_t ddp_plan_bucket_size(const ddp_plan *plan, int32_t b) {
+  if (plan == nullptr || b < 0 || b >= static_cast<int32_t>(plan->members.size())) return -1;
+  return static_cast<int32_t>(plan->members[b].size());
+}
+
+extern "C" ddp_status ddp_plan_bucket_params(const ddp_plan *plan, int32_t b,
+                                             int32_t *idx_out) {
+  clear_error();
+  if (plan == nullptr || idx_out == nullptr) {
+    return fail(DDP_EINVAL, "ddp_plan_bucket_params: NULL argument");
+  }
+  if (b < 0 || b >= static_cast<int32_t>(plan->members.size())) {
+    return fail(DDP_ERANGE, "ddp_plan_bucket_params: bucket %d out of range", b);
+  }
+  std::copy(plan->members[b].begin(), plan->members[b].end(), idx_out);
+  return DDP_OK;
+}
+
+extern "C" int32_t ddp_plan_param_bucket(const ddp_plan *plan, int32_t i) {
+  if (plan == nullptr || i < 0 || i >= plan->n_params) return -1;
+  return plan->bucket_of[i];
+}
+
+extern "C" int64_t ddp_plan_param_offset(const ddp_plan *plan, int32_t i) {
+  if (plan == nullptr || i < 0 || i >= plan->n_params) return -1;
+  return plan->offset[i];
+}
+
+extern "C" size_t ddp_plan_device_bytes(const ddp_plan *plan) {
+  return plan ? plan->desc.size() * sizeof(ParamDesc) : 0;
+}
+
+extern "C" ddp_status ddp_plan_upload(ddp_plan *plan, void *d_table, size_t bytes,
+                                      hipStream_t stream) {
+  clear_error();
+  if (plan == nullptr) return fail(DDP_EINVAL, "ddp_plan_upload: plan is NULL");
+  const size_t need = plan->desc.size() * sizeof(ParamDesc);
+  if (need == 0) {
+    plan->d_table = d_table;
+    plan->uploaded = true;
+    return DDP_OK;
+  }
+  if (d_table == nullptr || bytes < need) {
+    return fail(DDP_EINVAL, "ddp_plan_upload: needs %zu bytes of device memory", need);
+  }
+  if (reinterpret_cast<uintptr_t>(d_table) % kVecBytes != 0) {
+    return fail(DDP_EALIGN, "ddp_plan_upload: table is not 16-byte aligned");
+  }
+  ddp_status s = check_hip(
+      hipMemcpyAsync(d_table, plan->desc.data(), need, hipMemcpyHostToDevice, stream),
+      "ddp_plan_upload: hipMemcpyAsync");
+  if (s != DDP_OK) return s;
+  plan->d_table = d_table;
+  plan->uploaded = true;
+  return DDP_OK;
+}

@@ -1,0 +1,290 @@
+/*
+ * ddpsim.h -- C ABI of libddpsim.so: the data-parallel gradient
+ * synchronisation hot path (bucket plan, flatten, ring all-reduce with
+ * averaging, unflatten, and the standalone reduce-scatter / all-gather /
+ * broadcast), with p simulated ranks whose buffers all live in the HBM of
+ * one gfx950 GPU.
+ *
+ * Pages this interface follows, cited by title and section:
+ *   [DDP] "PyTorch DDP Deep Dive -- Initialization, Buffer Broadcast, the
+ *         Reducer, and the torch.compile Story"
+ *   [COL] "Collective Ops From Scratch"
+ *   [DP]  "Data parallelism" (zerotofrontier.app, distributed chapter)
+ *
+ * Conventions for every entry point
+ *   - Device memory (rank buffers, gradients, workspace, the plan's device
+ *     table) belongs to the caller. The library never allocates or frees
+ *     device memory and never synchronises a stream or the device.
+ *   - Host arrays passed in (pointer lists, token counts) are read during
+ *     the call only; their contents are copied into kernel arguments.
+ *   - Work is enqueued on `stream` (0 = the null stream). A fault inside a
+ *     kernel surfaces at the caller's next synchronisation, as with any
+ *     asynchronous HIP call.
+ *   - Every argument is validated before anything is enqueued: an error
+ *     return means no work was queued. ddp_last_error() then describes the
+ *     failure (thread-local, valid until the next call on that thread).
+ *   - "Simulated rank r" is index r of a pointer array of length p,
+ *     1 <= p <= DDP_MAX_RANKS. Rank buffers must be 16-byte aligned and must
+ *     not overlap one another.
+ *   - Element types: DDP_F32 (IEEE binary32) and DDP_BF16 (bfloat16).
+ *     Sums are always accumulated in fp32; bf16 results are rounded once,
+ *     to nearest even.
+ *   - Summation order: for the all-reduce, element i of an n-element buffer
+ *     lies in chunk c = i / C with C = ceil(n/p), and its sum is
+ *     x_c + x_{c+1} + ... + x_{c+p-1} (ranks mod p) accumulated left to
+ *     right, exactly the order in which the ring's reduce-scatter adds the
+ *     contributions ([COL] "Ring allreduce in two passes"; [DP] "Ring
+ *     all-reduce, derived"). Both algorithms below produce these bits.
+ *
+ * No C++ exception crosses this boundary.
+ */
+#ifndef DDPSIM_H
+#define DDPSIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDP_MAX_RANKS 64
+
+typedef enum {
+  DDP_OK = 0,
+  DDP_EINVAL = 1,        /* bad argument (null pointer, bad enum, n < 0, ...) */
+  DDP_ERANGE = 2,        /* p, bucket or step index out of range            */
+  DDP_EALIGN = 3,        /* a buffer is not 16-byte aligned                 */
+  DDP_EALIAS = 4,        /* buffers that must be distinct overlap           */
+  DDP_ENOTDIVISIBLE = 5, /* reduce-scatter / all-gather: n % p != 0         */
+  DDP_ENOTREADY = 6,     /* plan has no device table (ddp_plan_upload)      */
+  DDP_EWORKSPACE = 7,    /* workspace missing or too small                  */
+  DDP_EHIP = 8           /* a HIP call failed; ddp_last_error() has detail  */
+} ddp_status;
+
+typedef enum { DDP_F32 = 0, DDP_BF16 = 1 } ddp_dtype;
+
+/* Averaging applied to the finished sum: none; divide by p; or divide by
+ * the total token count summed over ranks ([DP] "Why averaging gradients is
+ * exactly large-batch training"; "Overlapping communication with the
+ * backward pass"). The division is one correctly rounded fp32 division by
+ * (float)p or (float)(sum of tokens). */
+typedef enum {
+  DDP_AVG_NONE = 0,
+  DDP_AVG_WORLD = 1,
+  DDP_AVG_TOKENS = 2
+} ddp_avg_mode;
+
+/* DDP_ALGO_FUSED: one kernel reads every rank's buffer once, folds each
+ *   element in ring order in registers, and writes the result to every rank.
+ * DDP_ALGO_RING: the ring schedule step by step, 2(p-1) launches, each rank
+ *   adding (reduce-scatter) or copying (all-gather) its neighbour's chunk in
+ *   HBM. Same bits as FUSED. */
+typedef enum { DDP_ALGO_FUSED = 0, DDP_ALGO_RING = 1 } ddp_algo;
+
+/* Communication accounting of the logical schedule a call implements
+ * ([COL] per-rank byte counter; [DP] "Ring all-reduce, derived"). For the
+ * ring all-reduce bytes_sent_per_rank = 2 (p-1) C w with w the wire element
+ * size (4: partial sums travel as fp32), which is 2T(p-1)/p for the padded
+ * tensor of T bytes. hbm_bytes is what the call's kernels must read plus
+ * write in device memory (the algorithmic traffic). */
+typedef struct {
+  int64_t steps;                /* ring steps or tree rounds            */
+  int64_t messages;             /* point-to-point messages              */
+  int64_t bytes_sent_per_rank;  /* max over ranks                       */
+  int64_t bytes_recv_per_rank;  /* max over ranks                       */
+  int64_t total_bytes;          /* sum over all messages                */
+  int64_t hbm_bytes;            /* algorithmic device-memory traffic    */
+} ddp_comm_stats;
+
+typedef struct ddp_plan ddp_plan;
+
+/* ----------------------------------------------------------------------- */
+/* Errors                                                                  */
+/* ----------------------------------------------------------------------- */
+
+const char *ddp_strerror(ddp_status status);
+/* Detail of the most recent failure on this thread ("" if none). */
+const char *ddp_last_error(void);
+/* Library version string. */
+const char *ddp_version(void);
+
+/* ----------------------------------------------------------------------- */
+/* Bucket plan (host)                                                      */
+/* ----------------------------------------------------------------------- */
+
+/* Assign parameters to buckets ([DDP] Part 1 "What _ddp_init_helper
+ * actually does"; Part 3, the DDPOptimizer's reverse walk; [DP]
+ * "Overlapping communication with the backward pass").
+ *
+ *   numel[i]   element count of parameter i, in registration order (>= 0)
+ *   n_params   number of parameters (>= 0)
+ *   elem_bytes bytes per element (2 or 4); the plan has one dtype
+ *   bucket_cap_bytes, first_bucket_cap_bytes   caps (>= 0); the defaults on
+ *              the pages are 25 MiB and 1 MiB
+ *
+ * Parameters are walked from the last registered to the first. Before a
+ * parameter is added, a non-empty open bucket whose byte size has reached
+ * its cap is closed. The first bucket's cap is min(first, cap), every
+ * later bucket's is `cap`. Inside a bucket, parameters sit in fill order at
+ * consecutive element offsets. No bucket is empty; a bucket may overshoot
+ * its cap by its last parameter.
+ *
+ * *out receives a host object owned by the caller, freed with
+ * ddp_plan_free. Errors: DDP_EINVAL (null out, negative size or cap,
+ * elem_bytes not 2 or 4, n_params < 0). */
+ddp_status ddp_bucket_plan(const int64_t *numel, int32_t n_params,
+                           int32_t elem_bytes, int64_t bucket_cap_bytes,
+                           int64_t first_bucket_cap_bytes, ddp_plan **out);
+void ddp_plan_free(ddp_plan *plan);
+
+int32_t ddp_plan_num_params(const ddp_plan *plan);
+int32_t ddp_plan_num_buckets(const ddp_plan *plan);
+/* Total elements of bucket b (-1 if b is out of range). */
+int64_t ddp_plan_bucket_numel(const ddp_plan *plan, int32_t b);
+/* Number of parameters in bucket b (-1 if out of range). */
+int32_t ddp_plan_bucket_size(const ddp_plan *plan, int32_t b);
+/* Writes bucket b's parameter indices, in fill order, to idx_out (room for
+ * ddp_plan_bucket_size(b) entries). */
+ddp_status ddp_plan_bucket_params(const ddp_plan *plan, int32_t b,
+                                  int32_t *idx_out);
+/* Bucket holding parameter i, and its element offset inside that bucket
+ * (-1 if i is out of range). */
+int32_t ddp_plan_param_bucket(const ddp_plan *plan, int32_t i);
+int64_t ddp_plan_param_offset(const ddp_plan *plan, int32_t i);
+
+/* Size in bytes of the plan's device-side descriptor table. */
+size_t ddp_plan_device_bytes(const ddp_plan *plan);
+/* Copy the descriptor table into caller-owned device memory `d_table`
+ * (at least ddp_plan_device_bytes bytes, 16-byte aligned) on `stream`, and
+ * remember that address for ddp_flatten / ddp_unflatten. The caller keeps
+ * d_table alive while the plan is used, and must not free the plan before
+ * the copy has completed on `stream`. */
+ddp_status ddp_plan_upload(ddp_plan *plan, void *d_table, size_t bytes,
+                           hipStream_t stream);
+
+/* ----------------------------------------------------------------------- */
+/* Flatten / unflatten                                                     */
+/* ----------------------------------------------------------------------- */
+
+/* Copy every gradient of bucket `bucket` into each rank's flat bucket
+ * buffer at its plan offset ([DDP] Part 2 "Step 2: backward", the copy into
+ * the bucket's slice), dividing each element by prescale_divisor on the way
+ * in unless it is 1 (the reducer's pre-divide; fp32 division, bf16 rounded
+ * once).
+ *
+ *   d_grad_ptrs  DEVICE array of p * n_params pointers, rank-major:
+ *                d_grad_ptrs[r * n_params + i] is rank r's gradient of
+ *                parameter i (numel[i] contiguous elements, any alignment
+ *                of the element type)
+ *   bucket_bufs  HOST array of p device pointers, each to a 16-byte aligned
+ *                buffer of ddp_plan_bucket_numel(bucket) elements
+ *   dtype        must match the plan's elem_bytes
+ * Errors: DDP_ENOTREADY (no ddp_plan_upload), DDP_ERANGE, DDP_EINVAL,
+ * DDP_EALIGN, DDP_EALIAS (bucket buffers overlap). Gradients and bucket
+ * buffers must not overlap (not checked: device-resident pointers). */
+ddp_status ddp_flatten(const ddp_plan *plan, int32_t bucket, int32_t p,
+                       const void *const *d_grad_ptrs,
+                       void *const *bucket_bufs, int32_t dtype,
+                       float prescale_divisor, hipStream_t stream);
+
+/* Copy each slice of the reduced flat bucket buffers back into the
+ * per-parameter gradients ([DDP] Part 2 "Step 3: finalize_backward").
+ * Same arguments and errors as ddp_flatten, in the other direction. */
+ddp_status ddp_unflatten(const ddp_plan *plan, int32_t bucket, int32_t p,
+                         const void *const *bucket_bufs,
+                         void *const *d_grad_ptrs, int32_t dtype,
+                         hipStream_t stream);
+
+/* ----------------------------------------------------------------------- */
+/* Ring all-reduce                                                         */
+/* ----------------------------------------------------------------------- */
+
+/* In-place all-reduce of p rank buffers of n elements each ([COL] "Ring
+ * allreduce in two passes"; [DP] "Ring all-reduce, derived"): zero-pad to a
+ * multiple of p (the padding is never stored), p-1 reduce-scatter steps,
+ * averaging by avg_mode, p-1 all-gather steps, trim. Afterwards every
+ * rank's buffer holds the same bits.
+ *
+ *   bufs       HOST array of p device pointers (16-byte aligned, disjoint)
+ *   n          elements per rank (>= 0; 0 is a no-op)
+ *   dtype      DDP_F32 or DDP_BF16
+ *   avg_mode   ddp_avg_mode; tokens is a HOST array of p counts (>= 0,
+ *              sum > 0) read only for DDP_AVG_TOKENS
+ *   algo       DDP_ALGO_FUSED or DDP_ALGO_RING
+ *   workspace  device memory for DDP_ALGO_RING with bf16 (fp32 partials),
+ *              ring_allreduce_sim_workspace() bytes, 16-byte aligned,
+ *              disjoint from bufs; otherwise may be NULL
+ *   stats      optional (NULL): filled with the schedule's accounting
+ * Errors: DDP_EINVAL, DDP_ERANGE (p), DDP_EALIGN, DDP_EALIAS,
+ * DDP_EWORKSPACE, DDP_EHIP (launch failure). */
+ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n,
+                              int32_t dtype, int32_t avg_mode,
+                              const int64_t *tokens, int32_t algo,
+                              void *workspace, size_t workspace_bytes,
+                              hipStream_t stream, ddp_comm_stats *stats);
+
+/* Workspace bytes ring_allreduce_sim needs (0 unless RING with bf16). */
+size_t ring_allreduce_sim_workspace(int32_t p, int64_t n, int32_t dtype,
+                                    int32_t algo);
+
+/* Run only ring steps [first_step, first_step + n_steps) of the 2(p-1)
+ * steps of the fp32 ring schedule, in place: steps 0..p-2 are the
+ * reduce-scatter steps (step p-2 also applies the averaging to each
+ * owner's finished chunk), steps p-1..2p-3 the all-gather steps. Running
+ * all steps in order equals ring_allreduce_sim with DDP_ALGO_RING. For
+ * checking the schedule's intermediate states: after steps 0..k, rank
+ * (j+k+1) mod p holds the partial sum of chunk j over ranks j..j+k+1.
+ * Requires p >= 2 and dtype fp32 (buffers are float*).
+ * Errors: as ring_allreduce_sim, plus DDP_ERANGE for the step range. */
+ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int64_t n,
+                                    int32_t avg_mode, const int64_t *tokens,
+                                    int32_t first_step, int32_t n_steps,
+                                    hipStream_t stream);
+
+/* ----------------------------------------------------------------------- */
+/* Standalone collectives                                                  */
+/* ----------------------------------------------------------------------- */
+
+/* Reduce-scatter ([COL], the implementation's reduce_scatter: the first ring
+ * pass pre-rotated so rank r ends with chunk r; [DP] "The collective
+ * operations"): out[r][i] = avg(sum over ranks of in[.][r*C + i]),
+ * C = n/p, folded in ring order starting at rank (r+1) mod p.
+ *   in   HOST array of p device pointers to n elements (read only)
+ *   out  HOST array of p device pointers to C elements; out[r] may equal
+ *        in[r] + r*C elements (in place), otherwise it must not overlap any
+ *        input or output
+ * Errors: DDP_ENOTDIVISIBLE when n % p != 0, plus those of
+ * ring_allreduce_sim. */
+ddp_status reduce_scatter_sim(const void *const *in, void *const *out,
+                              int32_t p, int64_t n, int32_t dtype,
+                              int32_t avg_mode, const int64_t *tokens,
+                              hipStream_t stream, ddp_comm_stats *stats);
+
+/* All-gather ([COL], allgather by ring rotations; [DP] "The collective
+ * operations"): out[r] = in[0] || in[1] || ... || in[p-1] for every r.
+ *   n    elements of each OUTPUT buffer (n % p == 0); shards hold n/p
+ *   in   HOST array of p device pointers to n/p elements; in[r] may equal
+ *        out[r] + r*(n/p) elements (in place: that slice is then not
+ *        rewritten), otherwise inputs must not overlap any output
+ *   out  HOST array of p device pointers to n elements, disjoint
+ * dtype only sets the element size. */
+ddp_status allgather_sim(const void *const *in, void *const *out, int32_t p,
+                         int64_t n, int32_t dtype, hipStream_t stream,
+                         ddp_comm_stats *stats);
+
+/* Broadcast ([COL], broadcast over a doubling tree): every rank's buffer
+ * receives a copy of bufs[src]'s n elements, in place. The stats describe
+ * the doubling tree (ceil(log2 p) rounds, p-1 messages); on one device the
+ * copy is one pass that reads the source once. */
+ddp_status broadcast_sim(void *const *bufs, int32_t p, int64_t n,
+                         int32_t src, int32_t dtype, hipStream_t stream,
+                         ddp_comm_stats *stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDPSIM_H */

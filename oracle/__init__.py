@@ -123,8 +123,9 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def _ptr_table(arrays: Sequence[np.ndarray]) -> np.ndarray:
-    return np.array([a.ctypes.data for a in arrays], dtype=np.uintp)
+def _ptr_table(arrays: Sequence[Optional[np.ndarray]]) -> np.ndarray:
+    """Addresses of the arrays (0 for None: parameters a call does not touch)."""
+    return np.array([0 if a is None else a.ctypes.data for a in arrays], dtype=np.uintp)
 
 
 def _dtype_code(arr: np.ndarray) -> int:
@@ -247,7 +248,7 @@ def flatten(grads: Sequence[np.ndarray], plan: Plan, b: int,
     """One rank's flat bucket buffer for bucket b (grads indexed by param)."""
     lib = _load()
     dt = _dtype_code(grads[plan.bucket_params(b)[0]]) if plan.bucket_params(b) else 0
-    arrs = [np.ascontiguousarray(g) for g in grads]
+    arrs = [None if g is None else np.ascontiguousarray(g) for g in grads]
     for i in plan.bucket_params(b):
         if arrs[i].size != plan.numel[i]:
             raise ValueError(f"gradient {i} has the wrong size")
@@ -265,7 +266,7 @@ def unflatten(flat: np.ndarray, plan: Plan, b: int,
     """Copy bucket b's flat buffer back into the (writable) gradient arrays."""
     lib = _load()
     for i in plan.bucket_params(b):
-        if not grads[i].flags.c_contiguous or grads[i].size != plan.numel[i]:
+        if grads[i] is None or not grads[i].flags.c_contiguous or grads[i].size != plan.numel[i]:
             raise ValueError(f"gradient {i} must be contiguous and sized")
     table = _ptr_table(grads)
     flat = np.ascontiguousarray(flat)

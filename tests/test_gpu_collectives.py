@@ -1,0 +1,90 @@
+"""GPU parity: standalone reduce-scatter, all-gather and broadcast against
+the CPU oracle (bit-exact), in and out of place, with shards that are and
+are not whole 16-byte vectors."""
+import numpy as np
+import pytest
+import torch
+
+import bucketed_gradient_all_ddp_amd as ddp
+from bucketed_gradient_all_ddp_amd import workloads as W
+from helpers import assert_bits_equal, to_dev, to_host, tokens_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _vals(p, n, seed, bf16, oracle):
+    h = [W.normal_np(n, 1.0, seed, r) for r in range(p)]
+    return [oracle.f32_to_bf16(x) for x in h] if bf16 else h
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("avg", ["none", "world", "tokens"])
+@pytest.mark.parametrize("p,C", [(1, 5), (2, 3), (3, 1001), (4, 4096), (8, 12_345), (8, 65_536), (64, 8), (64, 513)])
+def test_reduce_scatter(oracle, p, C, avg, in_place, bf16):
+    n = p * C
+    host = _vals(p, n, 400 + p, bf16, oracle)
+    tokens = tokens_for(p, 1) if avg == "tokens" else None
+    ins = [to_dev(h) for h in host]
+    if in_place:
+        outs = [ins[r][r * C:(r + 1) * C] for r in range(p)]
+    else:
+        outs = [torch.empty(C, dtype=ins[0].dtype, device="cuda") for _ in range(p)]
+    st = ddp.reduce_scatter_sim(ins, outs, avg=avg, tokens=tokens)
+    torch.cuda.synchronize()
+    want, log = oracle.reduce_scatter(host, avg=avg, tokens=tokens)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"rank {r}")
+    assert st.messages == len(log) and st.steps == p - 1
+    assert st.bytes_sent_per_rank == sum(m.bytes for m in log if m.src == 0)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("p,C", [(1, 7), (2, 3), (3, 1001), (4, 4096), (8, 12_345), (64, 9), (64, 1024)])
+def test_allgather(oracle, p, C, bf16, in_place):
+    host = _vals(p, C, 500 + p, bf16, oracle)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    outs = [torch.full((p * C,), 7.0, dtype=dt, device="cuda") for _ in range(p)]
+    if in_place:
+        ins = [outs[r][r * C:(r + 1) * C] for r in range(p)]
+        for r in range(p):
+            ins[r].copy_(to_dev(host[r]))
+    else:
+        ins = [to_dev(h) for h in host]
+    st = ddp.allgather_sim(ins, outs)
+    torch.cuda.synchronize()
+    want, log = oracle.allgather(host)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"rank {r}")
+    assert st.messages == len(log)
+    assert st.bytes_sent_per_rank == sum(m.bytes for m in log if m.src == 0)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("p,n,src", [(1, 5, 0), (2, 1, 1), (5, 4099, 3), (8, 1 << 20, 0), (13, 1001, 12), (64, 70_001, 17)])
+def test_broadcast(oracle, p, n, src, bf16):
+    host = _vals(p, n, 600 + p, bf16, oracle)
+    bufs = [to_dev(h) for h in host]
+    st = ddp.broadcast_sim(bufs, src=src)
+    torch.cuda.synchronize()
+    want, log = oracle.broadcast(host, src)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r]), want[r], f"rank {r}")
+    assert st.messages == len(log) and st.steps == len({m.step for m in log})
+
+
+def test_rs_then_ag_equals_allreduce_on_integers(oracle):
+    p, C = 8, 10_001
+    n = p * C
+    host = [W.integer_valued_np(n, 3, r) for r in range(p)]
+    ins = [to_dev(h) for h in host]
+    outs = [torch.empty(n, device="cuda") for _ in range(p)]
+    shards = [ins[r][r * C:(r + 1) * C] for r in range(p)]
+    ddp.reduce_scatter_sim(ins, shards)
+    ddp.allgather_sim(shards, outs)
+    ar = [to_dev(h) for h in host]
+    ddp.ring_allreduce_sim(ar)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), to_host(ar[r]))
