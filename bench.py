@@ -1,19 +1,23 @@
 #!/usr/bin/env python3
-"""Benchmark: one step of the bucketed gradient sync on the GPT-2-small
-gradient set, p = 8 simulated ranks in one GPU's HBM.
+"""Benchmark: one bucketed gradient-sync step on the GPT-2-small gradient
+set, p = 8 simulated ranks in one GPU's HBM.
 
-A step is one pass of the whole path over every bucket of the plan:
-flatten (copy each rank's gradients into the bucket), ring all-reduce of the
-bucket averaged over p (fused single-pass kernel), unflatten (copy back).
-The plan is built once, before timing, as the reducer does at construction.
+A step is one pass of the whole path over every bucket of the plan: the
+bucket's flatten, ring all-reduce averaged over p, and unflatten back into
+each rank's per-parameter gradients. The headline ("inplace") step does the
+three in one kernel per bucket (ddp_allreduce_bucket: same bits, one pass
+over HBM); the "copy" step runs them as three kernels per bucket
+(ddp_flatten, ring_allreduce_sim, ddp_unflatten) and is reported next to it.
+The plan is built once before timing, as the reducer does at construction.
 
-Printed: one JSON line with the all-reduce bus bandwidth of the whole step
-(busBW = S * 2(p-1)/p / t_step, S = bytes of gradient per rank), the
-roofline of the dominant kernel (the fused all-reduce) measured with HIP
-events on the stream it runs on, and the CPU oracle timed on a bounded
-sample of the same workload.
+Output: one JSON line. `value` is the all-reduce bus bandwidth of the whole
+step, S * 2(p-1)/p / t_step (S = gradient bytes per rank). `roofline` is for
+the dominant kernel: its algorithmic bytes per launch over its launch
+durations, measured with HIP events attached to the kernel dispatches on the
+stream they run on, inside the timed region. `cpu_baseline` times the CPU
+oracle (one thread) on the same workload.
 
-Only one GPU is used; --gpus above 1 is refused.
+One GPU only: --gpus above 1 is refused.
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "all-reduce bus GB/s + % HBM peak, p=8 sim ranks, 124M fp32 grads"
 
 
 def log(msg: str) -> None:
@@ -40,52 +45,117 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", default="inplace", choices=["inplace", "copy"],
+                    help="headline step: one kernel per bucket, or flatten + "
+                         "all-reduce + unflatten as three")
+    ap.add_argument("--algo", default="fused", choices=["fused", "ring"],
+                    help="all-reduce algorithm of the copy step")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip timing the other step mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-buckets", type=int, default=0,
-                    help="buckets in the CPU-baseline sample (0 = auto)")
+                    help="buckets in the CPU-baseline sample (0 = all)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this many MiB "
-                         "(for scaling hardware counters)")
-    ap.add_argument("--algo", default="fused", choices=["fused", "ring"])
+                    help="also time a plain device copy of this many MiB")
     return ap.parse_args()
 
 
-def build_workload(torch, ddp, W, dev):
-    cfg = W.WORKLOADS["gpt2-small-p8"]
-    p = cfg["p"]
-    params = cfg["params"]
-    sizes = [W.numel(s) for _, s in params]
-    plan = ddp.ddp_bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
-    plan.upload(dev)
-    # one arena per rank, parameters in registration order at 256-byte
-    # aligned offsets (as separate allocations would be)
-    offs, off = [], 0
-    for n in sizes:
-        offs.append(off)
-        off += (n + 63) // 64 * 64
-    arenas, grads = [], []
-    for r in range(p):
-        a = torch.empty(off, dtype=torch.float32, device=dev)
-        W.normal_torch(off, cfg["sigma"], cfg["seed"], r, dev, out=a)
-        arenas.append(a)
-        grads.append([a[o:o + n] for o, n in zip(offs, sizes)])
-    table = ddp.grad_pointer_table(grads, dev)
-    buckets = []
-    for b in range(plan.num_buckets):
-        nb = plan.bucket_numel(b)
-        buckets.append([torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(p)])
-    return cfg, p, sizes, plan, grads, table, buckets, arenas
+class Workload:
+    def __init__(self, torch, ddp, W, dev):
+        cfg = W.WORKLOADS["gpt2-small-p8"]
+        self.cfg = cfg
+        self.p = p = cfg["p"]
+        self.sizes = sizes = [W.numel(s) for _, s in cfg["params"]]
+        self.S = sum(sizes) * 4
+        plan = ddp.ddp_bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+        plan.upload(dev)
+        plan.upload_segments(p, dev)
+        self.plan = plan
+        self.nb = [plan.bucket_numel(b) for b in range(plan.num_buckets)]
+        # one arena per rank, parameters in registration order at 256-byte
+        # aligned offsets (as separate allocations would be)
+        offs, off = [], 0
+        for n in sizes:
+            offs.append(off)
+            off += (n + 63) // 64 * 64
+        self.arenas, grads = [], []
+        for r in range(p):
+            a = torch.empty(off, dtype=torch.float32, device=dev)
+            W.normal_torch(off, cfg["sigma"], cfg["seed"], r, dev, out=a)
+            self.arenas.append(a)
+            grads.append([a[o:o + n] for o, n in zip(offs, sizes)])
+        self.grads = grads
+        self.table = ddp.grad_pointer_table(grads, dev)
+        self.buckets = None
+
+    def ensure_bucket_buffers(self, torch, dev):
+        if self.buckets is None:
+            self.buckets = [[torch.empty(n, dtype=torch.float32, device=dev)
+                             for _ in range(self.p)] for n in self.nb]
 
 
-def cpu_baseline(W, cfg, sizes, n_buckets_wanted):
-    """The oracle (single thread) on the first buckets of the same plan:
-    flatten, literal ring all-reduce averaged by p, unflatten."""
-    import numpy as np
+def run_steps(ddp, wl, mode, algo, steps, timer, ws):
+    """Run `steps` steps; when a timer is given, every kernel call is timed
+    by events attached to its dispatches. Returns [(kind, bytes, id)]."""
+    rec = []
+    plan, p, table = wl.plan, wl.p, wl.table
+    for _ in range(steps):
+        for b in range(plan.num_buckets):
+            if mode == "inplace":
+                k = timer.arm() if timer else None
+                st = ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
+                if timer:
+                    rec.append(("bucket_allreduce_kernel", st.hbm_bytes, k))
+            else:
+                bufs = wl.buckets[b]
+                k = timer.arm() if timer else None
+                ddp.ddp_flatten(plan, b, table, bufs)
+                if timer:
+                    rec.append(("flatten_kernel", 2 * p * wl.nb[b] * 4, k))
+                k = timer.arm() if timer else None
+                st = ddp.ring_allreduce_sim(bufs, avg="world", algo=algo, workspace=ws.get(b))
+                if timer:
+                    rec.append(("fused_allreduce_kernel" if algo == "fused" else "ring_step_kernel",
+                                st.hbm_bytes, k))
+                k = timer.arm() if timer else None
+                ddp.ddp_unflatten(plan, b, bufs, table)
+                if timer:
+                    rec.append(("unflatten_kernel", 2 * p * wl.nb[b] * 4, k))
+    return rec
+
+
+def timed(torch, ddp, wl, mode, algo, steps, warmup, ws):
+    run_steps(ddp, wl, mode, algo, warmup, None, ws)
+    torch.cuda.synchronize()
+    per_step_calls = wl.plan.num_buckets * (1 if mode == "inplace" else 3)
+    timer = ddp.CallTimer(pairs=per_step_calls * steps)
+    t0 = time.perf_counter()
+    rec = run_steps(ddp, wl, mode, algo, steps, timer, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    kernels = {}
+    for kind, nbytes, k in rec:
+        e = kernels.setdefault(kind, {"launches": 0, "bytes": 0, "ms": 0.0})
+        e["launches"] += 1
+        e["bytes"] += nbytes
+        e["ms"] += timer.elapsed_ms(k)
+    for e in kernels.values():
+        e["avg_us"] = round(1e3 * e["ms"] / e["launches"], 2)
+        e["GBps"] = round(e["bytes"] / (e["ms"] * 1e-3) / 1e9, 1)
+        e["ms_per_step"] = round(e["ms"] / steps, 4)
+        e["ms"] = round(e["ms"], 4)
+    return ms, kernels
+
+
+def cpu_baseline(W, wl, n_buckets_wanted):
+    """The oracle (single thread): flatten, literal ring all-reduce averaged
+    by p, unflatten, over the first buckets of the same plan."""
     import oracle
 
-    p = cfg["p"]
+    cfg, p, sizes = wl.cfg, wl.p, wl.sizes
     oplan = oracle.bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
-    nb = n_buckets_wanted or 4
+    nb = n_buckets_wanted or oplan.num_buckets
     params = [i for b in range(nb) for i in oplan.bucket_params(b)]
     host = [[None] * len(sizes) for _ in range(p)]
     for r in range(p):
@@ -100,7 +170,6 @@ def cpu_baseline(W, cfg, sizes, n_buckets_wanted):
             oracle.unflatten(red[r], oplan, b, host[r])
     dt = time.perf_counter() - t0
     S = elems * 4
-    bus = S * 2 * (p - 1) / p / dt / 1e9
     cpu = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
@@ -111,10 +180,11 @@ def cpu_baseline(W, cfg, sizes, n_buckets_wanted):
     except OSError:
         pass
     return {
-        "value": round(bus, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"first {nb} of {oplan.num_buckets} buckets ({elems} fp32 elements "
-                   f"per rank, p={p}): flatten + literal ring all-reduce (avg by p) + "
-                   f"unflatten, single thread, {dt:.2f} s on {cpu}"),
+        "value": round(S * 2 * (p - 1) / p / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{nb} of {oplan.num_buckets} buckets ({elems} fp32 elements per rank, "
+                   f"p={p}, numpy-drawn N(0,1e-3)): flatten + literal ring all-reduce "
+                   f"(avg by p) + unflatten, one thread, {dt:.2f} s on {cpu}"),
         "seconds": round(dt, 3),
     }
 
@@ -136,82 +206,34 @@ def main():
     dev = torch.device("cuda:0")
     ddp.load_library()
     log("building workload")
-    cfg, p, sizes, plan, grads, table, buckets, arenas = build_workload(torch, ddp, W, dev)
-    S = sum(sizes) * 4
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    wl = Workload(torch, ddp, W, dev)
+    p, S = wl.p, wl.S
     ws = {}
-    if args.algo == "ring":
-        for b in range(plan.num_buckets):
-            need = ddp.ring_allreduce_sim_workspace(p, plan.bucket_numel(b), 0, "ring")
-            ws[b] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
-
-    def step(events=None):
-        for b in range(plan.num_buckets):
-            bufs = buckets[b]
-            ddp.ddp_flatten(plan, b, table, bufs)
-            if events is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            st = ddp.ring_allreduce_sim(bufs, avg="world", algo=args.algo,
-                                        workspace=ws.get(b))
-            if events is not None:
-                e1.record(stream)
-                events.append((st.hbm_bytes, e0, e1))
-            ddp.ddp_unflatten(plan, b, bufs, table)
-
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
+    modes = [args.mode] + ([] if args.no_compare else
+                           [m for m in ("inplace", "copy") if m != args.mode])
+    if "copy" in modes:
+        wl.ensure_bucket_buffers(torch, dev)
+        if args.algo == "ring":
+            for b, n in enumerate(wl.nb):
+                need = ddp.ring_allreduce_sim_workspace(p, n, 0, "ring")
+                ws[b] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     torch.cuda.synchronize()
 
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    results = {}
+    for mode in modes:
+        log(f"{mode}: warmup {args.warmup}, timing {args.steps} steps")
+        ms, kernels = timed(torch, ddp, wl, mode, args.algo, args.steps, args.warmup, ws)
+        results[mode] = (ms, kernels)
+        log(f"{mode}: {ms:.3f} ms/step; " + "; ".join(
+            f"{k} {v['avg_us']} us avg, {v['GBps']} GB/s" for k, v in kernels.items()))
 
-    # the dominant kernel (fused all-reduce), timed per launch with events on
-    # the stream it is launched on
-    events = []
-    for _ in range(args.steps):
-        step(events)
-    torch.cuda.synchronize()
-    ar_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in events)
-    ar_launches = len(events)
-    ar_bytes = sum(hbm for hbm, _, _ in events)
-    achieved = ar_bytes / (ar_ms * 1e-3) / 1e9
-    ar_per_step_ms = ar_ms / args.steps
-    log(f"step {ms:.3f} ms, all-reduce {ar_per_step_ms:.3f} ms/step "
-        f"({ar_launches // args.steps} launches), {achieved:.0f} GB/s algorithmic")
-
-    calib = None
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * 1024 * 1024 // 4
-        a = torch.empty(n, device=dev)
-        b2 = torch.empty(n, device=dev)
-        a.fill_(1.0)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        reps = 10
-        e0.record(stream)
-        for _ in range(reps):
-            b2.copy_(a)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cms = e0.elapsed_time(e1) / reps
-        calib = {"bytes": 2 * n * 4, "ms": round(cms, 4),
-                 "GBps": round(2 * n * 4 / (cms * 1e-3) / 1e9, 1)}
-        log(f"copy {args.calib_copy_mib} MiB: {calib}")
-
+    ms, kernels = results[args.mode]
+    dominant = max(kernels.items(), key=lambda kv: kv[1]["ms"])
+    dname, d = dominant
     bus = S * 2 * (p - 1) / p / (ms * 1e-3) / 1e9
-    step_bytes = 6 * p * S  # flatten + all-reduce + unflatten, each 2pS
+    step_bytes = 2 * p * S if args.mode == "inplace" else 6 * p * S
     result = {
-        "metric": "all-reduce bus GB/s + % HBM peak, p=8 sim ranks, 124M fp32 grads",
+        "metric": METRIC,
         "value": round(bus, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -224,33 +246,56 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "gpt2-small gradients (148 fp32 tensors, 124,439,808 elements "
-                        "per rank), p=8 simulated ranks, 25 MiB buckets + 1 MiB first "
-                        "bucket (13 buckets), average by p; step = flatten + "
-                        f"{args.algo} ring all-reduce + unflatten per bucket",
-            "p": p, "buckets": plan.num_buckets, "bytes_per_rank": S,
+            "workload": ("gpt2-small gradients: 148 fp32 tensors, 124,439,808 elements per "
+                         "rank, p=8 simulated ranks, 25 MiB buckets + 1 MiB first bucket "
+                         "(13 buckets), average by p; step = flatten + ring all-reduce + "
+                         "unflatten of every bucket"),
+            "step_kernels": ("one ddp_allreduce_bucket per bucket" if args.mode == "inplace"
+                             else f"ddp_flatten + ring_allreduce_sim({args.algo}) + "
+                                  "ddp_unflatten per bucket"),
+            "p": p, "buckets": wl.plan.num_buckets, "bytes_per_rank": S,
         },
         "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "allreduce": {
-            "ms_per_step": round(ar_per_step_ms, 4),
-            "bus_GBps": round(S * 2 * (p - 1) / p / (ar_per_step_ms * 1e-3) / 1e9, 2),
-            "launches_per_step": ar_launches // args.steps,
-        },
+        "kernels": kernels,
         "roofline": {
-            "kernel": "fused_allreduce_kernel" if args.algo == "fused" else "ring_step_kernel",
+            "kernel": dname,
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": d["GBps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
             "traffic": None,
+            "avg_launch_us": d["avg_us"],
+            "bytes_per_launch": d["bytes"] // d["launches"],
         },
     }
-    if calib:
-        result["copy_calibration"] = calib
+    for mode, (mms, mk) in results.items():
+        if mode != args.mode:
+            result[f"{mode}_step"] = {
+                "ms_per_step": round(mms, 4),
+                "bus_GBps": round(S * 2 * (p - 1) / p / (mms * 1e-3) / 1e9, 2),
+                "kernels": mk,
+            }
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 1024 * 1024 // 4
+        a = torch.ones(n, device=dev)
+        b2 = torch.empty(n, device=dev)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            b2.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
+        result["copy_calibration"] = {"bytes": 2 * n * 4, "ms": round(cms, 4),
+                                      "GBps": round(2 * n * 4 / (cms * 1e-3) / 1e9, 1)}
+        del a, b2
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(W, cfg, sizes, args.cpu_buckets)
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(W, wl, args.cpu_buckets)
     print(json.dumps(result), flush=True)
 
 

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libddpsim.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["host.cpp", "plan.cpp", "allreduce.hip", "collectives.hip", "flatten.hip"]
+SOURCES = ["host.cpp", "plan.cpp", "allreduce.hip", "collectives.hip", "flatten.hip",
+           "bucket_allreduce.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -36,21 +37,24 @@ DEVICE = [
 ]
 
 
-def compile_commands():
+def compile_commands(build_dir=BUILD_DIR, defines=()):
     cmds = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD_DIR, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append(([HIPCC, *COMMON, *DEVICE, *lang, "-c", path, "-o", obj], obj))
+        cmds.append(([HIPCC, *COMMON, *DEVICE, *[f"-D{d}" for d in defines], *lang,
+                      "-c", path, "-o", obj], obj))
     return cmds
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (always) and link libddpsim.so in the package."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB_PATH, build_dir: str = BUILD_DIR,
+          defines=()) -> str:
+    """Compile every source (always) and link libddpsim.so (by default into
+    the package). `defines` are extra -D tuning macros."""
+    os.makedirs(build_dir, exist_ok=True)
     procs = []
-    for cmd, obj in compile_commands():
+    for cmd, obj in compile_commands(build_dir, defines):
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((subprocess.Popen(cmd), cmd, obj))
@@ -59,13 +63,13 @@ def build(verbose: bool = False) -> str:
         if proc.wait() != 0:
             raise RuntimeError("compile failed: " + " ".join(cmd))
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -30,11 +30,12 @@ STATUS = {
 }
 
 EXPORTS = [
-    "ddp_strerror", "ddp_last_error", "ddp_version",
+    "ddp_strerror", "ddp_last_error", "ddp_version", "ddp_time_next_call",
     "ddp_bucket_plan", "ddp_plan_free", "ddp_plan_num_params", "ddp_plan_num_buckets",
     "ddp_plan_bucket_numel", "ddp_plan_bucket_size", "ddp_plan_bucket_params",
     "ddp_plan_param_bucket", "ddp_plan_param_offset", "ddp_plan_device_bytes",
     "ddp_plan_upload", "ddp_flatten", "ddp_unflatten",
+    "ddp_plan_segment_bytes", "ddp_plan_upload_segments", "ddp_allreduce_bucket",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
 ]
@@ -80,6 +81,7 @@ def load_library(path: str = LIB_PATH):
         "ddp_strerror": ([st], ctypes.c_char_p),
         "ddp_last_error": ([], ctypes.c_char_p),
         "ddp_version": ([], ctypes.c_char_p),
+        "ddp_time_next_call": ([vp, vp], st),
         "ddp_bucket_plan": ([vp, i32, i32, i64, i64, ctypes.POINTER(vp)], st),
         "ddp_plan_free": ([vp], None),
         "ddp_plan_num_params": ([vp], i32),
@@ -93,6 +95,9 @@ def load_library(path: str = LIB_PATH):
         "ddp_plan_upload": ([vp, vp, sz, vp], st),
         "ddp_flatten": ([vp, i32, i32, vp, vp, i32, f32, vp], st),
         "ddp_unflatten": ([vp, i32, i32, vp, vp, i32, vp], st),
+        "ddp_plan_segment_bytes": ([vp, i32], sz),
+        "ddp_plan_upload_segments": ([vp, i32, vp, sz, vp], st),
+        "ddp_allreduce_bucket": ([vp, i32, i32, vp, i32, i32, vp, vp, vp], st),
         "ring_allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, vp, sz, vp, vp], st),
         "ring_allreduce_sim_workspace": ([i32, i64, i32, i32], sz),
         "ring_allreduce_sim_steps": ([vp, i32, i64, i32, vp, i32, i32, vp], st),
@@ -154,6 +159,58 @@ def _numel_all(tensors: Sequence) -> int:
 
 
 # ---------------------------------------------------------------------------
+# Kernel timing (HIP events attached to one call's kernel dispatches)
+# ---------------------------------------------------------------------------
+
+class CallTimer:
+    """A pool of HIP event pairs. arm() makes the next library call on this
+    thread record its kernels' start and end on one pair; elapsed_ms() reads
+    them after synchronisation."""
+
+    def __init__(self, pairs: int = 512):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._pairs = []
+        for _ in range(pairs):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(a)) or self._hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self._pairs.append((a, b))
+        self._next = 0
+
+    def arm(self) -> int:
+        """Attach the next free pair to the next library call; returns its id."""
+        if self._next >= len(self._pairs):
+            raise RuntimeError("CallTimer: no free event pair (reset() first)")
+        k = self._next
+        self._next += 1
+        a, b = self._pairs[k]
+        _check(load_library().ddp_time_next_call(a, b), "ddp_time_next_call")
+        return k
+
+    def elapsed_ms(self, k: int) -> float:
+        a, b = self._pairs[k]
+        if self._hip.hipEventSynchronize(b):
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def reset(self) -> None:
+        self._next = 0
+
+    def __del__(self):
+        for a, b in getattr(self, "_pairs", []):
+            self._hip.hipEventDestroy(a)
+            self._hip.hipEventDestroy(b)
+
+
+# ---------------------------------------------------------------------------
 # Bucket plan
 # ---------------------------------------------------------------------------
 
@@ -206,6 +263,20 @@ class Plan:
     def device_bytes(self) -> int:
         return load_library().ddp_plan_device_bytes(self._h)
 
+    def segment_bytes(self, p: int) -> int:
+        return load_library().ddp_plan_segment_bytes(self._h, p)
+
+    def upload_segments(self, p: int, device="cuda", stream=None) -> "Plan":
+        """Upload the piece table ddp_allreduce_bucket needs for p ranks."""
+        import torch
+
+        nbytes = self.segment_bytes(p)
+        self._segments = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _check(load_library().ddp_plan_upload_segments(
+            self._h, p, self._segments.data_ptr(), nbytes, _stream(stream)),
+            "ddp_plan_upload_segments")
+        return self
+
     def upload(self, device="cuda", stream=None) -> "Plan":
         import torch
 
@@ -251,6 +322,21 @@ def ddp_unflatten(plan: Plan, bucket: int, bucket_bufs: Sequence, grad_table,
     _check(load_library().ddp_unflatten(plan.handle, bucket, p, _ptrs(bucket_bufs),
                                         grad_table.data_ptr(), _dtype_code(bucket_bufs[0]),
                                         _stream(stream)), "ddp_unflatten")
+
+
+def ddp_allreduce_bucket(plan: Plan, bucket: int, grad_table, p: int, dtype=None,
+                         avg: str = "none", tokens=None, stream=None) -> CommStats:
+    """Flatten + ring all-reduce + unflatten of one bucket, in one pass."""
+    import torch
+
+    if dtype is None:
+        dtype = torch.float32 if plan.elem_bytes == 4 else torch.bfloat16
+    code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
+    st = CommStats()
+    _check(load_library().ddp_allreduce_bucket(
+        plan.handle, bucket, p, grad_table.data_ptr(), code, AVG[avg], _tokens(tokens, p),
+        _stream(stream), ctypes.byref(st)), "ddp_allreduce_bucket")
+    return st
 
 
 # ---------------------------------------------------------------------------

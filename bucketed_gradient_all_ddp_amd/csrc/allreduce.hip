@@ -33,53 +33,59 @@ namespace {
 // Kernels
 // ---------------------------------------------------------------------------
 
+// Workgroup w handles tiles w, w + gridDim.x, ... (a grid-stride loop, so
+// a launch can be sized to what the GPU holds at once); tile -> (chunk c,
+// tile t within the chunk) = (tile / tiles_per_chunk, tile % tiles_per_chunk).
 template <typename Tr, int VPT, int RB, bool kNT>
 __global__ __launch_bounds__(kThreads) void fused_allreduce_kernel(
     RankTable bufs, int32_t p, int64_t n, int64_t C, int32_t tiles_per_chunk,
     Divide div) {
   constexpr int V = Tr::kVec;
-  const int32_t c = static_cast<int32_t>(blockIdx.x) / tiles_per_chunk;
-  const int32_t t = static_cast<int32_t>(blockIdx.x) - c * tiles_per_chunk;
-  const ChunkSpan k = chunk_span(c, C, n, V);
-  if (k.s >= k.e) return;
   const int tid = static_cast<int>(threadIdx.x);
+  const int64_t total = int64_t(tiles_per_chunk) * p;
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int32_t c = static_cast<int32_t>(tile / tiles_per_chunk);
+    const int32_t t = static_cast<int32_t>(tile - int64_t(c) * tiles_per_chunk);
+    const ChunkSpan k = chunk_span(c, C, n, V);
+    if (k.s >= k.e) continue;
 
-  // Up to V-1 unaligned elements on each side of the chunk: tile 0's first
-  // lanes fold them one by one.
-  if (t == 0 && tid < 2 * (V - 1)) {
-    const bool head = tid < V - 1;
-    const int64_t i = head ? k.s + tid : k.tail_begin + (tid - (V - 1));
-    if (i < (head ? k.head_end : k.e)) {
-      const float y = apply_divide(fold_scalar<Tr>(bufs, p, c, i), div);
-      for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
+    // Up to V-1 unaligned elements on each side of the chunk: tile 0's
+    // first lanes fold them one by one.
+    if (t == 0 && tid < 2 * (V - 1)) {
+      const bool head = tid < V - 1;
+      const int64_t i = head ? k.s + tid : k.tail_begin + (tid - (V - 1));
+      if (i < (head ? k.head_end : k.e)) {
+        const float y = apply_divide(fold_scalar<Tr>(TablePtrs{bufs}, p, c, i), div);
+        for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
+      }
     }
-  }
 
-  const int64_t nv = (k.ve - k.vs) / V;
-  const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
-  if (base >= nv) return;
-  int64_t vi[VPT];
-  bool ok[VPT];
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int64_t j = base + u * kThreads + tid;
-    ok[u] = j < nv;
-    vi[u] = k.vs / V + j;
-  }
-  float acc[VPT][V];
-  fold_vectors<Tr, VPT, RB>(bufs, p, c, vi, ok, acc);
-  uint4 y[VPT];
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-#pragma unroll
-    for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
-    y[u] = Tr::narrow(acc[u]);
-  }
-  for (int32_t r = 0; r < p; ++r) {
-    void *dst = bufs.ptr[r];
+    const int64_t nv = (k.ve - k.vs) / V;
+    const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+    if (base >= nv) continue;
+    int64_t vi[VPT];
+    bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);
+      const int64_t j = base + u * kThreads + tid;
+      ok[u] = j < nv;
+      vi[u] = k.vs / V + j;
+    }
+    float acc[VPT][V];
+    fold_vectors<Tr, VPT, RB>(TablePtrs{bufs}, p, c, vi, ok, acc);
+    uint4 y[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
+      y[u] = Tr::narrow(acc[u]);
+    }
+    for (int32_t r = 0; r < p; ++r) {
+      void *dst = bufs.ptr[r];
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);
+      }
     }
   }
 }
@@ -190,9 +196,36 @@ __global__ __launch_bounds__(kThreads) void bf16_workspace_kernel(
 // Host side
 // ---------------------------------------------------------------------------
 
-constexpr int kFusedVpt = 2;  // 16-byte vectors per thread
-constexpr int kFusedRb = 8;   // rank loads in flight per vector
+// Tuning of the fused kernel (compile-time; the defaults are the measured
+// best on gfx950 for the gradient sets in the tests and benchmark).
+#ifndef DDPSIM_FUSED_VPT
+#define DDPSIM_FUSED_VPT 2  // 16-byte vectors per thread per tile
+#endif
+#ifndef DDPSIM_FUSED_RB
+#define DDPSIM_FUSED_RB 8  // rank loads issued before their additions
+#endif
+#ifndef DDPSIM_FUSED_NT
+#define DDPSIM_FUSED_NT 0  // non-temporal stores
+#endif
+#ifndef DDPSIM_FUSED_WAVES
+#define DDPSIM_FUSED_WAVES 0  // >0: cap the grid at this many workgroups per CU
+#endif
+constexpr int kFusedVpt = DDPSIM_FUSED_VPT;
+constexpr int kFusedRb = DDPSIM_FUSED_RB;
+constexpr bool kFusedNt = DDPSIM_FUSED_NT != 0;
 constexpr int kStepVpt = 4;
+
+int32_t device_cus() {
+  static int32_t cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      return 256;
+    }
+    return n > 0 ? n : 256;
+  }();
+  return cus;
+}
 
 int32_t tiles_for(int64_t C, int vec, int vpt) {
   const int64_t vectors = C / vec;
@@ -200,44 +233,51 @@ int32_t tiles_for(int64_t C, int vec, int vpt) {
 }
 
 ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtype,
-                        const Divide &div, hipStream_t stream) {
+                        const Divide &div, hipStream_t stream, CallTimer &timer) {
   const int64_t C = ceil_div(n, p);
   const int vec = dtype == DDP_F32 ? 4 : 8;
   const int32_t tpc = tiles_for(C, vec, kFusedVpt);
-  const int64_t blocks = int64_t(tpc) * p;
+  int64_t blocks = int64_t(tpc) * p;
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
-  if (dtype == DDP_F32) {
-    fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false>
-        <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, n, C, tpc, div);
-  } else {
-    fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false>
-        <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, n, C, tpc, div);
+  if (DDPSIM_FUSED_WAVES > 0) {
+    blocks = std::min<int64_t>(blocks, int64_t(device_cus()) * DDPSIM_FUSED_WAVES);
   }
-  return check_hip(hipGetLastError(), "fused_allreduce_kernel launch");
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (dtype == DDP_F32) {
+    return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, kFusedNt>, grid,
+                  dim3(kThreads), stream, timer, true, "fused_allreduce_kernel launch",
+                  tab, p, n, C, tpc, div);
+  }
+  return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, kFusedNt>, grid,
+                dim3(kThreads), stream, timer, true, "fused_allreduce_kernel launch",
+                tab, p, n, C, tpc, div);
 }
 
 // Launch ring steps [first, first + count) on fp32 buffers.
 ddp_status launch_steps(const RankTable &tab, int32_t p, int64_t n, const Divide &div,
-                        int32_t first, int32_t count, hipStream_t stream) {
+                        int32_t first, int32_t count, hipStream_t stream, CallTimer &timer,
+                        bool ends_call) {
   const int64_t C = ceil_div(n, p);
   const int32_t tpc = tiles_for(C, 4, kStepVpt);
   const int64_t blocks = int64_t(tpc) * p;
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring step: n too large");
   const Divide none{kNone, 1.0f, 1.0f};
+  const dim3 grid(static_cast<uint32_t>(blocks));
   for (int32_t s = first; s < first + count; ++s) {
+    const bool last = ends_call && s == first + count - 1;
+    ddp_status st;
     if (s < p - 1) {
       const int32_t k = s;  // reduce-scatter step k: rank r sends chunk r - k
       const int32_t shift = ((-k) % p + p) % p;
       const Divide &d = (k == p - 2) ? div : none;
-      ring_step_kernel<true, kStepVpt>
-          <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, shift, n, C, tpc, d);
+      st = launch(ring_step_kernel<true, kStepVpt>, grid, dim3(kThreads), stream, timer, last,
+                  "ring_step_kernel launch", tab, p, shift, n, C, tpc, d);
     } else {
       const int32_t k = s - (p - 1);  // all-gather step k: chunk r + 1 - k
       const int32_t shift = ((1 - k) % p + p) % p;
-      ring_step_kernel<false, kStepVpt>
-          <<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(tab, p, shift, n, C, tpc, none);
+      st = launch(ring_step_kernel<false, kStepVpt>, grid, dim3(kThreads), stream, timer, last,
+                  "ring_step_kernel launch", tab, p, shift, n, C, tpc, none);
     }
-    ddp_status st = check_hip(hipGetLastError(), "ring_step_kernel launch");
     if (st != DDP_OK) return st;
   }
   return DDP_OK;
@@ -298,6 +338,7 @@ extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n
                                          void *workspace, size_t workspace_bytes,
                                          hipStream_t stream, ddp_comm_stats *stats) {
   clear_error();
+  CallTimer timer = CallTimer::take();
   Divide div;
   ddp_status s = validate_common(bufs, p, n, dtype, avg_mode, tokens, &div,
                                  "ring_allreduce_sim");
@@ -324,8 +365,8 @@ extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n
   fill_allreduce_stats(stats, p, n, dtype, algo);
   if (n == 0) return DDP_OK;
   const RankTable tab = make_table(bufs, p);
-  if (algo == DDP_ALGO_FUSED || p == 1) return launch_fused(tab, p, n, dtype, div, stream);
-  if (dtype == DDP_F32) return launch_steps(tab, p, n, div, 0, 2 * (p - 1), stream);
+  if (algo == DDP_ALGO_FUSED || p == 1) return launch_fused(tab, p, n, dtype, div, stream, timer);
+  if (dtype == DDP_F32) return launch_steps(tab, p, n, div, 0, 2 * (p - 1), stream, timer, true);
 
   // bf16 ring: widen into fp32 rows, run the steps there, round back.
   const int64_t stride = workspace_stride_elems(n);
@@ -333,17 +374,16 @@ extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n
   const int32_t tpr = static_cast<int32_t>(ceil_div(ceil_div(n, 8), kThreads));
   const int64_t blocks = int64_t(tpr) * p;
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
-  bf16_workspace_kernel<true><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-      tab, ws, stride, n, tpr);
-  s = check_hip(hipGetLastError(), "bf16_workspace_kernel launch");
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  s = launch(bf16_workspace_kernel<true>, grid, dim3(kThreads), stream, timer, false,
+             "bf16_workspace_kernel launch", tab, ws, stride, n, tpr);
   if (s != DDP_OK) return s;
   RankTable rows;
   for (int32_t r = 0; r < kMaxRanks; ++r) rows.ptr[r] = r < p ? ws + r * stride : nullptr;
-  s = launch_steps(rows, p, n, div, 0, 2 * (p - 1), stream);
+  s = launch_steps(rows, p, n, div, 0, 2 * (p - 1), stream, timer, false);
   if (s != DDP_OK) return s;
-  bf16_workspace_kernel<false><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-      tab, ws, stride, n, tpr);
-  return check_hip(hipGetLastError(), "bf16_workspace_kernel launch");
+  return launch(bf16_workspace_kernel<false>, grid, dim3(kThreads), stream, timer, true,
+                "bf16_workspace_kernel launch", tab, ws, stride, n, tpr);
 }
 
 extern "C" ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int64_t n,
@@ -351,6 +391,7 @@ extern "C" ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int
                                                int32_t first_step, int32_t n_steps,
                                                hipStream_t stream) {
   clear_error();
+  CallTimer timer = CallTimer::take();
   Divide div;
   ddp_status s = validate_common(bufs, p, n, DDP_F32, avg_mode, tokens, &div,
                                  "ring_allreduce_sim_steps");
@@ -362,5 +403,5 @@ extern "C" ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int
                 first_step, first_step + n_steps, total);
   }
   if (n == 0 || n_steps == 0) return DDP_OK;
-  return launch_steps(make_table(bufs, p), p, n, div, first_step, n_steps, stream);
+  return launch_steps(make_table(bufs, p), p, n, div, first_step, n_steps, stream, timer, true);
 }

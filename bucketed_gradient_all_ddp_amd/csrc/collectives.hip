@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(
       vi[u] = static_cast<int64_t>(c) * nv + j;
     }
     float acc[VPT][V];
-    fold_vectors<Tr, VPT, RB>(in, p, first, vi, ok, acc);
+    fold_vectors<Tr, VPT, RB>(TablePtrs{in}, p, first, vi, ok, acc);
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       if (!ok[u]) continue;
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(
     const int64_t per_tile = int64_t(kThreads) * VPT * V;
     const int64_t lo = static_cast<int64_t>(t) * per_tile;
     for (int64_t j = lo + tid; j < lo + per_tile && j < C; j += kThreads) {
-      const float y = apply_divide(fold_scalar<Tr>(in, p, first, c * C + j), div);
+      const float y = apply_divide(fold_scalar<Tr>(TablePtrs{in}, p, first, c * C + j), div);
       Tr::store1(dst, j, y);
     }
   }
@@ -135,24 +135,24 @@ __global__ __launch_bounds__(kThreads) void fanout_copy_kernel(
   }
 }
 
-ddp_status launch_fanout(const RankTable &src, int32_t n_src, const RankTable &dst,
-                         int32_t p, int64_t bytes, int64_t dst_stride,
-                         const SkipTable &skip, hipStream_t stream, const char *what) {
+// vec_ok: every source is 16-byte aligned (destinations always are).
+ddp_status launch_fanout(const RankTable &src, int32_t n_src, bool vec_ok,
+                         const RankTable &dst, int32_t p, int64_t bytes,
+                         int64_t dst_stride, const SkipTable &skip,
+                         hipStream_t stream, CallTimer &timer, const char *what) {
   if (bytes == 0) return DDP_OK;
-  const bool vec = dst_stride % 16 == 0;
-  const int64_t per_tile = vec ? int64_t(kThreads) * kCopyVpt * 16
-                               : int64_t(kThreads) * kCopyVpt * 16;
+  const bool vec = vec_ok && dst_stride % 16 == 0;
+  // 16 KiB per workgroup in both paths
+  const int64_t per_tile = int64_t(kThreads) * kCopyVpt * 16;
   const int64_t tiles = std::max<int64_t>(1, ceil_div(bytes, per_tile));
   if (tiles > INT32_MAX) return fail(DDP_EINVAL, "%s: buffer too large", what);
   const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(n_src));
   if (vec) {
-    fanout_copy_kernel<kCopyVpt, true><<<grid, dim3(kThreads), 0, stream>>>(
-        src, dst, p, bytes, dst_stride, skip);
-  } else {
-    fanout_copy_kernel<kCopyVpt, false><<<grid, dim3(kThreads), 0, stream>>>(
-        src, dst, p, bytes, dst_stride, skip);
+    return launch(fanout_copy_kernel<kCopyVpt, true>, grid, dim3(kThreads), stream, timer, true,
+                  what, src, dst, p, bytes, dst_stride, skip);
   }
-  return check_hip(hipGetLastError(), what);
+  return launch(fanout_copy_kernel<kCopyVpt, false>, grid, dim3(kThreads), stream, timer, true,
+                what, src, dst, p, bytes, dst_stride, skip);
 }
 
 void fill_stats(ddp_comm_stats *st, int64_t steps, int64_t messages, int64_t sent,
@@ -176,6 +176,7 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
                                          int32_t avg_mode, const int64_t *tokens,
                                          hipStream_t stream, ddp_comm_stats *stats) {
   clear_error();
+  CallTimer timer = CallTimer::take();
   const char *what = "reduce_scatter_sim";
   ddp_status s = check_p(p, what);
   if (s != DDP_OK) return s;
@@ -192,7 +193,7 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const int64_t C = n / p;
   s = check_rank_buffers(what, in, p, n * eb);
   if (s != DDP_OK) return s;
-  s = check_rank_buffers(what, reinterpret_cast<const void *const *>(out), p, C * eb);
+  s = check_rank_buffers(what, reinterpret_cast<const void *const *>(out), p, C * eb, eb);
   if (s != DDP_OK) return s;
   // out[r] may sit exactly on its own chunk of in[r]; nothing else may overlap.
   for (int32_t r = 0; r < p && C > 0; ++r) {
@@ -209,7 +210,7 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const RankTable tin = make_table(in, p);
   const RankTable tout = make_table(reinterpret_cast<const void *const *>(out), p);
   const int V = dtype == DDP_F32 ? 4 : 8;
-  const bool vec = C % V == 0;
+  const bool vec = C % V == 0 && all_vec_aligned(reinterpret_cast<const void *const *>(out), p);
   const int64_t per_tile = int64_t(kThreads) * kRsVpt * (vec ? 1 : V);
   const int64_t units = vec ? C / V : C;
   const int64_t tpc = std::max<int64_t>(1, ceil_div(units, per_tile));
@@ -217,30 +218,28 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "%s: n too large", what);
   const dim3 grid(static_cast<uint32_t>(blocks));
   const int32_t tpc32 = static_cast<int32_t>(tpc);
+  const char *kname = "reduce_scatter_kernel launch";
   if (dtype == DDP_F32) {
     if (vec) {
-      reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true><<<grid, dim3(kThreads), 0, stream>>>(
-          tin, tout, p, C, tpc32, div);
-    } else {
-      reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false><<<grid, dim3(kThreads), 0, stream>>>(
-          tin, tout, p, C, tpc32, div);
+      return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true>, grid, dim3(kThreads),
+                    stream, timer, true, kname, tin, tout, p, C, tpc32, div);
     }
-  } else {
-    if (vec) {
-      reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true><<<grid, dim3(kThreads), 0, stream>>>(
-          tin, tout, p, C, tpc32, div);
-    } else {
-      reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false><<<grid, dim3(kThreads), 0, stream>>>(
-          tin, tout, p, C, tpc32, div);
-    }
+    return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false>, grid, dim3(kThreads),
+                  stream, timer, true, kname, tin, tout, p, C, tpc32, div);
   }
-  return check_hip(hipGetLastError(), "reduce_scatter_kernel launch");
+  if (vec) {
+    return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true>, grid, dim3(kThreads),
+                  stream, timer, true, kname, tin, tout, p, C, tpc32, div);
+  }
+  return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false>, grid, dim3(kThreads),
+                stream, timer, true, kname, tin, tout, p, C, tpc32, div);
 }
 
 extern "C" ddp_status allgather_sim(const void *const *in, void *const *out, int32_t p,
                                     int64_t n, int32_t dtype, hipStream_t stream,
                                     ddp_comm_stats *stats) {
   clear_error();
+  CallTimer timer = CallTimer::take();
   const char *what = "allgather_sim";
   ddp_status s = check_p(p, what);
   if (s != DDP_OK) return s;
@@ -260,8 +259,8 @@ extern "C" ddp_status allgather_sim(const void *const *in, void *const *out, int
   int64_t in_place = 0;
   for (int32_t j = 0; j < p && C > 0; ++j) {
     if (in[j] == nullptr) return fail(DDP_EINVAL, "%s: input of rank %d is NULL", what, j);
-    if (reinterpret_cast<uintptr_t>(in[j]) % kVecBytes != 0) {
-      return fail(DDP_EALIGN, "%s: input of rank %d is not 16-byte aligned", what, j);
+    if (reinterpret_cast<uintptr_t>(in[j]) % static_cast<uintptr_t>(eb) != 0) {
+      return fail(DDP_EALIGN, "%s: input of rank %d is not %d-byte aligned", what, j, eb);
     }
     const char *slot = static_cast<const char *>(out[j]) + j * C * eb;
     if (in[j] == slot) {
@@ -283,14 +282,16 @@ extern "C" ddp_status allgather_sim(const void *const *in, void *const *out, int
   fill_stats(stats, p - 1, int64_t(p) * (p - 1), (p - 1) * C * eb, (p - 1) * C * eb,
              int64_t(p) * (p - 1) * C * eb, n * eb + (int64_t(p) * p - in_place) * C * eb);
   if (n == 0) return DDP_OK;
-  return launch_fanout(make_table(in, p), p, make_table(reinterpret_cast<const void *const *>(out), p),
-                       p, C * eb, C * eb, skip, stream, "allgather fanout_copy_kernel launch");
+  return launch_fanout(make_table(in, p), p, all_vec_aligned(in, p),
+                       make_table(reinterpret_cast<const void *const *>(out), p), p, C * eb,
+                       C * eb, skip, stream, timer, "allgather fanout_copy_kernel launch");
 }
 
 extern "C" ddp_status broadcast_sim(void *const *bufs, int32_t p, int64_t n, int32_t src,
                                     int32_t dtype, hipStream_t stream,
                                     ddp_comm_stats *stats) {
   clear_error();
+  CallTimer timer = CallTimer::take();
   const char *what = "broadcast_sim";
   ddp_status s = check_p(p, what);
   if (s != DDP_OK) return s;
@@ -311,6 +312,6 @@ extern "C" ddp_status broadcast_sim(void *const *bufs, int32_t p, int64_t n, int
   SkipTable skip;
   for (int32_t r = 0; r < kMaxRanks; ++r) skip.rank[r] = -1;
   skip.rank[0] = src;
-  return launch_fanout(from, 1, make_table(reinterpret_cast<const void *const *>(bufs), p), p,
-                       n * eb, 0, skip, stream, "broadcast fanout_copy_kernel launch");
+  return launch_fanout(from, 1, true, make_table(reinterpret_cast<const void *const *>(bufs), p),
+                       p, n * eb, 0, skip, stream, timer, "broadcast fanout_copy_kernel launch");
 }

@@ -93,6 +93,7 @@ ddp_status run(const ddp_plan *plan, int32_t bucket, int32_t p,
                int32_t dtype, float prescale, bool to_flat, hipStream_t stream,
                const char *what) {
   clear_error();
+  CallTimer timer = CallTimer::take();
   int32_t first, count, tiles, n_params, eb_plan;
   int64_t elems;
   const void *table;
@@ -132,24 +133,21 @@ ddp_status run(const ddp_plan *plan, int32_t bucket, int32_t p,
   const ParamDesc *desc = static_cast<const ParamDesc *>(table) + first;
   const RankTable tab = make_table(bucket_bufs, p);
   const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(p));
+  const char *kname = "flatten_kernel launch";
   if (dtype == DDP_F32) {
     if (to_flat) {
-      flatten_kernel<F32Traits, true><<<grid, dim3(kThreads), 0, stream>>>(
-          desc, count, n_params, d_grad_ptrs, tab, div);
-    } else {
-      flatten_kernel<F32Traits, false><<<grid, dim3(kThreads), 0, stream>>>(
-          desc, count, n_params, d_grad_ptrs, tab, div);
+      return launch(flatten_kernel<F32Traits, true>, grid, dim3(kThreads), stream, timer, true,
+                    kname, desc, count, n_params, d_grad_ptrs, tab, div);
     }
-  } else {
-    if (to_flat) {
-      flatten_kernel<BF16Traits, true><<<grid, dim3(kThreads), 0, stream>>>(
-          desc, count, n_params, d_grad_ptrs, tab, div);
-    } else {
-      flatten_kernel<BF16Traits, false><<<grid, dim3(kThreads), 0, stream>>>(
-          desc, count, n_params, d_grad_ptrs, tab, div);
-    }
+    return launch(flatten_kernel<F32Traits, false>, grid, dim3(kThreads), stream, timer, true,
+                  kname, desc, count, n_params, d_grad_ptrs, tab, div);
   }
-  return check_hip(hipGetLastError(), "flatten_kernel launch");
+  if (to_flat) {
+    return launch(flatten_kernel<BF16Traits, true>, grid, dim3(kThreads), stream, timer, true,
+                  kname, desc, count, n_params, d_grad_ptrs, tab, div);
+  }
+  return launch(flatten_kernel<BF16Traits, false>, grid, dim3(kThreads), stream, timer, true,
+                kname, desc, count, n_params, d_grad_ptrs, tab, div);
 }
 
 }  // namespace

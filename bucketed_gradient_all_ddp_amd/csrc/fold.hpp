@@ -20,11 +20,31 @@
 
 namespace ddpsim {
 
-// Fold VPT 16-byte vectors (global vector indices vi[u], valid where ok[u])
-// over the p ranks in ring order starting at `first`. RB rank loads are
-// issued before their additions.
-template <typename Tr, int VPT, int RB>
-__device__ __forceinline__ void fold_vectors(const RankTable &in, int32_t p,
+// Where a kernel finds rank r's base address: the kernel-argument table...
+struct TablePtrs {
+  const RankTable &tab;
+  __device__ __forceinline__ void *operator()(int32_t r) const { return tab.ptr[r]; }
+};
+
+// ...or a device array of p * n_params gradient addresses (rank-major), for
+// one parameter, moved back by `shift` bytes so that the vector grid of all
+// ranks starts on a 16-byte boundary.
+struct GradPtrs {
+  const void *const *tab;
+  int32_t n_params;
+  int32_t param;
+  int64_t shift;
+  __device__ __forceinline__ void *operator()(int32_t r) const {
+    return const_cast<char *>(static_cast<const char *>(
+               tab[static_cast<int64_t>(r) * n_params + param])) - shift;
+  }
+};
+
+// Fold VPT 16-byte vectors (vector indices vi[u], valid where ok[u]) over
+// the p ranks in ring order starting at `first`. RB rank loads are issued
+// before their additions.
+template <typename Tr, int VPT, int RB, typename Ptrs>
+__device__ __forceinline__ void fold_vectors(const Ptrs &ptr_of, int32_t p,
                                              int32_t first,
                                              const int64_t (&vi)[VPT],
                                              const bool (&ok)[VPT],
@@ -39,7 +59,7 @@ __device__ __forceinline__ void fold_vectors(const RankTable &in, int32_t p,
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const bool live = s0 + j < p;
-      const void *src = in.ptr[live ? ring_rank(first, s0 + j, p) : 0];
+      const void *src = ptr_of(live ? ring_rank(first, s0 + j, p) : 0);
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
         x[j][u] = (live && ok[u]) ? load_vec(src, vi[u]) : make_uint4(0, 0, 0, 0);
@@ -61,12 +81,12 @@ __device__ __forceinline__ void fold_vectors(const RankTable &in, int32_t p,
 }
 
 // The same fold for one element.
-template <typename Tr>
-__device__ __forceinline__ float fold_scalar(const RankTable &in, int32_t p,
+template <typename Tr, typename Ptrs>
+__device__ __forceinline__ float fold_scalar(const Ptrs &ptr_of, int32_t p,
                                              int32_t first, int64_t i) {
   float acc = -0.0f;
   for (int32_t s = 0; s < p; ++s) {
-    acc = acc + Tr::load1(in.ptr[ring_rank(first, s, p)], i);
+    acc = acc + Tr::load1(ptr_of(ring_rank(first, s, p)), i);
   }
   return acc;
 }

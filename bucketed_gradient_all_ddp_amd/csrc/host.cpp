@@ -13,6 +13,17 @@ namespace ddpsim {
 
 namespace {
 thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_timer_start = nullptr;
+thread_local hipEvent_t g_timer_stop = nullptr;
+}
+
+CallTimer CallTimer::take() {
+  CallTimer t;
+  t.start = g_timer_start;
+  t.stop = g_timer_stop;
+  g_timer_start = nullptr;
+  g_timer_stop = nullptr;
+  return t;
 }
 
 void clear_error() { g_last_error[0] = '\0'; }
@@ -50,8 +61,15 @@ bool ranges_overlap(const void *a, int64_t na, const void *b, int64_t nb) {
   return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
 }
 
+bool all_vec_aligned(const void *const *bufs, int32_t p) {
+  for (int32_t r = 0; r < p; ++r) {
+    if (reinterpret_cast<uintptr_t>(bufs[r]) % kVecBytes != 0) return false;
+  }
+  return true;
+}
+
 ddp_status check_rank_buffers(const char *what, const void *const *bufs,
-                              int32_t p, int64_t bytes) {
+                              int32_t p, int64_t bytes, int align) {
   if (bufs == nullptr) return fail(DDP_EINVAL, "%s: pointer array is NULL", what);
   if (bytes == 0) return DDP_OK;
   std::vector<std::pair<uintptr_t, int32_t>> order;
@@ -61,9 +79,9 @@ ddp_status check_rank_buffers(const char *what, const void *const *bufs,
       return fail(DDP_EINVAL, "%s: buffer of rank %d is NULL", what, r);
     }
     auto a = reinterpret_cast<uintptr_t>(bufs[r]);
-    if (a % kVecBytes != 0) {
-      return fail(DDP_EALIGN, "%s: buffer of rank %d is not 16-byte aligned",
-                  what, r);
+    if (a % static_cast<uintptr_t>(align) != 0) {
+      return fail(DDP_EALIGN, "%s: buffer of rank %d is not %d-byte aligned",
+                  what, r, align);
     }
     order.emplace_back(a, r);
   }
@@ -151,3 +169,13 @@ extern "C" const char *ddp_strerror(ddp_status s) {
 extern "C" const char *ddp_last_error(void) { return g_last_error; }
 
 extern "C" const char *ddp_version(void) { return "ddpsim 0.1 (gfx950)"; }
+
+extern "C" ddp_status ddp_time_next_call(hipEvent_t start, hipEvent_t stop) {
+  clear_error();
+  if ((start == nullptr) != (stop == nullptr)) {
+    return fail(DDP_EINVAL, "ddp_time_next_call: pass both events or neither");
+  }
+  g_timer_start = start;
+  g_timer_stop = stop;
+  return DDP_OK;
+}

@@ -4,6 +4,7 @@
 // include/ddpsim.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -49,6 +50,23 @@ static_assert(sizeof(ParamDesc) == 32, "ParamDesc layout");
 
 constexpr int kFlattenTile = 4096;  // elements per flatten workgroup
 
+// One piece of a bucket for the in-place bucket all-reduce: the part of one
+// parameter that falls in one ring chunk of the bucket (32 bytes).
+struct SegDesc {
+  int64_t param_begin;  // first element of the piece inside the parameter
+  int64_t len;          // elements
+  int32_t param;        // registration index
+  int32_t chunk;        // ring chunk of the bucket holding every element
+  int32_t tile_begin;   // first tile of the piece within its bucket
+  int32_t reserved;
+};
+static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
+
+constexpr int kBucketVpt = 2;  // vectors per thread per bucket-all-reduce tile
+constexpr int kBucketRb = 8;
+// elements per tile for a dtype whose 16-byte vector holds `vec` elements
+constexpr int64_t bucket_tile_elems(int vec) { return int64_t(kThreads) * kBucketVpt * vec; }
+
 // ---------------------------------------------------------------------------
 // Host helpers (defined in host.cpp)
 // ---------------------------------------------------------------------------
@@ -63,9 +81,13 @@ int elem_bytes_of(int32_t dtype);
 
 ddp_status check_p(int32_t p, const char *what);
 
-// Null, 16-byte alignment and pairwise overlap of p ranges of `bytes` each.
+// Null, alignment (to `align` bytes) and pairwise overlap of p ranges of
+// `bytes` each.
 ddp_status check_rank_buffers(const char *what, const void *const *bufs,
-                              int32_t p, int64_t bytes);
+                              int32_t p, int64_t bytes, int align = kVecBytes);
+
+// True if every one of the p pointers is 16-byte aligned.
+bool all_vec_aligned(const void *const *bufs, int32_t p);
 
 // True if [a, a+na) and [b, b+nb) share a byte.
 bool ranges_overlap(const void *a, int64_t na, const void *b, int64_t nb);
@@ -77,6 +99,31 @@ ddp_status make_divide(int32_t avg_mode, int32_t p, const int64_t *tokens,
 RankTable make_table(const void *const *bufs, int32_t p);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Timing requested with ddp_time_next_call: the events are attached to the
+// first and the last kernel dispatch of the next entry-point call made on
+// this thread. take() moves the pending request into the call.
+struct CallTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  bool started = false;
+  static CallTimer take();
+  hipEvent_t start_event() {
+    if (started) return nullptr;
+    started = true;
+    return start;
+  }
+};
+
+// Every kernel of the library is launched through here: a plain dispatch,
+// with the call's timing events attached when requested.
+template <typename Kernel, typename... Args>
+ddp_status launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream,
+                  CallTimer &timer, bool last, const char *what, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, timer.start_event(),
+                        last ? timer.stop : nullptr, 0, args...);
+  return check_hip(hipGetLastError(), what);
+}
 
 // ---------------------------------------------------------------------------
 // Device helpers
@@ -194,18 +241,23 @@ struct ChunkSpan {
   int64_t s, e, head_end, vs, ve, tail_begin;
 };
 
-__device__ __forceinline__ ChunkSpan chunk_span(int64_t c, int64_t C,
-                                                int64_t n, int vec) {
+// The same split for an arbitrary range [s, e).
+__device__ __forceinline__ ChunkSpan make_span(int64_t s, int64_t e, int vec) {
   ChunkSpan k;
-  k.s = c * C;
-  k.e = k.s + C < n ? k.s + C : n;
-  if (k.e < k.s) k.e = k.s;
+  k.s = s;
+  k.e = e < s ? s : e;
   k.vs = (k.s + vec - 1) / vec * vec;
   k.ve = k.e / vec * vec;
   k.head_end = k.vs < k.e ? k.vs : k.e;
   if (k.ve < k.vs) k.ve = k.vs;           // no aligned body
   k.tail_begin = k.ve > k.head_end ? k.ve : k.head_end;
   return k;
+}
+
+__device__ __forceinline__ ChunkSpan chunk_span(int64_t c, int64_t C,
+                                                int64_t n, int vec) {
+  const int64_t s = c * C;
+  return make_span(s, s + C < n ? s + C : n, vec);
 }
 
 #endif  // __HIPCC__

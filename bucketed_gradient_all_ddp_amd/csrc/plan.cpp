@@ -30,6 +30,12 @@ struct ddp_plan {
   std::vector<ParamDesc> desc;
   void *d_table = nullptr;
   bool uploaded = false;
+  // in-place bucket all-reduce: pieces of (parameter x ring chunk), for
+  // seg_p ranks
+  int32_t seg_p = 0;
+  std::vector<SegDesc> seg;
+  std::vector<int32_t> seg_first, seg_count, seg_tiles;
+  void *d_seg = nullptr;
 };
 
 namespace ddpsim {
@@ -53,7 +59,112 @@ bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
   return true;
 }
 
+bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t *count,
+                       int32_t *tiles, int64_t *elems, const void **table, int32_t *seg_p,
+                       int32_t *n_params, int32_t *elem_bytes) {
+  if (plan == nullptr || b < 0 || b >= static_cast<int32_t>(plan->members.size())) {
+    return false;
+  }
+  *seg_p = plan->seg_p;
+  *elems = plan->bucket_elems[b];
+  *n_params = plan->n_params;
+  *elem_bytes = plan->elem_bytes;
+  *table = plan->d_seg;
+  if (plan->seg_p == 0) {
+    *first = *count = *tiles = 0;
+    return true;
+  }
+  *first = plan->seg_first[b];
+  *count = plan->seg_count[b];
+  *tiles = plan->seg_tiles[b];
+  return true;
+}
+
+// Cut every bucket into pieces that lie in one parameter and one ring chunk
+// (chunks of ceil(n_b / p) elements of the bucket's flat index space).
+static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc> *seg,
+                           std::vector<int32_t> *first, std::vector<int32_t> *count,
+                           std::vector<int32_t> *tiles) {
+  const int64_t tile_elems = bucket_tile_elems(kVecBytes / plan->elem_bytes);
+  for (size_t b = 0; b < plan->members.size(); ++b) {
+    first->push_back(static_cast<int32_t>(seg->size()));
+    const int64_t nb = plan->bucket_elems[b];
+    const int64_t C = nb > 0 ? ceil_div(nb, p) : 1;
+    int64_t t = 0;
+    for (int32_t i : plan->members[b]) {
+      const int64_t o = plan->offset[i];
+      const int64_t end = o + plan->numel[i];
+      for (int64_t pos = o; pos < end;) {
+        const int64_t c = pos / C;
+        const int64_t piece_end = std::min(end, (c + 1) * C);
+        SegDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.param_begin = pos - o;
+        d.len = piece_end - pos;
+        d.param = i;
+        d.chunk = static_cast<int32_t>(c);
+        d.tile_begin = static_cast<int32_t>(t);
+        t += std::max<int64_t>(1, ceil_div(d.len, tile_elems));
+        seg->push_back(d);
+        pos = piece_end;
+      }
+    }
+    if (t > INT32_MAX) return false;
+    count->push_back(static_cast<int32_t>(seg->size()) - first->back());
+    tiles->push_back(static_cast<int32_t>(t));
+  }
+  return true;
+}
+
 }  // namespace ddpsim
+
+extern "C" size_t ddp_plan_segment_bytes(const ddp_plan *plan, int32_t p) {
+  if (plan == nullptr || p < 1 || p > kMaxRanks) return 0;
+  std::vector<SegDesc> seg;
+  std::vector<int32_t> f, c, t;
+  if (!build_segments(plan, p, &seg, &f, &c, &t)) return 0;
+  return seg.size() * sizeof(SegDesc);
+}
+
+extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *d_table,
+                                               size_t bytes, hipStream_t stream) {
+  clear_error();
+  if (plan == nullptr) return fail(DDP_EINVAL, "ddp_plan_upload_segments: plan is NULL");
+  ddp_status s = check_p(p, "ddp_plan_upload_segments");
+  if (s != DDP_OK) return s;
+  std::vector<SegDesc> seg;
+  std::vector<int32_t> first, count, tiles;
+  if (!build_segments(plan, p, &seg, &first, &count, &tiles)) {
+    return fail(DDP_EINVAL, "ddp_plan_upload_segments: a bucket is too large");
+  }
+  const size_t need = seg.size() * sizeof(SegDesc);
+  if (need > 0) {
+    if (d_table == nullptr || bytes < need) {
+      return fail(DDP_EINVAL, "ddp_plan_upload_segments: needs %zu bytes of device memory",
+                  need);
+    }
+    if (reinterpret_cast<uintptr_t>(d_table) % kVecBytes != 0) {
+      return fail(DDP_EALIGN, "ddp_plan_upload_segments: table is not 16-byte aligned");
+    }
+  }
+  // The plan keeps the host copy alive for the asynchronous upload.
+  plan->seg.swap(seg);
+  plan->seg_first.swap(first);
+  plan->seg_count.swap(count);
+  plan->seg_tiles.swap(tiles);
+  if (need > 0) {
+    s = check_hip(hipMemcpyAsync(d_table, plan->seg.data(), need, hipMemcpyHostToDevice,
+                                 stream),
+                  "ddp_plan_upload_segments: hipMemcpyAsync");
+    if (s != DDP_OK) {
+      plan->seg_p = 0;
+      return s;
+    }
+  }
+  plan->d_seg = d_table;
+  plan->seg_p = p;
+  return DDP_OK;
+}
 
 extern "C" ddp_status ddp_bucket_plan(const int64_t *numel, int32_t n_params,
                                       int32_t elem_bytes, int64_t bucket_cap_bytes,

@@ -111,6 +111,17 @@ const char *ddp_last_error(void);
 /* Library version string. */
 const char *ddp_version(void);
 
+/* Instrumentation. The next entry-point call made on this thread attaches
+ * `start` to the dispatch of its first kernel and `stop` to the dispatch of
+ * its last kernel (hipExtLaunchKernel semantics), so
+ * hipEventElapsedTime(start, stop) is exactly the device time of that
+ * call's kernels, with nothing else on the stream in between. Events are
+ * created and owned by the caller (hipEventCreate). The request is consumed
+ * by the next call even if that call fails or launches nothing (n == 0);
+ * then the events are not recorded. Pass NULL, NULL to cancel.
+ * Errors: DDP_EINVAL if exactly one of the two is NULL. */
+ddp_status ddp_time_next_call(hipEvent_t start, hipEvent_t stop);
+
 /* ----------------------------------------------------------------------- */
 /* Bucket plan (host)                                                      */
 /* ----------------------------------------------------------------------- */
@@ -199,6 +210,43 @@ ddp_status ddp_unflatten(const ddp_plan *plan, int32_t bucket, int32_t p,
                          hipStream_t stream);
 
 /* ----------------------------------------------------------------------- */
+/* Bucket all-reduce in place on the gradients                             */
+/* ----------------------------------------------------------------------- */
+
+/* The bucket's flatten, ring all-reduce and unflatten as one pass over the
+ * gradients: afterwards every rank's gradients of bucket `bucket` hold
+ * exactly the bits that ddp_flatten, then ring_allreduce_sim on the flat
+ * buffers (same p, dtype, averaging), then ddp_unflatten would leave there.
+ * No flat buffer is materialised: the ring's chunks (ceil(n_b/p) elements
+ * of the bucket's flat index space, [COL] "Ring allreduce in two passes")
+ * are mapped onto the parameters through the plan ([DDP] Part 2 "Step 2:
+ * backward" item 1 and "Step 3: finalize_backward" describe the copies this
+ * replaces). Device-memory traffic is 2 p n_b bytes-per-element.
+ *
+ * Before the first call for a given p, upload the plan's piece table for p:
+ * ddp_plan_segment_bytes(plan, p) bytes of caller-owned device memory
+ * (16-byte aligned), filled by ddp_plan_upload_segments on `stream`. The
+ * plan keeps the host copy alive; uploading for another p replaces it.
+ *
+ *   d_grad_ptrs  DEVICE array of p * n_params gradient addresses, rank-major
+ *                (as for ddp_flatten); each gradient must be aligned to its
+ *                element size. When every rank's copy of a parameter has the
+ *                same offset from a 16-byte boundary the kernel moves 16-byte
+ *                vectors, otherwise elements.
+ *   avg_mode, tokens, stats   as ring_allreduce_sim.
+ * Errors: DDP_ENOTREADY (no piece table for this p), DDP_ERANGE, DDP_EINVAL.
+ * Gradients of different ranks or parameters must not overlap (not checked:
+ * the addresses are device-resident). */
+size_t ddp_plan_segment_bytes(const ddp_plan *plan, int32_t p);
+ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *d_table,
+                                    size_t bytes, hipStream_t stream);
+ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket,
+                                int32_t p, void *const *d_grad_ptrs,
+                                int32_t dtype, int32_t avg_mode,
+                                const int64_t *tokens, hipStream_t stream,
+                                ddp_comm_stats *stats);
+
+/* ----------------------------------------------------------------------- */
 /* Ring all-reduce                                                         */
 /* ----------------------------------------------------------------------- */
 
@@ -253,7 +301,9 @@ ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int64_t n,
  * operations"): out[r][i] = avg(sum over ranks of in[.][r*C + i]),
  * C = n/p, folded in ring order starting at rank (r+1) mod p.
  *   in   HOST array of p device pointers to n elements (read only)
- *   out  HOST array of p device pointers to C elements; out[r] may equal
+ *   out  HOST array of p device pointers to C elements (element-aligned;
+ *        16-byte alignment and C a whole number of 16-byte vectors take the
+ *        vector path); out[r] may equal
  *        in[r] + r*C elements (in place), otherwise it must not overlap any
  *        input or output
  * Errors: DDP_ENOTDIVISIBLE when n % p != 0, plus those of

@@ -37,3 +37,33 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, what=""):
 def tokens_for(p: int, seed: int = 0):
     rng = np.random.default_rng(seed + 17 * p)
     return [int(v) for v in rng.integers(10, 10001, size=p)]
+
+
+def make_grads(p, sizes, seed, bf16, oracle, layout="aligned"):
+    """Per-rank gradients as views into one arena per rank.
+
+    layout: "aligned" (every view starts on a 32-byte boundary), "odd" (views
+    at odd element offsets, the same on every rank) or "mixed" (each rank
+    shifted differently, so ranks disagree on the 16-byte phase)."""
+    from bucketed_gradient_all_ddp_amd import workloads as W
+
+    host = [[W.normal_np(n, 1.0, seed, r, stream=i) for i, n in enumerate(sizes)]
+            for r in range(p)]
+    if bf16:
+        host = [[oracle.f32_to_bf16(g) for g in rank] for rank in host]
+    dt = torch.bfloat16 if bf16 else torch.float32
+    grads = []
+    for r in range(p):
+        total = sum(sizes) + 9 * len(sizes) + 16
+        arena = torch.zeros(total, dtype=dt, device="cuda")
+        off = {"aligned": 0, "odd": 1, "mixed": r % 3 + 1}[layout]
+        views = []
+        for i, n in enumerate(sizes):
+            if layout == "aligned":
+                off = (off + 7) // 8 * 8
+            v = arena[off:off + n]
+            v.copy_(to_dev(host[r][i]))
+            views.append(v)
+            off += n + (0 if layout == "aligned" else 1)
+        grads.append(views)
+    return host, grads

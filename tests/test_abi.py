@@ -163,3 +163,31 @@ def test_collective_argument_errors():
     assert L.broadcast_sim(ins, 4, 1000, 4, 0, None, None) == 2
     assert L.broadcast_sim(ins, 4, 1000, -1, 0, None, None) == 2
     assert L.ddp_strerror(5) == b"element count not divisible by the number of ranks"
+
+
+def test_segment_table_sizes():
+    """Pieces of (parameter x ring chunk): at least one per non-empty
+    parameter, at most that plus p - 1 per bucket."""
+    sizes = [5000, 0, 7, 4096, 4097, 1, 33_333, 12, 0, 65_545]
+    plan = ddp.ddp_bucket_plan(sizes, 4, 96 * 1024, 8 * 1024)
+    nonzero = sum(1 for s in sizes if s)
+    for p in (1, 2, 3, 8, 64):
+        nseg = plan.segment_bytes(p) // 32
+        assert plan.segment_bytes(p) % 32 == 0
+        assert nonzero <= nseg <= nonzero + plan.num_buckets * (p - 1)
+    assert plan.segment_bytes(1) // 32 == nonzero
+    assert plan.segment_bytes(0) == 0 and plan.segment_bytes(65) == 0
+
+
+def test_bucket_allreduce_argument_errors():
+    L = load_library()
+    plan = ddp.ddp_bucket_plan([100, 200], 4, 1024, 256)
+    fake = ctypes.c_void_p(0x100000000)
+    # no piece table yet
+    assert L.ddp_allreduce_bucket(plan.handle, 0, 4, fake, 0, 0, None, None, None) == 6
+    assert L.ddp_allreduce_bucket(plan.handle, 5, 4, fake, 0, 0, None, None, None) == 2
+    assert L.ddp_allreduce_bucket(plan.handle, 0, 0, fake, 0, 0, None, None, None) == 2
+    assert L.ddp_allreduce_bucket(None, 0, 4, fake, 0, 0, None, None, None) == 1
+    assert L.ddp_plan_upload_segments(plan.handle, 4, None, 0, None) == 1
+    assert L.ddp_time_next_call(fake, None) == 1
+    assert L.ddp_time_next_call(None, None) == 0

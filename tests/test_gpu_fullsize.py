@@ -1,0 +1,269 @@
+"""GPU parity at the workloads' full sizes.
+
+- GPT-2 small (124M fp32 per rank, p=8): every element of every rank is
+  compared with the oracle's flatten -> literal ring -> unflatten, for the
+  in-place bucket all-reduce, the three-kernel path and the ring-step path.
+- Llama-7B (6.7G bf16 per rank, p=8, 108 GB resident), the latency regime
+  (20,000 tensors, p=64) and the 2 GiB x 64 cost-model shape: sampled
+  elements (random ones plus every chunk's first and last element) are
+  checked bit for bit against the oracle's per-element ring fold, whose
+  equality with the literal ring is pinned on the CPU; every rank must hold
+  identical bits at every sample.
+Inputs are drawn on the GPU and the sampled inputs copied to the host before
+any kernel of the library runs.
+"""
+import bisect
+
+import numpy as np
+import pytest
+import torch
+
+import bucketed_gradient_all_ddp_amd as ddp
+from bucketed_gradient_all_ddp_amd import workloads as W
+from helpers import assert_bits_equal, to_host
+
+pytestmark = pytest.mark.gpu
+
+GiB = 1 << 30
+
+
+def _need(nbytes):
+    free, total = torch.cuda.mem_get_info()
+    if total < nbytes * 1.1:
+        pytest.skip(f"needs {nbytes / GiB:.0f} GiB of device memory")
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _arenas(p, sizes, sigma, seed, dtype, align=64):
+    """One arena per rank, parameters in registration order, each at an
+    `align`-element boundary. Drawn in fp32 pieces and cast."""
+    offs, off = [], 0
+    for n in sizes:
+        offs.append(off)
+        off += (n + align - 1) // align * align
+    arenas = []
+    piece = 1 << 28
+    for r in range(p):
+        a = torch.empty(off, dtype=dtype, device="cuda")
+        for k, lo in enumerate(range(0, off, piece)):
+            hi = min(off, lo + piece)
+            a[lo:hi].copy_(W.normal_torch(hi - lo, sigma, seed, r, "cuda", stream=k))
+        arenas.append(a)
+    grads = [[a[o:o + n] for o, n in zip(offs, sizes)] for a in arenas]
+    return arenas, offs, grads
+
+
+def _samples(n, p, k, rng):
+    """k random indices of [0, n) plus the first and last element of every
+    chunk of ceil(n/p)."""
+    C = -(-n // p)
+    edges = [v for c in range(p) for v in (c * C, min((c + 1) * C, n) - 1) if c * C < n]
+    idx = np.concatenate([rng.integers(0, n, size=k), np.array(edges, dtype=np.int64)])
+    return np.unique(idx)
+
+
+def _gather(bufs, idx_np):
+    idx = torch.from_numpy(idx_np).to("cuda")
+    return np.stack([to_host(b[idx]) for b in bufs], axis=1)
+
+
+class _BucketIndex:
+    """Maps (bucket, flat index) to the arena index of the element."""
+
+    def __init__(self, oplan, offs):
+        self.oplan, self.offs = oplan, offs
+        self.starts, self.params = [], []
+        for b in range(oplan.num_buckets):
+            ps = oplan.bucket_params(b)
+            self.params.append(ps)
+            self.starts.append([int(oplan.offset[i]) for i in ps])
+
+    def arena_index(self, b, flat):
+        out = np.empty(len(flat), dtype=np.int64)
+        for k, i in enumerate(flat):
+            j = bisect.bisect_right(self.starts[b], int(i)) - 1
+            prm = self.params[b][j]
+            out[k] = self.offs[prm] + int(i) - self.starts[b][j]
+        return out
+
+
+# ---------------------------------------------------------------------------
+
+def test_gpt2_small_full_compare(oracle):
+    cfg = W.WORKLOADS["gpt2-small-p8"]
+    p = cfg["p"]
+    sizes = [W.numel(s) for _, s in cfg["params"]]
+    _need(3 * p * sum(sizes) * 4)
+    plan = ddp.ddp_bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    plan.upload().upload_segments(p)
+    oplan = oracle.bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    assert plan.buckets() == oplan.buckets() and plan.num_buckets == 13
+    arenas, offs, grads = _arenas(p, sizes, cfg["sigma"], cfg["seed"], torch.float32)
+    host = [[to_host(g) for g in rank] for rank in grads]
+    want = [[g.copy() for g in rank] for rank in host]
+    for b in range(oplan.num_buckets):
+        flats = [oracle.flatten(want[r], oplan, b) for r in range(p)]
+        red, _ = oracle.ring_allreduce(flats, avg="world", want_log=False)
+        for r in range(p):
+            oracle.unflatten(red[r], oplan, b, want[r])
+        del flats, red
+    table = ddp.grad_pointer_table(grads)
+    for path in ("inplace", "copy-fused", "copy-ring"):
+        for r in range(p):
+            for i, g in enumerate(grads[r]):
+                g.copy_(torch.from_numpy(host[r][i]))
+        for b in range(plan.num_buckets):
+            if path == "inplace":
+                ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
+            else:
+                bufs = [torch.empty(plan.bucket_numel(b), device="cuda") for _ in range(p)]
+                ddp.ddp_flatten(plan, b, table, bufs)
+                ddp.ring_allreduce_sim(bufs, avg="world", algo=path.split("-")[1])
+                ddp.ddp_unflatten(plan, b, bufs, table)
+                del bufs
+        torch.cuda.synchronize()
+        for r in range(p):
+            got = to_host(arenas[r])
+            for i, n in enumerate(sizes):
+                assert_bits_equal(got[offs[i]:offs[i] + n], want[r][i], f"{path} rank {r} param {i}")
+    del arenas, grads, host, want
+    _free()
+
+
+def test_llama7b_bf16_sampled(oracle):
+    cfg = W.WORKLOADS["llama7b-bf16-p8"]
+    p = cfg["p"]
+    sizes = [W.numel(s) for _, s in cfg["params"]]
+    _need(p * sum(sizes) * 2 + 8 * GiB)
+    plan = ddp.ddp_bucket_plan(sizes, 2, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    plan.upload().upload_segments(p)
+    oplan = oracle.bucket_plan(sizes, 2, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    assert plan.num_buckets == 226 and plan.buckets() == oplan.buckets()
+    arenas, offs, grads = _arenas(p, sizes, cfg["sigma"], cfg["seed"], torch.bfloat16)
+    table = ddp.grad_pointer_table(grads)
+    index = _BucketIndex(oplan, offs)
+    rng = np.random.default_rng(3)
+    picks = []
+    for b in range(plan.num_buckets):
+        flat = _samples(plan.bucket_numel(b), p, 256, rng)
+        ai = index.arena_index(b, flat)
+        picks.append((b, flat, ai, _gather(arenas, ai)))
+    for b in range(plan.num_buckets):
+        ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
+    torch.cuda.synchronize()
+    for b, flat, ai, vals in picks:
+        want = oracle.allreduce_at(vals, flat, plan.bucket_numel(b), avg="world")
+        got = _gather(arenas, ai)
+        for r in range(p):
+            assert_bits_equal(got[:, r], want, f"bucket {b} rank {r}")
+        s = oracle.bf16_to_f32(vals).astype(np.float64).sum(1) / p
+        y = oracle.bf16_to_f32(want).astype(np.float64)
+        scale = np.abs(oracle.bf16_to_f32(vals)).astype(np.float64).sum(1) / p
+        assert np.all(np.abs(y - s) <= 1e-2 * np.abs(s) + (p - 1) * 2.0 ** -24 * scale + 1e-45)
+    del arenas, grads
+    _free()
+
+
+def test_latency_regime_per_tensor_and_bucketed(oracle):
+    cfg = W.WORKLOADS["latency-p64"]
+    p = cfg["p"]
+    sizes = cfg["sizes"]
+    _need(p * sum(sizes) * 4 + 4 * GiB)
+    rng = np.random.default_rng(4)
+    # per-tensor: each tensor is its own all-reduce (own padding and chunks)
+    arenas, offs, grads = _arenas(p, sizes, 1.0, cfg["seed"], torch.float32)
+    check = sorted(set(rng.choice(len(sizes), 60, replace=False).tolist())
+                   | {int(np.argmin(sizes)), int(np.argmax(sizes))})
+    before = {i: [to_host(grads[r][i]) for r in range(p)] for i in check}
+    for i in range(len(sizes)):
+        ddp.ring_allreduce_sim([grads[r][i] for r in range(p)], avg="world")
+    torch.cuda.synchronize()
+    for i in check:
+        want, _ = oracle.ring_allreduce(before[i], avg="world", want_log=False)
+        for r in range(p):
+            assert_bits_equal(to_host(grads[r][i]), want[r], f"tensor {i} rank {r}")
+    del arenas, grads, before
+    _free()
+    # bucketed, in place
+    plan = ddp.ddp_bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    plan.upload_segments(p)
+    oplan = oracle.bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    assert plan.buckets() == oplan.buckets()
+    arenas, offs, grads = _arenas(p, sizes, 1.0, cfg["seed"] + 100, torch.float32)
+    table = ddp.grad_pointer_table(grads)
+    index = _BucketIndex(oplan, offs)
+    picks = []
+    for b in range(plan.num_buckets):
+        flat = _samples(plan.bucket_numel(b), p, 512, rng)
+        ai = index.arena_index(b, flat)
+        picks.append((b, flat, ai, _gather(arenas, ai)))
+    for b in range(plan.num_buckets):
+        ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
+    torch.cuda.synchronize()
+    for b, flat, ai, vals in picks:
+        want = oracle.allreduce_at(vals, flat, plan.bucket_numel(b), avg="world")
+        got = _gather(arenas, ai)
+        for r in range(p):
+            assert_bits_equal(got[:, r], want, f"bucket {b} rank {r}")
+    del arenas, grads
+    _free()
+
+
+def test_cost_model_shape_p64_2gib(oracle):
+    cfg = W.WORKLOADS["cost-model-p64"]
+    p, n = cfg["p"], cfg["n"]
+    _need(p * n * 4 + 4 * GiB)
+    tokens = W.token_counts(p, cfg["seed"])
+    bufs = [W.normal_torch(n, 1.0, cfg["seed"], r, "cuda") for r in range(p)]
+    rng = np.random.default_rng(5)
+    C = n // p
+    idx = _samples(n, p, 4096, rng)
+    vals = _gather(bufs, idx)
+
+    # token-weighted all-reduce, fused
+    ddp.ring_allreduce_sim(bufs, avg="tokens", tokens=tokens)
+    torch.cuda.synchronize()
+    want = oracle.allreduce_at(vals, idx, n, avg="tokens", tokens=tokens)
+    got = _gather(bufs, idx)
+    for r in range(p):
+        assert_bits_equal(got[:, r], want, f"all-reduce rank {r}")
+
+    # standalone reduce-scatter (pre-rotated), on fresh values
+    for r in range(p):
+        W.normal_torch(n, 1.0, cfg["seed"] + 1, r, "cuda", out=bufs[r])
+    vals = _gather(bufs, idx)
+    outs = [torch.empty(C, device="cuda") for _ in range(p)]
+    ddp.reduce_scatter_sim(bufs, outs, avg="tokens", tokens=tokens)
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter_at(vals, idx, n, avg="tokens", tokens=tokens)
+    for k, i in enumerate(idx):
+        owner, pos = int(i) // C, int(i) % C
+        got = to_host(outs[owner][pos:pos + 1])
+        assert_bits_equal(got, want[k:k + 1], f"reduce-scatter element {i}")
+
+    # all-gather in place: shard r of rank r's buffer is its contribution
+    for r in range(p):
+        bufs[r][r * C:(r + 1) * C].copy_(outs[r])
+    shards = [bufs[r][r * C:(r + 1) * C] for r in range(p)]
+    ddp.allgather_sim(shards, bufs)
+    torch.cuda.synchronize()
+    got = _gather(bufs, idx)
+    for k, i in enumerate(idx):
+        owner, pos = int(i) // C, int(i) % C
+        expect = to_host(outs[owner][pos:pos + 1])[0]
+        assert np.all(got[k].view(np.uint32) == np.float32(expect).view(np.uint32))
+
+    # broadcast from rank 0 of fresh values
+    W.normal_torch(n, 1.0, cfg["seed"] + 2, 0, "cuda", out=bufs[0])
+    src = _gather(bufs[:1], idx)[:, 0]
+    ddp.broadcast_sim(bufs, src=0)
+    torch.cuda.synchronize()
+    got = _gather(bufs, idx)
+    for r in range(p):
+        assert_bits_equal(got[:, r], src, f"broadcast rank {r}")
+    del bufs, outs
+    _free()
