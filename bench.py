@@ -4,11 +4,13 @@ set, p = 8 simulated ranks in one GPU's HBM.
 
 A step is one pass of the whole path over every bucket of the plan: the
 bucket's flatten, ring all-reduce averaged over p, and unflatten back into
-each rank's per-parameter gradients. The headline ("inplace") step does the
-three in one kernel per bucket (ddp_allreduce_bucket: same bits, one pass
-over HBM); the "copy" step runs them as three kernels per bucket
-(ddp_flatten, ring_allreduce_sim, ddp_unflatten) and is reported next to it.
-The plan is built once before timing, as the reducer does at construction.
+each rank's per-parameter gradients. The headline ("batched") step does the
+three in place in one kernel launch covering all buckets
+(ddp_allreduce_buckets: same bits, one pass over HBM); "inplace" launches
+that kernel once per bucket; "copy" runs the three as three kernels per
+bucket (ddp_flatten, ring_allreduce_sim, ddp_unflatten). All three are
+timed and reported. The plan is built once before timing, as the reducer
+does at construction.
 
 Output: one JSON line. `value` is the all-reduce bus bandwidth of the whole
 step, S * 2(p-1)/p / t_step (S = gradient bytes per rank). `roofline` is for
@@ -35,6 +37,38 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "all-reduce bus GB/s + % HBM peak, p=8 sim ranks, 124M fp32 grads"
 
+# Device-memory traffic per launch of a kernel, from the two rocprofv3 --pmc
+# passes (FETCH_SIZE, WRITE_SIZE; scaled by a 1 GiB copy) summarised in
+# profiles/. A figure is used only while the kernel's sources hash to the
+# value it was measured with; after any change it is reported as null until
+# the counters are taken again.
+CSRC = os.path.join(ROOT, "bucketed_gradient_all_ddp_amd", "csrc")
+KERNEL_SOURCES = {
+    "bucket_allreduce_kernel": ["bucket_allreduce.hip", "fold.hpp", "internal.hpp"],
+    "fused_allreduce_kernel": ["allreduce.hip", "fold.hpp", "internal.hpp"],
+}
+MEASURED_TRAFFIC = {}
+
+
+def sources_sha256(kernel: str):
+    import hashlib
+
+    files = KERNEL_SOURCES.get(kernel)
+    if not files:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    m = MEASURED_TRAFFIC.get(kernel)
+    if m is None or m["sources_sha256"] != sources_sha256(kernel):
+        return None
+    return m["bytes_per_launch"]
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -45,9 +79,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="inplace", choices=["inplace", "copy"],
-                    help="headline step: one kernel per bucket, or flatten + "
-                         "all-reduce + unflatten as three")
+    ap.add_argument("--mode", default="batched", choices=["batched", "inplace", "copy"],
+                    help="headline step: one launch for all buckets "
+                         "(ddp_allreduce_buckets), one launch per bucket "
+                         "(ddp_allreduce_bucket), or flatten + all-reduce + "
+                         "unflatten as three launches per bucket")
     ap.add_argument("--algo", default="fused", choices=["fused", "ring"],
                     help="all-reduce algorithm of the copy step")
     ap.add_argument("--no-compare", action="store_true",
@@ -100,6 +136,12 @@ def run_steps(ddp, wl, mode, algo, steps, timer, ws):
     rec = []
     plan, p, table = wl.plan, wl.p, wl.table
     for _ in range(steps):
+        if mode == "batched":
+            k = timer.arm() if timer else None
+            st = ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg="world")
+            if timer:
+                rec.append(("bucket_allreduce_kernel", st.hbm_bytes, k))
+            continue
         for b in range(plan.num_buckets):
             if mode == "inplace":
                 k = timer.arm() if timer else None
@@ -127,7 +169,8 @@ def run_steps(ddp, wl, mode, algo, steps, timer, ws):
 def timed(torch, ddp, wl, mode, algo, steps, warmup, ws):
     run_steps(ddp, wl, mode, algo, warmup, None, ws)
     torch.cuda.synchronize()
-    per_step_calls = wl.plan.num_buckets * (1 if mode == "inplace" else 3)
+    per_step_calls = {"batched": 1, "inplace": wl.plan.num_buckets,
+                      "copy": 3 * wl.plan.num_buckets}[mode]
     timer = ddp.CallTimer(pairs=per_step_calls * steps)
     t0 = time.perf_counter()
     rec = run_steps(ddp, wl, mode, algo, steps, timer, ws)
@@ -210,7 +253,7 @@ def main():
     p, S = wl.p, wl.S
     ws = {}
     modes = [args.mode] + ([] if args.no_compare else
-                           [m for m in ("inplace", "copy") if m != args.mode])
+                           [m for m in ("batched", "inplace", "copy") if m != args.mode])
     if "copy" in modes:
         wl.ensure_bucket_buffers(torch, dev)
         if args.algo == "ring":
@@ -231,7 +274,7 @@ def main():
     dominant = max(kernels.items(), key=lambda kv: kv[1]["ms"])
     dname, d = dominant
     bus = S * 2 * (p - 1) / p / (ms * 1e-3) / 1e9
-    step_bytes = 2 * p * S if args.mode == "inplace" else 6 * p * S
+    step_bytes = 6 * p * S if args.mode == "copy" else 2 * p * S
     result = {
         "metric": METRIC,
         "value": round(bus, 2),
@@ -250,9 +293,11 @@ def main():
                          "rank, p=8 simulated ranks, 25 MiB buckets + 1 MiB first bucket "
                          "(13 buckets), average by p; step = flatten + ring all-reduce + "
                          "unflatten of every bucket"),
-            "step_kernels": ("one ddp_allreduce_bucket per bucket" if args.mode == "inplace"
-                             else f"ddp_flatten + ring_allreduce_sim({args.algo}) + "
-                                  "ddp_unflatten per bucket"),
+            "step_kernels": {
+                "batched": "one ddp_allreduce_buckets launch covering all 13 buckets",
+                "inplace": "one ddp_allreduce_bucket launch per bucket",
+                "copy": f"ddp_flatten + ring_allreduce_sim({args.algo}) + ddp_unflatten "
+                        "per bucket"}[args.mode],
             "p": p, "buckets": wl.plan.num_buckets, "bytes_per_rank": S,
         },
         "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -264,7 +309,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dname),
             "avg_launch_us": d["avg_us"],
             "bytes_per_launch": d["bytes"] // d["launches"],
         },

@@ -9,7 +9,8 @@ the seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
     ALGO, AVG, DTYPE_BF16, DTYPE_F32, EXPORTS, MAX_RANKS, CallTimer, CommStats, DDPError, Plan,
-    allgather_sim, broadcast_sim, ddp_allreduce_bucket, ddp_bucket_plan, ddp_flatten,
+    allgather_sim, broadcast_sim, ddp_allreduce_bucket, ddp_allreduce_buckets, ddp_bucket_plan,
+    ddp_flatten,
     ddp_unflatten,
     grad_pointer_table, load_library, reduce_scatter_sim, ring_allreduce_sim,
     ring_allreduce_sim_steps, ring_allreduce_sim_workspace,

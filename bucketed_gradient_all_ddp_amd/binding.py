@@ -36,6 +36,7 @@ EXPORTS = [
     "ddp_plan_param_bucket", "ddp_plan_param_offset", "ddp_plan_device_bytes",
     "ddp_plan_upload", "ddp_flatten", "ddp_unflatten",
     "ddp_plan_segment_bytes", "ddp_plan_upload_segments", "ddp_allreduce_bucket",
+    "ddp_allreduce_buckets",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
 ]
@@ -70,6 +71,10 @@ def load_library(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own HIP runtime; loading it first makes this library
+    # bind to that same runtime (one runtime per process, shared streams).
+    import torch  # noqa: F401
+
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
@@ -98,6 +103,7 @@ def load_library(path: str = LIB_PATH):
         "ddp_plan_segment_bytes": ([vp, i32], sz),
         "ddp_plan_upload_segments": ([vp, i32, vp, sz, vp], st),
         "ddp_allreduce_bucket": ([vp, i32, i32, vp, i32, i32, vp, vp, vp], st),
+        "ddp_allreduce_buckets": ([vp, i32, i32, i32, vp, i32, i32, vp, vp, vp], st),
         "ring_allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, vp, sz, vp, vp], st),
         "ring_allreduce_sim_workspace": ([i32, i64, i32, i32], sz),
         "ring_allreduce_sim_steps": ([vp, i32, i64, i32, vp, i32, i32, vp], st),
@@ -336,6 +342,21 @@ def ddp_allreduce_bucket(plan: Plan, bucket: int, grad_table, p: int, dtype=None
     _check(load_library().ddp_allreduce_bucket(
         plan.handle, bucket, p, grad_table.data_ptr(), code, AVG[avg], _tokens(tokens, p),
         _stream(stream), ctypes.byref(st)), "ddp_allreduce_bucket")
+    return st
+
+
+def ddp_allreduce_buckets(plan: Plan, first_bucket: int, n_buckets: int, grad_table, p: int,
+                          dtype=None, avg: str = "none", tokens=None, stream=None) -> CommStats:
+    """ddp_allreduce_bucket for a run of consecutive buckets, one launch."""
+    import torch
+
+    if dtype is None:
+        dtype = torch.float32 if plan.elem_bytes == 4 else torch.bfloat16
+    code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
+    st = CommStats()
+    _check(load_library().ddp_allreduce_buckets(
+        plan.handle, first_bucket, n_buckets, p, grad_table.data_ptr(), code, AVG[avg],
+        _tokens(tokens, p), _stream(stream), ctypes.byref(st)), "ddp_allreduce_buckets")
     return st
 
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void fused_allreduce_kernel(
       vi[u] = k.vs / V + j;
     }
     float acc[VPT][V];
-    fold_vectors<Tr, VPT, RB>(TablePtrs{bufs}, p, c, vi, ok, acc);
+    fold_vectors<Tr, VPT, RB, kNT>(TablePtrs{bufs}, p, c, vi, ok, acc);
     uint4 y[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
@@ -204,15 +204,17 @@ __global__ __launch_bounds__(kThreads) void bf16_workspace_kernel(
 #ifndef DDPSIM_FUSED_RB
 #define DDPSIM_FUSED_RB 8  // rank loads issued before their additions
 #endif
-#ifndef DDPSIM_FUSED_NT
-#define DDPSIM_FUSED_NT 0  // non-temporal stores
+#ifndef DDPSIM_FUSED_NT_BYTES
+// Rank buffers larger than this in total use non-temporal loads and stores.
+// Smaller ones may still sit in the 256 MB Infinity Cache (a bucket that
+// ddp_flatten has just written, say), where ordinary accesses are faster.
+#define DDPSIM_FUSED_NT_BYTES (int64_t(256) << 20)
 #endif
 #ifndef DDPSIM_FUSED_WAVES
 #define DDPSIM_FUSED_WAVES 0  // >0: cap the grid at this many workgroups per CU
 #endif
 constexpr int kFusedVpt = DDPSIM_FUSED_VPT;
 constexpr int kFusedRb = DDPSIM_FUSED_RB;
-constexpr bool kFusedNt = DDPSIM_FUSED_NT != 0;
 constexpr int kStepVpt = 4;
 
 int32_t device_cus() {
@@ -243,14 +245,22 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
     blocks = std::min<int64_t>(blocks, int64_t(device_cus()) * DDPSIM_FUSED_WAVES);
   }
   const dim3 grid(static_cast<uint32_t>(blocks));
+  const char *kname = "fused_allreduce_kernel launch";
+  const bool nt = int64_t(p) * n * elem_bytes_of(dtype) > DDPSIM_FUSED_NT_BYTES;
   if (dtype == DDP_F32) {
-    return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, kFusedNt>, grid,
-                  dim3(kThreads), stream, timer, true, "fused_allreduce_kernel launch",
-                  tab, p, n, C, tpc, div);
+    if (nt) {
+      return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, true>, grid,
+                    dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
+    }
+    return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false>, grid,
+                  dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
   }
-  return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, kFusedNt>, grid,
-                dim3(kThreads), stream, timer, true, "fused_allreduce_kernel launch",
-                tab, p, n, C, tpc, div);
+  if (nt) {
+    return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, true>, grid,
+                  dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
+  }
+  return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false>, grid,
+                dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
 }
 
 // Launch ring steps [first, first + count) on fp32 buffers.

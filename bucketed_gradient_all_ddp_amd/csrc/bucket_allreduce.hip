@@ -21,19 +21,26 @@
 #include "internal.hpp"
 
 namespace ddpsim {
+int32_t plan_num_buckets(const ddp_plan *plan);
 bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t *count,
-                       int32_t *tiles, int64_t *elems, const void **table, int32_t *seg_p,
-                       int32_t *n_params, int32_t *elem_bytes);
+                       int32_t *tiles, int32_t *tile_first, int64_t *elems,
+                       const void **table, int32_t *seg_p, int32_t *n_params,
+                       int32_t *elem_bytes);
 
 namespace {
 
-template <typename Tr, int VPT, int RB>
+// Workgroup w handles tile tile_base + w of the plan's numbering; the pieces
+// seg[0..nseg) are those of the launched buckets, in order.
+template <typename Tr, int VPT, int RB, bool kNT>
 __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
-    const SegDesc *__restrict__ seg, int32_t nseg, int32_t n_params,
+    const SegDesc *__restrict__ seg, int32_t nseg, int32_t tile_base, int32_t n_params,
     const void *const *__restrict__ grads, int32_t p, Divide div) {
   constexpr int V = Tr::kVec;
   constexpr int64_t kElemBytes = sizeof(typename Tr::elem);
-  const int32_t tile = static_cast<int32_t>(blockIdx.x);
+  const int32_t tile =
+      tile_base + static_cast<int32_t>(DDPSIM_BUCKET_XCD
+                                           ? xcd_contiguous(blockIdx.x, gridDim.x)
+                                           : static_cast<int64_t>(blockIdx.x));
   int32_t lo = 0, hi = nseg - 1;
   while (lo < hi) {
     const int32_t mid = (lo + hi + 1) >> 1;
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
     vi[u] = k.vs / V + jj;
   }
   float acc[VPT][V];
-  fold_vectors<Tr, VPT, RB>(at, p, d.chunk, vi, ok, acc);
+  fold_vectors<Tr, VPT, RB, kNT>(at, p, d.chunk, vi, ok, acc);
   uint4 y[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
     void *dst = at(r);
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      if (ok[u]) store_vec<false>(dst, vi[u], y[u]);
+      if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);
     }
   }
 }
@@ -119,25 +126,42 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
 
 using namespace ddpsim;
 
-extern "C" ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket, int32_t p,
-                                           void *const *d_grad_ptrs, int32_t dtype,
-                                           int32_t avg_mode, const int64_t *tokens,
-                                           hipStream_t stream, ddp_comm_stats *stats) {
+extern "C" ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_bucket,
+                                            int32_t n_buckets, int32_t p,
+                                            void *const *d_grad_ptrs, int32_t dtype,
+                                            int32_t avg_mode, const int64_t *tokens,
+                                            hipStream_t stream, ddp_comm_stats *stats) {
   clear_error();
   CallTimer timer = CallTimer::take();
-  const char *what = "ddp_allreduce_bucket";
+  const char *what = "ddp_allreduce_buckets";
   if (plan == nullptr) return fail(DDP_EINVAL, "%s: plan is NULL", what);
-  int32_t first, count, tiles, seg_p, n_params, eb_plan;
-  int64_t elems;
-  const void *table;
-  if (!plan_segment_info(plan, bucket, &first, &count, &tiles, &elems, &table, &seg_p,
-                         &n_params, &eb_plan)) {
-    return fail(DDP_ERANGE, "%s: bucket %d out of range", what, bucket);
+  const int32_t nbk = plan_num_buckets(plan);
+  if (n_buckets < 1 || first_bucket < 0 || first_bucket >= nbk ||
+      n_buckets > nbk - first_bucket) {
+    return fail(DDP_ERANGE, "%s: buckets [%d, %d) outside [0, %d)", what, first_bucket,
+                first_bucket + n_buckets, nbk);
   }
   ddp_status s = check_p(p, what);
   if (s != DDP_OK) return s;
-  if (seg_p != p) {
-    return fail(DDP_ENOTREADY, "%s: call ddp_plan_upload_segments with p=%d first", what, p);
+  int32_t seg0 = 0, nseg = 0, tiles = 0, tile0 = 0, seg_p = 0, n_params = 0, eb_plan = 0;
+  int64_t elems = 0;
+  const void *table = nullptr;
+  int64_t C_sum = 0;
+  for (int32_t b = first_bucket; b < first_bucket + n_buckets; ++b) {
+    int32_t f, c, t, tf;
+    int64_t e;
+    plan_segment_info(plan, b, &f, &c, &t, &tf, &e, &table, &seg_p, &n_params, &eb_plan);
+    if (seg_p != p) {
+      return fail(DDP_ENOTREADY, "%s: call ddp_plan_upload_segments with p=%d first", what, p);
+    }
+    if (b == first_bucket) {
+      seg0 = f;
+      tile0 = tf;
+    }
+    nseg += c;
+    tiles += t;
+    elems += e;
+    C_sum += e > 0 ? ceil_div(e, p) : 0;
   }
   const int eb = elem_bytes_of(dtype);
   if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
@@ -151,24 +175,37 @@ extern "C" ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket,
   s = make_divide(avg_mode, p, tokens, &div);
   if (s != DDP_OK) return s;
   if (stats != nullptr) {
-    const int64_t C = elems > 0 ? ceil_div(elems, p) : 0;
-    stats->steps = 2 * int64_t(p - 1);
-    stats->messages = 2 * int64_t(p) * (p - 1);
-    stats->bytes_sent_per_rank = 2 * int64_t(p - 1) * C * 4;
+    // one ring all-reduce per bucket
+    stats->steps = 2 * int64_t(p - 1) * n_buckets;
+    stats->messages = 2 * int64_t(p) * (p - 1) * n_buckets;
+    stats->bytes_sent_per_rank = 2 * int64_t(p - 1) * C_sum * 4;
     stats->bytes_recv_per_rank = stats->bytes_sent_per_rank;
-    stats->total_bytes = stats->messages * C * 4;
+    stats->total_bytes = 2 * int64_t(p) * (p - 1) * C_sum * 4;
     stats->hbm_bytes = 2 * int64_t(p) * elems * eb;
   }
   if (tiles == 0) return DDP_OK;
-  const SegDesc *seg = static_cast<const SegDesc *>(table) + first;
+  const SegDesc *seg = static_cast<const SegDesc *>(table) + seg0;
   const void *const *grads = d_grad_ptrs;
   const dim3 grid(static_cast<uint32_t>(tiles));
   if (dtype == DDP_F32) {
-    return launch(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb>, grid,
+    return launch(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                   dim3(kThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
-                  count, n_params, grads, p, div);
+                  nseg, tile0, n_params, grads, p, div);
   }
-  return launch(bucket_allreduce_kernel<BF16Traits, kBucketVpt, kBucketRb>, grid,
+  return launch(bucket_allreduce_kernel<BF16Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                 dim3(kThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
-                count, n_params, grads, p, div);
+                nseg, tile0, n_params, grads, p, div);
+}
+
+extern "C" ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket, int32_t p,
+                                           void *const *d_grad_ptrs, int32_t dtype,
+                                           int32_t avg_mode, const int64_t *tokens,
+                                           hipStream_t stream, ddp_comm_stats *stats) {
+  if (plan != nullptr && (bucket < 0 || bucket >= plan_num_buckets(plan))) {
+    clear_error();
+    CallTimer::take();
+    return fail(DDP_ERANGE, "ddp_allreduce_bucket: bucket %d out of range", bucket);
+  }
+  return ddp_allreduce_buckets(plan, bucket, 1, p, d_grad_ptrs, dtype, avg_mode, tokens,
+                               stream, stats);
 }

@@ -53,13 +53,13 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(
       vi[u] = static_cast<int64_t>(c) * nv + j;
     }
     float acc[VPT][V];
-    fold_vectors<Tr, VPT, RB>(TablePtrs{in}, p, first, vi, ok, acc);
+    fold_vectors<Tr, VPT, RB, true>(TablePtrs{in}, p, first, vi, ok, acc);
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       if (!ok[u]) continue;
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
-      store_vec<false>(dst, vi[u] - static_cast<int64_t>(c) * nv, Tr::narrow(acc[u]));
+      store_vec<true>(dst, vi[u] - static_cast<int64_t>(c) * nv, Tr::narrow(acc[u]));
     }
   } else {
     // Element-wise path for shards that are not a whole number of vectors.

@@ -42,8 +42,8 @@ struct GradPtrs {
 
 // Fold VPT 16-byte vectors (vector indices vi[u], valid where ok[u]) over
 // the p ranks in ring order starting at `first`. RB rank loads are issued
-// before their additions.
-template <typename Tr, int VPT, int RB, typename Ptrs>
+// before their additions; kNT makes them non-temporal.
+template <typename Tr, int VPT, int RB, bool kNT, typename Ptrs>
 __device__ __forceinline__ void fold_vectors(const Ptrs &ptr_of, int32_t p,
                                              int32_t first,
                                              const int64_t (&vi)[VPT],
@@ -62,7 +62,7 @@ __device__ __forceinline__ void fold_vectors(const Ptrs &ptr_of, int32_t p,
       const void *src = ptr_of(live ? ring_rank(first, s0 + j, p) : 0);
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        x[j][u] = (live && ok[u]) ? load_vec(src, vi[u]) : make_uint4(0, 0, 0, 0);
+        x[j][u] = (live && ok[u]) ? load_vec<kNT>(src, vi[u]) : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll

@@ -62,8 +62,26 @@ struct SegDesc {
 };
 static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 
-constexpr int kBucketVpt = 2;  // vectors per thread per bucket-all-reduce tile
+#ifndef DDPSIM_BUCKET_NT
+#define DDPSIM_BUCKET_NT 1  // non-temporal loads and stores
+#endif
+#ifndef DDPSIM_BUCKET_VPT
+#define DDPSIM_BUCKET_VPT 2  // 16-byte vectors per thread per tile
+#endif
+#ifndef DDPSIM_BUCKET_XCD
+#define DDPSIM_BUCKET_XCD 0  // 1: give each XCD a contiguous range of tiles
+#endif
+constexpr int kBucketVpt = DDPSIM_BUCKET_VPT;
 constexpr int kBucketRb = 8;
+constexpr bool kBucketNt = DDPSIM_BUCKET_NT != 0;
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD
+// b % 8). This bijection on [0, G) hands XCD x the contiguous block of
+// tiles [x q + min(x, r), ...), q = G / 8, r = G % 8.
+__host__ __device__ inline int64_t xcd_contiguous(int64_t b, int64_t G) {
+  const int64_t q = G / 8, r = G % 8, x = b % 8, k = b / 8;
+  return x * q + (x < r ? x : r) + k;
+}
 // elements per tile for a dtype whose 16-byte vector holds `vec` elements
 constexpr int64_t bucket_tile_elems(int vec) { return int64_t(kThreads) * kBucketVpt * vec; }
 
@@ -208,20 +226,31 @@ struct BF16Traits {
   }
 };
 
+// 16-byte accesses. The non-temporal forms mark the access as streaming
+// (no reuse expected), which on gfx950 lets the memory system sustain more
+// bandwidth when many independent streams are read and written at once.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kNonTemporal = false>
 __device__ __forceinline__ uint4 load_vec(const void *base, int64_t v) {
-  return static_cast<const uint4 *>(base)[v];
+  const u32x4 *p = static_cast<const u32x4 *>(base) + v;
+  u32x4 x;
+  if constexpr (kNonTemporal) {
+    x = __builtin_nontemporal_load(p);
+  } else {
+    x = *p;
+  }
+  return make_uint4(x.x, x.y, x.z, x.w);
 }
 
 template <bool kNonTemporal>
 __device__ __forceinline__ void store_vec(void *base, int64_t v, uint4 x) {
-  uint4 *p = static_cast<uint4 *>(base) + v;
+  u32x4 *p = static_cast<u32x4 *>(base) + v;
+  const u32x4 y = {x.x, x.y, x.z, x.w};
   if constexpr (kNonTemporal) {
-    __builtin_nontemporal_store(x.x, &p->x);
-    __builtin_nontemporal_store(x.y, &p->y);
-    __builtin_nontemporal_store(x.z, &p->z);
-    __builtin_nontemporal_store(x.w, &p->w);
+    __builtin_nontemporal_store(y, p);
   } else {
-    *p = x;
+    *p = y;
   }
 }
 

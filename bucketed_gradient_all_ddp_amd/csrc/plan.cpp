@@ -34,7 +34,7 @@ struct ddp_plan {
   // seg_p ranks
   int32_t seg_p = 0;
   std::vector<SegDesc> seg;
-  std::vector<int32_t> seg_first, seg_count, seg_tiles;
+  std::vector<int32_t> seg_first, seg_count, seg_tiles, seg_tile_first;
   void *d_seg = nullptr;
 };
 
@@ -59,9 +59,14 @@ bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
   return true;
 }
 
+int32_t plan_num_buckets(const ddp_plan *plan) {
+  return plan ? static_cast<int32_t>(plan->members.size()) : 0;
+}
+
 bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t *count,
-                       int32_t *tiles, int64_t *elems, const void **table, int32_t *seg_p,
-                       int32_t *n_params, int32_t *elem_bytes) {
+                       int32_t *tiles, int32_t *tile_first, int64_t *elems,
+                       const void **table, int32_t *seg_p, int32_t *n_params,
+                       int32_t *elem_bytes) {
   if (plan == nullptr || b < 0 || b >= static_cast<int32_t>(plan->members.size())) {
     return false;
   }
@@ -71,26 +76,31 @@ bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t 
   *elem_bytes = plan->elem_bytes;
   *table = plan->d_seg;
   if (plan->seg_p == 0) {
-    *first = *count = *tiles = 0;
+    *first = *count = *tiles = *tile_first = 0;
     return true;
   }
   *first = plan->seg_first[b];
   *count = plan->seg_count[b];
   *tiles = plan->seg_tiles[b];
+  *tile_first = plan->seg_tile_first[b];
   return true;
 }
 
 // Cut every bucket into pieces that lie in one parameter and one ring chunk
-// (chunks of ceil(n_b / p) elements of the bucket's flat index space).
+// (chunks of ceil(n_b / p) elements of the bucket's flat index space). Tiles
+// are numbered across the whole plan, bucket after bucket, so one launch can
+// cover a run of consecutive buckets.
 static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc> *seg,
                            std::vector<int32_t> *first, std::vector<int32_t> *count,
-                           std::vector<int32_t> *tiles) {
+                           std::vector<int32_t> *tiles, std::vector<int32_t> *tile_first) {
   const int64_t tile_elems = bucket_tile_elems(kVecBytes / plan->elem_bytes);
+  int64_t t = 0;
   for (size_t b = 0; b < plan->members.size(); ++b) {
     first->push_back(static_cast<int32_t>(seg->size()));
+    tile_first->push_back(static_cast<int32_t>(t));
+    const int64_t t0 = t;
     const int64_t nb = plan->bucket_elems[b];
     const int64_t C = nb > 0 ? ceil_div(nb, p) : 1;
-    int64_t t = 0;
     for (int32_t i : plan->members[b]) {
       const int64_t o = plan->offset[i];
       const int64_t end = o + plan->numel[i];
@@ -111,7 +121,7 @@ static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc>
     }
     if (t > INT32_MAX) return false;
     count->push_back(static_cast<int32_t>(seg->size()) - first->back());
-    tiles->push_back(static_cast<int32_t>(t));
+    tiles->push_back(static_cast<int32_t>(t - t0));
   }
   return true;
 }
@@ -121,8 +131,8 @@ static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc>
 extern "C" size_t ddp_plan_segment_bytes(const ddp_plan *plan, int32_t p) {
   if (plan == nullptr || p < 1 || p > kMaxRanks) return 0;
   std::vector<SegDesc> seg;
-  std::vector<int32_t> f, c, t;
-  if (!build_segments(plan, p, &seg, &f, &c, &t)) return 0;
+  std::vector<int32_t> f, c, t, tf;
+  if (!build_segments(plan, p, &seg, &f, &c, &t, &tf)) return 0;
   return seg.size() * sizeof(SegDesc);
 }
 
@@ -133,8 +143,8 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
   ddp_status s = check_p(p, "ddp_plan_upload_segments");
   if (s != DDP_OK) return s;
   std::vector<SegDesc> seg;
-  std::vector<int32_t> first, count, tiles;
-  if (!build_segments(plan, p, &seg, &first, &count, &tiles)) {
+  std::vector<int32_t> first, count, tiles, tile_first;
+  if (!build_segments(plan, p, &seg, &first, &count, &tiles, &tile_first)) {
     return fail(DDP_EINVAL, "ddp_plan_upload_segments: a bucket is too large");
   }
   const size_t need = seg.size() * sizeof(SegDesc);
@@ -152,6 +162,7 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
   plan->seg_first.swap(first);
   plan->seg_count.swap(count);
   plan->seg_tiles.swap(tiles);
+  plan->seg_tile_first.swap(tile_first);
   if (need > 0) {
     s = check_hip(hipMemcpyAsync(d_table, plan->seg.data(), need, hipMemcpyHostToDevice,
                                  stream),

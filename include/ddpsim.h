@@ -246,6 +246,20 @@ ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket,
                                 const int64_t *tokens, hipStream_t stream,
                                 ddp_comm_stats *stats);
 
+/* ddp_allreduce_bucket for the run of buckets [first_bucket,
+ * first_bucket + n_buckets) in one kernel launch: the reducer fires every
+ * consecutive ready bucket starting at its next bucket ([DDP] Part 2 "Step
+ * 2: backward", item 3), and one dispatch for the run avoids a kernel
+ * boundary per bucket. Each bucket keeps its own ring chunks; the result is
+ * bit-identical to calling ddp_allreduce_bucket on each. Stats add up the
+ * buckets' ring schedules. Errors: as ddp_allreduce_bucket, DDP_ERANGE for
+ * an empty or out-of-range run. */
+ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_bucket,
+                                 int32_t n_buckets, int32_t p,
+                                 void *const *d_grad_ptrs, int32_t dtype,
+                                 int32_t avg_mode, const int64_t *tokens,
+                                 hipStream_t stream, ddp_comm_stats *stats);
+
 /* ----------------------------------------------------------------------- */
 /* Ring all-reduce                                                         */
 /* ----------------------------------------------------------------------- */

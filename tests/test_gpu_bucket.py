@@ -73,3 +73,32 @@ def test_bucket_allreduce_needs_segments_for_p():
         ddp.ddp_allreduce_bucket(plan, 0, table, 4)
     with pytest.raises(ddp.DDPError, match="ERANGE"):
         ddp.ddp_allreduce_bucket(plan, 9, table, 3)
+
+
+@pytest.mark.parametrize("p", [2, 8])
+def test_bucket_run_in_one_launch_equals_per_bucket(oracle, p):
+    """ddp_allreduce_buckets over every run of buckets gives the bits of one
+    ddp_allreduce_bucket per bucket (and of the oracle)."""
+    cap, first = 64 * 1024, 8 * 1024
+    plan = ddp.ddp_bucket_plan(SIZES, 4, cap, first).upload_segments(p)
+    nb = plan.num_buckets
+    assert nb >= 3
+    host, grads = make_grads(p, SIZES, 990 + p, False, oracle, "aligned")
+    table = ddp.grad_pointer_table(grads)
+    # runs: [0, 1), [1, nb-1), [nb-1, nb)
+    runs = [(0, 1), (1, nb - 2), (nb - 1, 1)]
+    total = 0
+    for b0, k in runs:
+        st = ddp.ddp_allreduce_buckets(plan, b0, k, table, p, avg="world")
+        total += st.hbm_bytes
+        assert st.steps == 2 * (p - 1) * k
+    assert total == 2 * p * sum(SIZES) * 4
+    torch.cuda.synchronize()
+    want = _oracle_sync(oracle, host, SIZES, 4, cap, first, "world", None)
+    for r in range(p):
+        for i in range(len(SIZES)):
+            assert_bits_equal(to_host(grads[r][i]), want[r][i], f"rank {r} param {i}")
+    with pytest.raises(ddp.DDPError, match="ERANGE"):
+        ddp.ddp_allreduce_buckets(plan, nb - 1, 2, table, p)
+    with pytest.raises(ddp.DDPError, match="ERANGE"):
+        ddp.ddp_allreduce_buckets(plan, 0, 0, table, p)

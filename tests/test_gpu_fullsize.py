@@ -27,6 +27,10 @@ pytestmark = pytest.mark.gpu
 GiB = 1 << 30
 
 
+def _say(msg):
+    print(f"[fullsize] {msg}", flush=True)
+
+
 def _need(nbytes):
     free, total = torch.cuda.mem_get_info()
     if total < nbytes * 1.1:
@@ -103,6 +107,7 @@ def test_gpt2_small_full_compare(oracle):
     oplan = oracle.bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
     assert plan.buckets() == oplan.buckets() and plan.num_buckets == 13
     arenas, offs, grads = _arenas(p, sizes, cfg["sigma"], cfg["seed"], torch.float32)
+    _say("gpt2: inputs drawn; running the oracle")
     host = [[to_host(g) for g in rank] for rank in grads]
     want = [[g.copy() for g in rank] for rank in host]
     for b in range(oplan.num_buckets):
@@ -113,6 +118,7 @@ def test_gpt2_small_full_compare(oracle):
         del flats, red
     table = ddp.grad_pointer_table(grads)
     for path in ("inplace", "copy-fused", "copy-ring"):
+        _say(f"gpt2: {path}")
         for r in range(p):
             for i, g in enumerate(grads[r]):
                 g.copy_(torch.from_numpy(host[r][i]))
@@ -144,6 +150,7 @@ def test_llama7b_bf16_sampled(oracle):
     oplan = oracle.bucket_plan(sizes, 2, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
     assert plan.num_buckets == 226 and plan.buckets() == oplan.buckets()
     arenas, offs, grads = _arenas(p, sizes, cfg["sigma"], cfg["seed"], torch.bfloat16)
+    _say("llama7b: inputs drawn (%.1f GB)" % (p * sum(sizes) * 2 / 1e9))
     table = ddp.grad_pointer_table(grads)
     index = _BucketIndex(oplan, offs)
     rng = np.random.default_rng(3)
@@ -152,9 +159,11 @@ def test_llama7b_bf16_sampled(oracle):
         flat = _samples(plan.bucket_numel(b), p, 256, rng)
         ai = index.arena_index(b, flat)
         picks.append((b, flat, ai, _gather(arenas, ai)))
+    _say("llama7b: samples taken; all-reducing 226 buckets")
     for b in range(plan.num_buckets):
         ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
     torch.cuda.synchronize()
+    _say("llama7b: checking")
     for b, flat, ai, vals in picks:
         want = oracle.allreduce_at(vals, flat, plan.bucket_numel(b), avg="world")
         got = _gather(arenas, ai)
@@ -179,6 +188,7 @@ def test_latency_regime_per_tensor_and_bucketed(oracle):
     check = sorted(set(rng.choice(len(sizes), 60, replace=False).tolist())
                    | {int(np.argmin(sizes)), int(np.argmax(sizes))})
     before = {i: [to_host(grads[r][i]) for r in range(p)] for i in check}
+    _say("latency: per-tensor all-reduce of 20,000 tensors")
     for i in range(len(sizes)):
         ddp.ring_allreduce_sim([grads[r][i] for r in range(p)], avg="world")
     torch.cuda.synchronize()
@@ -189,6 +199,7 @@ def test_latency_regime_per_tensor_and_bucketed(oracle):
     del arenas, grads, before
     _free()
     # bucketed, in place
+    _say("latency: bucketed")
     plan = ddp.ddp_bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
     plan.upload_segments(p)
     oplan = oracle.bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
@@ -225,6 +236,7 @@ def test_cost_model_shape_p64_2gib(oracle):
     vals = _gather(bufs, idx)
 
     # token-weighted all-reduce, fused
+    _say("cost-model shape: all-reduce of 64 x 2 GiB")
     ddp.ring_allreduce_sim(bufs, avg="tokens", tokens=tokens)
     torch.cuda.synchronize()
     want = oracle.allreduce_at(vals, idx, n, avg="tokens", tokens=tokens)
@@ -237,6 +249,7 @@ def test_cost_model_shape_p64_2gib(oracle):
         W.normal_torch(n, 1.0, cfg["seed"] + 1, r, "cuda", out=bufs[r])
     vals = _gather(bufs, idx)
     outs = [torch.empty(C, device="cuda") for _ in range(p)]
+    _say("cost-model shape: reduce-scatter, all-gather, broadcast")
     ddp.reduce_scatter_sim(bufs, outs, avg="tokens", tokens=tokens)
     torch.cuda.synchronize()
     want = oracle.reduce_scatter_at(vals, idx, n, avg="tokens", tokens=tokens)
