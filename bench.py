@@ -4,12 +4,12 @@ set, p = 8 simulated ranks in one GPU's HBM.
 
 A step is one pass of the whole path over every bucket of the plan: the
 bucket's flatten, ring all-reduce averaged over p, and unflatten back into
-each rank's per-parameter gradients. The headline ("batched") step does the
-three in place in one kernel launch covering all buckets
-(ddp_allreduce_buckets: same bits, one pass over HBM); "inplace" launches
-that kernel once per bucket; "copy" runs the three as three kernels per
-bucket (ddp_flatten, ring_allreduce_sim, ddp_unflatten). All three are
-timed and reported. The plan is built once before timing, as the reducer
+each rank's per-parameter gradients. The headline ("inplace") step does the
+three in place, one kernel launch per bucket (ddp_allreduce_bucket: same
+bits, one pass over HBM); "batched" covers all buckets with one launch
+(ddp_allreduce_buckets); "copy" runs the three as three kernels per bucket
+(ddp_flatten, ring_allreduce_sim, ddp_unflatten). All three are timed and
+reported. The plan is built once before timing, as the reducer
 does at construction.
 
 Output: one JSON line. `value` is the all-reduce bus bandwidth of the whole
@@ -79,10 +79,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="batched", choices=["batched", "inplace", "copy"],
-                    help="headline step: one launch for all buckets "
-                         "(ddp_allreduce_buckets), one launch per bucket "
-                         "(ddp_allreduce_bucket), or flatten + all-reduce + "
+    ap.add_argument("--mode", default="inplace", choices=["batched", "inplace", "copy"],
+                    help="headline step: one launch per bucket "
+                         "(ddp_allreduce_bucket), one launch for all buckets "
+                         "(ddp_allreduce_buckets), or flatten + all-reduce + "
                          "unflatten as three launches per bucket")
     ap.add_argument("--algo", default="fused", choices=["fused", "ring"],
                     help="all-reduce algorithm of the copy step")
@@ -253,7 +253,7 @@ def main():
     p, S = wl.p, wl.S
     ws = {}
     modes = [args.mode] + ([] if args.no_compare else
-                           [m for m in ("batched", "inplace", "copy") if m != args.mode])
+                           [m for m in ("inplace", "batched", "copy") if m != args.mode])
     if "copy" in modes:
         wl.ensure_bucket_buffers(torch, dev)
         if args.algo == "ring":

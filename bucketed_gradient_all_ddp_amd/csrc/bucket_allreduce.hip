@@ -22,6 +22,7 @@
 
 namespace ddpsim {
 int32_t plan_num_buckets(const ddp_plan *plan);
+const int32_t *plan_tile_map(const ddp_plan *plan);
 bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t *count,
                        int32_t *tiles, int32_t *tile_first, int64_t *elems,
                        const void **table, int32_t *seg_p, int32_t *n_params,
@@ -29,28 +30,20 @@ bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t 
 
 namespace {
 
-// Workgroup w handles tile tile_base + w of the plan's numbering; the pieces
-// seg[0..nseg) are those of the launched buckets, in order.
+// Workgroup w handles tile tile_base + w of the plan's numbering; the tile
+// map names the piece (index into seg) each tile belongs to.
 template <typename Tr, int VPT, int RB, bool kNT>
 __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
-    const SegDesc *__restrict__ seg, int32_t nseg, int32_t tile_base, int32_t n_params,
-    const void *const *__restrict__ grads, int32_t p, Divide div) {
+    const SegDesc *__restrict__ seg, const int32_t *__restrict__ tile_seg,
+    int32_t tile_base, int32_t n_params, const void *const *__restrict__ grads,
+    int32_t p, Divide div) {
   constexpr int V = Tr::kVec;
   constexpr int64_t kElemBytes = sizeof(typename Tr::elem);
   const int32_t tile =
       tile_base + static_cast<int32_t>(DDPSIM_BUCKET_XCD
                                            ? xcd_contiguous(blockIdx.x, gridDim.x)
                                            : static_cast<int64_t>(blockIdx.x));
-  int32_t lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (seg[mid].tile_begin <= tile) {
-      lo = mid;
-    } else {
-      hi = mid - 1;
-    }
-  }
-  const SegDesc d = seg[lo];
+  const SegDesc d = seg[tile_seg[tile]];
   const int32_t t = tile - d.tile_begin;
   const int tid = static_cast<int>(threadIdx.x);
   constexpr int64_t kTile = int64_t(kThreads) * VPT * V;
@@ -184,17 +177,20 @@ extern "C" ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_
     stats->hbm_bytes = 2 * int64_t(p) * elems * eb;
   }
   if (tiles == 0) return DDP_OK;
-  const SegDesc *seg = static_cast<const SegDesc *>(table) + seg0;
+  (void)seg0;
+  (void)nseg;
+  const SegDesc *seg = static_cast<const SegDesc *>(table);
+  const int32_t *tile_seg = plan_tile_map(plan);
   const void *const *grads = d_grad_ptrs;
   const dim3 grid(static_cast<uint32_t>(tiles));
   if (dtype == DDP_F32) {
     return launch(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                   dim3(kThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
-                  nseg, tile0, n_params, grads, p, div);
+                  tile_seg, tile0, n_params, grads, p, div);
   }
   return launch(bucket_allreduce_kernel<BF16Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                 dim3(kThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
-                nseg, tile0, n_params, grads, p, div);
+                tile_seg, tile0, n_params, grads, p, div);
 }
 
 extern "C" ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket, int32_t p,

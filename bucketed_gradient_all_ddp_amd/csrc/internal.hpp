@@ -66,7 +66,7 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #define DDPSIM_BUCKET_NT 1  // non-temporal loads and stores
 #endif
 #ifndef DDPSIM_BUCKET_VPT
-#define DDPSIM_BUCKET_VPT 2  // 16-byte vectors per thread per tile
+#define DDPSIM_BUCKET_VPT 1  // 16-byte vectors per thread per tile
 #endif
 #ifndef DDPSIM_BUCKET_XCD
 #define DDPSIM_BUCKET_XCD 0  // 1: give each XCD a contiguous range of tiles

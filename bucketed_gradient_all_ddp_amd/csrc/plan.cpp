@@ -35,6 +35,8 @@ struct ddp_plan {
   int32_t seg_p = 0;
   std::vector<SegDesc> seg;
   std::vector<int32_t> seg_first, seg_count, seg_tiles, seg_tile_first;
+  std::vector<unsigned char> seg_staged;  // host copy of the device table
+  size_t seg_bytes = 0;                   // the tile map starts here
   void *d_seg = nullptr;
 };
 
@@ -61,6 +63,12 @@ bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
 
 int32_t plan_num_buckets(const ddp_plan *plan) {
   return plan ? static_cast<int32_t>(plan->members.size()) : 0;
+}
+
+const int32_t *plan_tile_map(const ddp_plan *plan) {
+  if (plan == nullptr || plan->d_seg == nullptr) return nullptr;
+  return reinterpret_cast<const int32_t *>(static_cast<const char *>(plan->d_seg) +
+                                           plan->seg_bytes);
 }
 
 bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t *count,
@@ -92,7 +100,8 @@ bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t 
 // cover a run of consecutive buckets.
 static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc> *seg,
                            std::vector<int32_t> *first, std::vector<int32_t> *count,
-                           std::vector<int32_t> *tiles, std::vector<int32_t> *tile_first) {
+                           std::vector<int32_t> *tiles, std::vector<int32_t> *tile_first,
+                           std::vector<int32_t> *tile_seg) {
   const int64_t tile_elems = bucket_tile_elems(kVecBytes / plan->elem_bytes);
   int64_t t = 0;
   for (size_t b = 0; b < plan->members.size(); ++b) {
@@ -114,7 +123,11 @@ static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc>
         d.param = i;
         d.chunk = static_cast<int32_t>(c);
         d.tile_begin = static_cast<int32_t>(t);
-        t += std::max<int64_t>(1, ceil_div(d.len, tile_elems));
+        const int64_t nt = std::max<int64_t>(1, ceil_div(d.len, tile_elems));
+        t += nt;
+        if (t > INT32_MAX) return false;
+        tile_seg->insert(tile_seg->end(), static_cast<size_t>(nt),
+                         static_cast<int32_t>(seg->size()));
         seg->push_back(d);
         pos = piece_end;
       }
@@ -131,9 +144,9 @@ static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc>
 extern "C" size_t ddp_plan_segment_bytes(const ddp_plan *plan, int32_t p) {
   if (plan == nullptr || p < 1 || p > kMaxRanks) return 0;
   std::vector<SegDesc> seg;
-  std::vector<int32_t> f, c, t, tf;
-  if (!build_segments(plan, p, &seg, &f, &c, &t, &tf)) return 0;
-  return seg.size() * sizeof(SegDesc);
+  std::vector<int32_t> f, c, t, tf, ts;
+  if (!build_segments(plan, p, &seg, &f, &c, &t, &tf, &ts)) return 0;
+  return seg.size() * sizeof(SegDesc) + ts.size() * sizeof(int32_t);
 }
 
 extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *d_table,
@@ -143,11 +156,14 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
   ddp_status s = check_p(p, "ddp_plan_upload_segments");
   if (s != DDP_OK) return s;
   std::vector<SegDesc> seg;
-  std::vector<int32_t> first, count, tiles, tile_first;
-  if (!build_segments(plan, p, &seg, &first, &count, &tiles, &tile_first)) {
+  std::vector<int32_t> first, count, tiles, tile_first, tile_seg;
+  if (!build_segments(plan, p, &seg, &first, &count, &tiles, &tile_first, &tile_seg)) {
     return fail(DDP_EINVAL, "ddp_plan_upload_segments: a bucket is too large");
   }
-  const size_t need = seg.size() * sizeof(SegDesc);
+  // Device layout: the pieces, then one int32 per tile naming its piece.
+  // Both parts are staged in one host buffer that the plan keeps alive.
+  const size_t seg_bytes = seg.size() * sizeof(SegDesc);
+  const size_t need = seg_bytes + tile_seg.size() * sizeof(int32_t);
   if (need > 0) {
     if (d_table == nullptr || bytes < need) {
       return fail(DDP_EINVAL, "ddp_plan_upload_segments: needs %zu bytes of device memory",
@@ -157,15 +173,21 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
       return fail(DDP_EALIGN, "ddp_plan_upload_segments: table is not 16-byte aligned");
     }
   }
-  // The plan keeps the host copy alive for the asynchronous upload.
+  std::vector<unsigned char> staged(need);
+  if (need > 0) {
+    std::memcpy(staged.data(), seg.data(), seg_bytes);
+    std::memcpy(staged.data() + seg_bytes, tile_seg.data(), need - seg_bytes);
+  }
   plan->seg.swap(seg);
   plan->seg_first.swap(first);
   plan->seg_count.swap(count);
   plan->seg_tiles.swap(tiles);
   plan->seg_tile_first.swap(tile_first);
+  plan->seg_staged.swap(staged);
+  plan->seg_bytes = seg_bytes;
   if (need > 0) {
-    s = check_hip(hipMemcpyAsync(d_table, plan->seg.data(), need, hipMemcpyHostToDevice,
-                                 stream),
+    s = check_hip(hipMemcpyAsync(d_table, plan->seg_staged.data(), need,
+                                 hipMemcpyHostToDevice, stream),
                   "ddp_plan_upload_segments: hipMemcpyAsync");
     if (s != DDP_OK) {
       plan->seg_p = 0;

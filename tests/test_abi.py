@@ -166,16 +166,18 @@ def test_collective_argument_errors():
 
 
 def test_segment_table_sizes():
-    """Pieces of (parameter x ring chunk): at least one per non-empty
-    parameter, at most that plus p - 1 per bucket."""
+    """The piece table holds 32 bytes per piece of (parameter x ring chunk) --
+    at least one per non-empty parameter, at most that plus p - 1 per
+    bucket -- and 4 bytes per tile (at least one tile per piece)."""
     sizes = [5000, 0, 7, 4096, 4097, 1, 33_333, 12, 0, 65_545]
     plan = ddp.ddp_bucket_plan(sizes, 4, 96 * 1024, 8 * 1024)
     nonzero = sum(1 for s in sizes if s)
     for p in (1, 2, 3, 8, 64):
-        nseg = plan.segment_bytes(p) // 32
-        assert plan.segment_bytes(p) % 32 == 0
-        assert nonzero <= nseg <= nonzero + plan.num_buckets * (p - 1)
-    assert plan.segment_bytes(1) // 32 == nonzero
+        nbytes = plan.segment_bytes(p)
+        assert nbytes % 4 == 0
+        assert 36 * nonzero <= nbytes
+        assert nbytes <= 36 * (nonzero + plan.num_buckets * (p - 1)) + 4 * sum(sizes)
+    assert plan.segment_bytes(2) >= plan.segment_bytes(1)
     assert plan.segment_bytes(0) == 0 and plan.segment_bytes(65) == 0
 
 
