@@ -47,7 +47,13 @@ KERNEL_SOURCES = {
     "bucket_allreduce_kernel": ["bucket_allreduce.hip", "fold.hpp", "internal.hpp"],
     "fused_allreduce_kernel": ["allreduce.hip", "fold.hpp", "internal.hpp"],
 }
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: mean over the 13 buckets
+    "bucket_allreduce_kernel": {
+        "bytes_per_launch": 613317852,
+        "sources_sha256": "263f4cd06d0ab078a11e8cad7fd145aff3b0fefe43cdaf56cd847b13e3761f07",
+    },
+}
 
 
 def sources_sha256(kernel: str):
@@ -93,6 +99,11 @@ def parse():
                     help="buckets in the CPU-baseline sample (0 = all)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also time a plain device copy of this many MiB")
+    ap.add_argument("--workload", default="gpt2-small-p8",
+                    choices=["gpt2-small-p8", "ragged-ring-p4", "llama7b-bf16-p8",
+                             "latency-p64", "cost-model-p64"],
+                    help="the default is the headline; the others print their own "
+                         "line for the record")
     return ap.parse_args()
 
 
@@ -232,6 +243,194 @@ def cpu_baseline(W, wl, n_buckets_wanted):
     }
 
 
+# ---------------------------------------------------------------------------
+# Other workloads (not the headline): one JSON line each
+# ---------------------------------------------------------------------------
+
+def _events_ms(torch, fn, reps):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _timed_calls(torch, ddp, calls, reps):
+    """Each call once per rep, every call's kernels timed by dispatch events.
+    Returns (host wall ms per rep, device ms per rep)."""
+    timer = ddp.CallTimer(pairs=len(calls) * reps)
+    ids = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for c in calls:
+            ids.append(timer.arm())
+            c()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    dev = sum(timer.elapsed_ms(k) for k in ids) / reps
+    return wall, dev
+
+
+def _line(metric, value, unit, workload, extra):
+    d = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+         "higher_is_better": True, "data": "synthetic", "config": {"workload": workload}}
+    d.update(extra)
+    print(json.dumps(d), flush=True)
+
+
+def bench_ragged(torch, ddp, W, dev, args):
+    cfg = W.WORKLOADS["ragged-ring-p4"]
+    p, n = cfg["p"], cfg["n"]
+    bufs = [W.normal_torch(n, 1.0, cfg["seed"], r, dev) for r in range(p)]
+    out = {}
+    for algo in ("fused", "ring"):
+        for _ in range(args.warmup):
+            ddp.ring_allreduce_sim(bufs, avg="world", algo=algo)
+        wall, dms = _timed_calls(torch, ddp, [lambda: ddp.ring_allreduce_sim(
+            bufs, avg="world", algo=algo)], args.steps)
+        S = n * 4
+        st = ddp.ring_allreduce_sim(bufs, avg="world", algo=algo)
+        out[algo] = {"device_us": round(dms * 1e3, 2), "wall_us": round(wall * 1e3, 2),
+                     "bus_GBps": round(S * 2 * (p - 1) / p / (dms * 1e-3) / 1e9, 1),
+                     "hbm_GBps": round(st.hbm_bytes / (dms * 1e-3) / 1e9, 1),
+                     "launches": 1 if algo == "fused" else 2 * (p - 1)}
+    _line("all-reduce bus GB/s, p=4, 1,000,003 fp32 per rank", out["fused"]["bus_GBps"], "GB/s",
+          "ragged ring: one 1,000,003-element fp32 tensor per rank, p=4, average by p",
+          {"algorithms": out})
+
+
+def bench_llama(torch, ddp, W, dev, args):
+    cfg = W.WORKLOADS["llama7b-bf16-p8"]
+    p = cfg["p"]
+    sizes = [W.numel(s) for _, s in cfg["params"]]
+    plan = ddp.ddp_bucket_plan(sizes, 2, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    plan.upload_segments(p, dev)
+    offs, off = [], 0
+    for n in sizes:
+        offs.append(off)
+        off += (n + 127) // 128 * 128
+    arenas = []
+    for r in range(p):
+        a = torch.empty(off, dtype=torch.bfloat16, device=dev)
+        piece = 1 << 28
+        for k, lo in enumerate(range(0, off, piece)):
+            hi = min(off, lo + piece)
+            a[lo:hi].copy_(W.normal_torch(hi - lo, cfg["sigma"], cfg["seed"], r, dev, stream=k))
+        arenas.append(a)
+    grads = [[a[o:o + n] for o, n in zip(offs, sizes)] for a in arenas]
+    table = ddp.grad_pointer_table(grads, dev)
+    calls = [lambda b=b: ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
+             for b in range(plan.num_buckets)]
+    for _ in range(max(1, args.warmup // 2)):
+        for c in calls:
+            c()
+    reps = max(2, args.steps // 4)
+    wall, dms = _timed_calls(torch, ddp, calls, reps)
+    S = sum(sizes) * 2
+    hbm = 2 * p * S
+    _line("all-reduce bus GB/s, p=8, Llama-7B bf16 grads", S * 2 * (p - 1) / p / (wall * 1e-3) / 1e9,
+          "GB/s", "llama-7b gradients: 291 bf16 tensors, 6,738,415,616 elements per rank, p=8, "
+                  "226 buckets (25 MiB / 1 MiB), fp32 accumulation, average by p; step = one "
+                  "ddp_allreduce_bucket per bucket",
+          {"ms_per_step": round(wall, 3), "kernel_ms_per_step": round(dms, 3),
+           "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
+           "kernel_frac_of_8TBps": round(hbm / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "dtype": "bf16 (fp32 accumulate)", "steps": reps})
+
+
+def bench_latency(torch, ddp, W, dev, args):
+    cfg = W.WORKLOADS["latency-p64"]
+    p, sizes = cfg["p"], cfg["sizes"]
+    offs, off = [], 0
+    for n in sizes:
+        offs.append(off)
+        off += (n + 63) // 64 * 64
+    arenas = [W.normal_torch(off, 1.0, cfg["seed"], r, dev) for r in range(p)]
+    grads = [[a[o:o + n] for o, n in zip(offs, sizes)] for a in arenas]
+    per_tensor = [[grads[r][i] for r in range(p)] for i in range(len(sizes))]
+    S = sum(sizes) * 4
+    hbm = 2 * p * S
+
+    def tensor_step():
+        for bufs in per_tensor:
+            ddp.ring_allreduce_sim(bufs, avg="world")
+
+    tensor_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tensor_step()
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3
+    # the same 20,000 launches replayed from a captured HIP graph
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tensor_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tensor_step()
+    g.replay()
+    torch.cuda.synchronize()
+    graph_ms = _events_ms(torch, g.replay, 3)
+    del g
+    plan = ddp.ddp_bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    plan.upload_segments(p, dev)
+    table = ddp.grad_pointer_table(grads, dev)
+    calls = [lambda b=b: ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
+             for b in range(plan.num_buckets)]
+    for c in calls:
+        c()
+    wall, dms = _timed_calls(torch, ddp, calls, 5)
+    _line("all-reduce step time, p=64, 20,000 tensors: bucketed vs per-tensor",
+          graph_ms / wall, "x (per-tensor graph time / bucketed time)",
+          "latency regime: 20,000 fp32 tensors of 64..65,536 elements (189,015,250 per rank), "
+          "p=64, average by p",
+          {"per_tensor": {"launches": len(sizes), "host_loop_ms": round(host_ms, 2),
+                          "graph_replay_ms": round(graph_ms, 2),
+                          "graph_us_per_launch": round(graph_ms * 1e3 / len(sizes), 2),
+                          "hbm_GBps_graph": round(hbm / (graph_ms * 1e-3) / 1e9, 1)},
+           "bucketed": {"buckets": plan.num_buckets, "ms_per_step": round(wall, 3),
+                        "kernel_ms_per_step": round(dms, 3),
+                        "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1)}})
+
+
+def bench_costmodel(torch, ddp, W, dev, args):
+    cfg = W.WORKLOADS["cost-model-p64"]
+    p, n = cfg["p"], cfg["n"]
+    tokens = W.token_counts(p, cfg["seed"])
+    bufs = [W.normal_torch(n, 1.0, cfg["seed"], r, dev) for r in range(p)]
+    S = n * 4
+    C = n // p
+    outs = [torch.empty(C, device=dev) for _ in range(p)]
+    shards = [bufs[r][r * C:(r + 1) * C] for r in range(p)]
+    ops = {
+        "allreduce_tokens": (lambda: ddp.ring_allreduce_sim(bufs, avg="tokens", tokens=tokens),
+                             2 * (p - 1) / p, 2 * p * S),
+        "reduce_scatter": (lambda: ddp.reduce_scatter_sim(bufs, outs), (p - 1) / p, (p + 1) * S),
+        "allgather_inplace": (lambda: ddp.allgather_sim(shards, bufs), (p - 1) / p, p * S),
+        "broadcast": (lambda: ddp.broadcast_sim(bufs, src=0), 1.0, p * S),
+    }
+    res = {}
+    for name, (fn, busf, hbm) in ops.items():
+        fn()
+        wall, dms = _timed_calls(torch, ddp, [fn], 3)
+        res[name] = {"device_ms": round(dms, 3), "alg_GBps": round(S / (dms * 1e-3) / 1e9, 1),
+                     "bus_GBps": round(S * busf / (dms * 1e-3) / 1e9, 1),
+                     "hbm_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(hbm / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    _line("all-reduce bus GB/s, p=64, 2 GiB fp32 per rank, token-weighted",
+          res["allreduce_tokens"]["bus_GBps"], "GB/s",
+          "cost-model shape: one 2^29-element fp32 tensor per rank (2 GiB), p=64, tokens "
+          "U{10..10000}; plus reduce-scatter, in-place all-gather and broadcast",
+          {"ops": res})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -248,6 +447,12 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     ddp.load_library()
+    other = {"ragged-ring-p4": bench_ragged, "llama7b-bf16-p8": bench_llama,
+             "latency-p64": bench_latency, "cost-model-p64": bench_costmodel}
+    if args.workload in other:
+        log(f"workload {args.workload}")
+        other[args.workload](torch, ddp, W, dev, args)
+        return
     log("building workload")
     wl = Workload(torch, ddp, W, dev)
     p, S = wl.p, wl.S
