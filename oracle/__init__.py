@@ -104,6 +104,8 @@ def _load():
     lib.orc_bf16_to_f32_array.restype = None
     lib.orc_avg_divisor.argtypes = [i32, i32, P, P]
     lib.orc_avg_divisor.restype = ctypes.c_int
+    lib.orc_reducer_schedule.argtypes = [P, i32, i32, P, i32, P, P, P]
+    lib.orc_reducer_schedule.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -428,3 +430,27 @@ def reduce_scatter_at(vals: np.ndarray, index: np.ndarray, n: int,
     f = bf16_to_f32(vals) if vals.dtype == np.uint16 else vals
     out = _fold(f, start, p, avg_divisor(avg, p, tokens), avg != "none")
     return f32_to_bf16(out) if vals.dtype == np.uint16 else out
+
+
+# ---------------------------------------------------------------------------
+# Reducer schedule
+# ---------------------------------------------------------------------------
+
+def reducer_schedule(plan: Plan, order: Sequence[int]):
+    """Buckets launched by each ready mark, as (mark index, first bucket,
+    count) for every mark that launches something, and the total launched
+    (the number of buckets when every bucket became ready)."""
+    lib = _load()
+    o = np.ascontiguousarray(np.asarray(order, dtype=np.int32))
+    m = o.size
+    first = np.zeros(max(m, 1), dtype=np.int32)
+    count = np.zeros(max(m, 1), dtype=np.int32)
+    total = np.zeros(1, dtype=np.int32)
+    bucket_of = np.ascontiguousarray(plan.bucket_of, dtype=np.int32)
+    rc = lib.orc_reducer_schedule(_ptr(bucket_of) if bucket_of.size else None,
+                                  bucket_of.size, plan.num_buckets,
+                                  _ptr(o) if m else None, m, _ptr(first),
+                                  _ptr(count), _ptr(total))
+    _check(rc, "reducer_schedule")
+    runs = [(k, int(first[k]), int(count[k])) for k in range(m) if count[k] > 0]
+    return runs, int(total[0])

@@ -574,3 +574,60 @@ void orc_fold_samples(const float *vals, const int64_t *start, int32_t p,
     out[s] = do_divide ? acc / divisor : acc;
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Reducer schedule: when each bucket's all-reduce is launched             */
+/* ------------------------------------------------------------------------ */
+
+/* The reducer's readiness bookkeeping ("PyTorch DDP Deep Dive", Part 2
+ * "Step 2: backward"): every bucket starts with a pending count equal to
+ * its number of parameters. Marking a parameter ready decrements its
+ * bucket's count; when a count reaches zero and that bucket is the next one
+ * to reduce, the reducer launches it and keeps launching following buckets
+ * while they are complete too. A bucket that completes out of turn waits.
+ *
+ * Inputs: bucket_of[n_params]; n_buckets; order[n_marks] = parameters in the
+ * order they are marked ready.
+ * Outputs, per mark m: run_first[m], run_count[m] = the buckets launched by
+ * that mark (run_count 0 if none). *n_launched = buckets launched in all.
+ * Returns ORC_EINVAL if a parameter index is out of range or marked twice
+ * (the source asserts that a ready bucket is never at or behind the next one
+ * twice). */
+int orc_reducer_schedule(const int32_t *bucket_of, int32_t n_params,
+                         int32_t n_buckets, const int32_t *order,
+                         int32_t n_marks, int32_t *run_first,
+                         int32_t *run_count, int32_t *n_launched) {
+  if (n_params < 0 || n_buckets < 0 || n_marks < 0) return ORC_EINVAL;
+  int32_t *pending = (int32_t *)calloc((size_t)(n_buckets + 1), sizeof(int32_t));
+  char *seen = (char *)calloc((size_t)(n_params + 1), 1);
+  if (pending == NULL || seen == NULL) {
+    free(pending);
+    free(seen);
+    return ORC_ENOMEM;
+  }
+  for (int32_t i = 0; i < n_params; ++i) pending[bucket_of[i]] += 1;
+  int32_t next = 0;
+  int rc = ORC_OK;
+  for (int32_t m = 0; m < n_marks; ++m) {
+    run_first[m] = next;
+    run_count[m] = 0;
+    int32_t i = order[m];
+    if (i < 0 || i >= n_params || seen[i]) {
+      rc = ORC_EINVAL;
+      break;
+    }
+    seen[i] = 1;
+    int32_t b = bucket_of[i];
+    pending[b] -= 1;
+    if (pending[b] == 0 && b == next) {
+      while (next < n_buckets && pending[next] == 0) {
+        next += 1;
+        run_count[m] += 1;
+      }
+    }
+  }
+  *n_launched = next;
+  free(pending);
+  free(seen);
+  return rc;
+}
