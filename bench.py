@@ -101,9 +101,11 @@ def parse():
                     help="also time a plain device copy of this many MiB")
     ap.add_argument("--workload", default="gpt2-small-p8",
                     choices=["gpt2-small-p8", "ragged-ring-p4", "llama7b-bf16-p8",
-                             "latency-p64", "cost-model-p64"],
+                             "latency-p64", "cost-model-p64", "overlap-gpt2-p8"],
                     help="the default is the headline; the others print their own "
                          "line for the record")
+    ap.add_argument("--tokens", type=int, default=2048,
+                    help="tokens per synthetic backward GEMM (overlap workload)")
     return ap.parse_args()
 
 
@@ -431,6 +433,90 @@ def bench_costmodel(torch, ddp, W, dev, args):
           {"ops": res})
 
 
+def bench_overlap(torch, ddp, W, dev, args):
+    """Synthetic backward on one stream, bucket all-reduces on another,
+    launched by the reducer as parameters are marked ready."""
+    wl = Workload(torch, ddp, W, dev)
+    p, sizes, plan = wl.p, wl.sizes, wl.plan
+    params = wl.cfg["params"]
+    # gradient values the "backward" writes: a copy of the drawn gradients
+    sources = [a.clone() for a in wl.arenas]
+    offs, off = [], 0
+    for n in sizes:
+        offs.append(off)
+        off += (n + 63) // 64 * 64
+    src_views = [[s_[o:o + n] for o, n in zip(offs, sizes)] for s_ in sources]
+    # compute: per 2-D parameter (a, b) one bf16 GEMM [a, T] x [T, b], the
+    # shape of a weight gradient over T tokens
+    T = args.tokens
+    gemms = {}
+    for i, (_, shape) in enumerate(params):
+        if len(shape) == 2:
+            a, b = shape
+            gemms[i] = (torch.randn(a, T, device=dev, dtype=torch.bfloat16),
+                        torch.randn(T, b, device=dev, dtype=torch.bfloat16),
+                        torch.empty(a, b, device=dev, dtype=torch.bfloat16))
+    producer = torch.cuda.Stream()
+    comm = torch.cuda.Stream()
+    reducer = ddp.Reducer(plan, p, wl.table, avg="world", comm_stream=comm)
+    order = list(range(len(sizes)))[::-1]
+    events = [torch.cuda.Event() for _ in sizes]  # created once, re-recorded
+    dsts = [[wl.grads[r][i] for r in range(p)] for i in range(len(sizes))]
+    srcs = [[src_views[r][i] for r in range(p)] for i in range(len(sizes))]
+
+    def backward(mark):
+        with torch.cuda.stream(producer):
+            for i in order:
+                if i in gemms:
+                    A, B, O = gemms[i]
+                    torch.mm(A, B, out=O)
+                torch._foreach_copy_(dsts[i], srcs[i])
+                if mark:
+                    events[i].record(producer)
+                    reducer.mark_ready(i, events[i])
+
+    def run(kind):
+        cur = torch.cuda.current_stream()
+        producer.wait_stream(cur)
+        comm.wait_stream(cur)
+        if kind == "overlap":
+            reducer.prepare()
+            backward(True)
+            reducer.finalize(cur)
+            cur.wait_stream(producer)
+        else:
+            backward(False)
+            cur.wait_stream(producer)
+            if kind == "sequential":
+                for b in range(plan.num_buckets):
+                    ddp.ddp_allreduce_bucket(plan, b, wl.table, p, avg="world")
+
+    res = {}
+    for kind in ("backward_only", "sequential", "overlap"):
+        for _ in range(args.warmup):
+            run(kind)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run(kind)
+        torch.cuda.synchronize()
+        res[kind] = (time.perf_counter() - t0) * 1e3 / args.steps
+    gemm_flops = sum(2 * T * W.numel(params[i][1]) for i in gemms)
+    exposed_seq = res["sequential"] - res["backward_only"]
+    exposed_ovl = res["overlap"] - res["backward_only"]
+    _line("exposed all-reduce time per step, overlapped vs after backward",
+          exposed_ovl, "ms", "gpt2-small gradients, p=8: synthetic backward (per parameter "
+          f"in reverse order: a bf16 GEMM [a,{T}]x[{T},b] for each 2-D parameter, then its "
+          "gradients written for all ranks) on one stream; the reducer launches bucket "
+          "all-reduces on a second stream as parameters are marked ready",
+          {"higher_is_better": False,
+           "ms_per_step": {k: round(v, 3) for k, v in res.items()},
+           "exposed_ms": {"sequential": round(exposed_seq, 3), "overlap": round(exposed_ovl, 3)},
+           "hidden_fraction": round(1 - exposed_ovl / exposed_seq, 3) if exposed_seq > 0 else None,
+           "backward_gemm_tflop": round(gemm_flops / 1e12, 3),
+           "runs_per_pass": len(reducer.launch_log())})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -448,7 +534,8 @@ def main():
     dev = torch.device("cuda:0")
     ddp.load_library()
     other = {"ragged-ring-p4": bench_ragged, "llama7b-bf16-p8": bench_llama,
-             "latency-p64": bench_latency, "cost-model-p64": bench_costmodel}
+             "latency-p64": bench_latency, "cost-model-p64": bench_costmodel,
+             "overlap-gpt2-p8": bench_overlap}
     if args.workload in other:
         log(f"workload {args.workload}")
         other[args.workload](torch, ddp, W, dev, args)

@@ -9,6 +9,7 @@ the seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
     ALGO, AVG, DTYPE_BF16, DTYPE_F32, EXPORTS, MAX_RANKS, CallTimer, CommStats, DDPError, Plan,
+    Reducer,
     allgather_sim, broadcast_sim, ddp_allreduce_bucket, ddp_allreduce_buckets, ddp_bucket_plan,
     ddp_flatten,
     ddp_unflatten,

@@ -37,6 +37,8 @@ EXPORTS = [
     "ddp_plan_upload", "ddp_flatten", "ddp_unflatten",
     "ddp_plan_segment_bytes", "ddp_plan_upload_segments", "ddp_allreduce_bucket",
     "ddp_allreduce_buckets",
+    "ddp_reducer_create", "ddp_reducer_free", "ddp_reducer_prepare", "ddp_reducer_mark_ready",
+    "ddp_reducer_finalize", "ddp_reducer_launch_log",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
 ]
@@ -104,6 +106,12 @@ def load_library(path: str = LIB_PATH):
         "ddp_plan_upload_segments": ([vp, i32, vp, sz, vp], st),
         "ddp_allreduce_bucket": ([vp, i32, i32, vp, i32, i32, vp, vp, vp], st),
         "ddp_allreduce_buckets": ([vp, i32, i32, i32, vp, i32, i32, vp, vp, vp], st),
+        "ddp_reducer_create": ([vp, i32, vp, i32, i32, vp, vp, ctypes.POINTER(vp)], st),
+        "ddp_reducer_free": ([vp], None),
+        "ddp_reducer_prepare": ([vp], st),
+        "ddp_reducer_mark_ready": ([vp, i32, vp], st),
+        "ddp_reducer_finalize": ([vp, vp], st),
+        "ddp_reducer_launch_log": ([vp, vp, vp, vp, i32], i32),
         "ring_allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, vp, sz, vp, vp], st),
         "ring_allreduce_sim_workspace": ([i32, i64, i32, i32], sz),
         "ring_allreduce_sim_steps": ([vp, i32, i64, i32, vp, i32, i32, vp], st),
@@ -358,6 +366,53 @@ def ddp_allreduce_buckets(plan: Plan, first_bucket: int, n_buckets: int, grad_ta
         plan.handle, first_bucket, n_buckets, p, grad_table.data_ptr(), code, AVG[avg],
         _tokens(tokens, p), _stream(stream), ctypes.byref(st)), "ddp_allreduce_buckets")
     return st
+
+
+class Reducer:
+    """Owner of a ddp_reducer: bucket all-reduces launched on `comm_stream`
+    as parameters are marked ready (see include/ddpsim.h)."""
+
+    def __init__(self, plan: Plan, p: int, grad_table, dtype=None, avg: str = "none",
+                 tokens=None, comm_stream=None):
+        import torch
+
+        if dtype is None:
+            dtype = torch.float32 if plan.elem_bytes == 4 else torch.bfloat16
+        code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
+        self._plan, self._table = plan, grad_table  # kept alive
+        self._h = ctypes.c_void_p()
+        self.comm_stream = comm_stream if comm_stream is not None else torch.cuda.current_stream()
+        _check(load_library().ddp_reducer_create(
+            plan.handle, p, grad_table.data_ptr() if grad_table is not None else None, code,
+            AVG[avg], _tokens(tokens, p), _stream(self.comm_stream), ctypes.byref(self._h)),
+            "ddp_reducer_create")
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value and _lib is not None:
+            _lib.ddp_reducer_free(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    def prepare(self) -> None:
+        _check(load_library().ddp_reducer_prepare(self._h), "ddp_reducer_prepare")
+
+    def mark_ready(self, param: int, event=None) -> None:
+        """event: a torch.cuda.Event recorded after the gradients were written."""
+        handle = event.cuda_event if event is not None else None
+        _check(load_library().ddp_reducer_mark_ready(self._h, param, handle),
+               "ddp_reducer_mark_ready")
+
+    def finalize(self, wait_stream=None) -> None:
+        _check(load_library().ddp_reducer_finalize(self._h, _stream(wait_stream)),
+               "ddp_reducer_finalize")
+
+    def launch_log(self):
+        L = load_library()
+        n = L.ddp_reducer_launch_log(self._h, None, None, None, 0)
+        a = (ctypes.c_int32 * max(n, 1))()
+        b = (ctypes.c_int32 * max(n, 1))()
+        c = (ctypes.c_int32 * max(n, 1))()
+        L.ddp_reducer_launch_log(self._h, a, b, c, n)
+        return [(a[k], b[k], c[k]) for k in range(n)]
 
 
 # ---------------------------------------------------------------------------

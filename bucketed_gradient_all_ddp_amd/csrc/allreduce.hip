@@ -51,9 +51,12 @@ __global__ __launch_bounds__(kThreads) void fused_allreduce_kernel(
 
     // Up to V-1 unaligned elements on each side of the chunk: tile 0's
     // first lanes fold them one by one.
-    if (t == 0 && tid < 2 * (V - 1)) {
-      const bool head = tid < V - 1;
-      const int64_t i = head ? k.s + tid : k.tail_begin + (tid - (V - 1));
+    if (t == 0 && tid >= kThreads - 2 * (V - 1)) {
+      // the last wave's top lanes: for a short chunk the vector body sits in
+      // the first wave, so the two run side by side
+      const int lane = tid - (kThreads - 2 * (V - 1));
+      const bool head = lane < V - 1;
+      const int64_t i = head ? k.s + lane : k.tail_begin + (lane - (V - 1));
       if (i < (head ? k.head_end : k.e)) {
         const float y = apply_divide(fold_scalar<Tr>(TablePtrs{bufs}, p, c, i), div);
         for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
@@ -109,9 +112,10 @@ __global__ __launch_bounds__(kThreads) void ring_step_kernel(
   float *out = static_cast<float *>(bufs.ptr[dst]);
   const int tid = static_cast<int>(threadIdx.x);
 
-  if (t == 0 && tid < 2 * (V - 1)) {
-    const bool head = tid < V - 1;
-    const int64_t i = head ? k.s + tid : k.tail_begin + (tid - (V - 1));
+  if (t == 0 && tid >= kThreads - 2 * (V - 1)) {
+    const int lane = tid - (kThreads - 2 * (V - 1));
+    const bool head = lane < V - 1;
+    const int64_t i = head ? k.s + lane : k.tail_begin + (lane - (V - 1));
     if (i < (head ? k.head_end : k.e)) {
       out[i] = kReduce ? apply_divide(out[i] + src[i], div) : src[i];
     }
@@ -215,6 +219,11 @@ __global__ __launch_bounds__(kThreads) void bf16_workspace_kernel(
 #endif
 constexpr int kFusedVpt = DDPSIM_FUSED_VPT;
 constexpr int kFusedRb = DDPSIM_FUSED_RB;
+// Small problems (few workgroups) are latency-bound: the fold's load batches
+// run one after another, so there the kernel keeps 32 rank loads in flight
+// per thread (one vector each) instead of 8.
+constexpr int kSmallRb = 32;
+constexpr int64_t kSmallBlocks = 512;
 constexpr int kStepVpt = 4;
 
 int32_t device_cus() {
@@ -244,9 +253,20 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
   if (DDPSIM_FUSED_WAVES > 0) {
     blocks = std::min<int64_t>(blocks, int64_t(device_cus()) * DDPSIM_FUSED_WAVES);
   }
-  const dim3 grid(static_cast<uint32_t>(blocks));
   const char *kname = "fused_allreduce_kernel launch";
   const bool nt = int64_t(p) * n * elem_bytes_of(dtype) > DDPSIM_FUSED_NT_BYTES;
+  if (p > kFusedRb && blocks * 2 <= kSmallBlocks) {
+    // latency-bound: one vector per thread, 32 loads in flight
+    const int32_t tpc1 = tiles_for(C, vec, 1);
+    const dim3 grid1(static_cast<uint32_t>(int64_t(tpc1) * p));
+    if (dtype == DDP_F32) {
+      return launch(fused_allreduce_kernel<F32Traits, 1, kSmallRb, false>, grid1,
+                    dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc1, div);
+    }
+    return launch(fused_allreduce_kernel<BF16Traits, 1, kSmallRb, false>, grid1,
+                  dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc1, div);
+  }
+  const dim3 grid(static_cast<uint32_t>(blocks));
   if (dtype == DDP_F32) {
     if (nt) {
       return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, true>, grid,

@@ -76,9 +76,10 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
   const GradPtrs at{grads, n_params, d.param, m * kElemBytes};
   const ChunkSpan k = make_span(d.param_begin + m, d.param_begin + d.len + m, V);
 
-  if (t == 0 && tid < 2 * (V - 1)) {
-    const bool head = tid < V - 1;
-    const int64_t J = head ? k.s + tid : k.tail_begin + (tid - (V - 1));
+  if (t == 0 && tid >= kThreads - 2 * (V - 1)) {
+    const int lane = tid - (kThreads - 2 * (V - 1));
+    const bool head = lane < V - 1;
+    const int64_t J = head ? k.s + lane : k.tail_begin + (lane - (V - 1));
     if (J < (head ? k.head_end : k.e)) {
       const float y = apply_divide(fold_scalar<Tr>(at, p, d.chunk, J), div);
       for (int32_t r = 0; r < p; ++r) Tr::store1(at(r), J, y);

@@ -261,6 +261,55 @@ ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_bucket,
                                  hipStream_t stream, ddp_comm_stats *stats);
 
 /* ----------------------------------------------------------------------- */
+/* Reducer: bucket all-reduces launched as gradients become ready           */
+/* ----------------------------------------------------------------------- */
+
+/* The reducer's bookkeeping ([DDP] Part 2 "Step 2: backward", items 2-3,
+ * and "Step 3: finalize_backward"; [DP] "Overlapping communication with the
+ * backward pass"). Each bucket has a pending count equal to its number of
+ * parameters. ddp_reducer_mark_ready(param, ev) decrements the count of the
+ * parameter's bucket; when a count reaches zero and that bucket is the next
+ * to reduce, the reducer makes `comm_stream` wait for the events given with
+ * the parameters of that bucket and of every following bucket that is also
+ * complete, then launches that run of buckets with ddp_allreduce_buckets on
+ * `comm_stream`. Buckets thus start in index order, each as soon as its
+ * gradients and its predecessors allow, overlapping the producers' work.
+ *
+ *   create    plan (with ddp_plan_upload_segments done for p), p, the DEVICE
+ *             gradient pointer table, dtype, averaging (tokens copied), and
+ *             the stream the all-reduces run on. Plan and table must outlive
+ *             the reducer. Errors: DDP_EINVAL, DDP_ERANGE.
+ *   prepare   starts a backward pass (all counts reset).
+ *   mark_ready  param in [0, n_params); `ready` is an event recorded after
+ *             that parameter's gradients of all ranks were written (NULL if
+ *             they already were when the call is made). DDP_EINVAL for a
+ *             second mark of a parameter in one pass or a mark outside a
+ *             pass, DDP_ERANGE for a bad index; a failed launch returns its
+ *             error and leaves the pass unusable until the next prepare.
+ *   finalize  ends the pass. DDP_ENOTREADY (with the bucket and counts in
+ *             ddp_last_error) if some bucket never became ready -- what DDP
+ *             would wait for forever without find_unused_parameters.
+ *             Otherwise `wait_stream` is made to wait for the all-reduces.
+ *   launch_log  the runs launched in the current or last pass: the mark (0-
+ *             based, in call order) that launched each run, its first bucket
+ *             and its length; returns the number of runs (writes at most
+ *             `capacity`).
+ * Not thread-safe: one host thread drives a reducer. */
+typedef struct ddp_reducer ddp_reducer;
+ddp_status ddp_reducer_create(const ddp_plan *plan, int32_t p,
+                              void *const *d_grad_ptrs, int32_t dtype,
+                              int32_t avg_mode, const int64_t *tokens,
+                              hipStream_t comm_stream, ddp_reducer **out);
+void ddp_reducer_free(ddp_reducer *reducer);
+ddp_status ddp_reducer_prepare(ddp_reducer *reducer);
+ddp_status ddp_reducer_mark_ready(ddp_reducer *reducer, int32_t param,
+                                  hipEvent_t ready);
+ddp_status ddp_reducer_finalize(ddp_reducer *reducer, hipStream_t wait_stream);
+int32_t ddp_reducer_launch_log(const ddp_reducer *reducer, int32_t *at_mark,
+                               int32_t *first_bucket, int32_t *n_buckets,
+                               int32_t capacity);
+
+/* ----------------------------------------------------------------------- */
 /* Ring all-reduce                                                         */
 /* ----------------------------------------------------------------------- */
 

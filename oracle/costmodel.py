@@ -58,3 +58,33 @@ def ring_crossover(p: int, alpha: float, beta: float) -> float:
 def overlap_tokens(flops_per_s: float, bandwidth: float) -> float:
     """Tokens per GPU per step needed to hide the all-reduce under backward."""
     return flops_per_s / bandwidth
+
+
+def ddp_step_time(grads, bucket_cap, p, alpha, beta):
+    """Step time with bucketed, overlapped all-reduce ("Data parallelism",
+    section "Overlapping communication with the backward pass").
+
+    grads: [(bytes, t_ready)] in the order backward produces them. Buckets
+    are filled in that order and closed once they reach bucket_cap bytes.
+    A bucket's ring all-reduce starts when its last gradient is ready and
+    the previous bucket's all-reduce has finished, and takes
+    2(p-1)(alpha + beta * M_b / p). Returns (step time, exposed time), the
+    exposed time being what sticks out past the end of backward.
+    """
+    end_bwd = max((t for _, t in grads), default=0.0)
+    buckets = []
+    size, ready = 0.0, 0.0
+    for n, t in grads:
+        if size >= bucket_cap and size > 0:
+            buckets.append((size, ready))
+            size, ready = 0.0, 0.0
+        size += n
+        ready = max(ready, t)
+    if size > 0 or not buckets:
+        buckets.append((size, ready))
+    finish = 0.0
+    for m, t in buckets:
+        start = max(t, finish)
+        finish = start + allreduce_time(m, p, alpha, beta, "ring")
+    step = max(end_bwd, finish)
+    return step, step - end_bwd

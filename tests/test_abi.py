@@ -193,3 +193,36 @@ def test_bucket_allreduce_argument_errors():
     assert L.ddp_plan_upload_segments(plan.handle, 4, None, 0, None) == 1
     assert L.ddp_time_next_call(fake, None) == 1
     assert L.ddp_time_next_call(None, None) == 0
+
+
+def test_reducer_errors_without_launching():
+    """Bucket 0 never completes, so nothing is launched: every check here is
+    host logic."""
+    L = load_library()
+    sizes = [5, 7, 3, 9, 4]
+    plan = ddp.ddp_bucket_plan(sizes, 4, 32, 16)
+    assert plan.num_buckets >= 2
+    fake = ctypes.c_void_p(0x100000000)
+    out = ctypes.c_void_p()
+    assert L.ddp_reducer_create(plan.handle, 0, fake, 0, 0, None, None, ctypes.byref(out)) == 2
+    assert L.ddp_reducer_create(plan.handle, 4, None, 0, 0, None, None, ctypes.byref(out)) == 1
+    assert L.ddp_reducer_create(plan.handle, 4, fake, 1, 0, None, None, ctypes.byref(out)) == 1
+    assert L.ddp_reducer_create(plan.handle, 4, fake, 0, 2, None, None, ctypes.byref(out)) == 1
+    assert L.ddp_reducer_create(plan.handle, 4, fake, 0, 1, None, None, ctypes.byref(out)) == 0
+    r = out
+    try:
+        assert L.ddp_reducer_mark_ready(r, 0, None) == 1      # no pass yet
+        assert L.ddp_reducer_finalize(r, None) == 1
+        assert L.ddp_reducer_prepare(r) == 0
+        assert L.ddp_reducer_mark_ready(r, 5, None) == 2      # out of range
+        held = plan.bucket_params(0)[0]
+        for i in range(len(sizes)):
+            if i != held:
+                assert L.ddp_reducer_mark_ready(r, i, None) == 0
+        assert L.ddp_reducer_mark_ready(r, (held + 1) % len(sizes), None) == 1  # twice
+        assert L.ddp_reducer_launch_log(r, None, None, None, 0) == 0
+        assert L.ddp_reducer_finalize(r, None) == 6
+        assert b"never became ready" in L.ddp_last_error()
+        assert L.ddp_reducer_finalize(r, None) == 1            # pass already ended
+    finally:
+        L.ddp_reducer_free(r)

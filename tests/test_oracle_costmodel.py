@@ -55,3 +55,30 @@ def test_bytes_per_rank_and_caps():
     caps = GOLD["default_caps_bytes"]
     assert W.BUCKET_CAP_BYTES == caps["bucket_cap"]
     assert W.FIRST_BUCKET_CAP_BYTES == caps["first_bucket_cap"]
+
+
+def test_ddp_step_time_limits():
+    """The overlap model against what the page's prose fixes: with every
+    gradient ready only at the end of backward and one bucket it is the
+    no-overlap time of the page's stub; splitting into buckets then only adds
+    latency terms; gradients ready early hide all but the last bucket."""
+    p, a, beta = 8, 10e-6, 1 / 50e9
+    M = 100e6
+    end = 0.05
+    one = [(M, end)]
+    t, exposed = cm.ddp_step_time(one, bucket_cap=1e12, p=p, alpha=a, beta=beta)
+    stub = end + 2 * (p - 1) * a + 2 * (p - 1) / p * M * beta
+    assert abs(t - stub) < 1e-12 and abs(exposed - (t - end)) < 1e-15
+    # ten equal gradients all ready at the end, one bucket each
+    ten = [(M / 10, end)] * 10
+    t10, _ = cm.ddp_step_time(ten, bucket_cap=M / 10, p=p, alpha=a, beta=beta)
+    assert abs(t10 - (stub + 9 * 2 * (p - 1) * a)) < 1e-12
+    # ready early and spread out: only the last bucket is exposed
+    spread = [(M / 10, end * (k + 1) / 10) for k in range(10)]
+    ts, ex = cm.ddp_step_time(spread, bucket_cap=M / 10, p=p, alpha=a, beta=beta)
+    last = cm.allreduce_time(M / 10, p, a, beta, "ring")
+    assert abs(ex - last) < 1e-12
+    # tiny buckets pay the latency floor many times: worse than one bucket
+    tiny = [(M / 1000, end)] * 1000
+    tt, _ = cm.ddp_step_time(tiny, bucket_cap=M / 1000, p=p, alpha=a, beta=beta)
+    assert tt > stub + 999 * 2 * (p - 1) * a * 0.999
