@@ -4,12 +4,15 @@ set, p = 8 simulated ranks in one GPU's HBM.
 
 A step is one pass of the whole path over every bucket of the plan: the
 bucket's flatten, ring all-reduce averaged over p, and unflatten back into
-each rank's per-parameter gradients. The headline ("inplace") step does the
-three in place, one kernel launch per bucket (ddp_allreduce_bucket: same
-bits, one pass over HBM); "batched" covers all buckets with one launch
-(ddp_allreduce_buckets); "copy" runs the three as three kernels per bucket
-(ddp_flatten, ring_allreduce_sim, ddp_unflatten). All three are timed and
-reported. The plan is built once before timing, as the reducer
+each rank's per-parameter gradients. With no backward pass in the step,
+every bucket is ready at once, and the reducer's rule -- launch the next
+bucket and every following complete one -- makes them one run: the headline
+("batched") step does flatten + all-reduce + unflatten in place for that
+run in one kernel launch (ddp_allreduce_buckets; each bucket keeps its own
+ring chunks, same bits as one launch per bucket). "inplace" launches that
+kernel once per bucket (ddp_allreduce_bucket); "copy" runs the three steps
+as three kernels per bucket (ddp_flatten, ring_allreduce_sim,
+ddp_unflatten). All three are timed and reported. The plan is built once before timing, as the reducer
 does at construction.
 
 Output: one JSON line. `value` is the all-reduce bus bandwidth of the whole
@@ -48,10 +51,11 @@ KERNEL_SOURCES = {
     "fused_allreduce_kernel": ["allreduce.hip", "fold.hpp", "internal.hpp"],
 }
 MEASURED_TRAFFIC = {
-    # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: mean over the 13 buckets
+    # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
+    # (all 13 buckets in one dispatch)
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 613317852,
-        "sources_sha256": "263f4cd06d0ab078a11e8cad7fd145aff3b0fefe43cdaf56cd847b13e3761f07",
+        "bytes_per_launch": 7995570146,
+        "sources_sha256": "e5c17e274277b5192cfec1175e83ef59c9bfac4da0848f4b02fdec4e369ef61a",
     },
 }
 
@@ -85,10 +89,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="inplace", choices=["batched", "inplace", "copy"],
-                    help="headline step: one launch per bucket "
-                         "(ddp_allreduce_bucket), one launch for all buckets "
-                         "(ddp_allreduce_buckets), or flatten + all-reduce + "
+    ap.add_argument("--mode", default="batched", choices=["batched", "inplace", "copy"],
+                    help="headline step: one launch for the run of all ready "
+                         "buckets (ddp_allreduce_buckets), one launch per bucket "
+                         "(ddp_allreduce_bucket), or flatten + all-reduce + "
                          "unflatten as three launches per bucket")
     ap.add_argument("--algo", default="fused", choices=["fused", "ring"],
                     help="all-reduce algorithm of the copy step")
@@ -545,7 +549,7 @@ def main():
     p, S = wl.p, wl.S
     ws = {}
     modes = [args.mode] + ([] if args.no_compare else
-                           [m for m in ("inplace", "batched", "copy") if m != args.mode])
+                           [m for m in ("batched", "inplace", "copy") if m != args.mode])
     if "copy" in modes:
         wl.ensure_bucket_buffers(torch, dev)
         if args.algo == "ring":
@@ -586,7 +590,8 @@ def main():
                          "(13 buckets), average by p; step = flatten + ring all-reduce + "
                          "unflatten of every bucket"),
             "step_kernels": {
-                "batched": "one ddp_allreduce_buckets launch covering all 13 buckets",
+                "batched": "one ddp_allreduce_buckets launch for the run of all 13 ready "
+                           "buckets (each with its own ring chunks)",
                 "inplace": "one ddp_allreduce_bucket launch per bucket",
                 "copy": f"ddp_flatten + ring_allreduce_sim({args.algo}) + ddp_unflatten "
                         "per bucket"}[args.mode],

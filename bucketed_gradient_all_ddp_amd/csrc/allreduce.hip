@@ -36,8 +36,8 @@ namespace {
 // Workgroup w handles tiles w, w + gridDim.x, ... (a grid-stride loop, so
 // a launch can be sized to what the GPU holds at once); tile -> (chunk c,
 // tile t within the chunk) = (tile / tiles_per_chunk, tile % tiles_per_chunk).
-template <typename Tr, int VPT, int RB, bool kNT>
-__global__ __launch_bounds__(kThreads) void fused_allreduce_kernel(
+template <typename Tr, int VPT, int RB, bool kNT, int THR>
+__global__ __launch_bounds__(THR) void fused_allreduce_kernel(
     RankTable bufs, int32_t p, int64_t n, int64_t C, int32_t tiles_per_chunk,
     Divide div) {
   constexpr int V = Tr::kVec;
@@ -51,10 +51,10 @@ __global__ __launch_bounds__(kThreads) void fused_allreduce_kernel(
 
     // Up to V-1 unaligned elements on each side of the chunk: tile 0's
     // first lanes fold them one by one.
-    if (t == 0 && tid >= kThreads - 2 * (V - 1)) {
+    if (t == 0 && tid >= THR - 2 * (V - 1)) {
       // the last wave's top lanes: for a short chunk the vector body sits in
       // the first wave, so the two run side by side
-      const int lane = tid - (kThreads - 2 * (V - 1));
+      const int lane = tid - (THR - 2 * (V - 1));
       const bool head = lane < V - 1;
       const int64_t i = head ? k.s + lane : k.tail_begin + (lane - (V - 1));
       if (i < (head ? k.head_end : k.e)) {
@@ -64,13 +64,13 @@ __global__ __launch_bounds__(kThreads) void fused_allreduce_kernel(
     }
 
     const int64_t nv = (k.ve - k.vs) / V;
-    const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+    const int64_t base = static_cast<int64_t>(t) * (THR * VPT);
     if (base >= nv) continue;
     int64_t vi[VPT];
     bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int64_t j = base + u * kThreads + tid;
+      const int64_t j = base + u * THR + tid;
       ok[u] = j < nv;
       vi[u] = k.vs / V + j;
     }
@@ -205,6 +205,9 @@ __global__ __launch_bounds__(kThreads) void bf16_workspace_kernel(
 #ifndef DDPSIM_FUSED_VPT
 #define DDPSIM_FUSED_VPT 2  // 16-byte vectors per thread per tile
 #endif
+#ifndef DDPSIM_FUSED_THREADS
+#define DDPSIM_FUSED_THREADS 256  // threads per workgroup
+#endif
 #ifndef DDPSIM_FUSED_RB
 #define DDPSIM_FUSED_RB 8  // rank loads issued before their additions
 #endif
@@ -214,11 +217,9 @@ __global__ __launch_bounds__(kThreads) void bf16_workspace_kernel(
 // ddp_flatten has just written, say), where ordinary accesses are faster.
 #define DDPSIM_FUSED_NT_BYTES (int64_t(256) << 20)
 #endif
-#ifndef DDPSIM_FUSED_WAVES
-#define DDPSIM_FUSED_WAVES 0  // >0: cap the grid at this many workgroups per CU
-#endif
 constexpr int kFusedVpt = DDPSIM_FUSED_VPT;
 constexpr int kFusedRb = DDPSIM_FUSED_RB;
+constexpr int kFusedThreads = DDPSIM_FUSED_THREADS;
 // Small problems (few workgroups) are latency-bound: the fold's load batches
 // run one after another, so there the kernel keeps 32 rank loads in flight
 // per thread (one vector each) instead of 8.
@@ -226,61 +227,48 @@ constexpr int kSmallRb = 32;
 constexpr int64_t kSmallBlocks = 512;
 constexpr int kStepVpt = 4;
 
-int32_t device_cus() {
-  static int32_t cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-      return 256;
-    }
-    return n > 0 ? n : 256;
-  }();
-  return cus;
-}
 
-int32_t tiles_for(int64_t C, int vec, int vpt) {
+int32_t tiles_for(int64_t C, int vec, int vpt, int threads = kThreads) {
   const int64_t vectors = C / vec;
-  return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(vectors, int64_t(kThreads) * vpt)));
+  return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(vectors, int64_t(threads) * vpt)));
 }
 
 ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtype,
                         const Divide &div, hipStream_t stream, CallTimer &timer) {
   const int64_t C = ceil_div(n, p);
   const int vec = dtype == DDP_F32 ? 4 : 8;
-  const int32_t tpc = tiles_for(C, vec, kFusedVpt);
-  int64_t blocks = int64_t(tpc) * p;
-  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
-  if (DDPSIM_FUSED_WAVES > 0) {
-    blocks = std::min<int64_t>(blocks, int64_t(device_cus()) * DDPSIM_FUSED_WAVES);
-  }
   const char *kname = "fused_allreduce_kernel launch";
   const bool nt = int64_t(p) * n * elem_bytes_of(dtype) > DDPSIM_FUSED_NT_BYTES;
+  const int32_t tpc = tiles_for(C, vec, kFusedVpt, kFusedThreads);
+  const int64_t blocks = int64_t(tpc) * p;
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
   if (p > kFusedRb && blocks * 2 <= kSmallBlocks) {
     // latency-bound: one vector per thread, 32 loads in flight
     const int32_t tpc1 = tiles_for(C, vec, 1);
     const dim3 grid1(static_cast<uint32_t>(int64_t(tpc1) * p));
     if (dtype == DDP_F32) {
-      return launch(fused_allreduce_kernel<F32Traits, 1, kSmallRb, false>, grid1,
+      return launch(fused_allreduce_kernel<F32Traits, 1, kSmallRb, false, kThreads>, grid1,
                     dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc1, div);
     }
-    return launch(fused_allreduce_kernel<BF16Traits, 1, kSmallRb, false>, grid1,
+    return launch(fused_allreduce_kernel<BF16Traits, 1, kSmallRb, false, kThreads>, grid1,
                   dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc1, div);
   }
   const dim3 grid(static_cast<uint32_t>(blocks));
+  const dim3 block(kFusedThreads);
   if (dtype == DDP_F32) {
     if (nt) {
-      return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, true>, grid,
-                    dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
+      return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
+                    grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
     }
-    return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false>, grid,
-                  dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
+    return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
+                  grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
   }
   if (nt) {
-    return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, true>, grid,
-                  dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
+    return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
+                  grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
   }
-  return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false>, grid,
-                dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc, div);
+  return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
+                grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
 }
 
 // Launch ring steps [first, first + count) on fp32 buffers.

@@ -33,7 +33,7 @@ namespace {
 // Workgroup w handles tile tile_base + w of the plan's numbering; the tile
 // map names the piece (index into seg) each tile belongs to.
 template <typename Tr, int VPT, int RB, bool kNT>
-__global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
+__global__ __launch_bounds__(kBucketThreads) void bucket_allreduce_kernel(
     const SegDesc *__restrict__ seg, const int32_t *__restrict__ tile_seg,
     int32_t tile_base, int32_t n_params, const void *const *__restrict__ grads,
     int32_t p, Divide div) {
@@ -46,7 +46,8 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
   const SegDesc d = seg[tile_seg[tile]];
   const int32_t t = tile - d.tile_begin;
   const int tid = static_cast<int>(threadIdx.x);
-  constexpr int64_t kTile = int64_t(kThreads) * VPT * V;
+  constexpr int kThr = kBucketThreads;
+  constexpr int64_t kTile = int64_t(kThr) * VPT * V;
 
   // The vector path needs every rank's copy of this parameter to sit at the
   // same offset from a 16-byte boundary.
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
     const GradPtrs at{grads, n_params, d.param, 0};
     const int64_t j0 = d.param_begin + static_cast<int64_t>(t) * kTile;
     const int64_t j1 = std::min(j0 + kTile, d.param_begin + d.len);
-    for (int64_t j = j0 + tid; j < j1; j += kThreads) {
+    for (int64_t j = j0 + tid; j < j1; j += kThr) {
       const float y = apply_divide(fold_scalar<Tr>(at, p, d.chunk, j), div);
       for (int32_t r = 0; r < p; ++r) Tr::store1(at(r), j, y);
     }
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
   const GradPtrs at{grads, n_params, d.param, m * kElemBytes};
   const ChunkSpan k = make_span(d.param_begin + m, d.param_begin + d.len + m, V);
 
-  if (t == 0 && tid >= kThreads - 2 * (V - 1)) {
-    const int lane = tid - (kThreads - 2 * (V - 1));
+  if (t == 0 && tid >= kThr - 2 * (V - 1)) {
+    const int lane = tid - (kThr - 2 * (V - 1));
     const bool head = lane < V - 1;
     const int64_t J = head ? k.s + lane : k.tail_begin + (lane - (V - 1));
     if (J < (head ? k.head_end : k.e)) {
@@ -87,13 +88,13 @@ __global__ __launch_bounds__(kThreads) void bucket_allreduce_kernel(
   }
 
   const int64_t nv = (k.ve - k.vs) / V;
-  const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+  const int64_t base = static_cast<int64_t>(t) * (kThr * VPT);
   if (base >= nv) return;
   int64_t vi[VPT];
   bool ok[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    const int64_t jj = base + u * kThreads + tid;
+    const int64_t jj = base + u * kThr + tid;
     ok[u] = jj < nv;
     vi[u] = k.vs / V + jj;
   }
@@ -186,11 +187,11 @@ extern "C" ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_
   const dim3 grid(static_cast<uint32_t>(tiles));
   if (dtype == DDP_F32) {
     return launch(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
-                  dim3(kThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
+                  dim3(kBucketThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
                   tile_seg, tile0, n_params, grads, p, div);
   }
   return launch(bucket_allreduce_kernel<BF16Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
-                dim3(kThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
+                dim3(kBucketThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
                 tile_seg, tile0, n_params, grads, p, div);
 }
 

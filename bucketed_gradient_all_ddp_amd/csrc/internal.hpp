@@ -71,7 +71,11 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #ifndef DDPSIM_BUCKET_XCD
 #define DDPSIM_BUCKET_XCD 0  // 1: give each XCD a contiguous range of tiles
 #endif
+#ifndef DDPSIM_BUCKET_THREADS
+#define DDPSIM_BUCKET_THREADS 64  // threads per workgroup (one wave)
+#endif
 constexpr int kBucketVpt = DDPSIM_BUCKET_VPT;
+constexpr int kBucketThreads = DDPSIM_BUCKET_THREADS;
 constexpr int kBucketRb = 8;
 constexpr bool kBucketNt = DDPSIM_BUCKET_NT != 0;
 
@@ -83,7 +87,7 @@ __host__ __device__ inline int64_t xcd_contiguous(int64_t b, int64_t G) {
   return x * q + (x < r ? x : r) + k;
 }
 // elements per tile for a dtype whose 16-byte vector holds `vec` elements
-constexpr int64_t bucket_tile_elems(int vec) { return int64_t(kThreads) * kBucketVpt * vec; }
+constexpr int64_t bucket_tile_elems(int vec) { return int64_t(kBucketThreads) * kBucketVpt * vec; }
 
 // ---------------------------------------------------------------------------
 // Host helpers (defined in host.cpp)

@@ -102,3 +102,24 @@ def test_bucket_run_in_one_launch_equals_per_bucket(oracle, p):
         ddp.ddp_allreduce_buckets(plan, nb - 1, 2, table, p)
     with pytest.raises(ddp.DDPError, match="ERANGE"):
         ddp.ddp_allreduce_buckets(plan, 0, 0, table, p)
+
+
+@pytest.mark.parametrize("bf16,layout", [(False, "mixed"), (True, "odd"), (False, "aligned")])
+def test_bucket_allreduce_at_max_ranks(oracle, bf16, layout):
+    """p = 64 (the library's maximum), small parameters so that many pieces
+    are shorter than a vector and most chunks have unaligned ends."""
+    p = 64
+    sizes = [129, 0, 1, 4096 + 3, 640, 7, 2049]
+    eb = 2 if bf16 else 4
+    cap, first = 8 * 1024, 1024
+    plan = ddp.ddp_bucket_plan(sizes, eb, cap, first).upload_segments(p)
+    host, grads = make_grads(p, sizes, 1300, bf16, oracle, layout)
+    table = ddp.grad_pointer_table(grads)
+    tokens = tokens_for(p, 9)
+    for b in range(plan.num_buckets):
+        ddp.ddp_allreduce_bucket(plan, b, table, p, avg="tokens", tokens=tokens)
+    torch.cuda.synchronize()
+    want = _oracle_sync(oracle, host, sizes, eb, cap, first, "tokens", tokens)
+    for r in range(p):
+        for i in range(len(sizes)):
+            assert_bits_equal(to_host(grads[r][i]), want[r][i], f"rank {r} param {i}")
