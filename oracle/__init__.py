@@ -20,7 +20,9 @@ Pages cited (by title and section):
       reduce_scatter pre-rotation, allgather rotations, doubling-tree
       broadcast, the 1e-5 gloo check.
   "Data parallelism" (zerotofrontier) -- ring all-reduce derived, chunk
-      ownership (q+1) mod p, bytes per rank, averaging by tokens.
+      ownership (q+1) mod p, bytes per rank, averaging by tokens; recursive
+      doubling and recursive halving/doubling ("Latency, trees, and choosing
+      an algorithm").
 
 Parity pins for every function are in tests/test_oracle_*.py.
 """
@@ -49,6 +51,12 @@ DTYPES = {"f32": 0, "bf16": 1}
 PHASE_REDUCE_SCATTER = 0
 PHASE_ALLGATHER = 1
 PHASE_BROADCAST = 2
+PHASE_EXCHANGE = 3
+PHASE_FOLD_IN = 4
+PHASE_FOLD_OUT = 5
+PHASE_REDUCE = 6
+
+SCHEDULES = {"ring": 0, "recursive_doubling": 1, "rabenseifner": 2, "tree": 3}
 
 _lib = None
 
@@ -106,6 +114,10 @@ def _load():
     lib.orc_avg_divisor.restype = ctypes.c_int
     lib.orc_reducer_schedule.argtypes = [P, i32, i32, P, i32, P, P, P]
     lib.orc_reducer_schedule.restype = ctypes.c_int
+    lib.orc_allreduce.argtypes = [P, i32, i64, i32, i32, P, i32, P, i64, P]
+    lib.orc_allreduce.restype = ctypes.c_int
+    lib.orc_tree_fold_samples.argtypes = [P, i32, i64, i32, i32, f32, P]
+    lib.orc_tree_fold_samples.restype = None
     _lib = lib
     return lib
 
@@ -371,6 +383,32 @@ def broadcast(bufs: Sequence[np.ndarray], src: int = 0
     return work, _messages(log, int(count[0]))
 
 
+def allreduce(bufs: Sequence[np.ndarray], schedule: str = "ring",
+              avg: str = "none", tokens=None, want_log: bool = True
+              ) -> Tuple[List[np.ndarray], List[Message]]:
+    """All-reduce under a schedule ("ring", "recursive_doubling",
+    "rabenseifner", "tree"); returns (results, message log). Inputs are not
+    modified."""
+    lib = _load()
+    p = len(bufs)
+    work = [np.array(b, copy=True).ravel() for b in bufs]
+    n = work[0].size if p else 0
+    dt = _dtype_code(work[0])
+    for w in work:
+        if w.size != n or w.dtype != work[0].dtype:
+            raise ValueError("rank buffers must match in size and dtype")
+    t = _tokens_array(tokens, p)
+    cap = max(2 * p * max(p - 1, 0), 4 * p * 7, 1) if want_log else 0
+    log = np.zeros(max(cap, 1), dtype=_MSG_DTYPE)
+    count = np.zeros(1, dtype=np.int64)
+    table = _ptr_table(work)
+    rc = lib.orc_allreduce(_ptr(table), p, n, dt, AVG_MODES[avg],
+                           None if t is None else _ptr(t), SCHEDULES[schedule],
+                           _ptr(log) if want_log else None, cap, _ptr(count))
+    _check(rc, "allreduce")
+    return work, (_messages(log, int(count[0])) if want_log else [])
+
+
 # ---------------------------------------------------------------------------
 # The ring's result at sampled elements (for checks at full size)
 # ---------------------------------------------------------------------------
@@ -429,6 +467,25 @@ def reduce_scatter_at(vals: np.ndarray, index: np.ndarray, n: int,
     start = index // C + 1
     f = bf16_to_f32(vals) if vals.dtype == np.uint16 else vals
     out = _fold(f, start, p, avg_divisor(avg, p, tokens), avg != "none")
+    return f32_to_bf16(out) if vals.dtype == np.uint16 else out
+
+
+def tree_allreduce_at(vals: np.ndarray, schedule: str, avg: str = "none",
+                      tokens=None) -> np.ndarray:
+    """Result of a logarithmic schedule at selected elements: vals[s, r] is
+    rank r's input at that element (float32, or uint16 bf16 patterns, which
+    come back rounded to bf16). The value does not depend on the element's
+    position."""
+    lib = _load()
+    vals = np.asarray(vals)
+    p = vals.shape[1]
+    f = np.ascontiguousarray(bf16_to_f32(vals) if vals.dtype == np.uint16 else vals,
+                             dtype=np.float32)
+    k = f.shape[0]
+    out = np.empty(k, dtype=np.float32)
+    lib.orc_tree_fold_samples(_ptr(f), p, k, SCHEDULES[schedule],
+                              1 if avg != "none" else 0,
+                              avg_divisor(avg, p, tokens), _ptr(out))
     return f32_to_bf16(out) if vals.dtype == np.uint16 else out
 
 

@@ -18,6 +18,16 @@ tests/golden/cost_model.json):
 
 Bytes per rank: all-reduce 2 (p-1) M / p; reduce-scatter or all-gather alone
 (p-1) M / p ("Ring all-reduce, derived"; "Collective Ops From Scratch").
+
+schedule_time prices the literal schedules of the oracle's orc_allreduce
+message by message (one alpha per step, the largest message of a step for
+the beta term). For p a power of two it is the page's formula for each
+schedule: ring 2(p-1)(alpha + beta M/p); recursive doubling
+log2 p (alpha + beta M); recursive halving/doubling 2 log2 p alpha +
+2 (p-1)/p M beta. For other p, two whole-buffer steps (an extra rank's data
+in, the result back out) are added to the power-of-two core, the reading
+the oracle takes. The tree all-reduce (reduce up, broadcast down the
+doubling tree) takes 2 ceil(log2 p) whole-buffer steps.
 """
 from __future__ import annotations
 
@@ -88,3 +98,45 @@ def ddp_step_time(grads, bucket_cap, p, alpha, beta):
         finish = start + allreduce_time(m, p, alpha, beta, "ring")
     step = max(end_bwd, finish)
     return step, step - end_bwd
+
+
+SCHEDULES = ("ring", "recursive_doubling", "rabenseifner", "tree")
+
+
+def _pow2_floor(p: int) -> int:
+    q = 1
+    while q * 2 <= p:
+        q *= 2
+    return q
+
+
+def schedule_time(schedule: str, M: float, p: int, alpha: float, beta: float) -> float:
+    """Hockney-model time of one all-reduce of M bytes under a schedule."""
+    if p == 1:
+        return 0.0
+    q = _pow2_floor(p)
+    k = int(math.log2(q))
+    extra = 2 * (alpha + beta * M) if q < p else 0.0
+    if schedule == "ring":
+        return allreduce_time(M, p, alpha, beta, "ring")
+    if schedule == "recursive_doubling":
+        return k * (alpha + beta * M) + extra
+    if schedule == "rabenseifner":
+        return 2 * k * alpha + 2.0 * (q - 1) / q * M * beta + extra
+    if schedule == "tree":
+        K = math.ceil(math.log2(p))
+        return 2 * K * (alpha + beta * M)
+    raise ValueError(schedule)
+
+
+def choose_schedule(p: int, M: float, alpha: float, beta: float,
+                    candidates=("ring", "recursive_doubling")) -> str:
+    """The candidate with the smallest modelled time; ties go to the one
+    listed first ("Latency, trees, and choosing an algorithm": libraries pick
+    per call from the message size)."""
+    best, best_t = None, None
+    for c in candidates:
+        t = schedule_time(c, M, p, alpha, beta)
+        if best is None or t < best_t:
+            best, best_t = c, t
+    return best

@@ -43,6 +43,16 @@
  *                       fold over ranks (derived from the chunk's journey in
  *                       [DP] "Ring all-reduce, derived"); pinned in tests to
  *                       the literal simulation.
+ *   orc_allreduce       the all-reduce under a chosen schedule: the ring, or
+ *                       one of the logarithmic-latency schedules of [DP]
+ *                       "Latency, trees, and choosing an algorithm"
+ *                       (recursive doubling; recursive halving then doubling,
+ *                       i.e. Rabenseifner's algorithm) or the tree all-reduce
+ *                       that [COL] sets as an exercise (reduce up the
+ *                       doubling tree, broadcast down it).
+ *   orc_tree_fold_samples  the per-element value those schedules reach,
+ *                       written as a pairwise fold; pinned to the literal
+ *                       simulations in tests.
  *
  * Readings where the pages leave a step open (also listed in the design
  * notes): equal chunks of ceil(n/p) with the padding at the end; averaging is
@@ -67,6 +77,15 @@
 #define ORC_PHASE_REDUCE_SCATTER 0
 #define ORC_PHASE_ALLGATHER 1
 #define ORC_PHASE_BROADCAST 2
+#define ORC_PHASE_EXCHANGE 3  /* recursive doubling: whole buffers swapped  */
+#define ORC_PHASE_FOLD_IN 4   /* p not a power of two: extra rank -> core   */
+#define ORC_PHASE_FOLD_OUT 5  /* ... and the result back to the extra rank  */
+#define ORC_PHASE_REDUCE 6    /* tree all-reduce: towards rank 0            */
+
+#define ORC_SCHED_RING 0
+#define ORC_SCHED_RECURSIVE_DOUBLING 1
+#define ORC_SCHED_RABENSEIFNER 2
+#define ORC_SCHED_TREE 3
 
 /* One logged message: who sent which chunk to whom, in which step. */
 typedef struct {
@@ -630,4 +649,259 @@ int orc_reducer_schedule(const int32_t *bucket_of, int32_t n_params,
   free(pending);
   free(seen);
   return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Logarithmic-latency all-reduce schedules                                  */
+/* ------------------------------------------------------------------------ */
+
+/* [DP] "Latency, trees, and choosing an algorithm" describes recursive
+ * doubling and recursive halving/doubling for p a power of two. For any
+ * other p the pages say nothing; the reading taken here (listed with the
+ * other readings) is the usual one: with q the largest power of two <= p,
+ * each "extra" rank r >= q first hands its whole buffer to rank r - q, which
+ * adds it (FOLD_IN); the q core ranks run the schedule; then every extra
+ * rank receives the finished result from rank r - q (FOLD_OUT). */
+static int32_t pow2_floor(int32_t p) {
+  int32_t q = 1;
+  while (q * 2 <= p) q *= 2;
+  return q;
+}
+
+/* Extra ranks fold into their partners (whole buffers, no send buffer
+ * needed: senders r >= q are never receivers in this step). */
+static void fold_in(float **work, int32_t p, int32_t q, int64_t len, int64_t n,
+                    int64_t wire_bytes, msg_log *log) {
+  for (int32_t r = q; r < p; ++r) {
+    log_msg(log, ORC_PHASE_FOLD_IN, 0, r, r - q, -1, n * wire_bytes);
+    for (int64_t i = 0; i < len; ++i) work[r - q][i] = work[r - q][i] + work[r][i];
+  }
+}
+
+static void fold_out(float **work, int32_t p, int32_t q, int64_t len, int64_t n,
+                     int32_t step, int64_t wire_bytes, msg_log *log) {
+  for (int32_t r = q; r < p; ++r) {
+    log_msg(log, ORC_PHASE_FOLD_OUT, step, r - q, r, -1, n * wire_bytes);
+    memcpy(work[r], work[r - q], (size_t)len * sizeof(float));
+  }
+}
+
+/* Recursive doubling: in step j every core rank r exchanges its whole
+ * current buffer with rank r XOR 2^j and both add what they received. Each
+ * step first copies every outgoing buffer, then delivers. After log2(q)
+ * steps every core rank holds the sum, which it then divides. */
+static void rd_on_work(float **work, float **send, int32_t p, int64_t n,
+                       int32_t do_divide, float divisor, int64_t wire_bytes,
+                       msg_log *log) {
+  int32_t q = pow2_floor(p);
+  int32_t step = 0;
+  if (q < p) {
+    fold_in(work, p, q, n, n, wire_bytes, log);
+    step += 1;
+  }
+  for (int32_t d = 1; d < q; d *= 2, ++step) {
+    for (int32_t r = 0; r < q; ++r) {
+      memcpy(send[r], work[r], (size_t)n * sizeof(float));
+      log_msg(log, ORC_PHASE_EXCHANGE, step, r, r ^ d, -1, n * wire_bytes);
+    }
+    for (int32_t r = 0; r < q; ++r) {
+      const float *got = send[r ^ d];
+      for (int64_t i = 0; i < n; ++i) work[r][i] = work[r][i] + got[i];
+    }
+  }
+  if (do_divide) {
+    for (int32_t r = 0; r < q; ++r) {
+      for (int64_t i = 0; i < n; ++i) work[r][i] = work[r][i] / divisor;
+    }
+  }
+  if (q < p) fold_out(work, p, q, n, n, step, wire_bytes, log);
+}
+
+/* Recursive halving, then recursive doubling (Rabenseifner). The padded
+ * buffer is cut into q chunks of C = ceil(n/q). Halving step s = 1..log2(q)
+ * pairs rank r with r XOR q/2^s: the two share a range of chunks; each keeps
+ * the half whose chunk indices agree with its own rank in that bit, sends
+ * the other half to its partner, and adds the half it receives. After the
+ * last halving step rank r owns the finished chunk r, which it divides.
+ * Doubling steps then run the pairings in reverse order (distance 1 first),
+ * each rank sending everything it owns and storing what it receives, until
+ * every core rank holds the whole buffer. */
+static void rab_on_work(float **work, float **send, int32_t p, int64_t n,
+                        int64_t C, int32_t do_divide, float divisor,
+                        int64_t wire_bytes, msg_log *log) {
+  int32_t q = pow2_floor(p);
+  int64_t len = C * q;
+  int32_t step = 0;
+  if (q < p) {
+    fold_in(work, p, q, len, n, wire_bytes, log);
+    step += 1;
+  }
+  int64_t lo[64 + 1];
+  for (int32_t r = 0; r < q; ++r) lo[r] = 0;
+  int64_t cnt = q; /* chunks in each rank's current range */
+  for (int32_t d = q / 2; d >= 1; d /= 2, ++step) {
+    int64_t half = cnt / 2;
+    for (int32_t r = 0; r < q; ++r) {
+      int64_t give = (r & d) ? lo[r] : lo[r] + half;
+      memcpy(send[r], work[r] + give * C, (size_t)(half * C) * sizeof(float));
+      log_msg(log, ORC_PHASE_REDUCE_SCATTER, step, r, r ^ d, (int32_t)give,
+              half * C * wire_bytes);
+    }
+    for (int32_t r = 0; r < q; ++r) {
+      int64_t keep = (r & d) ? lo[r] + half : lo[r];
+      float *mine = work[r] + keep * C;
+      const float *got = send[r ^ d];
+      for (int64_t i = 0; i < half * C; ++i) mine[i] = mine[i] + got[i];
+    }
+    for (int32_t r = 0; r < q; ++r) {
+      if (r & d) lo[r] += half;
+    }
+    cnt = half;
+  }
+  if (do_divide) {
+    for (int32_t r = 0; r < q; ++r) {
+      float *mine = work[r] + lo[r] * C;
+      for (int64_t i = 0; i < C; ++i) mine[i] = mine[i] / divisor;
+    }
+  }
+  for (int32_t d = 1; d < q; d *= 2, ++step) {
+    for (int32_t r = 0; r < q; ++r) {
+      memcpy(send[r], work[r] + lo[r] * C, (size_t)(cnt * C) * sizeof(float));
+      log_msg(log, ORC_PHASE_ALLGATHER, step, r, r ^ d, (int32_t)lo[r],
+              cnt * C * wire_bytes);
+    }
+    for (int32_t r = 0; r < q; ++r) {
+      memcpy(work[r] + lo[r ^ d] * C, send[r ^ d],
+             (size_t)(cnt * C) * sizeof(float));
+    }
+    for (int32_t r = 0; r < q; ++r) {
+      if (r & d) lo[r] -= cnt;
+    }
+    cnt *= 2;
+  }
+  if (q < p) fold_out(work, p, q, len, n, step, wire_bytes, log);
+}
+
+/* Tree all-reduce: reduce up the doubling tree to rank 0, then broadcast
+ * down the same tree ([COL] exercise: a tree allreduce variant beside the
+ * ring; its broadcast already uses the doubling tree). Reduction runs the
+ * broadcast's rounds backwards: for span = 2^(K-1), ..., 2, 1 (K =
+ * ceil(log2 p)) every rank v < span with v + span < p receives v + span's
+ * buffer and adds it. Senders (v >= span) are never receivers in the same
+ * round, so no send buffer is needed. Rank 0 divides the finished sum. */
+static void tree_on_work(float **work, int32_t p, int64_t n, int32_t do_divide,
+                         float divisor, int64_t wire_bytes, msg_log *log) {
+  int32_t K = 0;
+  while ((1 << K) < p) K += 1;
+  int32_t step = 0;
+  for (int32_t j = K - 1; j >= 0; --j, ++step) {
+    int32_t span = 1 << j;
+    for (int32_t v = 0; v < span; ++v) {
+      if (v + span >= p) continue;
+      log_msg(log, ORC_PHASE_REDUCE, step, v + span, v, -1, n * wire_bytes);
+      for (int64_t i = 0; i < n; ++i) work[v][i] = work[v][i] + work[v + span][i];
+    }
+  }
+  if (do_divide) {
+    for (int64_t i = 0; i < n; ++i) work[0][i] = work[0][i] / divisor;
+  }
+  for (int32_t j = 0; j < K; ++j, ++step) {
+    int32_t span = 1 << j;
+    for (int32_t v = 0; v < span; ++v) {
+      if (v + span >= p) continue;
+      log_msg(log, ORC_PHASE_BROADCAST, step, v, v + span, -1, n * wire_bytes);
+      memcpy(work[v + span], work[v], (size_t)n * sizeof(float));
+    }
+  }
+}
+
+/* All-reduce of p rank arrays of n elements, in place, under `schedule`
+ * (ORC_SCHED_*). dtype, avg_mode, tokens, log, log_capacity and n_msgs as
+ * for orc_ring_allreduce (which ORC_SCHED_RING runs). Every schedule's wire
+ * carries fp32 values. */
+int orc_allreduce(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
+                  int32_t avg_mode, const int64_t *tokens, int32_t schedule,
+                  orc_msg *log, int64_t log_capacity, int64_t *n_msgs) {
+  if (schedule == ORC_SCHED_RING) {
+    return orc_ring_allreduce(bufs, p, n, dtype, avg_mode, tokens, -1, log,
+                              log_capacity, n_msgs);
+  }
+  if (p < 1 || p > 64 || n < 0 || (dtype != 0 && dtype != 1)) return ORC_EINVAL;
+  if (schedule < ORC_SCHED_RECURSIVE_DOUBLING || schedule > ORC_SCHED_TREE) {
+    return ORC_EINVAL;
+  }
+  float divisor = 1.0f;
+  int rc = avg_divisor(avg_mode, p, tokens, &divisor);
+  if (rc != ORC_OK) return rc;
+  int32_t q = pow2_floor(p);
+  int64_t C = (n + q - 1) / q;
+  int64_t len = schedule == ORC_SCHED_RABENSEIFNER ? C * q : n;
+  float **work = alloc_arrays(p, len);
+  float **send = alloc_arrays(p, len);
+  if (work == NULL || send == NULL) {
+    free_arrays(work, p);
+    free_arrays(send, p);
+    return ORC_ENOMEM;
+  }
+  for (int32_t r = 0; r < p; ++r) {
+    if (dtype == 0) {
+      memcpy(work[r], bufs[r], (size_t)n * sizeof(float));
+    } else {
+      orc_bf16_to_f32_array((const uint16_t *)bufs[r], work[r], n);
+    }
+  }
+  msg_log lg = {log, log_capacity, 0};
+  int32_t do_divide = avg_mode != ORC_AVG_NONE;
+  int64_t wire = (int64_t)sizeof(float);
+  if (schedule == ORC_SCHED_RECURSIVE_DOUBLING) {
+    rd_on_work(work, send, p, n, do_divide, divisor, wire, &lg);
+  } else if (schedule == ORC_SCHED_RABENSEIFNER) {
+    rab_on_work(work, send, p, n, C, do_divide, divisor, wire, &lg);
+  } else {
+    tree_on_work(work, p, n, do_divide, divisor, wire, &lg);
+  }
+  for (int32_t r = 0; r < p; ++r) {
+    if (dtype == 0) {
+      memcpy(bufs[r], work[r], (size_t)n * sizeof(float));
+    } else {
+      orc_f32_to_bf16_array(work[r], (uint16_t *)bufs[r], n);
+    }
+  }
+  if (n_msgs != NULL) *n_msgs = lg.count;
+  free_arrays(work, p);
+  free_arrays(send, p);
+  return ORC_OK;
+}
+
+/* The value the logarithmic schedules reach at one element, as a pairwise
+ * fold of that element's p values (vals[s*p + r] = rank r's value for
+ * sample s). With q the largest power of two <= p, leaf v < q is
+ * x[v] + x[v+q] when rank v+q exists, else x[v]. Then pairs of partial sums
+ * combine level by level:
+ *   recursive doubling   distance 1 first: (leaf 0 + leaf 1), (2 + 3), ...
+ *                        then those pairs at distance 2, and so on;
+ *   Rabenseifner, tree   distance q/2 first: (leaf 0 + leaf q/2), ... then
+ *                        q/4, and so on.
+ * Every rank of a pair computes a + b or b + a, the same number, so the
+ * pairing alone fixes the result. Derived from the exchanges each schedule
+ * performs; pinned to the literal simulations in tests. */
+void orc_tree_fold_samples(const float *vals, int32_t p, int64_t count,
+                           int32_t schedule, int32_t do_divide, float divisor,
+                           float *out) {
+  int32_t q = pow2_floor(p);
+  float t[64];
+  for (int64_t s = 0; s < count; ++s) {
+    const float *x = vals + s * p;
+    for (int32_t v = 0; v < q; ++v) t[v] = v + q < p ? x[v] + x[v + q] : x[v];
+    if (schedule == ORC_SCHED_RECURSIVE_DOUBLING) {
+      for (int32_t d = 1; d < q; d *= 2) {
+        for (int32_t v = 0; v < q; v += 2 * d) t[v] = t[v] + t[v + d];
+      }
+    } else {
+      for (int32_t d = q / 2; d >= 1; d /= 2) {
+        for (int32_t v = 0; v < d; ++v) t[v] = t[v] + t[v + d];
+      }
+    }
+    out[s] = do_divide ? t[0] / divisor : t[0];
+  }
 }
