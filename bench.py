@@ -105,7 +105,8 @@ def parse():
                     help="also time a plain device copy of this many MiB")
     ap.add_argument("--workload", default="gpt2-small-p8",
                     choices=["gpt2-small-p8", "ragged-ring-p4", "llama7b-bf16-p8",
-                             "latency-p64", "cost-model-p64", "overlap-gpt2-p8"],
+                             "latency-p64", "cost-model-p64", "overlap-gpt2-p8",
+                             "crossover-p4"],
                     help="the default is the headline; the others print their own "
                          "line for the record")
     ap.add_argument("--tokens", type=int, default=2048,
@@ -521,6 +522,65 @@ def bench_overlap(torch, ddp, W, dev, args):
            "runs_per_pass": len(reducer.launch_log())})
 
 
+def bench_crossover(torch, ddp, W, dev, args):
+    """Ring versus the logarithmic schedules on 4 ranks, step by step (one
+    launch per step: the launch is the simulated message round, so its
+    latency plays alpha and device-memory time plays beta), from 1 KB to
+    64 MB per rank. Fits alpha and beta to the ring's times, predicts the
+    ring / recursive-doubling crossover with the latency-bandwidth model,
+    and reports where the measured times cross."""
+    import numpy as np
+
+    p = 4
+    sizes = [1 << k for k in range(8, 25)]  # fp32 elements: 1 KB .. 64 MB per rank
+    scheds = ["ring", "recursive_doubling", "rabenseifner", "tree"]
+    nmax = sizes[-1]
+    arena = [W.normal_torch(nmax, 1.0, 44, r, dev) for r in range(p)]
+    table = {}
+    for n in sizes:
+        bufs = [a[:n] for a in arena]
+        reps = 200 if n * 4 <= (1 << 20) else (40 if n * 4 <= (1 << 24) else 10)
+        row = {}
+        for sch in scheds:
+            for steps in (True, False):
+                fn = (lambda b=bufs, s=sch, st=steps:
+                      ddp.allreduce_sim(b, s, st, avg="world"))
+                for _ in range(3):
+                    fn()
+                _, dms = _timed_calls(torch, ddp, [fn], reps)
+                row[f"{sch}{'_steps' if steps else '_fused'}_us"] = round(dms * 1e3, 2)
+        table[n * 4] = row
+        log(f"crossover: {n * 4} bytes done")
+    # alpha, beta from the ring's step form: t = 2(p-1)(alpha + beta M / p)
+    xs = np.array([float(m) for m in table])
+    ts = np.array([table[m]["ring_steps_us"] * 1e-6 for m in table])
+    A = np.stack([np.full_like(xs, 2.0 * (p - 1)), 2.0 * (p - 1) * xs / p], axis=1)
+    (alpha, beta), *_ = np.linalg.lstsq(A, ts, rcond=None)
+    lg = np.log2(p)
+    mstar = (alpha / beta) * (2 * (p - 1) - lg) / (lg - 2 * (p - 1) / p)
+    cross = None
+    ms = sorted(table)
+    for a, b in zip(ms, ms[1:]):
+        da = table[a]["recursive_doubling_steps_us"] - table[a]["ring_steps_us"]
+        db = table[b]["recursive_doubling_steps_us"] - table[b]["ring_steps_us"]
+        if da < 0 <= db:
+            # log-linear interpolation of where the difference changes sign
+            f = -da / (db - da)
+            cross = float(np.exp(np.log(a) + f * (np.log(b) - np.log(a))))
+            break
+    pick = {m: min(scheds, key=lambda s: table[m][f"{s}_steps_us"]) for m in ms}
+    _line("ring vs recursive-doubling crossover, p=4, step-by-step schedules",
+          cross if cross is not None else float("nan"), "bytes per rank",
+          "crossover sweep: p=4, one fp32 tensor of 1 KB .. 64 MB per rank, average by p, "
+          "each schedule step by step (one launch per message round) and fused",
+          {"higher_is_better": False,
+           "model": {"alpha_us": round(alpha * 1e6, 3), "beta_ns_per_byte": round(beta * 1e9, 6),
+                     "predicted_crossover_bytes": round(float(mstar), 1)},
+           "fastest_step_schedule": {str(m): pick[m] for m in ms},
+           "the_three_sizes": {str(m): table[m] for m in (1 << 10, 1 << 20, 1 << 24)},
+           "sweep_us": {str(m): table[m] for m in ms}})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -539,7 +599,7 @@ def main():
     ddp.load_library()
     other = {"ragged-ring-p4": bench_ragged, "llama7b-bf16-p8": bench_llama,
              "latency-p64": bench_latency, "cost-model-p64": bench_costmodel,
-             "overlap-gpt2-p8": bench_overlap}
+             "overlap-gpt2-p8": bench_overlap, "crossover-p4": bench_crossover}
     if args.workload in other:
         log(f"workload {args.workload}")
         other[args.workload](torch, ddp, W, dev, args)

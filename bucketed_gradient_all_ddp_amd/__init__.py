@@ -1,18 +1,18 @@
 """bucketed_gradient_all_ddp_amd -- the data-parallel gradient-synchronisation
 hot path (bucket plan, flatten, ring all-reduce with averaging, unflatten,
-standalone reduce-scatter / all-gather / broadcast) for p simulated ranks in
-one gfx950 GPU's HBM.
+standalone reduce-scatter / all-gather / broadcast, the logarithmic-latency
+all-reduce schedules and their choice by size) for p simulated ranks in one
+gfx950 GPU's HBM.
 
 The compute lives in libddpsim.so (HIP kernels behind the C ABI declared in
 include/ddpsim.h); `binding` marshals torch tensors to it. `workloads` holds
 the seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
-    ALGO, AVG, DTYPE_BF16, DTYPE_F32, EXPORTS, MAX_RANKS, CallTimer, CommStats, DDPError, Plan,
-    Reducer,
-    allgather_sim, broadcast_sim, ddp_allreduce_bucket, ddp_allreduce_buckets, ddp_bucket_plan,
-    ddp_flatten,
-    ddp_unflatten,
+    ALGO, AVG, DTYPE_BF16, DTYPE_F32, EXPORTS, MAX_RANKS, SCHEDULES, CallTimer, CommStats,
+    DDPError, Plan, Reducer,
+    allgather_sim, allreduce_sim, allreduce_sim_workspace, broadcast_sim, choose_schedule,
+    ddp_allreduce_bucket, ddp_allreduce_buckets, ddp_bucket_plan, ddp_flatten, ddp_unflatten,
     grad_pointer_table, load_library, reduce_scatter_sim, ring_allreduce_sim,
-    ring_allreduce_sim_steps, ring_allreduce_sim_workspace,
+    ring_allreduce_sim_steps, ring_allreduce_sim_workspace, schedule_time,
 )

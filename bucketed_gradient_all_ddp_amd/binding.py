@@ -40,8 +40,11 @@ EXPORTS = [
     "ddp_reducer_create", "ddp_reducer_free", "ddp_reducer_prepare", "ddp_reducer_mark_ready",
     "ddp_reducer_finalize", "ddp_reducer_launch_log",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
+    "allreduce_sim", "allreduce_sim_workspace", "ddp_schedule_time", "ddp_choose_schedule",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
 ]
+
+SCHEDULES = {"ring": 0, "recursive_doubling": 1, "rabenseifner": 2, "tree": 3}
 
 
 class DDPError(RuntimeError):
@@ -115,6 +118,12 @@ def load_library(path: str = LIB_PATH):
         "ring_allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, vp, sz, vp, vp], st),
         "ring_allreduce_sim_workspace": ([i32, i64, i32, i32], sz),
         "ring_allreduce_sim_steps": ([vp, i32, i64, i32, vp, i32, i32, vp], st),
+        "allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, i32, vp, sz, vp, vp], st),
+        "allreduce_sim_workspace": ([i32, i64, i32, i32, i32], sz),
+        "ddp_schedule_time": ([i32, i32, ctypes.c_double, ctypes.c_double, ctypes.c_double],
+                              ctypes.c_double),
+        "ddp_choose_schedule": ([i32, i64, ctypes.c_double, ctypes.c_double, ctypes.c_uint32],
+                                i32),
         "reduce_scatter_sim": ([vp, vp, i32, i64, i32, i32, vp, vp, vp], st),
         "allgather_sim": ([vp, vp, i32, i64, i32, vp, vp], st),
         "broadcast_sim": ([vp, i32, i64, i32, i32, vp, vp], st),
@@ -446,6 +455,47 @@ def ring_allreduce_sim_steps(bufs: Sequence, first_step: int, n_steps: int,
     _check(load_library().ring_allreduce_sim_steps(
         _ptrs(bufs), p, n, AVG[avg], _tokens(tokens, p), first_step, n_steps,
         _stream(stream)), "ring_allreduce_sim_steps")
+
+
+def allreduce_sim_workspace(p: int, n: int, dtype: int, schedule: str = "ring",
+                            steps: bool = False) -> int:
+    return load_library().allreduce_sim_workspace(p, n, dtype, SCHEDULES[schedule],
+                                                  1 if steps else 0)
+
+
+def allreduce_sim(bufs: Sequence, schedule: str = "ring", steps: bool = False,
+                  avg: str = "none", tokens=None, workspace=None, stream=None) -> CommStats:
+    """In-place all-reduce under a schedule ("ring", "recursive_doubling",
+    "rabenseifner", "tree"), as one fused pass or step by step."""
+    p = len(bufs)
+    n = _numel_all(bufs)
+    st = CommStats()
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().allreduce_sim(
+        _ptrs(bufs), p, n, _dtype_code(bufs[0]), AVG[avg], _tokens(tokens, p),
+        SCHEDULES[schedule], 1 if steps else 0, ws_ptr, ws_bytes, _stream(stream),
+        ctypes.byref(st)), "allreduce_sim")
+    return st
+
+
+def schedule_time(schedule: str, p: int, nbytes: float, alpha: float, beta: float) -> float:
+    """Latency-bandwidth model time of one all-reduce of nbytes."""
+    return load_library().ddp_schedule_time(SCHEDULES[schedule], p, nbytes, alpha, beta)
+
+
+def choose_schedule(p: int, nbytes: int, alpha: float, beta: float,
+                    candidates: Sequence[str] = ("ring", "recursive_doubling")) -> str:
+    """The candidate schedule with the smallest model time (ties to the lower
+    schedule number)."""
+    mask = 0
+    for c in candidates:
+        mask |= 1 << SCHEDULES[c]
+    s = load_library().ddp_choose_schedule(p, nbytes, alpha, beta, mask)
+    if s < 0:
+        raise DDPError(1, "ddp_choose_schedule",
+                       load_library().ddp_last_error().decode(errors="replace"))
+    return {v: k for k, v in SCHEDULES.items()}[s]
 
 
 def reduce_scatter_sim(inputs: Sequence, outputs: Sequence, avg: str = "none",

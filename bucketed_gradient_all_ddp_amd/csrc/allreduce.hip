@@ -25,6 +25,7 @@
 
 #include "fold.hpp"
 #include "internal.hpp"
+#include "workspace.hpp"
 
 namespace ddpsim {
 namespace {
@@ -153,49 +154,6 @@ __global__ __launch_bounds__(kThreads) void ring_step_kernel(
   }
 }
 
-// bf16 rank buffers <-> fp32 workspace rows (row r at ws + r * stride).
-template <bool kToWorkspace>
-__global__ __launch_bounds__(kThreads) void bf16_workspace_kernel(
-    RankTable bufs, float *ws, int64_t ws_stride, int64_t n,
-    int32_t tiles_per_rank) {
-  constexpr int kElems = 8;  // one 16-byte bf16 vector, two fp32 vectors
-  const int32_t r = static_cast<int32_t>(blockIdx.x) / tiles_per_rank;
-  const int32_t t = static_cast<int32_t>(blockIdx.x) - r * tiles_per_rank;
-  uint16_t *b = static_cast<uint16_t *>(bufs.ptr[r]);
-  float *w = ws + r * ws_stride;
-  const int64_t v = static_cast<int64_t>(t) * kThreads + threadIdx.x;
-  const int64_t i0 = v * kElems;
-  if (i0 >= n) return;
-  if (i0 + kElems <= n) {
-    if (kToWorkspace) {
-      float f[8];
-      BF16Traits::widen(load_vec(b, v), f);
-      store_vec<false>(w, 2 * v, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
-                                            __float_as_uint(f[2]), __float_as_uint(f[3])));
-      store_vec<false>(w, 2 * v + 1, make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]),
-                                                __float_as_uint(f[6]), __float_as_uint(f[7])));
-    } else {
-      float f[8];
-      float lo[4], hi[4];
-      F32Traits::widen(load_vec(w, 2 * v), lo);
-      F32Traits::widen(load_vec(w, 2 * v + 1), hi);
-      for (int e = 0; e < 4; ++e) {
-        f[e] = lo[e];
-        f[e + 4] = hi[e];
-      }
-      store_vec<false>(b, v, BF16Traits::narrow(f));
-    }
-  } else {
-    for (int64_t i = i0; i < n; ++i) {
-      if (kToWorkspace) {
-        w[i] = BF16Traits::load1(b, i);
-      } else {
-        BF16Traits::store1(b, i, w[i]);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -301,10 +259,6 @@ ddp_status launch_steps(const RankTable &tab, int32_t p, int64_t n, const Divide
   return DDP_OK;
 }
 
-int64_t workspace_stride_elems(int64_t n) {
-  // fp32 rows rounded up to 256 bytes
-  return ceil_div(n * 4, 256) * 256 / 4;
-}
 
 void fill_allreduce_stats(ddp_comm_stats *st, int32_t p, int64_t n, int32_t dtype,
                           int32_t algo) {
@@ -325,18 +279,6 @@ void fill_allreduce_stats(ddp_comm_stats *st, int32_t p, int64_t n, int32_t dtyp
   }
 }
 
-ddp_status validate_common(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
-                           int32_t avg_mode, const int64_t *tokens, Divide *div,
-                           const char *what) {
-  ddp_status s = check_p(p, what);
-  if (s != DDP_OK) return s;
-  if (n < 0) return fail(DDP_EINVAL, "%s: n=%lld is negative", what, (long long)n);
-  const int eb = elem_bytes_of(dtype);
-  if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
-  s = make_divide(avg_mode, p, tokens, div);
-  if (s != DDP_OK) return s;
-  return check_rank_buffers(what, bufs, p, n * eb);
-}
 
 }  // namespace
 }  // namespace ddpsim
@@ -358,28 +300,16 @@ extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n
   clear_error();
   CallTimer timer = CallTimer::take();
   Divide div;
-  ddp_status s = validate_common(bufs, p, n, dtype, avg_mode, tokens, &div,
+  ddp_status s = validate_allreduce(bufs, p, n, dtype, avg_mode, tokens, &div,
                                  "ring_allreduce_sim");
   if (s != DDP_OK) return s;
   if (algo != DDP_ALGO_FUSED && algo != DDP_ALGO_RING) {
     return fail(DDP_EINVAL, "ring_allreduce_sim: unknown algorithm %d", algo);
   }
   const size_t need = ring_allreduce_sim_workspace(p, n, dtype, algo);
-  if (need > 0) {
-    if (workspace == nullptr || workspace_bytes < need) {
-      return fail(DDP_EWORKSPACE, "ring_allreduce_sim: needs %zu workspace bytes, got %zu",
-                  need, workspace == nullptr ? size_t(0) : workspace_bytes);
-    }
-    if (reinterpret_cast<uintptr_t>(workspace) % kVecBytes != 0) {
-      return fail(DDP_EALIGN, "ring_allreduce_sim: workspace is not 16-byte aligned");
-    }
-    const int64_t eb = elem_bytes_of(dtype);
-    for (int32_t r = 0; r < p; ++r) {
-      if (ranges_overlap(workspace, int64_t(need), bufs[r], n * eb)) {
-        return fail(DDP_EALIAS, "ring_allreduce_sim: workspace overlaps rank %d", r);
-      }
-    }
-  }
+  s = check_workspace("ring_allreduce_sim", workspace, workspace_bytes, need, bufs, p,
+                      n * elem_bytes_of(dtype));
+  if (s != DDP_OK) return s;
   fill_allreduce_stats(stats, p, n, dtype, algo);
   if (n == 0) return DDP_OK;
   const RankTable tab = make_table(bufs, p);
@@ -411,7 +341,7 @@ extern "C" ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int
   clear_error();
   CallTimer timer = CallTimer::take();
   Divide div;
-  ddp_status s = validate_common(bufs, p, n, DDP_F32, avg_mode, tokens, &div,
+  ddp_status s = validate_allreduce(bufs, p, n, DDP_F32, avg_mode, tokens, &div,
                                  "ring_allreduce_sim_steps");
   if (s != DDP_OK) return s;
   if (p < 2) return fail(DDP_ERANGE, "ring_allreduce_sim_steps: needs p >= 2");

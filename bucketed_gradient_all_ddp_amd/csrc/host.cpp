@@ -140,6 +140,38 @@ ddp_status make_divide(int32_t avg_mode, int32_t p, const int64_t *tokens,
   return DDP_OK;
 }
 
+ddp_status validate_allreduce(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
+                              int32_t avg_mode, const int64_t *tokens, Divide *div,
+                              const char *what) {
+  ddp_status s = check_p(p, what);
+  if (s != DDP_OK) return s;
+  if (n < 0) return fail(DDP_EINVAL, "%s: n=%lld is negative", what, (long long)n);
+  const int eb = elem_bytes_of(dtype);
+  if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  s = make_divide(avg_mode, p, tokens, div);
+  if (s != DDP_OK) return s;
+  return check_rank_buffers(what, bufs, p, n * eb);
+}
+
+ddp_status check_workspace(const char *what, const void *workspace, size_t workspace_bytes,
+                           size_t need, const void *const *bufs, int32_t p,
+                           int64_t buf_bytes) {
+  if (need == 0) return DDP_OK;
+  if (workspace == nullptr || workspace_bytes < need) {
+    return fail(DDP_EWORKSPACE, "%s: needs %zu workspace bytes, got %zu", what, need,
+                workspace == nullptr ? size_t(0) : workspace_bytes);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kVecBytes != 0) {
+    return fail(DDP_EALIGN, "%s: workspace is not 16-byte aligned", what);
+  }
+  for (int32_t r = 0; r < p; ++r) {
+    if (ranges_overlap(workspace, int64_t(need), bufs[r], buf_bytes)) {
+      return fail(DDP_EALIAS, "%s: workspace overlaps rank %d", what, r);
+    }
+  }
+  return DDP_OK;
+}
+
 RankTable make_table(const void *const *bufs, int32_t p) {
   RankTable t;
   std::memset(&t, 0, sizeof t);

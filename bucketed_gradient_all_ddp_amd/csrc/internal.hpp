@@ -120,6 +120,17 @@ ddp_status make_divide(int32_t avg_mode, int32_t p, const int64_t *tokens,
 
 RankTable make_table(const void *const *bufs, int32_t p);
 
+// p, n, dtype, averaging and rank buffers of an in-place all-reduce.
+ddp_status validate_allreduce(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
+                              int32_t avg_mode, const int64_t *tokens, Divide *div,
+                              const char *what);
+
+// A workspace of `need` bytes (nothing to check when need is 0): present,
+// large enough, 16-byte aligned, disjoint from the p rank buffers.
+ddp_status check_workspace(const char *what, const void *workspace, size_t workspace_bytes,
+                           size_t need, const void *const *bufs, int32_t p,
+                           int64_t buf_bytes);
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Timing requested with ddp_time_next_call: the events are attached to the

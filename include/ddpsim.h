@@ -356,6 +356,87 @@ ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int64_t n,
                                     hipStream_t stream);
 
 /* ----------------------------------------------------------------------- */
+/* All-reduce schedules and their choice by message size                   */
+/* ----------------------------------------------------------------------- */
+
+/* The all-reduce schedules ([DP] "Latency, trees, and choosing an
+ * algorithm"; [COL], its exercise of a tree all-reduce beside the ring):
+ *   DDP_SCHED_RING                the ring of ring_allreduce_sim.
+ *   DDP_SCHED_RECURSIVE_DOUBLING  log2 p steps; in step j every rank swaps
+ *                                 its whole buffer with rank r XOR 2^j and
+ *                                 both add.
+ *   DDP_SCHED_RABENSEIFNER        recursive halving (partner at distance
+ *                                 p/2, then p/4, ...; each keeps the half
+ *                                 of its range matching its own rank and
+ *                                 adds the partner's copy of it), then
+ *                                 recursive doubling of the owned ranges.
+ *   DDP_SCHED_TREE                reduce up the doubling tree of
+ *                                 broadcast_sim to rank 0, then broadcast
+ *                                 down it; 2 ceil(log2 p) steps.
+ * For p not a power of two (q = the largest power of two below p),
+ * recursive doubling and Rabenseifner first fold each extra rank r >= q into
+ * rank r - q and finally copy the result back to it. Each schedule fixes
+ * its own summation order: the ring folds chunk c from rank c; recursive
+ * doubling is a pairwise sum over ranks, nearest neighbours first;
+ * Rabenseifner and the tree are the pairwise sum that pairs ranks q/2
+ * apart first. Results differ between schedules in the last bits; each is
+ * bit-identical to its literal schedule. */
+typedef enum {
+  DDP_SCHED_RING = 0,
+  DDP_SCHED_RECURSIVE_DOUBLING = 1,
+  DDP_SCHED_RABENSEIFNER = 2,
+  DDP_SCHED_TREE = 3
+} ddp_schedule;
+
+/* In-place all-reduce of p rank buffers under `schedule`. Arguments as for
+ * ring_allreduce_sim, except:
+ *   schedule   ddp_schedule
+ *   steps      0: one fused pass that reads each buffer once, folds every
+ *              element in the schedule's order and writes all ranks
+ *              (device traffic 2 p n bytes-per-element); 1: the schedule
+ *              step by step, one kernel launch per step, each step moving
+ *              the data its messages carry between rank buffers in device
+ *              memory (bf16 runs on an fp32 workspace). Same bits either way.
+ *   workspace  allreduce_sim_workspace() bytes (0 unless steps with bf16).
+ * The stats describe the logical schedule (steps, messages, bytes per
+ * rank on an fp32 wire) and the device traffic of the form that ran.
+ * DDP_SCHED_RING is ring_allreduce_sim (steps selects DDP_ALGO_RING).
+ * Errors: as ring_allreduce_sim; DDP_EINVAL for an unknown schedule. */
+ddp_status allreduce_sim(void *const *bufs, int32_t p, int64_t n,
+                         int32_t dtype, int32_t avg_mode,
+                         const int64_t *tokens, int32_t schedule,
+                         int32_t steps, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream,
+                         ddp_comm_stats *stats);
+
+/* Workspace bytes allreduce_sim needs (0 unless steps == 1 with bf16). */
+size_t allreduce_sim_workspace(int32_t p, int64_t n, int32_t dtype,
+                               int32_t schedule, int32_t steps);
+
+/* Latency-bandwidth (Hockney) time of one all-reduce of `bytes` under a
+ * schedule ([DP] "Ring all-reduce, derived" and "Latency, trees, and
+ * choosing an algorithm"): alpha seconds per step plus beta seconds per
+ * byte of each step's largest message. For p a power of two: ring
+ * 2(p-1)(alpha + beta bytes/p); recursive doubling
+ * log2 p (alpha + beta bytes); Rabenseifner 2 log2 p alpha +
+ * 2(p-1)/p bytes beta; tree 2 log2 p (alpha + beta bytes). Other p add the
+ * two whole-buffer steps of the extra ranks (the tree takes
+ * 2 ceil(log2 p) steps). Returns a negative value for bad arguments. */
+double ddp_schedule_time(int32_t schedule, int32_t p, double bytes,
+                         double alpha, double beta);
+
+/* The schedule with the smallest ddp_schedule_time among the candidates
+ * (bit s of `candidates` set = schedule s allowed), ties to the lower
+ * schedule number: libraries pick the algorithm per call from the message
+ * size ([DP] "Latency, trees, and choosing an algorithm"; [COL] describes
+ * NCCL taking the ring for large messages and a tree for small ones).
+ * With the ring and recursive doubling as candidates the choice flips at
+ * the crossover size the page derives.
+ * Returns -1 (with ddp_last_error) for bad arguments or no candidate. */
+int32_t ddp_choose_schedule(int32_t p, int64_t bytes, double alpha,
+                            double beta, uint32_t candidates);
+
+/* ----------------------------------------------------------------------- */
 /* Standalone collectives                                                  */
 /* ----------------------------------------------------------------------- */
 

@@ -226,3 +226,64 @@ def test_reducer_errors_without_launching():
         assert L.ddp_reducer_finalize(r, None) == 1            # pass already ended
     finally:
         L.ddp_reducer_free(r)
+
+
+def test_schedule_argument_errors():
+    L = load_library()
+    n = 1000
+    f = L.allreduce_sim
+    ok = _fake(4, n * 4)
+    assert f(ok, 4, n, 0, 0, None, 4, 0, None, 0, None, None) == 1   # unknown schedule
+    assert f(ok, 4, n, 0, 0, None, -1, 0, None, 0, None, None) == 1
+    assert f(ok, 4, n, 0, 0, None, 1, 2, None, 0, None, None) == 1   # steps not 0/1
+    assert f(_fake(1, 4), 0, n, 0, 0, None, 2, 0, None, 0, None, None) == 2
+    assert f(_fake(65, 4), 65, 1, 0, 0, None, 3, 1, None, 0, None, None) == 2
+    assert f(ok, 4, n, 5, 0, None, 1, 0, None, 0, None, None) == 1
+    assert f(_fake(4, n * 4, misalign=1), 4, n, 0, 0, None, 1, 0, None, 0, None, None) == 3
+    # bf16 step by step needs the fp32 workspace
+    need = L.allreduce_sim_workspace(4, n, 1, 2, 1)
+    assert need >= 4 * n * 4
+    assert f(ok, 4, n, 1, 0, None, 2, 1, None, 0, None, None) == 7
+    small = ctypes.c_void_p(0x500000000)
+    assert f(ok, 4, n, 1, 0, None, 2, 1, small, need - 1, None, None) == 7
+    assert f(ok, 4, n, 1, 0, None, 2, 1, ctypes.c_void_p(0x100000000 + 64), need,
+             None, None) == 4  # workspace over the rank buffers
+    for sched in (1, 2, 3):
+        assert L.allreduce_sim_workspace(4, n, 1, sched, 0) == 0
+        assert L.allreduce_sim_workspace(4, n, 0, sched, 1) == 0
+        assert L.allreduce_sim_workspace(1, n, 1, sched, 1) == 0
+    # the ring schedule is ring_allreduce_sim
+    assert L.allreduce_sim_workspace(4, n, 1, 0, 1) == L.ring_allreduce_sim_workspace(4, n, 1, 1)
+    # n == 0: no-op with the schedule's accounting
+    st = ddp.CommStats()
+    assert f(ok, 8, 0, 0, 1, None, 1, 0, None, 0, None, ctypes.byref(st)) == 0
+    assert st.steps == 3 and st.messages == 24 and st.bytes_sent_per_rank == 0
+
+
+@pytest.mark.parametrize("schedule", ["ring", "recursive_doubling", "rabenseifner", "tree"])
+@pytest.mark.parametrize("p", [1, 2, 3, 4, 5, 8, 12, 64, 512, 1000])
+def test_schedule_time_matches_oracle_model(schedule, p):
+    from oracle import costmodel as cm
+    for M, a, b in [(0.0, 10e-6, 2e-11), (1e3, 10e-6, 2e-11), (4.4e6, 10e-6, 2e-11),
+                    (1e9, 3e-6, 1 / 150e9)]:
+        got = ddp.schedule_time(schedule, p, M, a, b)
+        assert got == pytest.approx(cm.schedule_time(schedule, M, p, a, b), rel=1e-12, abs=0)
+
+
+def test_choose_schedule_matches_oracle_and_flips_at_crossover():
+    from oracle import costmodel as cm
+    a, b = 10e-6, 1 / 50e9
+    sets = [("ring", "recursive_doubling"), ("ring", "tree"),
+            ("ring", "recursive_doubling", "rabenseifner", "tree"), ("tree",)]
+    for cand in sets:
+        for p in (2, 3, 4, 8, 17, 64, 512):
+            for M in (1, 1000, 10 ** 5, 10 ** 6, 4_400_000, 10 ** 7, 10 ** 8, 10 ** 9):
+                assert ddp.choose_schedule(p, M, a, b, cand) == cm.choose_schedule(p, M, a, b, cand)
+    for p, mstar in ((8, 4.4e6), (512, 72.3e6)):
+        assert ddp.choose_schedule(p, int(0.99 * mstar), a, b) == "recursive_doubling"
+        assert ddp.choose_schedule(p, int(1.01 * mstar), a, b) == "ring"
+    L = load_library()
+    assert L.ddp_choose_schedule(8, 100, a, b, 0) == -1
+    assert L.ddp_choose_schedule(0, 100, a, b, 3) == -1
+    assert L.ddp_choose_schedule(8, -1, a, b, 3) == -1
+    assert L.ddp_schedule_time(9, 8, 1.0, a, b) < 0
