@@ -423,6 +423,11 @@ def bench_costmodel(torch, ddp, W, dev, args):
         "allgather_inplace": (lambda: ddp.allgather_sim(shards, bufs), (p - 1) / p, p * S),
         "broadcast": (lambda: ddp.broadcast_sim(bufs, src=0), 1.0, p * S),
     }
+    # the same all-reduce under the logarithmic schedules, fused (one pass each)
+    for sch in ("recursive_doubling", "rabenseifner", "tree"):
+        ops[f"allreduce_tokens_{sch}"] = (
+            lambda s=sch: ddp.allreduce_sim(bufs, s, False, avg="tokens", tokens=tokens),
+            2 * (p - 1) / p, 2 * p * S)
     res = {}
     for name, (fn, busf, hbm) in ops.items():
         fn()
@@ -434,7 +439,8 @@ def bench_costmodel(torch, ddp, W, dev, args):
     _line("all-reduce bus GB/s, p=64, 2 GiB fp32 per rank, token-weighted",
           res["allreduce_tokens"]["bus_GBps"], "GB/s",
           "cost-model shape: one 2^29-element fp32 tensor per rank (2 GiB), p=64, tokens "
-          "U{10..10000}; plus reduce-scatter, in-place all-gather and broadcast",
+          "U{10..10000}; plus reduce-scatter, in-place all-gather, broadcast, and the "
+          "all-reduce under recursive doubling, Rabenseifner and the tree (fused)",
           {"ops": res})
 
 
