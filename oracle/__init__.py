@@ -92,6 +92,12 @@ def _load():
     i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     lib.orc_bucket_plan.argtypes = [P, i32, i32, i64, i64, P, P, P, P, P]
     lib.orc_bucket_plan.restype = ctypes.c_int
+    lib.orc_bucket_plan_ordered.argtypes = [P, i32, P, i32, i64, i64, P, P, P, P, P]
+    lib.orc_bucket_plan_ordered.restype = ctypes.c_int
+    lib.orc_coalesce_plan.argtypes = [P, i32, i32, i64, P, P, P, P, P]
+    lib.orc_coalesce_plan.restype = ctypes.c_int
+    lib.orc_broadcast_coalesced.argtypes = [P, P, i32, i32, i32, i64, i32, P, i64, P, P]
+    lib.orc_broadcast_coalesced.restype = ctypes.c_int
     lib.orc_flatten.argtypes = [P, P, P, P, P, i32, i32, f32, P]
     lib.orc_flatten.restype = ctypes.c_int
     lib.orc_unflatten.argtypes = [P, P, P, P, P, i32, i32, P]
@@ -237,8 +243,11 @@ class Plan:
 
 def bucket_plan(numel: Sequence[int], elem_bytes: int = 4,
                 bucket_cap_bytes: int = 25 * 1024 * 1024,
-                first_bucket_cap_bytes: int = 1024 * 1024) -> Plan:
-    """Greedy reverse-registration bucketing with a small first bucket."""
+                first_bucket_cap_bytes: int = 1024 * 1024,
+                order: Optional[Sequence[int]] = None) -> Plan:
+    """Greedy bucketing with a small first bucket, walking the parameters in
+    reverse registration order, or in `order` (a permutation: the order in
+    which gradients became ready, for a rebuild)."""
     lib = _load()
     nm = np.ascontiguousarray(np.asarray(numel, dtype=np.int64))
     P = len(nm)
@@ -247,14 +256,70 @@ def bucket_plan(numel: Sequence[int], elem_bytes: int = 4,
     offset = np.zeros(max(P, 1), dtype=np.int64)
     bucket_of = np.zeros(max(P, 1), dtype=np.int32)
     nb = np.zeros(1, dtype=np.int32)
-    rc = lib.orc_bucket_plan(_ptr(nm) if P else None, P, elem_bytes,
-                             bucket_cap_bytes, first_bucket_cap_bytes,
-                             _ptr(fill), _ptr(begin), _ptr(offset),
-                             _ptr(bucket_of), _ptr(nb))
+    if order is None:
+        rc = lib.orc_bucket_plan(_ptr(nm) if P else None, P, elem_bytes,
+                                 bucket_cap_bytes, first_bucket_cap_bytes,
+                                 _ptr(fill), _ptr(begin), _ptr(offset),
+                                 _ptr(bucket_of), _ptr(nb))
+    else:
+        walk = np.ascontiguousarray(np.asarray(order, dtype=np.int32))
+        if walk.shape != (P,):
+            raise ValueError("order must list every parameter once")
+        rc = lib.orc_bucket_plan_ordered(_ptr(nm) if P else None, P,
+                                         _ptr(walk) if P else None, elem_bytes,
+                                         bucket_cap_bytes, first_bucket_cap_bytes,
+                                         _ptr(fill), _ptr(begin), _ptr(offset),
+                                         _ptr(bucket_of), _ptr(nb))
     _check(rc, "bucket_plan")
     B = int(nb[0])
     return Plan(nm, elem_bytes, fill[:P].copy(), begin[:B + 1].copy(),
                 offset[:P].copy(), bucket_of[:P].copy())
+
+
+def coalesce_plan(numel: Sequence[int], elem_bytes: int,
+                  cap_bytes: int = 250 * 1024 * 1024) -> Plan:
+    """Buckets of a coalesced broadcast: list order, none past the cap unless
+    one tensor alone is."""
+    lib = _load()
+    nm = np.ascontiguousarray(np.asarray(numel, dtype=np.int64))
+    P = len(nm)
+    fill = np.zeros(max(P, 1), dtype=np.int32)
+    begin = np.zeros(P + 2, dtype=np.int32)
+    offset = np.zeros(max(P, 1), dtype=np.int64)
+    bucket_of = np.zeros(max(P, 1), dtype=np.int32)
+    nb = np.zeros(1, dtype=np.int32)
+    rc = lib.orc_coalesce_plan(_ptr(nm) if P else None, P, elem_bytes, cap_bytes,
+                               _ptr(fill), _ptr(begin), _ptr(offset), _ptr(bucket_of),
+                               _ptr(nb))
+    _check(rc, "coalesce_plan")
+    B = int(nb[0])
+    return Plan(nm, elem_bytes, fill[:P].copy(), begin[:B + 1].copy(),
+                offset[:P].copy(), bucket_of[:P].copy())
+
+
+def broadcast_coalesced(tensors: Sequence[Sequence[np.ndarray]], root: int = 0,
+                        cap_bytes: int = 250 * 1024 * 1024):
+    """tensors[r][i] = rank r's copy of tensor i (one dtype). Returns
+    (results in the same layout, message log, bucket of each tensor)."""
+    lib = _load()
+    p = len(tensors)
+    n_t = len(tensors[0]) if p else 0
+    work = [[np.array(t, copy=True).ravel() for t in row] for row in tensors]
+    eb = work[0][0].itemsize if n_t else 4
+    numel = np.array([work[0][i].size for i in range(n_t)], dtype=np.int64)
+    for row in work:
+        if [t.size for t in row] != list(numel):
+            raise ValueError("every rank must hold the same tensor shapes")
+    table = _ptr_table([t for row in work for t in row])
+    cap = p * max(n_t, 1) + 1
+    log = np.zeros(cap, dtype=_MSG_DTYPE)
+    count = np.zeros(1, dtype=np.int64)
+    bof = np.zeros(max(n_t, 1), dtype=np.int32)
+    rc = lib.orc_broadcast_coalesced(_ptr(table), _ptr(numel) if n_t else None, n_t, p,
+                                     eb, cap_bytes, root, _ptr(log), cap, _ptr(count),
+                                     _ptr(bof))
+    _check(rc, "broadcast_coalesced")
+    return work, _messages(log, int(count[0])), [int(b) for b in bof[:n_t]]
 
 
 def flatten(grads: Sequence[np.ndarray], plan: Plan, b: int,

@@ -50,6 +50,11 @@
  *                       i.e. Rabenseifner's algorithm) or the tree all-reduce
  *                       that [COL] sets as an exercise (reduce up the
  *                       doubling tree, broadcast down it).
+ *   orc_bucket_plan_ordered  the bucketing rule over an explicit order (the
+ *                       rebuild from the observed ready order, [DDP] Part 2).
+ *   orc_broadcast_coalesced  many tensors broadcast in capped buckets:
+ *                       flatten at the root, doubling-tree broadcast,
+ *                       unflatten everywhere ([DDP] Parts 1 and 2).
  *   orc_tree_fold_samples  the per-element value those schedules reach,
  *                       written as a pairwise fold; pinned to the literal
  *                       simulations in tests.
@@ -221,21 +226,42 @@ int orc_avg_divisor(int32_t mode, int32_t p, const int64_t *tokens,
  *   offset[i]         element offset of parameter i inside its bucket
  *   bucket_of[i]      bucket that holds parameter i
  */
-int orc_bucket_plan(const int64_t *numel, int32_t n_params, int32_t elem_bytes,
-                    int64_t cap, int64_t first_cap, int32_t *fill_order,
-                    int32_t *bucket_begin, int64_t *offset, int32_t *bucket_of,
-                    int32_t *n_buckets) {
+/* The same greedy bucketing over an explicit walk order: walk[k] is the
+ * k-th parameter to place (a permutation of 0..n_params-1), or NULL for the
+ * reverse registration order above. DDP rebuilds its buckets once from the
+ * order in which gradients actually became ready in the first backward pass
+ * ("PyTorch DDP Deep Dive", Part 2: the hook records each ready parameter
+ * while buckets are due for a rebuild, and the rebuild runs before the next
+ * forward); the rule applied to that order is the same. */
+int orc_bucket_plan_ordered(const int64_t *numel, int32_t n_params,
+                            const int32_t *walk, int32_t elem_bytes,
+                            int64_t cap, int64_t first_cap,
+                            int32_t *fill_order, int32_t *bucket_begin,
+                            int64_t *offset, int32_t *bucket_of,
+                            int32_t *n_buckets) {
   if (n_params < 0 || elem_bytes <= 0 || cap < 0 || first_cap < 0) {
     return ORC_EINVAL;
   }
   for (int32_t i = 0; i < n_params; ++i) {
     if (numel[i] < 0) return ORC_EINVAL;
   }
+  if (walk != NULL) {
+    char *seen = (char *)calloc((size_t)n_params + 1, 1);
+    if (seen == NULL) return ORC_ENOMEM;
+    int bad = 0;
+    for (int32_t k = 0; k < n_params && !bad; ++k) {
+      if (walk[k] < 0 || walk[k] >= n_params || seen[walk[k]]) bad = 1;
+      else seen[walk[k]] = 1;
+    }
+    free(seen);
+    if (bad) return ORC_EINVAL;
+  }
   int32_t buckets = 0;       /* buckets opened so far */
   int32_t filled = 0;        /* parameters placed so far */
   int64_t open_elems = 0;    /* elements in the open bucket */
   int32_t open_count = 0;    /* parameters in the open bucket */
-  for (int32_t i = n_params - 1; i >= 0; --i) {
+  for (int32_t k = 0; k < n_params; ++k) {
+    int32_t i = walk != NULL ? walk[k] : n_params - 1 - k;
     if (buckets == 0) {
       buckets = 1;
       bucket_begin[0] = 0;
@@ -257,6 +283,53 @@ int orc_bucket_plan(const int64_t *numel, int32_t n_params, int32_t elem_bytes,
     filled += 1;
   }
   bucket_begin[buckets] = filled;
+  *n_buckets = buckets;
+  return ORC_OK;
+}
+
+int orc_bucket_plan(const int64_t *numel, int32_t n_params, int32_t elem_bytes,
+                    int64_t cap, int64_t first_cap, int32_t *fill_order,
+                    int32_t *bucket_begin, int64_t *offset, int32_t *bucket_of,
+                    int32_t *n_buckets) {
+  return orc_bucket_plan_ordered(numel, n_params, NULL, elem_bytes, cap,
+                                 first_cap, fill_order, bucket_begin, offset,
+                                 bucket_of, n_buckets);
+}
+
+/* Coalescing for a broadcast of many tensors ("PyTorch DDP Deep Dive", Part
+ * 2, the buffer broadcast and the chain down to the coalesced broadcast,
+ * whose buckets are capped at 250 MiB): tensors are taken in list order and
+ * a bucket is closed before a tensor that would take it past the cap, so no
+ * bucket exceeds the cap unless one tensor alone does. (The pages give only
+ * the cap; "never past it" is the reading taken.) Outputs as for
+ * orc_bucket_plan; fill order is list order. */
+int orc_coalesce_plan(const int64_t *numel, int32_t n, int32_t elem_bytes,
+                      int64_t cap, int32_t *fill_order, int32_t *bucket_begin,
+                      int64_t *offset, int32_t *bucket_of, int32_t *n_buckets) {
+  if (n < 0 || elem_bytes <= 0 || cap < 0) return ORC_EINVAL;
+  for (int32_t i = 0; i < n; ++i) {
+    if (numel[i] < 0) return ORC_EINVAL;
+  }
+  int32_t buckets = 0;
+  int64_t open_elems = 0;
+  int32_t open_count = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (buckets == 0) {
+      buckets = 1;
+      bucket_begin[0] = 0;
+    } else if (open_count > 0 && (open_elems + numel[i]) * elem_bytes > cap) {
+      bucket_begin[buckets] = i;
+      buckets += 1;
+      open_elems = 0;
+      open_count = 0;
+    }
+    fill_order[i] = i;
+    offset[i] = open_elems;
+    bucket_of[i] = buckets - 1;
+    open_elems += numel[i];
+    open_count += 1;
+  }
+  bucket_begin[buckets] = n;
   *n_buckets = buckets;
   return ORC_OK;
 }
@@ -904,4 +977,92 @@ void orc_tree_fold_samples(const float *vals, int32_t p, int64_t count,
     }
     out[s] = do_divide ? t[0] / divisor : t[0];
   }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Coalesced broadcast of many tensors                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Broadcast n_t tensors from rank `root` to every rank, coalesced ("PyTorch
+ * DDP Deep Dive", Part 1, the init-time broadcast of parameters and buffers,
+ * and Part 2, the per-forward buffer broadcast): the tensors are grouped by
+ * orc_coalesce_plan; for each bucket the root's tensors are flattened into
+ * one buffer, that buffer is broadcast over the doubling tree (as
+ * orc_broadcast, relative to the root), and every rank unflattens it into
+ * its own tensors. tensors[r * n_t + i] is rank r's copy of tensor i, of
+ * numel[i] elements of elem_bytes bytes. Logged messages carry the bucket
+ * number in `chunk`. bucket_of (may be NULL) receives each tensor's bucket. */
+int orc_broadcast_coalesced(void *const *tensors, const int64_t *numel,
+                            int32_t n_t, int32_t p, int32_t elem_bytes,
+                            int64_t cap, int32_t root, orc_msg *log,
+                            int64_t log_capacity, int64_t *n_msgs,
+                            int32_t *bucket_of) {
+  if (p < 1 || n_t < 0 || elem_bytes <= 0 || root < 0 || root >= p) {
+    return ORC_EINVAL;
+  }
+  int32_t m = n_t > 0 ? n_t : 1;
+  int32_t *fill = (int32_t *)calloc((size_t)m, sizeof(int32_t));
+  int32_t *begin = (int32_t *)calloc((size_t)m + 1, sizeof(int32_t));
+  int64_t *off = (int64_t *)calloc((size_t)m, sizeof(int64_t));
+  int32_t *bof = (int32_t *)calloc((size_t)m, sizeof(int32_t));
+  char **flat = (char **)calloc((size_t)p, sizeof(char *));
+  int rc = ORC_OK;
+  int32_t nb = 0;
+  if (fill == NULL || begin == NULL || off == NULL || bof == NULL || flat == NULL) {
+    rc = ORC_ENOMEM;
+  } else {
+    rc = orc_coalesce_plan(numel, n_t, elem_bytes, cap, fill, begin, off, bof, &nb);
+  }
+  msg_log lg = {log, log_capacity, 0};
+  int32_t round = 0;
+  for (int32_t b = 0; b < nb && rc == ORC_OK; ++b) {
+    int64_t bytes = 0;
+    for (int32_t k = begin[b]; k < begin[b + 1]; ++k) bytes += numel[fill[k]] * elem_bytes;
+    for (int32_t r = 0; r < p && rc == ORC_OK; ++r) {
+      flat[r] = (char *)calloc((size_t)bytes + 1, 1);
+      if (flat[r] == NULL) rc = ORC_ENOMEM;
+    }
+    if (rc == ORC_OK) {
+      /* the root flattens its tensors */
+      for (int32_t k = begin[b]; k < begin[b + 1]; ++k) {
+        int32_t i = fill[k];
+        memcpy(flat[root] + off[i] * elem_bytes, tensors[(int64_t)root * n_t + i],
+               (size_t)(numel[i] * elem_bytes));
+      }
+      /* doubling tree on relative rank v = (r - root) mod p */
+      for (int64_t span = 1; span < p; span *= 2, ++round) {
+        for (int64_t v = 0; v < span; ++v) {
+          if (v + span >= p) continue;
+          int32_t s = (int32_t)((v + root) % p);
+          int32_t d = (int32_t)((v + span + root) % p);
+          memcpy(flat[d], flat[s], (size_t)bytes);
+          log_msg(&lg, ORC_PHASE_BROADCAST, round, s, d, b, bytes);
+        }
+      }
+      /* every rank unflattens */
+      for (int32_t r = 0; r < p; ++r) {
+        for (int32_t k = begin[b]; k < begin[b + 1]; ++k) {
+          int32_t i = fill[k];
+          memcpy(tensors[(int64_t)r * n_t + i], flat[r] + off[i] * elem_bytes,
+                 (size_t)(numel[i] * elem_bytes));
+        }
+      }
+    }
+    for (int32_t r = 0; r < p; ++r) {
+      free(flat[r]);
+      flat[r] = NULL;
+    }
+  }
+  if (rc == ORC_OK) {
+    if (n_msgs != NULL) *n_msgs = lg.count;
+    if (bucket_of != NULL) {
+      for (int32_t i = 0; i < n_t; ++i) bucket_of[i] = bof[i];
+    }
+  }
+  free(fill);
+  free(begin);
+  free(off);
+  free(bof);
+  free(flat);
+  return rc;
 }
