@@ -11,8 +11,10 @@ the seeded synthetic inputs.
 from .binding import (  # noqa: F401
     ALGO, AVG, DTYPE_BF16, DTYPE_F32, EXPORTS, MAX_RANKS, SCHEDULES, CallTimer, CommStats,
     DDPError, Plan, Reducer,
-    allgather_sim, allreduce_sim, allreduce_sim_workspace, broadcast_sim, choose_schedule,
-    ddp_allreduce_bucket, ddp_allreduce_buckets, ddp_bucket_plan, ddp_flatten, ddp_unflatten,
+    BROADCAST_BUCKET_BYTES,
+    allgather_sim, allreduce_sim, allreduce_sim_workspace, broadcast_coalesced, broadcast_sim,
+    choose_schedule, ddp_allreduce_bucket, ddp_allreduce_buckets, ddp_broadcast_coalesced,
+    ddp_bucket_plan, ddp_coalesce_plan, ddp_flatten, ddp_unflatten, sync_module_states,
     grad_pointer_table, load_library, reduce_scatter_sim, ring_allreduce_sim,
     ring_allreduce_sim_steps, ring_allreduce_sim_workspace, schedule_time,
 )

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libddpsim.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["host.cpp", "plan.cpp", "allreduce.hip", "collectives.hip", "flatten.hip",
-           "bucket_allreduce.hip", "reducer.cpp", "schedules.hip"]
+           "bucket_allreduce.hip", "reducer.cpp", "schedules.hip",
+           "coalesced.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

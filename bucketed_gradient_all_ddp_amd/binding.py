@@ -38,7 +38,8 @@ EXPORTS = [
     "ddp_plan_segment_bytes", "ddp_plan_upload_segments", "ddp_allreduce_bucket",
     "ddp_allreduce_buckets",
     "ddp_reducer_create", "ddp_reducer_free", "ddp_reducer_prepare", "ddp_reducer_mark_ready",
-    "ddp_reducer_finalize", "ddp_reducer_launch_log",
+    "ddp_reducer_finalize", "ddp_reducer_launch_log", "ddp_reducer_ready_order",
+    "ddp_bucket_plan_ordered", "ddp_coalesce_plan", "ddp_broadcast_coalesced",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
     "allreduce_sim", "allreduce_sim_workspace", "ddp_schedule_time", "ddp_choose_schedule",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
@@ -115,6 +116,10 @@ def load_library(path: str = LIB_PATH):
         "ddp_reducer_mark_ready": ([vp, i32, vp], st),
         "ddp_reducer_finalize": ([vp, vp], st),
         "ddp_reducer_launch_log": ([vp, vp, vp, vp, i32], i32),
+        "ddp_reducer_ready_order": ([vp, vp, i32], i32),
+        "ddp_bucket_plan_ordered": ([vp, i32, vp, i32, i64, i64, ctypes.POINTER(vp)], st),
+        "ddp_coalesce_plan": ([vp, i32, i32, i64, ctypes.POINTER(vp)], st),
+        "ddp_broadcast_coalesced": ([vp, i32, vp, i32, vp, vp], st),
         "ring_allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, vp, sz, vp, vp], st),
         "ring_allreduce_sim_workspace": ([i32, i64, i32, i32], sz),
         "ring_allreduce_sim_steps": ([vp, i32, i64, i32, vp, i32, i32, vp], st),
@@ -312,14 +317,87 @@ class Plan:
 
 def ddp_bucket_plan(numel: Sequence[int], elem_bytes: int = 4,
                     bucket_cap_bytes: int = 25 * 1024 * 1024,
-                    first_bucket_cap_bytes: int = 1024 * 1024) -> Plan:
+                    first_bucket_cap_bytes: int = 1024 * 1024,
+                    order: Optional[Sequence[int]] = None) -> Plan:
+    """Gradient buckets: reverse registration order, or `order` (the order in
+    which gradients became ready, for the rebuild)."""
     L = load_library()
     n = len(numel)
     arr = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in numel])
     out = ctypes.c_void_p()
-    _check(L.ddp_bucket_plan(arr, n, elem_bytes, bucket_cap_bytes, first_bucket_cap_bytes,
-                             ctypes.byref(out)), "ddp_bucket_plan")
+    if order is None:
+        _check(L.ddp_bucket_plan(arr, n, elem_bytes, bucket_cap_bytes, first_bucket_cap_bytes,
+                                 ctypes.byref(out)), "ddp_bucket_plan")
+    else:
+        walk = (ctypes.c_int32 * max(len(order), 1))(*[int(v) for v in order])
+        if len(order) != n:
+            raise ValueError("order must list every parameter once")
+        _check(L.ddp_bucket_plan_ordered(arr, n, walk, elem_bytes, bucket_cap_bytes,
+                                         first_bucket_cap_bytes, ctypes.byref(out)),
+               "ddp_bucket_plan_ordered")
     return Plan(out.value, elem_bytes)
+
+
+BROADCAST_BUCKET_BYTES = 250 * 1024 * 1024
+
+
+def ddp_coalesce_plan(numel: Sequence[int], elem_bytes: int,
+                      cap_bytes: int = BROADCAST_BUCKET_BYTES) -> Plan:
+    """Buckets of a coalesced broadcast (list order, none past the cap)."""
+    L = load_library()
+    n = len(numel)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in numel])
+    out = ctypes.c_void_p()
+    _check(L.ddp_coalesce_plan(arr, n, elem_bytes, cap_bytes, ctypes.byref(out)),
+           "ddp_coalesce_plan")
+    return Plan(out.value, elem_bytes)
+
+
+def ddp_broadcast_coalesced(plan: Plan, tensor_table, p: int, root: int = 0,
+                            stream=None) -> CommStats:
+    """Broadcast every tensor of an uploaded coalesce plan from `root`;
+    tensor_table is grad_pointer_table(tensors_per_rank)."""
+    st = CommStats()
+    _check(load_library().ddp_broadcast_coalesced(
+        plan.handle, p, tensor_table.data_ptr() if tensor_table is not None else None, root,
+        _stream(stream), ctypes.byref(st)), "ddp_broadcast_coalesced")
+    return st
+
+
+def broadcast_coalesced(tensors: Sequence[Sequence], root: int = 0,
+                        cap_bytes: int = BROADCAST_BUCKET_BYTES, stream=None):
+    """tensors[r][i] = rank r's copy of tensor i (contiguous device tensors).
+    Tensors are grouped by element size (one coalesced broadcast per group,
+    as flattening needs one element type), bucketed in list order and
+    broadcast from `root`. Returns the per-group stats."""
+    p = len(tensors)
+    n_t = len(tensors[0]) if p else 0
+    groups = {}
+    for i in range(n_t):
+        groups.setdefault(tensors[0][i].element_size(), []).append(i)
+    out = []
+    for eb, idx in sorted(groups.items()):
+        plan = ddp_coalesce_plan([tensors[0][i].numel() for i in idx], eb, cap_bytes)
+        plan.upload(tensors[0][idx[0]].device, stream)
+        table = grad_pointer_table([[tensors[r][i] for i in idx] for r in range(p)],
+                                   tensors[0][idx[0]].device)
+        out.append(ddp_broadcast_coalesced(plan, table, p, root, stream))
+        if stream is not None:
+            # allocated on the current stream, used on `stream`: keep the
+            # memory from being reused before the kernels there have run
+            plan._table.record_stream(stream)
+            table.record_stream(stream)
+    return out
+
+
+def sync_module_states(params: Sequence[Sequence], buffers: Sequence[Sequence] = (),
+                       root: int = 0, stream=None):
+    """Make every rank's parameters and buffers equal to the root's: the
+    init-time broadcast of parameters and buffers, coalesced (params[r][i],
+    buffers[r][j] = rank r's copies)."""
+    p = len(params)
+    rows = [list(params[r]) + (list(buffers[r]) if buffers else []) for r in range(p)]
+    return broadcast_coalesced(rows, root, BROADCAST_BUCKET_BYTES, stream)
 
 
 def grad_pointer_table(grads: Sequence[Sequence], device="cuda"):
@@ -413,6 +491,15 @@ class Reducer:
     def finalize(self, wait_stream=None) -> None:
         _check(load_library().ddp_reducer_finalize(self._h, _stream(wait_stream)),
                "ddp_reducer_finalize")
+
+    def ready_order(self) -> List[int]:
+        """Parameters in the order they were marked ready this (or the last)
+        pass: the order to rebuild the buckets from."""
+        L = load_library()
+        n = L.ddp_reducer_ready_order(self._h, None, 0)
+        a = (ctypes.c_int32 * max(n, 1))()
+        L.ddp_reducer_ready_order(self._h, a, n)
+        return list(a[:n])
 
     def launch_log(self):
         L = load_library()

@@ -1,0 +1,177 @@
+// coalesced.hip -- broadcast of many tensors from one rank, coalesced into
+// capped buckets ("PyTorch DDP Deep Dive", Part 1: the init-time broadcast
+// of parameters and buffers that makes the replicas identical; Part 2: the
+// buffer broadcast before every forward, down to the coalesced broadcast
+// with its 250 MiB buckets).
+//
+// On the pages each bucket is flattened at the root, broadcast as one flat
+// buffer over the doubling tree, and unflattened on every rank. On one
+// device the flat buffer is only a staging copy: each bucket is one launch
+// that reads the root's tensors once and writes them straight into the other
+// p - 1 ranks' tensors, so a bucket costs p bytes-per-element of device
+// traffic instead of the 2 + 2p of flatten, fan-out and unflatten. Buckets
+// run one after another on the stream. The tree's rounds and messages are
+// kept in the accounting.
+#include <algorithm>
+
+#include "internal.hpp"
+
+namespace ddpsim {
+bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
+                      int32_t *count, int32_t *tiles, int64_t *elems,
+                      const void **table, int32_t *n_params, int32_t *elem_bytes,
+                      bool *uploaded);
+int32_t plan_num_buckets(const ddp_plan *plan);
+
+namespace {
+
+template <int EB>
+struct Unit;
+template <>
+struct Unit<1> { using type = uint8_t; };
+template <>
+struct Unit<2> { using type = uint16_t; };
+template <>
+struct Unit<4> { using type = uint32_t; };
+template <>
+struct Unit<8> { using type = uint64_t; };
+
+// One workgroup per tile of kFlattenTile elements of one tensor (found by
+// binary search over the bucket's descriptors, as in flatten_kernel). The
+// root's slice is loaded once and stored to every other rank. 16-byte
+// vectors when every rank's copy of the tensor is 16-byte aligned (tiles
+// start at multiples of kFlattenTile elements, so the tensor's base decides),
+// elements of EB bytes otherwise.
+template <int EB>
+__global__ __launch_bounds__(kThreads) void coalesced_broadcast_kernel(
+    const ParamDesc *__restrict__ desc, int32_t count, int32_t n_params,
+    const void *const *__restrict__ ptrs, int32_t p, int32_t root) {
+  using U = typename Unit<EB>::type;
+  constexpr int kVpt = kFlattenTile * EB / kVecBytes / kThreads;
+  const int32_t tile = static_cast<int32_t>(blockIdx.x);
+  int32_t lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (desc[mid].tile_begin <= tile) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  const ParamDesc d = desc[lo];
+  const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile;
+  const int64_t left = d.numel - start;
+  if (left <= 0) return;
+  const int64_t cnt = left < kFlattenTile ? left : kFlattenTile;
+  const int tid = static_cast<int>(threadIdx.x);
+  auto slice = [&](int32_t r) {
+    return static_cast<U *>(const_cast<void *>(ptrs[static_cast<int64_t>(r) * n_params +
+                                                    d.param])) + start;
+  };
+  const U *src = slice(root);
+  bool aligned = true;
+  for (int32_t r = 0; r < p; ++r) {
+    aligned = aligned && reinterpret_cast<uintptr_t>(slice(r)) % kVecBytes == 0;
+  }
+  int64_t done = 0;
+  if (aligned) {
+    const int64_t nv = cnt * EB / kVecBytes;
+    uint4 x[kVpt];
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) {
+      const int64_t v = u * kThreads + tid;
+      if (v < nv) x[u] = load_vec(src, v);
+    }
+    for (int32_t r = 0; r < p; ++r) {
+      if (r == root) continue;
+      U *dst = slice(r);
+#pragma unroll
+      for (int u = 0; u < kVpt; ++u) {
+        const int64_t v = u * kThreads + tid;
+        if (v < nv) store_vec<false>(dst, v, x[u]);
+      }
+    }
+    done = nv * kVecBytes / EB;
+  }
+  for (int64_t i = done + tid; i < cnt; i += kThreads) {
+    const U v = src[i];
+    for (int32_t r = 0; r < p; ++r) {
+      if (r != root) slice(r)[i] = v;
+    }
+  }
+}
+
+template <int EB>
+ddp_status launch_bucket(const ParamDesc *desc, int32_t count, int32_t tiles, int32_t n_params,
+                         const void *const *ptrs, int32_t p, int32_t root, hipStream_t stream,
+                         CallTimer &timer, bool last) {
+  return launch(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(tiles)),
+                dim3(kThreads), stream, timer, last, "coalesced_broadcast_kernel launch", desc,
+                count, n_params, ptrs, p, root);
+}
+
+}  // namespace
+}  // namespace ddpsim
+
+using namespace ddpsim;
+
+extern "C" ddp_status ddp_broadcast_coalesced(const ddp_plan *plan, int32_t p,
+                                              void *const *d_tensor_ptrs, int32_t root,
+                                              hipStream_t stream, ddp_comm_stats *stats) {
+  clear_error();
+  CallTimer timer = CallTimer::take();
+  const char *what = "ddp_broadcast_coalesced";
+  if (plan == nullptr) return fail(DDP_EINVAL, "%s: plan is NULL", what);
+  ddp_status s = check_p(p, what);
+  if (s != DDP_OK) return s;
+  if (root < 0 || root >= p) return fail(DDP_ERANGE, "%s: root=%d outside [0, %d)", what, root, p);
+  const int32_t nb = plan_num_buckets(plan);
+  int32_t eb = 0, n_params = 0;
+  int64_t total = 0;
+  int32_t last = -1;
+  bool uploaded = true;
+  for (int32_t b = 0; b < nb; ++b) {
+    int32_t first, count, tiles;
+    int64_t elems;
+    const void *table;
+    bool up;
+    plan_bucket_info(plan, b, &first, &count, &tiles, &elems, &table, &n_params, &eb, &up);
+    uploaded = up;
+    total += elems * eb;
+    if (tiles > 0) last = b;
+  }
+  if (nb > 0 && !uploaded) return fail(DDP_ENOTREADY, "%s: call ddp_plan_upload first", what);
+  if (last >= 0 && d_tensor_ptrs == nullptr) {
+    return fail(DDP_EINVAL, "%s: tensor pointer table is NULL", what);
+  }
+  if (stats != nullptr) {
+    int64_t rounds = 0;
+    while ((int64_t(1) << rounds) < p) ++rounds;
+    stats->steps = rounds * nb;
+    stats->messages = int64_t(p - 1) * nb;
+    stats->bytes_sent_per_rank = rounds * total;
+    stats->bytes_recv_per_rank = p > 1 ? total : 0;
+    stats->total_bytes = int64_t(p - 1) * total;
+    stats->hbm_bytes = int64_t(p) * total;
+  }
+  if (p == 1 || last < 0) return DDP_OK;
+  const void *const *ptrs = reinterpret_cast<const void *const *>(d_tensor_ptrs);
+  for (int32_t b = 0; b <= last; ++b) {
+    int32_t first, count, tiles;
+    int64_t elems;
+    const void *table;
+    bool up;
+    plan_bucket_info(plan, b, &first, &count, &tiles, &elems, &table, &n_params, &eb, &up);
+    if (tiles == 0) continue;
+    const ParamDesc *desc = static_cast<const ParamDesc *>(table) + first;
+    const bool fin = b == last;
+    switch (eb) {
+      case 1: s = launch_bucket<1>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 2: s = launch_bucket<2>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 4: s = launch_bucket<4>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      default: s = launch_bucket<8>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+    }
+    if (s != DDP_OK) return s;
+  }
+  return DDP_OK;
+}

@@ -7,7 +7,10 @@
 // starts from the last registered parameter and the first bucket it fills is
 // the one whose all-reduce can start first; that bucket has the small cap.
 // A bucket is closed, before the next parameter would join it, once its
-// bytes have reached its cap.
+// bytes have reached its cap. The same walk over an explicit order rebuilds
+// the buckets from the order in which gradients were observed to become
+// ready (Part 2, the rebuild before the next forward). Coalesced broadcasts
+// group tensors in list order into buckets no larger than their cap.
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -199,37 +202,61 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
   return DDP_OK;
 }
 
-extern "C" ddp_status ddp_bucket_plan(const int64_t *numel, int32_t n_params,
-                                      int32_t elem_bytes, int64_t bucket_cap_bytes,
-                                      int64_t first_bucket_cap_bytes, ddp_plan **out) {
+namespace {
+
+// How a walk closes buckets.
+//   kGradient  close a non-empty bucket whose bytes have reached its cap,
+//              before the next parameter joins (the gradient buckets; the
+//              first bucket's cap is min(first, cap));
+//   kCoalesce  close a non-empty bucket that the next tensor would take past
+//              the cap (the coalesced broadcast's buckets).
+enum CloseRule { kGradient, kCoalesce };
+
+ddp_status build_plan(const int64_t *numel, int32_t n_params, const int32_t *walk,
+                      int32_t elem_bytes, int64_t cap, int64_t first_cap, CloseRule rule,
+                      const char *what, ddp_plan **out) {
   clear_error();
-  if (out == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: out is NULL");
+  if (out == nullptr) return fail(DDP_EINVAL, "%s: out is NULL", what);
   *out = nullptr;
-  if (n_params < 0) return fail(DDP_EINVAL, "ddp_bucket_plan: n_params < 0");
-  if (n_params > 0 && numel == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: numel is NULL");
-  if (elem_bytes != 2 && elem_bytes != 4) {
-    return fail(DDP_EINVAL, "ddp_bucket_plan: elem_bytes must be 2 or 4");
-  }
-  if (bucket_cap_bytes < 0 || first_bucket_cap_bytes < 0) {
-    return fail(DDP_EINVAL, "ddp_bucket_plan: caps must be >= 0");
-  }
+  if (n_params < 0) return fail(DDP_EINVAL, "%s: n_params < 0", what);
+  if (n_params > 0 && numel == nullptr) return fail(DDP_EINVAL, "%s: numel is NULL", what);
+  if (cap < 0 || first_cap < 0) return fail(DDP_EINVAL, "%s: caps must be >= 0", what);
   for (int32_t i = 0; i < n_params; ++i) {
-    if (numel[i] < 0) return fail(DDP_EINVAL, "ddp_bucket_plan: numel[%d] < 0", i);
+    if (numel[i] < 0) return fail(DDP_EINVAL, "%s: numel[%d] < 0", what, i);
+  }
+  std::vector<int32_t> order(n_params);
+  if (walk != nullptr) {
+    std::vector<char> seen(n_params, 0);
+    for (int32_t k = 0; k < n_params; ++k) {
+      const int32_t i = walk[k];
+      if (i < 0 || i >= n_params || seen[i]) {
+        return fail(DDP_EINVAL, "%s: order is not a permutation (entry %d)", what, k);
+      }
+      seen[i] = 1;
+      order[k] = i;
+    }
+  } else {
+    for (int32_t k = 0; k < n_params; ++k) order[k] = n_params - 1 - k;
   }
   ddp_plan *plan = new (std::nothrow) ddp_plan;
-  if (plan == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: out of host memory");
+  if (plan == nullptr) return fail(DDP_EINVAL, "%s: out of host memory", what);
   plan->n_params = n_params;
   plan->elem_bytes = elem_bytes;
   plan->numel.assign(numel, numel + n_params);
   plan->bucket_of.assign(n_params, -1);
   plan->offset.assign(n_params, 0);
 
-  const int64_t small_cap = std::min(first_bucket_cap_bytes, bucket_cap_bytes);
+  const int64_t small_cap = std::min(first_cap, cap);
   int64_t open_bytes = 0;
-  for (int32_t i = n_params - 1; i >= 0; --i) {
+  for (int32_t i : order) {
     const bool have_open = !plan->members.empty() && !plan->members.back().empty();
-    const int64_t cap = plan->members.size() <= 1 ? small_cap : bucket_cap_bytes;
-    if (!have_open || open_bytes >= cap) {
+    bool close = !have_open;
+    if (have_open && rule == kGradient) {
+      close = open_bytes >= (plan->members.size() <= 1 ? small_cap : cap);
+    } else if (have_open) {
+      close = open_bytes + numel[i] * elem_bytes > cap;
+    }
+    if (close) {
       plan->members.emplace_back();
       plan->bucket_elems.push_back(0);
       open_bytes = 0;
@@ -259,12 +286,57 @@ extern "C" ddp_status ddp_bucket_plan(const int64_t *numel, int32_t n_params,
     }
     if (tiles > INT32_MAX) {
       delete plan;
-      return fail(DDP_EINVAL, "ddp_bucket_plan: bucket %zu is too large", b);
+      return fail(DDP_EINVAL, "%s: bucket %zu is too large", what, b);
     }
     plan->tiles.push_back(static_cast<int32_t>(tiles));
   }
   *out = plan;
   return DDP_OK;
+}
+
+}  // namespace
+
+extern "C" ddp_status ddp_bucket_plan(const int64_t *numel, int32_t n_params,
+                                      int32_t elem_bytes, int64_t bucket_cap_bytes,
+                                      int64_t first_bucket_cap_bytes, ddp_plan **out) {
+  if (elem_bytes != 2 && elem_bytes != 4) {
+    clear_error();
+    if (out != nullptr) *out = nullptr;
+    return fail(DDP_EINVAL, "ddp_bucket_plan: elem_bytes must be 2 or 4");
+  }
+  return build_plan(numel, n_params, nullptr, elem_bytes, bucket_cap_bytes,
+                    first_bucket_cap_bytes, kGradient, "ddp_bucket_plan", out);
+}
+
+extern "C" ddp_status ddp_bucket_plan_ordered(const int64_t *numel, int32_t n_params,
+                                              const int32_t *order, int32_t elem_bytes,
+                                              int64_t bucket_cap_bytes,
+                                              int64_t first_bucket_cap_bytes, ddp_plan **out) {
+  if (elem_bytes != 2 && elem_bytes != 4) {
+    clear_error();
+    if (out != nullptr) *out = nullptr;
+    return fail(DDP_EINVAL, "ddp_bucket_plan_ordered: elem_bytes must be 2 or 4");
+  }
+  if (n_params > 0 && order == nullptr) {
+    clear_error();
+    if (out != nullptr) *out = nullptr;
+    return fail(DDP_EINVAL, "ddp_bucket_plan_ordered: order is NULL");
+  }
+  return build_plan(numel, n_params, order, elem_bytes, bucket_cap_bytes,
+                    first_bucket_cap_bytes, kGradient, "ddp_bucket_plan_ordered", out);
+}
+
+extern "C" ddp_status ddp_coalesce_plan(const int64_t *numel, int32_t n_tensors,
+                                        int32_t elem_bytes, int64_t cap_bytes, ddp_plan **out) {
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) {
+    clear_error();
+    if (out != nullptr) *out = nullptr;
+    return fail(DDP_EINVAL, "ddp_coalesce_plan: elem_bytes must be 1, 2, 4 or 8");
+  }
+  std::vector<int32_t> forward(n_tensors > 0 ? n_tensors : 0);
+  for (int32_t i = 0; i < n_tensors; ++i) forward[i] = i;
+  return build_plan(numel, n_tensors, n_tensors > 0 ? forward.data() : nullptr, elem_bytes,
+                    cap_bytes, cap_bytes, kCoalesce, "ddp_coalesce_plan", out);
 }
 
 extern "C" void ddp_plan_free(ddp_plan *plan) { delete plan; }

@@ -13,7 +13,10 @@
 // in index order, each as early as its own gradients and its predecessors
 // allow, overlapping whatever the producer streams still compute.
 // finalize() reports a bucket that never became ready instead of waiting for
-// it forever.
+// it forever. The order of the marks is kept, so the buckets can be rebuilt
+// from the order in which gradients actually became ready (Part 2: the hook
+// records each ready parameter while a rebuild is due, and the rebuild runs
+// before the next forward).
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -47,6 +50,7 @@ struct ddp_reducer {
   int32_t marks = 0;
   bool active = false;
   std::vector<int32_t> log_mark, log_first, log_count;
+  std::vector<int32_t> ready_order;  // parameters in the order marked, this pass
   hipEvent_t done = nullptr;
 };
 
@@ -114,6 +118,7 @@ extern "C" ddp_status ddp_reducer_prepare(ddp_reducer *r) {
   r->log_mark.clear();
   r->log_first.clear();
   r->log_count.clear();
+  r->ready_order.clear();
   r->active = true;
   return DDP_OK;
 }
@@ -131,6 +136,7 @@ extern "C" ddp_status ddp_reducer_mark_ready(ddp_reducer *r, int32_t param,
     return fail(DDP_EINVAL, "%s: parameter %d marked ready twice in one pass", what, param);
   }
   r->ready[param] = 1;
+  r->ready_order.push_back(param);
   const int32_t b = r->bucket_of[param];
   if (ready != nullptr &&
       std::find(r->events[b].begin(), r->events[b].end(), ready) == r->events[b].end()) {
@@ -199,5 +205,13 @@ extern "C" int32_t ddp_reducer_launch_log(const ddp_reducer *r, int32_t *at_mark
     if (first_bucket) first_bucket[k] = r->log_first[k];
     if (n_buckets) n_buckets[k] = r->log_count[k];
   }
+  return n;
+}
+
+extern "C" int32_t ddp_reducer_ready_order(const ddp_reducer *r, int32_t *order,
+                                           int32_t capacity) {
+  if (r == nullptr) return -1;
+  const int32_t n = static_cast<int32_t>(r->ready_order.size());
+  for (int32_t k = 0; k < n && k < capacity && order != nullptr; ++k) order[k] = r->ready_order[k];
   return n;
 }

@@ -151,6 +151,33 @@ ddp_status ddp_bucket_plan(const int64_t *numel, int32_t n_params,
                            int64_t first_bucket_cap_bytes, ddp_plan **out);
 void ddp_plan_free(ddp_plan *plan);
 
+/* The same bucketing over an explicit walk order: order[k] is the k-th
+ * parameter to place (a permutation of 0..n_params-1). DDP rebuilds its
+ * buckets once, before the next forward, from the order in which the
+ * gradients were observed to become ready in the first backward ([DDP] Part
+ * 2, "Step 2: backward": the hook records each ready parameter while a
+ * rebuild is due; "_pre_forward" runs the rebuild); pass the order that
+ * ddp_reducer_ready_order reports. Bucket 0 (the first filled) has the small
+ * cap. Errors: as ddp_bucket_plan, plus DDP_EINVAL when order is NULL or
+ * not a permutation. */
+ddp_status ddp_bucket_plan_ordered(const int64_t *numel, int32_t n_params,
+                                   const int32_t *order, int32_t elem_bytes,
+                                   int64_t bucket_cap_bytes,
+                                   int64_t first_bucket_cap_bytes,
+                                   ddp_plan **out);
+
+/* Buckets for a coalesced broadcast ([DDP] Part 2, the buffer broadcast:
+ * tensors are coalesced into buckets capped at 250 MiB by default, each
+ * flattened and broadcast as one message): tensors in list order; a bucket
+ * is closed before a tensor that would take it past cap_bytes, so no bucket
+ * exceeds the cap unless one tensor alone does. elem_bytes 1, 2, 4 or 8
+ * (broadcasts copy bytes; one plan per element size). Upload the plan's
+ * descriptor table (ddp_plan_upload) before ddp_broadcast_coalesced.
+ * Errors: DDP_EINVAL. */
+ddp_status ddp_coalesce_plan(const int64_t *numel, int32_t n_tensors,
+                             int32_t elem_bytes, int64_t cap_bytes,
+                             ddp_plan **out);
+
 int32_t ddp_plan_num_params(const ddp_plan *plan);
 int32_t ddp_plan_num_buckets(const ddp_plan *plan);
 /* Total elements of bucket b (-1 if b is out of range). */
@@ -308,6 +335,11 @@ ddp_status ddp_reducer_finalize(ddp_reducer *reducer, hipStream_t wait_stream);
 int32_t ddp_reducer_launch_log(const ddp_reducer *reducer, int32_t *at_mark,
                                int32_t *first_bucket, int32_t *n_buckets,
                                int32_t capacity);
+/* The parameters in the order they were marked ready in the current or last
+ * pass (writes at most `capacity`; returns the count, -1 for NULL): the
+ * order from which ddp_bucket_plan_ordered rebuilds the buckets. */
+int32_t ddp_reducer_ready_order(const ddp_reducer *reducer, int32_t *order,
+                                int32_t capacity);
 
 /* ----------------------------------------------------------------------- */
 /* Ring all-reduce                                                         */
@@ -476,6 +508,28 @@ ddp_status allgather_sim(const void *const *in, void *const *out, int32_t p,
 ddp_status broadcast_sim(void *const *bufs, int32_t p, int64_t n,
                          int32_t src, int32_t dtype, hipStream_t stream,
                          ddp_comm_stats *stats);
+
+/* Broadcast of many tensors from rank `root`, coalesced into the buckets of
+ * a plan from ddp_coalesce_plan (or any uploaded plan): afterwards every
+ * rank's copy of every tensor holds the root's bytes. This is DDP's
+ * init-time synchronisation of parameters and buffers (root 0; [DDP] Part 1,
+ * "_sync_module_states") and its per-forward buffer broadcast from the
+ * authoritative rank ([DDP] Part 2, "_pre_forward" and the chain to the
+ * coalesced broadcast). One launch per bucket, in bucket order, reads the
+ * root's tensors once and writes the other p - 1 copies (no staging buffer;
+ * device traffic p bytes-per-element). The stats describe the pages' form:
+ * per bucket one flat message down the doubling tree (ceil(log2 p) rounds,
+ * p - 1 messages of the bucket's bytes).
+ *   d_tensor_ptrs  DEVICE array of p * n_tensors addresses, rank-major
+ *                  (rank r's copy of tensor i at r * n_tensors + i), each
+ *                  aligned to the element size; copies of different ranks
+ *                  or tensors must not overlap (not checked)
+ * Errors: DDP_ENOTREADY (plan not uploaded), DDP_ERANGE (p, root),
+ * DDP_EINVAL. */
+ddp_status ddp_broadcast_coalesced(const ddp_plan *plan, int32_t p,
+                                   void *const *d_tensor_ptrs, int32_t root,
+                                   hipStream_t stream, ddp_comm_stats *stats);
+
 
 #ifdef __cplusplus
 }

@@ -221,6 +221,11 @@ def test_reducer_errors_without_launching():
                 assert L.ddp_reducer_mark_ready(r, i, None) == 0
         assert L.ddp_reducer_mark_ready(r, (held + 1) % len(sizes), None) == 1  # twice
         assert L.ddp_reducer_launch_log(r, None, None, None, 0) == 0
+        marked = [i for i in range(len(sizes)) if i != held]
+        got = (ctypes.c_int32 * 8)()
+        assert L.ddp_reducer_ready_order(r, got, 8) == len(marked)
+        assert list(got[:len(marked)]) == marked   # failed marks are not recorded
+        assert L.ddp_reducer_ready_order(None, got, 8) == -1
         assert L.ddp_reducer_finalize(r, None) == 6
         assert b"never became ready" in L.ddp_last_error()
         assert L.ddp_reducer_finalize(r, None) == 1            # pass already ended
@@ -287,3 +292,48 @@ def test_choose_schedule_matches_oracle_and_flips_at_crossover():
     assert L.ddp_choose_schedule(0, 100, a, b, 3) == -1
     assert L.ddp_choose_schedule(8, -1, a, b, 3) == -1
     assert L.ddp_schedule_time(9, 8, 1.0, a, b) < 0
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_ordered_and_coalesce_planners_match_oracle(oracle, seed):
+    rng = np.random.default_rng(500 + seed)
+    P = int(rng.integers(0, 64))
+    sizes = [int(v) for v in rng.integers(0, 5000, size=P)]
+    order = [int(v) for v in rng.permutation(P)]
+    eb = int(rng.choice([2, 4]))
+    cap, first = int(rng.integers(0, 40000)), int(rng.integers(0, 40000))
+    a = ddp.ddp_bucket_plan(sizes, eb, cap, first, order=order)
+    b = oracle.bucket_plan(sizes, eb, cap, first, order=order)
+    assert a.buckets() == b.buckets()
+    assert [a.param_offset(i) for i in range(P)] == list(b.offset)
+    eb2 = int(rng.choice([1, 2, 4, 8]))
+    c = ddp.ddp_coalesce_plan(sizes, eb2, cap)
+    d = oracle.coalesce_plan(sizes, eb2, cap)
+    assert c.buckets() == d.buckets()
+    assert [c.param_offset(i) for i in range(P)] == list(d.offset)
+
+
+def test_coalesced_broadcast_argument_errors():
+    L = load_library()
+    out = ctypes.c_void_p()
+    sizes = (ctypes.c_int64 * 3)(5, 6, 7)
+    assert L.ddp_coalesce_plan(sizes, 3, 3, 100, ctypes.byref(out)) == 1     # elem size
+    assert L.ddp_coalesce_plan(sizes, 3, 4, -1, ctypes.byref(out)) == 1      # cap
+    bad = (ctypes.c_int32 * 3)(0, 0, 2)
+    assert L.ddp_bucket_plan_ordered(sizes, 3, bad, 4, 100, 10, ctypes.byref(out)) == 1
+    assert L.ddp_bucket_plan_ordered(sizes, 3, None, 4, 100, 10, ctypes.byref(out)) == 1
+    big = (ctypes.c_int32 * 3)(0, 1, 3)
+    assert L.ddp_bucket_plan_ordered(sizes, 3, big, 4, 100, 10, ctypes.byref(out)) == 1
+    plan = ddp.ddp_coalesce_plan([5, 6, 7], 8, 100)
+    fake = ctypes.c_void_p(0x100000000)
+    assert L.ddp_broadcast_coalesced(None, 4, fake, 0, None, None) == 1
+    assert L.ddp_broadcast_coalesced(plan.handle, 0, fake, 0, None, None) == 2
+    assert L.ddp_broadcast_coalesced(plan.handle, 4, fake, 4, None, None) == 2
+    assert L.ddp_broadcast_coalesced(plan.handle, 4, fake, -1, None, None) == 2
+    assert L.ddp_broadcast_coalesced(plan.handle, 4, fake, 0, None, None) == 6  # not uploaded
+    # stats are filled before the upload check only when the call succeeds;
+    # p = 1 with an uploaded-free empty plan is a no-op
+    empty = ddp.ddp_coalesce_plan([], 4, 100)
+    st = ddp.CommStats()
+    assert L.ddp_broadcast_coalesced(empty.handle, 3, None, 1, None, ctypes.byref(st)) == 0
+    assert st.messages == 0 and st.hbm_bytes == 0
