@@ -106,7 +106,7 @@ def parse():
     ap.add_argument("--workload", default="gpt2-small-p8",
                     choices=["gpt2-small-p8", "ragged-ring-p4", "llama7b-bf16-p8",
                              "latency-p64", "cost-model-p64", "overlap-gpt2-p8",
-                             "crossover-p4"],
+                             "crossover-p4", "sync-gpt2-p8"],
                     help="the default is the headline; the others print their own "
                          "line for the record")
     ap.add_argument("--tokens", type=int, default=2048,
@@ -339,6 +339,11 @@ def bench_llama(torch, ddp, W, dev, args):
     wall, dms = _timed_calls(torch, ddp, calls, reps)
     S = sum(sizes) * 2
     hbm = 2 * p * S
+    # every bucket ready at once: one launch for the whole run
+    nb = plan.num_buckets
+    batched = [lambda: ddp.ddp_allreduce_buckets(plan, 0, nb, table, p, avg="world")]
+    batched[0]()
+    bwall, bdms = _timed_calls(torch, ddp, batched, reps)
     _line("all-reduce bus GB/s, p=8, Llama-7B bf16 grads", S * 2 * (p - 1) / p / (wall * 1e-3) / 1e9,
           "GB/s", "llama-7b gradients: 291 bf16 tensors, 6,738,415,616 elements per rank, p=8, "
                   "226 buckets (25 MiB / 1 MiB), fp32 accumulation, average by p; step = one "
@@ -346,6 +351,11 @@ def bench_llama(torch, ddp, W, dev, args):
           {"ms_per_step": round(wall, 3), "kernel_ms_per_step": round(dms, 3),
            "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
            "kernel_frac_of_8TBps": round(hbm / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "one_launch_for_all_buckets": {
+               "ms_per_step": round(bwall, 3), "kernel_ms_per_step": round(bdms, 3),
+               "bus_GBps": round(S * 2 * (p - 1) / p / (bwall * 1e-3) / 1e9, 1),
+               "kernel_GBps": round(hbm / (bdms * 1e-3) / 1e9, 1),
+               "kernel_frac_of_8TBps": round(hbm / (bdms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
            "dtype": "bf16 (fp32 accumulate)", "steps": reps})
 
 
@@ -587,6 +597,59 @@ def bench_crossover(torch, ddp, W, dev, args):
            "sweep_us": {str(m): table[m] for m in ms}})
 
 
+def bench_sync(torch, ddp, W, dev, args):
+    """The init-time synchronisation of the GPT-2-small parameters (148 fp32
+    tensors, 124,439,808 elements per rank) from rank 0 to 8 ranks, coalesced
+    into 250 MiB buckets, plus a per-forward buffer broadcast of BatchNorm-like
+    statistics (two fp32 buffers per layer and an int64 counter)."""
+    p = 8
+    sizes = [W.numel(s) for _, s in W.gpt2_small_params()]
+    offs, off = [], 0
+    for n in sizes:
+        offs.append(off)
+        off += (n + 63) // 64 * 64
+    arenas = [W.normal_torch(off, 1e-3, 2, r, dev) for r in range(p)]
+    views = [[a[o:o + n] for o, n in zip(offs, sizes)] for a in arenas]
+    plan = ddp.ddp_coalesce_plan(sizes, 4, ddp.BROADCAST_BUCKET_BYTES).upload(dev)
+    table = ddp.grad_pointer_table(views, dev)
+    fn = lambda: ddp.ddp_broadcast_coalesced(plan, table, p, 0)  # noqa: E731
+    for _ in range(args.warmup):
+        fn()
+    wall, dms = _timed_calls(torch, ddp, [fn], args.steps)
+    S = sum(sizes) * 4
+    hbm = p * S
+    st = fn()
+    # per-forward buffer broadcast: 12 layers x (running mean, running var)
+    # of 3072 fp32 each, plus an int64 counter per layer
+    bn = [[torch.randn(3072, device=dev) for _ in range(24)] +
+          [torch.zeros(1, dtype=torch.int64, device=dev) for _ in range(12)] for _ in range(p)]
+    groups = {}
+    for i, t in enumerate(bn[0]):
+        groups.setdefault(t.element_size(), []).append(i)
+    calls = []
+    keep = []
+    for eb, idx in sorted(groups.items()):
+        bplan = ddp.ddp_coalesce_plan([bn[0][i].numel() for i in idx], eb).upload(dev)
+        btab = ddp.grad_pointer_table([[bn[r][i] for i in idx] for r in range(p)], dev)
+        keep.append((bplan, btab))
+        calls.append(lambda bp=bplan, bt=btab: ddp.ddp_broadcast_coalesced(bp, bt, p, 0))
+    for c in calls:
+        c()
+    bwall, bdms = _timed_calls(torch, ddp, calls, max(args.steps, 50))
+    _line("parameter sync GB/s per rank, p=8, GPT-2-small fp32 parameters from rank 0",
+          S / (wall * 1e-3) / 1e9, "GB/s",
+          "init-time sync: 148 fp32 GPT-2-small parameter tensors (124,439,808 elements per "
+          "rank) broadcast from rank 0 to 8 ranks in 250 MiB coalesced buckets",
+          {"ms": round(wall, 3), "kernel_ms": round(dms, 3), "buckets": plan.num_buckets,
+           "launches": plan.num_buckets,
+           "kernel_hbm_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
+           "kernel_frac_of_8TBps": round(hbm / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "tree_messages": st.messages, "tree_rounds": st.steps,
+           "buffer_broadcast": {"tensors": 36, "groups": len(calls),
+                                "us_per_forward": round(bwall * 1e3, 2),
+                                "kernel_us_per_forward": round(bdms * 1e3, 2)}})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -605,7 +668,8 @@ def main():
     ddp.load_library()
     other = {"ragged-ring-p4": bench_ragged, "llama7b-bf16-p8": bench_llama,
              "latency-p64": bench_latency, "cost-model-p64": bench_costmodel,
-             "overlap-gpt2-p8": bench_overlap, "crossover-p4": bench_crossover}
+             "overlap-gpt2-p8": bench_overlap, "crossover-p4": bench_crossover,
+             "sync-gpt2-p8": bench_sync}
     if args.workload in other:
         log(f"workload {args.workload}")
         other[args.workload](torch, ddp, W, dev, args)

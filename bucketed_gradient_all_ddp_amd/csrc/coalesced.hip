@@ -19,11 +19,26 @@
 namespace ddpsim {
 bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
                       int32_t *count, int32_t *tiles, int64_t *elems,
-                      const void **table, int32_t *n_params, int32_t *elem_bytes,
-                      bool *uploaded);
+                      const void **table, const int32_t **tile_map, int32_t *n_params,
+                      int32_t *elem_bytes, bool *uploaded);
 int32_t plan_num_buckets(const ddp_plan *plan);
 
 namespace {
+
+#ifndef DDPSIM_BCAST_NT
+// 0: ordinary accesses; 1: non-temporal stores; 2: non-temporal loads and
+// stores
+#define DDPSIM_BCAST_NT 0
+#endif
+constexpr bool kBcastNtStore = DDPSIM_BCAST_NT >= 1;
+constexpr bool kBcastNtLoad = DDPSIM_BCAST_NT >= 2;
+#ifndef DDPSIM_BCAST_THREADS
+#define DDPSIM_BCAST_THREADS 256  // threads per workgroup (one tile)
+#endif
+constexpr int kBcastThreads = DDPSIM_BCAST_THREADS;
+#ifndef DDPSIM_BCAST_LANEPTR
+#define DDPSIM_BCAST_LANEPTR 1  // rank addresses by one vector load + readlane
+#endif
 
 template <int EB>
 struct Unit;
@@ -36,78 +51,89 @@ struct Unit<4> { using type = uint32_t; };
 template <>
 struct Unit<8> { using type = uint64_t; };
 
-// One workgroup per tile of kFlattenTile elements of one tensor (found by
-// binary search over the bucket's descriptors, as in flatten_kernel). The
+// One workgroup per tile of kFlattenTile elements of one tensor (named by
+// the plan's tile map, as in flatten_kernel). The
 // root's slice is loaded once and stored to every other rank. 16-byte
 // vectors when every rank's copy of the tensor is 16-byte aligned (tiles
 // start at multiples of kFlattenTile elements, so the tensor's base decides),
 // elements of EB bytes otherwise.
 template <int EB>
-__global__ __launch_bounds__(kThreads) void coalesced_broadcast_kernel(
-    const ParamDesc *__restrict__ desc, int32_t count, int32_t n_params,
+__global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
+    const ParamDesc *__restrict__ desc, const int32_t *__restrict__ tile_map, int32_t n_params,
     const void *const *__restrict__ ptrs, int32_t p, int32_t root) {
   using U = typename Unit<EB>::type;
-  constexpr int kVpt = kFlattenTile * EB / kVecBytes / kThreads;
+  constexpr int kVpt = kFlattenTile * EB / kVecBytes / kBcastThreads;
+  static_assert(kVpt >= 1 && kVpt * kBcastThreads * kVecBytes == kFlattenTile * EB,
+                "a workgroup moves one tile in whole 16-byte vectors");
   const int32_t tile = static_cast<int32_t>(blockIdx.x);
-  int32_t lo = 0, hi = count - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (desc[mid].tile_begin <= tile) {
-      lo = mid;
-    } else {
-      hi = mid - 1;
-    }
-  }
-  const ParamDesc d = desc[lo];
+  const ParamDesc d = desc[tile_map[tile]];
   const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile;
   const int64_t left = d.numel - start;
   if (left <= 0) return;
   const int64_t cnt = left < kFlattenTile ? left : kFlattenTile;
   const int tid = static_cast<int>(threadIdx.x);
-  auto slice = [&](int32_t r) {
+  const int lane = tid & 63;
+  // rank r's slice, read from the device table (uniform: scalar loads)
+  auto slice_mem = [&](int32_t r) {
     return static_cast<U *>(const_cast<void *>(ptrs[static_cast<int64_t>(r) * n_params +
                                                     d.param])) + start;
   };
-  const U *src = slice(root);
+#if DDPSIM_BCAST_LANEPTR
+  // Lane r of every wave loads rank r's address once; the vector path takes
+  // it from that lane (readlane, in wave-uniform code only), so the p
+  // addresses cost one vector load instead of p scalar loads.
+  uintptr_t mine = 0;
+  if (lane < p) mine = reinterpret_cast<uintptr_t>(slice_mem(lane));
+  auto slice = [&](int32_t r) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine), r);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine >> 32), r);
+    return reinterpret_cast<U *>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  const bool aligned = __all(lane >= p || mine % kVecBytes == 0);
+#else
+  auto slice = slice_mem;
   bool aligned = true;
   for (int32_t r = 0; r < p; ++r) {
     aligned = aligned && reinterpret_cast<uintptr_t>(slice(r)) % kVecBytes == 0;
   }
+#endif
+  const U *src = slice(root);
   int64_t done = 0;
   if (aligned) {
     const int64_t nv = cnt * EB / kVecBytes;
     uint4 x[kVpt];
 #pragma unroll
     for (int u = 0; u < kVpt; ++u) {
-      const int64_t v = u * kThreads + tid;
-      if (v < nv) x[u] = load_vec(src, v);
+      const int64_t v = u * kBcastThreads + tid;
+      if (v < nv) x[u] = load_vec<kBcastNtLoad>(src, v);
     }
     for (int32_t r = 0; r < p; ++r) {
       if (r == root) continue;
       U *dst = slice(r);
 #pragma unroll
       for (int u = 0; u < kVpt; ++u) {
-        const int64_t v = u * kThreads + tid;
-        if (v < nv) store_vec<false>(dst, v, x[u]);
+        const int64_t v = u * kBcastThreads + tid;
+        if (v < nv) store_vec<kBcastNtStore>(dst, v, x[u]);
       }
     }
     done = nv * kVecBytes / EB;
   }
-  for (int64_t i = done + tid; i < cnt; i += kThreads) {
+  for (int64_t i = done + tid; i < cnt; i += kBcastThreads) {
     const U v = src[i];
     for (int32_t r = 0; r < p; ++r) {
-      if (r != root) slice(r)[i] = v;
+      if (r != root) slice_mem(r)[i] = v;
     }
   }
 }
 
 template <int EB>
-ddp_status launch_bucket(const ParamDesc *desc, int32_t count, int32_t tiles, int32_t n_params,
+ddp_status launch_bucket(const ParamDesc *desc, const int32_t *tile_map, int32_t tiles,
+                         int32_t n_params,
                          const void *const *ptrs, int32_t p, int32_t root, hipStream_t stream,
                          CallTimer &timer, bool last) {
   return launch(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(tiles)),
-                dim3(kThreads), stream, timer, last, "coalesced_broadcast_kernel launch", desc,
-                count, n_params, ptrs, p, root);
+                dim3(kBcastThreads), stream, timer, last, "coalesced_broadcast_kernel launch", desc,
+                tile_map, n_params, ptrs, p, root);
 }
 
 }  // namespace
@@ -134,8 +160,10 @@ extern "C" ddp_status ddp_broadcast_coalesced(const ddp_plan *plan, int32_t p,
     int32_t first, count, tiles;
     int64_t elems;
     const void *table;
+    const int32_t *tile_map;
     bool up;
-    plan_bucket_info(plan, b, &first, &count, &tiles, &elems, &table, &n_params, &eb, &up);
+    plan_bucket_info(plan, b, &first, &count, &tiles, &elems, &table, &tile_map, &n_params, &eb,
+                     &up);
     uploaded = up;
     total += elems * eb;
     if (tiles > 0) last = b;
@@ -160,16 +188,18 @@ extern "C" ddp_status ddp_broadcast_coalesced(const ddp_plan *plan, int32_t p,
     int32_t first, count, tiles;
     int64_t elems;
     const void *table;
+    const int32_t *tile_map;
     bool up;
-    plan_bucket_info(plan, b, &first, &count, &tiles, &elems, &table, &n_params, &eb, &up);
+    plan_bucket_info(plan, b, &first, &count, &tiles, &elems, &table, &tile_map, &n_params, &eb,
+                     &up);
     if (tiles == 0) continue;
     const ParamDesc *desc = static_cast<const ParamDesc *>(table) + first;
     const bool fin = b == last;
     switch (eb) {
-      case 1: s = launch_bucket<1>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
-      case 2: s = launch_bucket<2>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
-      case 4: s = launch_bucket<4>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
-      default: s = launch_bucket<8>(desc, count, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 1: s = launch_bucket<1>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 2: s = launch_bucket<2>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 4: s = launch_bucket<4>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      default: s = launch_bucket<8>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
     }
     if (s != DDP_OK) return s;
   }

@@ -5,9 +5,8 @@
 //
 // One launch handles one bucket for all p ranks: grid (tiles, p). Each
 // parameter of the bucket is cut into tiles of kFlattenTile elements, and a
-// workgroup finds its parameter by binary search over the tiles' starting
-// indices in the plan's device table (uniform across the workgroup, so the
-// search runs on scalar loads). A tile whose source and destination are both
+// workgroup finds its parameter through the tile map that follows the
+// descriptors in the plan's device table (one scalar load). A tile whose source and destination are both
 // 16-byte aligned moves 16-byte vectors; any other tile moves elements.
 #include <cmath>
 
@@ -16,14 +15,14 @@
 namespace ddpsim {
 bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
                       int32_t *count, int32_t *tiles, int64_t *elems,
-                      const void **table, int32_t *n_params, int32_t *elem_bytes,
-                      bool *uploaded);
+                      const void **table, const int32_t **tile_map, int32_t *n_params,
+                      int32_t *elem_bytes, bool *uploaded);
 
 namespace {
 
 template <typename Tr, bool kToFlat>
 __global__ __launch_bounds__(kThreads) void flatten_kernel(
-    const ParamDesc *__restrict__ desc, int32_t count, int32_t n_params,
+    const ParamDesc *__restrict__ desc, const int32_t *__restrict__ tile_map, int32_t n_params,
     const void *const *__restrict__ grad_ptrs, RankTable flat, Divide div) {
   constexpr int V = Tr::kVec;
   constexpr int kVpt = kFlattenTile / V / kThreads;
@@ -31,16 +30,7 @@ __global__ __launch_bounds__(kThreads) void flatten_kernel(
   const int32_t tile = static_cast<int32_t>(blockIdx.x);
   const int32_t r = static_cast<int32_t>(blockIdx.y);
   // last descriptor whose first tile is <= this tile
-  int32_t lo = 0, hi = count - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (desc[mid].tile_begin <= tile) {
-      lo = mid;
-    } else {
-      hi = mid - 1;
-    }
-  }
-  const ParamDesc d = desc[lo];
+  const ParamDesc d = desc[tile_map[tile]];
   const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile;
   const int64_t left = d.numel - start;
   if (left <= 0) return;
@@ -97,9 +87,10 @@ ddp_status run(const ddp_plan *plan, int32_t bucket, int32_t p,
   int32_t first, count, tiles, n_params, eb_plan;
   int64_t elems;
   const void *table;
+  const int32_t *tile_map;
   bool uploaded;
   if (plan == nullptr) return fail(DDP_EINVAL, "%s: plan is NULL", what);
-  if (!plan_bucket_info(plan, bucket, &first, &count, &tiles, &elems, &table,
+  if (!plan_bucket_info(plan, bucket, &first, &count, &tiles, &elems, &table, &tile_map,
                         &n_params, &eb_plan, &uploaded)) {
     return fail(DDP_ERANGE, "%s: bucket %d out of range", what, bucket);
   }
@@ -137,17 +128,17 @@ ddp_status run(const ddp_plan *plan, int32_t bucket, int32_t p,
   if (dtype == DDP_F32) {
     if (to_flat) {
       return launch(flatten_kernel<F32Traits, true>, grid, dim3(kThreads), stream, timer, true,
-                    kname, desc, count, n_params, d_grad_ptrs, tab, div);
+                    kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
     }
     return launch(flatten_kernel<F32Traits, false>, grid, dim3(kThreads), stream, timer, true,
-                  kname, desc, count, n_params, d_grad_ptrs, tab, div);
+                  kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
   }
   if (to_flat) {
     return launch(flatten_kernel<BF16Traits, true>, grid, dim3(kThreads), stream, timer, true,
-                  kname, desc, count, n_params, d_grad_ptrs, tab, div);
+                  kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
   }
   return launch(flatten_kernel<BF16Traits, false>, grid, dim3(kThreads), stream, timer, true,
-                kname, desc, count, n_params, d_grad_ptrs, tab, div);
+                kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
 }
 
 }  // namespace

@@ -30,7 +30,12 @@ struct ddp_plan {
   std::vector<int64_t> bucket_elems;
   std::vector<int32_t> desc_first;           // first ParamDesc of each bucket
   std::vector<int32_t> tiles;                // flatten tiles of each bucket
+  std::vector<int32_t> tile_first;           // first tile-map entry of each bucket
   std::vector<ParamDesc> desc;
+  // device table: the descriptors, then one int32 per flatten tile naming
+  // its descriptor (relative to the bucket's first); the host copy stays
+  // alive for the asynchronous upload
+  std::vector<unsigned char> staged;
   void *d_table = nullptr;
   bool uploaded = false;
   // in-place bucket all-reduce: pieces of (parameter x ring chunk), for
@@ -48,8 +53,8 @@ namespace ddpsim {
 // Accessors used by flatten.hip.
 bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
                       int32_t *count, int32_t *tiles, int64_t *elems,
-                      const void **table, int32_t *n_params, int32_t *elem_bytes,
-                      bool *uploaded) {
+                      const void **table, const int32_t **tile_map, int32_t *n_params,
+                      int32_t *elem_bytes, bool *uploaded) {
   if (plan == nullptr || b < 0 || b >= static_cast<int32_t>(plan->members.size())) {
     return false;
   }
@@ -58,6 +63,12 @@ bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
   *tiles = plan->tiles[b];
   *elems = plan->bucket_elems[b];
   *table = plan->d_table;
+  *tile_map = plan->d_table == nullptr
+                  ? nullptr
+                  : reinterpret_cast<const int32_t *>(
+                        static_cast<const char *>(plan->d_table) +
+                        plan->desc.size() * sizeof(ParamDesc)) +
+                        plan->tile_first[b];
   *n_params = plan->n_params;
   *elem_bytes = plan->elem_bytes;
   *uploaded = plan->uploaded;
@@ -270,10 +281,13 @@ ddp_status build_plan(const int64_t *numel, int32_t n_params, const int32_t *wal
   }
 
   // Device descriptors, bucket after bucket, each parameter cut into
-  // flatten tiles of kFlattenTile elements.
+  // flatten tiles of kFlattenTile elements, and the tile -> descriptor map.
+  std::vector<int32_t> tile_desc;
   for (size_t b = 0; b < plan->members.size(); ++b) {
     plan->desc_first.push_back(static_cast<int32_t>(plan->desc.size()));
+    plan->tile_first.push_back(static_cast<int32_t>(tile_desc.size()));
     int64_t tiles = 0;
+    int32_t k = 0;
     for (int32_t i : plan->members[b]) {
       ParamDesc d;
       std::memset(&d, 0, sizeof d);
@@ -281,14 +295,24 @@ ddp_status build_plan(const int64_t *numel, int32_t n_params, const int32_t *wal
       d.numel = numel[i];
       d.param = i;
       d.tile_begin = static_cast<int32_t>(tiles);
-      tiles += ceil_div(numel[i], kFlattenTile);
+      const int64_t nt = ceil_div(numel[i], kFlattenTile);
+      tiles += nt;
+      if (tiles > INT32_MAX || tile_desc.size() + nt > size_t(INT32_MAX)) {
+        delete plan;
+        return fail(DDP_EINVAL, "%s: bucket %zu is too large", what, b);
+      }
+      tile_desc.insert(tile_desc.end(), static_cast<size_t>(nt), k);
       plan->desc.push_back(d);
-    }
-    if (tiles > INT32_MAX) {
-      delete plan;
-      return fail(DDP_EINVAL, "%s: bucket %zu is too large", what, b);
+      ++k;
     }
     plan->tiles.push_back(static_cast<int32_t>(tiles));
+  }
+  const size_t desc_bytes = plan->desc.size() * sizeof(ParamDesc);
+  plan->staged.resize(desc_bytes + tile_desc.size() * sizeof(int32_t));
+  if (!plan->staged.empty()) {
+    std::memcpy(plan->staged.data(), plan->desc.data(), desc_bytes);
+    std::memcpy(plan->staged.data() + desc_bytes, tile_desc.data(),
+                tile_desc.size() * sizeof(int32_t));
   }
   *out = plan;
   return DDP_OK;
@@ -383,14 +407,14 @@ extern "C" int64_t ddp_plan_param_offset(const ddp_plan *plan, int32_t i) {
 }
 
 extern "C" size_t ddp_plan_device_bytes(const ddp_plan *plan) {
-  return plan ? plan->desc.size() * sizeof(ParamDesc) : 0;
+  return plan ? plan->staged.size() : 0;
 }
 
 extern "C" ddp_status ddp_plan_upload(ddp_plan *plan, void *d_table, size_t bytes,
                                       hipStream_t stream) {
   clear_error();
   if (plan == nullptr) return fail(DDP_EINVAL, "ddp_plan_upload: plan is NULL");
-  const size_t need = plan->desc.size() * sizeof(ParamDesc);
+  const size_t need = plan->staged.size();
   if (need == 0) {
     plan->d_table = d_table;
     plan->uploaded = true;
@@ -403,7 +427,7 @@ extern "C" ddp_status ddp_plan_upload(ddp_plan *plan, void *d_table, size_t byte
     return fail(DDP_EALIGN, "ddp_plan_upload: table is not 16-byte aligned");
   }
   ddp_status s = check_hip(
-      hipMemcpyAsync(d_table, plan->desc.data(), need, hipMemcpyHostToDevice, stream),
+      hipMemcpyAsync(d_table, plan->staged.data(), need, hipMemcpyHostToDevice, stream),
       "ddp_plan_upload: hipMemcpyAsync");
   if (s != DDP_OK) return s;
   plan->d_table = d_table;

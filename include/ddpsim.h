@@ -193,7 +193,9 @@ ddp_status ddp_plan_bucket_params(const ddp_plan *plan, int32_t b,
 int32_t ddp_plan_param_bucket(const ddp_plan *plan, int32_t i);
 int64_t ddp_plan_param_offset(const ddp_plan *plan, int32_t i);
 
-/* Size in bytes of the plan's device-side descriptor table. */
+/* Size in bytes of the plan's device-side table: 32 bytes per parameter
+ * descriptor, then 4 bytes per tile of 4096 elements naming the tile's
+ * descriptor. */
 size_t ddp_plan_device_bytes(const ddp_plan *plan);
 /* Copy the descriptor table into caller-owned device memory `d_table`
  * (at least ddp_plan_device_bytes bytes, 16-byte aligned) on `stream`, and

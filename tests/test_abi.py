@@ -55,7 +55,7 @@ def test_planner_matches_oracle_on_workloads(oracle, name, eb):
         assert a.param_offset(i) == b.offset[i]
     assert [a.bucket_numel(k) for k in range(a.num_buckets)] == \
         [b.bucket_numel(k) for k in range(b.num_buckets)]
-    assert a.device_bytes() == 32 * len(sizes)
+    assert a.device_bytes() == 32 * len(sizes) + 4 * sum(-(-n // 4096) for n in sizes)
 
 
 @pytest.mark.parametrize("seed", range(60))
