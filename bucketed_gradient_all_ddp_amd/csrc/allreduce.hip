@@ -84,8 +84,9 @@ __global__ __launch_bounds__(THR) void fused_allreduce_kernel(
       for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
       y[u] = Tr::narrow(acc[u]);
     }
-    for (int32_t r = 0; r < p; ++r) {
-      void *dst = bufs.ptr[r];
+    const int32_t rot = store_rotation(p);
+    for (int32_t k = 0; k < p; ++k) {
+      void *dst = bufs.ptr[ring_rank(rot, k, p)];
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
         if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
       const int64_t v = u * kBcastThreads + tid;
       if (v < nv) x[u] = load_vec<kBcastNtLoad>(src, v);
     }
-    for (int32_t r = 0; r < p; ++r) {
+    const int32_t rot = store_rotation(p);
+    for (int32_t k = 0; k < p; ++k) {
+      const int32_t r = ring_rank(rot, k, p);
       if (r == root) continue;
       U *dst = slice(r);
 #pragma unroll

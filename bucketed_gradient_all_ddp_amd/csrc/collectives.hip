@@ -100,7 +100,9 @@ __global__ __launch_bounds__(kThreads) void fanout_copy_kernel(
       ok[u] = j < nv;
       if (ok[u]) x[u] = load_vec(from, j);
     }
-    for (int32_t r = 0; r < p; ++r) {
+    const int32_t rot = store_rotation(p);
+    for (int32_t k = 0; k < p; ++k) {
+      const int32_t r = ring_rank(rot, k, p);
       if (r == no) continue;
       char *to = static_cast<char *>(dst.ptr[r]) + off;
 #pragma unroll

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(RankTable bufs
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = apply_divide(acc[e], div);
     const uint4 y = Tr::narrow(acc);
-    for (int32_t r = 0; r < p; ++r) store_vec<kNT>(bufs.ptr[r], g, y);
+    const int32_t rot = store_rotation(p);
+    for (int32_t k = 0; k < p; ++k) store_vec<kNT>(bufs.ptr[ring_rank(rot, k, p)], g, y);
   } else if (g == nv) {
     for (int64_t i = nv * V; i < n; ++i) {
       float acc[1];
