@@ -54,8 +54,8 @@ MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
     # (all 13 buckets in one dispatch)
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7995570146,
-        "sources_sha256": "e5c17e274277b5192cfec1175e83ef59c9bfac4da0848f4b02fdec4e369ef61a",
+        "bytes_per_launch": 7995590101,
+        "sources_sha256": "89358148f1f154fe49935f82b4a482d7b29923fd7ebd8c74ac1b0e85576f7bfd",
     },
 }
 
