@@ -209,6 +209,30 @@ def timed(torch, ddp, wl, mode, algo, steps, warmup, ws):
     return ms, kernels
 
 
+def _host_cpu() -> str:
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return cpu
+
+
+def cpu_oracle_ring(bufs, avg="world", tokens=None, what=""):
+    """The oracle's literal ring all-reduce on host arrays, one thread: the
+    CPU-baseline leg of the non-headline workloads. Returns (seconds, the
+    cpu_baseline object's text)."""
+    import oracle
+
+    t0 = time.perf_counter()
+    oracle.ring_allreduce(bufs, avg=avg, tokens=tokens, want_log=False)
+    dt = time.perf_counter() - t0
+    return dt, f"{what}: literal ring all-reduce, one thread, {dt:.2f} s on {_host_cpu()}"
+
+
 def cpu_baseline(W, wl, n_buckets_wanted):
     """The oracle (single thread): flatten, literal ring all-reduce averaged
     by p, unflatten, over the first buckets of the same plan."""
@@ -231,15 +255,7 @@ def cpu_baseline(W, wl, n_buckets_wanted):
             oracle.unflatten(red[r], oplan, b, host[r])
     dt = time.perf_counter() - t0
     S = elems * 4
-    cpu = platform.processor() or platform.machine()
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    cpu = _host_cpu()
     return {
         "value": round(S * 2 * (p - 1) / p / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
         "kind": "oracle",
@@ -305,9 +321,14 @@ def bench_ragged(torch, ddp, W, dev, args):
                      "bus_GBps": round(S * 2 * (p - 1) / p / (dms * 1e-3) / 1e9, 1),
                      "hbm_GBps": round(st.hbm_bytes / (dms * 1e-3) / 1e9, 1),
                      "launches": 1 if algo == "fused" else 2 * (p - 1)}
+    extra = {"algorithms": out}
+    if not args.no_cpu_baseline:
+        host = [W.normal_np(n, 1.0, cfg["seed"], r) for r in range(p)]
+        dt, text = cpu_oracle_ring(host, "world", None, f"the whole workload (p={p}, n={n})")
+        extra["cpu_baseline"] = {"value": round(n * 4 * 2 * (p - 1) / p / dt / 1e9, 4),
+                                 "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": text}
     _line("all-reduce bus GB/s, p=4, 1,000,003 fp32 per rank", out["fused"]["bus_GBps"], "GB/s",
-          "ragged ring: one 1,000,003-element fp32 tensor per rank, p=4, average by p",
-          {"algorithms": out})
+          "ragged ring: one 1,000,003-element fp32 tensor per rank, p=4, average by p", extra)
 
 
 def bench_llama(torch, ddp, W, dev, args):
@@ -356,7 +377,29 @@ def bench_llama(torch, ddp, W, dev, args):
                "bus_GBps": round(S * 2 * (p - 1) / p / (bwall * 1e-3) / 1e9, 1),
                "kernel_GBps": round(hbm / (bdms * 1e-3) / 1e9, 1),
                "kernel_frac_of_8TBps": round(hbm / (bdms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-           "dtype": "bf16 (fp32 accumulate)", "steps": reps})
+           "dtype": "bf16 (fp32 accumulate)", "steps": reps,
+           **({} if args.no_cpu_baseline else {"cpu_baseline": _llama_cpu(W, cfg, sizes, p)})})
+
+
+def _llama_cpu(W, cfg, sizes, p):
+    """Oracle on a streamed sample of the Llama-7B buckets (the whole set
+    does not fit a host comfortably): bucket 1 of the plan (one 4096 x 11008
+    tensor), drawn in fp32 and rounded to bf16 like the device inputs."""
+    import oracle
+
+    oplan = oracle.bucket_plan(sizes, 2, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
+    total, elems = 0.0, 0
+    for b in (1,):
+        n = oplan.bucket_numel(b)
+        flats = [oracle.f32_to_bf16(W.normal_np(n, cfg["sigma"], cfg["seed"], r, stream=b))
+                 for r in range(p)]
+        dt, _ = cpu_oracle_ring(flats, "world")
+        total += dt
+        elems += n
+    return {"value": round(elems * 2 * 2 * (p - 1) / p / total / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": (f"bucket 1 of 226 ({elems} bf16 elements per rank, p={p}): literal "
+                       f"ring all-reduce in fp32, one thread, {total:.2f} s on {_host_cpu()}")}
 
 
 def bench_latency(torch, ddp, W, dev, args):
@@ -414,7 +457,24 @@ def bench_latency(torch, ddp, W, dev, args):
                           "hbm_GBps_graph": round(hbm / (graph_ms * 1e-3) / 1e9, 1)},
            "bucketed": {"buckets": plan.num_buckets, "ms_per_step": round(wall, 3),
                         "kernel_ms_per_step": round(dms, 3),
-                        "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1)}})
+                        "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1)},
+           **({} if args.no_cpu_baseline else {"cpu_baseline": _latency_cpu(W, cfg, sizes, p)})})
+
+
+def _latency_cpu(W, cfg, sizes, p, k=1000):
+    """Oracle on the first k of the 20,000 tensors, one ring all-reduce per
+    tensor (the per-tensor mode's arithmetic)."""
+    total, elems = 0.0, 0
+    for i, n in enumerate(sizes[:k]):
+        bufs = [W.normal_np(n, 1.0, cfg["seed"] + i, r) for r in range(p)]
+        dt, _ = cpu_oracle_ring(bufs, "world")
+        total += dt
+        elems += n
+    return {"value": round(elems * 4 * 2 * (p - 1) / p / total / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": (f"the first {k} of {len(sizes)} tensors ({elems} fp32 elements per rank, "
+                       f"p={p}), one literal ring all-reduce each, one thread, {total:.2f} s on "
+                       f"{_host_cpu()}")}
 
 
 def bench_costmodel(torch, ddp, W, dev, args):
@@ -451,7 +511,18 @@ def bench_costmodel(torch, ddp, W, dev, args):
           "cost-model shape: one 2^29-element fp32 tensor per rank (2 GiB), p=64, tokens "
           "U{10..10000}; plus reduce-scatter, in-place all-gather, broadcast, and the "
           "all-reduce under recursive doubling, Rabenseifner and the tree (fused)",
-          {"ops": res})
+          {"ops": res, **({} if args.no_cpu_baseline else {"cpu_baseline": _costmodel_cpu(
+              W, cfg, p, tokens)})})
+
+
+def _costmodel_cpu(W, cfg, p, tokens, window=1 << 21):
+    """Oracle on one window of 2^21 elements (8 MiB) of every rank's 2 GiB
+    tensor, token-weighted: the full tensors do not fit a host."""
+    bufs = [W.normal_np(window, 1.0, cfg["seed"], r) for r in range(p)]
+    dt, text = cpu_oracle_ring(bufs, "tokens", tokens,
+                               f"one 8 MiB window of each rank's tensor (p={p})")
+    return {"value": round(window * 4 * 2 * (p - 1) / p / dt / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle", "sample": text}
 
 
 def bench_overlap(torch, ddp, W, dev, args):
