@@ -13,7 +13,6 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -172,10 +171,9 @@ def _ptrs(tensors: Sequence) -> ctypes.Array:
 def _tokens(tokens, p: int):
     if tokens is None:
         return None
-    arr = (ctypes.c_int64 * p)(*[int(t) for t in tokens])
     if len(tokens) != p:
         raise ValueError("tokens needs one count per rank")
-    return arr
+    return (ctypes.c_int64 * p)(*[int(t) for t in tokens])
 
 
 def _numel_all(tensors: Sequence) -> int:

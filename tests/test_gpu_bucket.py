@@ -1,7 +1,6 @@
 """GPU parity: the in-place bucket all-reduce (one pass over the gradients)
 must leave exactly the bits that the oracle's flatten -> ring all-reduce ->
 unflatten leaves, for every bucket of a plan."""
-import numpy as np
 import pytest
 import torch
 

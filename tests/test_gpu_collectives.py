@@ -1,7 +1,6 @@
 """GPU parity: standalone reduce-scatter, all-gather and broadcast against
 the CPU oracle (bit-exact), in and out of place, with shards that are and
 are not whole 16-byte vectors."""
-import numpy as np
 import pytest
 import torch
 

@@ -2,7 +2,6 @@
 the bucketed path end to end (flatten -> all-reduce -> unflatten) on small
 gradient sets, including gradients at unaligned addresses, zero-size
 parameters, pre-division and bf16."""
-import numpy as np
 import pytest
 import torch
 

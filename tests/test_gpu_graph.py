@@ -1,7 +1,6 @@
 """The library's launches inside a captured HIP graph: replaying the graph
 several times, with fresh inputs and eager work in between, must give the
 eager result bit for bit every time."""
-import numpy as np
 import pytest
 import torch
 

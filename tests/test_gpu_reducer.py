@@ -8,7 +8,6 @@ import pytest
 import torch
 
 import bucketed_gradient_all_ddp_amd as ddp
-from bucketed_gradient_all_ddp_amd import workloads as W
 from helpers import assert_bits_equal, make_grads, to_dev, to_host, tokens_for
 
 pytestmark = pytest.mark.gpu
