@@ -26,19 +26,14 @@ int32_t plan_num_buckets(const ddp_plan *plan);
 namespace {
 
 #ifndef DDPSIM_BCAST_NT
-// 0: ordinary accesses; 1: non-temporal stores; 2: non-temporal loads and
-// stores
-#define DDPSIM_BCAST_NT 0
+#define DDPSIM_BCAST_NT 0  // bit 0: non-temporal loads; bit 1: non-temporal stores
 #endif
-constexpr bool kBcastNtStore = DDPSIM_BCAST_NT >= 1;
-constexpr bool kBcastNtLoad = DDPSIM_BCAST_NT >= 2;
+constexpr bool kBcastNtLoad = (DDPSIM_BCAST_NT & 1) != 0;
+constexpr bool kBcastNtStore = (DDPSIM_BCAST_NT & 2) != 0;
 #ifndef DDPSIM_BCAST_THREADS
-#define DDPSIM_BCAST_THREADS 256  // threads per workgroup (one tile)
+#define DDPSIM_BCAST_THREADS 64  // threads per workgroup, one 16-byte vector each
 #endif
 constexpr int kBcastThreads = DDPSIM_BCAST_THREADS;
-#ifndef DDPSIM_BCAST_LANEPTR
-#define DDPSIM_BCAST_LANEPTR 1  // rank addresses by one vector load + readlane
-#endif
 
 template <int EB>
 struct Unit;
@@ -51,34 +46,35 @@ struct Unit<4> { using type = uint32_t; };
 template <>
 struct Unit<8> { using type = uint64_t; };
 
-// One workgroup per tile of kFlattenTile elements of one tensor (named by
-// the plan's tile map, as in flatten_kernel). The
-// root's slice is loaded once and stored to every other rank. 16-byte
-// vectors when every rank's copy of the tensor is 16-byte aligned (tiles
-// start at multiples of kFlattenTile elements, so the tensor's base decides),
-// elements of EB bytes otherwise.
+// Each plan tile of kFlattenTile elements of one tensor (named by the plan's
+// tile map, as in flatten_kernel) is split into spans of one 16-byte vector
+// per lane, one span per workgroup. The root's span is loaded once and
+// stored to every other rank. 16-byte vectors when every rank's copy of the
+// tensor is 16-byte aligned (spans start at multiples of 16 bytes from the
+// tensor's base, so the base decides), elements of EB bytes otherwise.
 template <int EB>
 __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
     const ParamDesc *__restrict__ desc, const int32_t *__restrict__ tile_map, int32_t n_params,
     const void *const *__restrict__ ptrs, int32_t p, int32_t root) {
   using U = typename Unit<EB>::type;
-  constexpr int kVpt = kFlattenTile * EB / kVecBytes / kBcastThreads;
-  static_assert(kVpt >= 1 && kVpt * kBcastThreads * kVecBytes == kFlattenTile * EB,
-                "a workgroup moves one tile in whole 16-byte vectors");
-  const int32_t tile = static_cast<int32_t>(blockIdx.x);
+  constexpr int kSpan = kBcastThreads * kVecBytes / EB;  // elements per workgroup
+  constexpr int kSubs = kFlattenTile / kSpan;
+  static_assert(kSubs >= 1 && kSubs * kSpan == kFlattenTile, "spans must tile a plan tile");
+  const int32_t tile = static_cast<int32_t>(blockIdx.x) / kSubs;
+  const int32_t sub = static_cast<int32_t>(blockIdx.x) - tile * kSubs;
   const ParamDesc d = desc[tile_map[tile]];
-  const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile;
+  const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile +
+                        static_cast<int64_t>(sub) * kSpan;
   const int64_t left = d.numel - start;
   if (left <= 0) return;
-  const int64_t cnt = left < kFlattenTile ? left : kFlattenTile;
+  const int64_t cnt = left < kSpan ? left : kSpan;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & 63;
-  // rank r's slice, read from the device table (uniform: scalar loads)
+  // rank r's span, read from the device table (uniform: scalar loads)
   auto slice_mem = [&](int32_t r) {
     return static_cast<U *>(const_cast<void *>(ptrs[static_cast<int64_t>(r) * n_params +
                                                     d.param])) + start;
   };
-#if DDPSIM_BCAST_LANEPTR
   // Lane r of every wave loads rank r's address once; the vector path takes
   // it from that lane (readlane, in wave-uniform code only), so the p
   // addresses cost one vector load instead of p scalar loads.
@@ -90,33 +86,18 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
     return reinterpret_cast<U *>((static_cast<uint64_t>(hi) << 32) | lo);
   };
   const bool aligned = __all(lane >= p || mine % kVecBytes == 0);
-#else
-  auto slice = slice_mem;
-  bool aligned = true;
-  for (int32_t r = 0; r < p; ++r) {
-    aligned = aligned && reinterpret_cast<uintptr_t>(slice(r)) % kVecBytes == 0;
-  }
-#endif
   const U *src = slice(root);
   int64_t done = 0;
   if (aligned) {
     const int64_t nv = cnt * EB / kVecBytes;
-    uint4 x[kVpt];
-#pragma unroll
-    for (int u = 0; u < kVpt; ++u) {
-      const int64_t v = u * kBcastThreads + tid;
-      if (v < nv) x[u] = load_vec<kBcastNtLoad>(src, v);
-    }
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (tid < nv) x = load_vec<kBcastNtLoad>(src, tid);
     const int32_t rot = store_rotation(p);
     for (int32_t k = 0; k < p; ++k) {
       const int32_t r = ring_rank(rot, k, p);
       if (r == root) continue;
       U *dst = slice(r);
-#pragma unroll
-      for (int u = 0; u < kVpt; ++u) {
-        const int64_t v = u * kBcastThreads + tid;
-        if (v < nv) store_vec<kBcastNtStore>(dst, v, x[u]);
-      }
+      if (tid < nv) store_vec<kBcastNtStore>(dst, tid, x);
     }
     done = nv * kVecBytes / EB;
   }
@@ -133,7 +114,9 @@ ddp_status launch_bucket(const ParamDesc *desc, const int32_t *tile_map, int32_t
                          int32_t n_params,
                          const void *const *ptrs, int32_t p, int32_t root, hipStream_t stream,
                          CallTimer &timer, bool last) {
-  return launch(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(tiles)),
+  const int64_t blocks = int64_t(tiles) * (kFlattenTile * EB / (kBcastThreads * kVecBytes));
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ddp_broadcast_coalesced: bucket too large");
+  return launch(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(blocks)),
                 dim3(kBcastThreads), stream, timer, last, "coalesced_broadcast_kernel launch", desc,
                 tile_map, n_params, ptrs, p, root);
 }

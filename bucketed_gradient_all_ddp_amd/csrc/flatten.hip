@@ -3,8 +3,9 @@
 // each gradient into its slice of the bucket, with the optional pre-divide;
 // "Step 3: finalize_backward", the copy back into each .grad).
 //
-// One launch handles one bucket for all p ranks: grid (tiles, p). Each
-// parameter of the bucket is cut into tiles of kFlattenTile elements, and a
+// One launch handles one bucket for all p ranks: grid (spans, p). Each
+// parameter of the bucket is cut into tiles of kFlattenTile elements, each
+// tile into spans of one 16-byte vector per lane of a workgroup, and a
 // workgroup finds its parameter through the tile map that follows the
 // descriptors in the plan's device table (one scalar load). A tile whose source and destination are both
 // 16-byte aligned moves 16-byte vectors; any other tile moves elements.
@@ -20,21 +21,40 @@ bool plan_bucket_info(const ddp_plan *plan, int32_t b, int32_t *first,
 
 namespace {
 
+#ifndef DDPSIM_FLAT_THREADS
+#define DDPSIM_FLAT_THREADS 64  // threads per workgroup, one 16-byte vector each
+#endif
+#ifndef DDPSIM_FLAT_NT
+// bit 0: non-temporal loads; bit 1: non-temporal stores. Loads only: the
+// flat bucket ddp_flatten writes is read next by the all-reduce, which finds
+// it in the Infinity Cache when the stores are ordinary.
+#define DDPSIM_FLAT_NT 1
+#endif
+constexpr int kFlatThreads = DDPSIM_FLAT_THREADS;
+constexpr bool kFlatNtLoad = (DDPSIM_FLAT_NT & 1) != 0;
+constexpr bool kFlatNtStore = (DDPSIM_FLAT_NT & 2) != 0;
+
+// Workgroup (w, r) copies the w % S-th span of kFlatThreads vectors of plan
+// tile w / S (S = spans per tile) for rank r: many small workgroups with one
+// vector per lane stream best on gfx950.
 template <typename Tr, bool kToFlat>
-__global__ __launch_bounds__(kThreads) void flatten_kernel(
+__global__ __launch_bounds__(kFlatThreads) void flatten_kernel(
     const ParamDesc *__restrict__ desc, const int32_t *__restrict__ tile_map, int32_t n_params,
     const void *const *__restrict__ grad_ptrs, RankTable flat, Divide div) {
   constexpr int V = Tr::kVec;
-  constexpr int kVpt = kFlattenTile / V / kThreads;
+  constexpr int kSpan = kFlatThreads * V;  // elements per workgroup
+  constexpr int kSubs = kFlattenTile / kSpan;
+  static_assert(kSubs >= 1 && kSubs * kSpan == kFlattenTile, "spans must tile a plan tile");
   using E = typename Tr::elem;
-  const int32_t tile = static_cast<int32_t>(blockIdx.x);
+  const int32_t tile = static_cast<int32_t>(blockIdx.x) / kSubs;
+  const int32_t sub = static_cast<int32_t>(blockIdx.x) - tile * kSubs;
   const int32_t r = static_cast<int32_t>(blockIdx.y);
-  // last descriptor whose first tile is <= this tile
   const ParamDesc d = desc[tile_map[tile]];
-  const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile;
+  const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile +
+                        static_cast<int64_t>(sub) * kSpan;
   const int64_t left = d.numel - start;
   if (left <= 0) return;
-  const int64_t cnt = left < kFlattenTile ? left : kFlattenTile;
+  const int64_t cnt = left < kSpan ? left : kSpan;
   E *grad = static_cast<E *>(const_cast<void *>(
                 grad_ptrs[static_cast<int64_t>(r) * n_params + d.param])) + start;
   E *bucket = static_cast<E *>(flat.ptr[r]) + d.bucket_offset + start;
@@ -48,28 +68,20 @@ __global__ __launch_bounds__(kThreads) void flatten_kernel(
   int64_t done = 0;
   if (aligned) {
     const int64_t nv = cnt / V;
-    uint4 x[kVpt];
-#pragma unroll
-    for (int u = 0; u < kVpt; ++u) {
-      const int64_t v = u * kThreads + tid;
-      if (v < nv) x[u] = load_vec(src, v);
-    }
-#pragma unroll
-    for (int u = 0; u < kVpt; ++u) {
-      const int64_t v = u * kThreads + tid;
-      if (v >= nv) continue;
+    if (tid < nv) {
+      uint4 x = load_vec<kFlatNtLoad>(src, tid);
       if (scale) {
         float f[V];
-        Tr::widen(x[u], f);
+        Tr::widen(x, f);
 #pragma unroll
         for (int e = 0; e < V; ++e) f[e] = apply_divide(f[e], div);
-        x[u] = Tr::narrow(f);
+        x = Tr::narrow(f);
       }
-      store_vec<false>(dst, v, x[u]);
+      store_vec<kFlatNtStore>(dst, tid, x);
     }
     done = nv * V;
   }
-  for (int64_t i = done + tid; i < cnt; i += kThreads) {
+  for (int64_t i = done + tid; i < cnt; i += kFlatThreads) {
     if (scale) {
       Tr::store1(dst, i, apply_divide(Tr::load1(src, i), div));
     } else {
@@ -123,21 +135,24 @@ ddp_status run(const ddp_plan *plan, int32_t bucket, int32_t p,
   }
   const ParamDesc *desc = static_cast<const ParamDesc *>(table) + first;
   const RankTable tab = make_table(bucket_bufs, p);
-  const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(p));
+  const int vec = dtype == DDP_F32 ? 4 : 8;
+  const int64_t blocks = int64_t(tiles) * (kFlattenTile / (kFlatThreads * vec));
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "%s: bucket too large", what);
+  const dim3 grid(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p));
   const char *kname = "flatten_kernel launch";
   if (dtype == DDP_F32) {
     if (to_flat) {
-      return launch(flatten_kernel<F32Traits, true>, grid, dim3(kThreads), stream, timer, true,
+      return launch(flatten_kernel<F32Traits, true>, grid, dim3(kFlatThreads), stream, timer, true,
                     kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
     }
-    return launch(flatten_kernel<F32Traits, false>, grid, dim3(kThreads), stream, timer, true,
+    return launch(flatten_kernel<F32Traits, false>, grid, dim3(kFlatThreads), stream, timer, true,
                   kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
   }
   if (to_flat) {
-    return launch(flatten_kernel<BF16Traits, true>, grid, dim3(kThreads), stream, timer, true,
+    return launch(flatten_kernel<BF16Traits, true>, grid, dim3(kFlatThreads), stream, timer, true,
                   kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
   }
-  return launch(flatten_kernel<BF16Traits, false>, grid, dim3(kThreads), stream, timer, true,
+  return launch(flatten_kernel<BF16Traits, false>, grid, dim3(kFlatThreads), stream, timer, true,
                 kname, desc, tile_map, n_params, d_grad_ptrs, tab, div);
 }
 
