@@ -23,15 +23,29 @@
 namespace ddpsim {
 namespace {
 
-constexpr int kRsVpt = 2;
+#ifndef DDPSIM_RS_THREADS
+#define DDPSIM_RS_THREADS 256
+#endif
+#ifndef DDPSIM_RS_VPT
+#define DDPSIM_RS_VPT 2
+#endif
+#ifndef DDPSIM_COPY_THREADS
+#define DDPSIM_COPY_THREADS 256
+#endif
+#ifndef DDPSIM_COPY_VPT
+#define DDPSIM_COPY_VPT 4
+#endif
+constexpr int kRsThreads = DDPSIM_RS_THREADS;  // reduce-scatter workgroup
+constexpr int kRsVpt = DDPSIM_RS_VPT;          // 16-byte vectors per thread
 constexpr int kRsRb = 8;
-constexpr int kCopyVpt = 4;
+constexpr int kCopyThreads = DDPSIM_COPY_THREADS;  // fan-out copy workgroup
+constexpr int kCopyVpt = DDPSIM_COPY_VPT;
 
 // Reduce-scatter, C = n/p elements per shard. Workgroups of shard c:
 // blockIdx.x / tiles_per_chunk. kVector: C is a whole number of 16-byte
 // vectors, so input chunk c and output c are both vector aligned.
 template <typename Tr, int VPT, int RB, bool kVector>
-__global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(
+__global__ __launch_bounds__(kRsThreads) void reduce_scatter_kernel(
     RankTable in, RankTable out, int32_t p, int64_t C, int32_t tiles_per_chunk,
     Divide div) {
   constexpr int V = Tr::kVec;
@@ -42,13 +56,13 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(
   const int tid = static_cast<int>(threadIdx.x);
   if constexpr (kVector) {
     const int64_t nv = C / V;
-    const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+    const int64_t base = static_cast<int64_t>(t) * (kRsThreads * VPT);
     if (base >= nv) return;
     int64_t vi[VPT];
     bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int64_t j = base + u * kThreads + tid;
+      const int64_t j = base + u * kRsThreads + tid;
       ok[u] = j < nv;
       vi[u] = static_cast<int64_t>(c) * nv + j;
     }
@@ -63,9 +77,9 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(
     }
   } else {
     // Element-wise path for shards that are not a whole number of vectors.
-    const int64_t per_tile = int64_t(kThreads) * VPT * V;
+    const int64_t per_tile = int64_t(kRsThreads) * VPT * V;
     const int64_t lo = static_cast<int64_t>(t) * per_tile;
-    for (int64_t j = lo + tid; j < lo + per_tile && j < C; j += kThreads) {
+    for (int64_t j = lo + tid; j < lo + per_tile && j < C; j += kRsThreads) {
       const float y = apply_divide(fold_scalar<Tr>(TablePtrs{in}, p, first, c * C + j), div);
       Tr::store1(dst, j, y);
     }
@@ -81,7 +95,7 @@ struct SkipTable {
 };
 
 template <int VPT, bool kVector>
-__global__ __launch_bounds__(kThreads) void fanout_copy_kernel(
+__global__ __launch_bounds__(kCopyThreads) void fanout_copy_kernel(
     RankTable src, RankTable dst, int32_t p, int64_t bytes, int64_t dst_stride,
     SkipTable skip) {
   const int32_t s = static_cast<int32_t>(blockIdx.y);
@@ -91,12 +105,12 @@ __global__ __launch_bounds__(kThreads) void fanout_copy_kernel(
   const int tid = static_cast<int>(threadIdx.x);
   if constexpr (kVector) {
     const int64_t nv = bytes / 16;
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * VPT);
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kCopyThreads * VPT);
     uint4 x[VPT];
     bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int64_t j = base + u * kThreads + tid;
+      const int64_t j = base + u * kCopyThreads + tid;
       ok[u] = j < nv;
       if (ok[u]) x[u] = load_vec(from, j);
     }
@@ -107,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void fanout_copy_kernel(
       char *to = static_cast<char *>(dst.ptr[r]) + off;
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        if (ok[u]) store_vec<false>(to, base + u * kThreads + tid, x[u]);
+        if (ok[u]) store_vec<false>(to, base + u * kCopyThreads + tid, x[u]);
       }
     }
     // trailing bytes, by the last workgroup
@@ -125,9 +139,9 @@ __global__ __launch_bounds__(kThreads) void fanout_copy_kernel(
     }
   } else {
     const int64_t units = bytes / 2;
-    const int64_t per_tile = int64_t(kThreads) * VPT * 8;
+    const int64_t per_tile = int64_t(kCopyThreads) * VPT * 8;
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * per_tile;
-    for (int64_t j = lo + tid; j < lo + per_tile && j < units; j += kThreads) {
+    for (int64_t j = lo + tid; j < lo + per_tile && j < units; j += kCopyThreads) {
       const uint16_t v = reinterpret_cast<const uint16_t *>(from)[j];
       for (int32_t r = 0; r < p; ++r) {
         if (r == no) continue;
@@ -145,15 +159,15 @@ ddp_status launch_fanout(const RankTable &src, int32_t n_src, bool vec_ok,
   if (bytes == 0) return DDP_OK;
   const bool vec = vec_ok && dst_stride % 16 == 0;
   // 16 KiB per workgroup in both paths
-  const int64_t per_tile = int64_t(kThreads) * kCopyVpt * 16;
+  const int64_t per_tile = int64_t(kCopyThreads) * kCopyVpt * 16;
   const int64_t tiles = std::max<int64_t>(1, ceil_div(bytes, per_tile));
   if (tiles > INT32_MAX) return fail(DDP_EINVAL, "%s: buffer too large", what);
   const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(n_src));
   if (vec) {
-    return launch(fanout_copy_kernel<kCopyVpt, true>, grid, dim3(kThreads), stream, timer, true,
+    return launch(fanout_copy_kernel<kCopyVpt, true>, grid, dim3(kCopyThreads), stream, timer, true,
                   what, src, dst, p, bytes, dst_stride, skip);
   }
-  return launch(fanout_copy_kernel<kCopyVpt, false>, grid, dim3(kThreads), stream, timer, true,
+  return launch(fanout_copy_kernel<kCopyVpt, false>, grid, dim3(kCopyThreads), stream, timer, true,
                 what, src, dst, p, bytes, dst_stride, skip);
 }
 
@@ -213,7 +227,7 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const RankTable tout = make_table(reinterpret_cast<const void *const *>(out), p);
   const int V = dtype == DDP_F32 ? 4 : 8;
   const bool vec = C % V == 0 && all_vec_aligned(reinterpret_cast<const void *const *>(out), p);
-  const int64_t per_tile = int64_t(kThreads) * kRsVpt * (vec ? 1 : V);
+  const int64_t per_tile = int64_t(kRsThreads) * kRsVpt * (vec ? 1 : V);
   const int64_t units = vec ? C / V : C;
   const int64_t tpc = std::max<int64_t>(1, ceil_div(units, per_tile));
   const int64_t blocks = tpc * p;
@@ -223,17 +237,17 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const char *kname = "reduce_scatter_kernel launch";
   if (dtype == DDP_F32) {
     if (vec) {
-      return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true>, grid, dim3(kThreads),
+      return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true>, grid, dim3(kRsThreads),
                     stream, timer, true, kname, tin, tout, p, C, tpc32, div);
     }
-    return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false>, grid, dim3(kThreads),
+    return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false>, grid, dim3(kRsThreads),
                   stream, timer, true, kname, tin, tout, p, C, tpc32, div);
   }
   if (vec) {
-    return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true>, grid, dim3(kThreads),
+    return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true>, grid, dim3(kRsThreads),
                   stream, timer, true, kname, tin, tout, p, C, tpc32, div);
   }
-  return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false>, grid, dim3(kThreads),
+  return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false>, grid, dim3(kRsThreads),
                 stream, timer, true, kname, tin, tout, p, C, tpc32, div);
 }
 

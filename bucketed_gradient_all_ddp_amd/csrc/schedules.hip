@@ -146,13 +146,18 @@ struct ElementLeaf {
 // One thread per 16-byte vector; thread nv (one past the last vector) folds
 // the fewer-than-V tail elements one by one. Ranks Q..p-1 (extra = p - Q of
 // them) are folded into ranks 0..extra-1 first.
+#ifndef DDPSIM_TREE_THREADS
+#define DDPSIM_TREE_THREADS 256
+#endif
+constexpr int kTreeThreads = DDPSIM_TREE_THREADS;
+
 template <typename Tr, int Q, bool kHalvingFirst, bool kNT>
-__global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(RankTable bufs, int32_t p,
+__global__ __launch_bounds__(kTreeThreads) void tree_allreduce_kernel(RankTable bufs, int32_t p,
                                                                   int64_t n, Divide div) {
   constexpr int V = Tr::kVec;
   const int32_t extra = p - Q;
   const int64_t nv = n / V;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kTreeThreads + threadIdx.x;
   if (g < nv) {
     float acc[V];
     tree_fold<Q, kHalvingFirst>(VectorLeaf<Tr, kNT>{bufs, g}, extra, acc);
@@ -422,15 +427,15 @@ template <typename Tr, int Q, bool kHalvingFirst>
 ddp_status launch_tree_q(const RankTable &tab, int32_t p, int64_t n, const Divide &div,
                          bool nt, hipStream_t stream, CallTimer &timer) {
   const int64_t nv = n / Tr::kVec;
-  const int64_t blocks = ceil_div(nv + 1, kThreads);
+  const int64_t blocks = ceil_div(nv + 1, kTreeThreads);
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "allreduce_sim: n too large");
   const dim3 grid(static_cast<uint32_t>(blocks));
   const char *what = "tree_allreduce_kernel launch";
   if (nt) {
-    return launch(tree_allreduce_kernel<Tr, Q, kHalvingFirst, true>, grid, dim3(kThreads), stream,
+    return launch(tree_allreduce_kernel<Tr, Q, kHalvingFirst, true>, grid, dim3(kTreeThreads), stream,
                   timer, true, what, tab, p, n, div);
   }
-  return launch(tree_allreduce_kernel<Tr, Q, kHalvingFirst, false>, grid, dim3(kThreads), stream,
+  return launch(tree_allreduce_kernel<Tr, Q, kHalvingFirst, false>, grid, dim3(kTreeThreads), stream,
                 timer, true, what, tab, p, n, div);
 }
 
