@@ -178,3 +178,28 @@ def test_rebuild_from_observed_ready_order(oracle, bf16):
     for r in range(p):
         for i in range(len(SIZES_R)):
             assert_bits_equal(to_host(grads[r][i]), want[r][i], f"rank {r} param {i}")
+
+
+def test_gpt2_small_parameter_sync_full_size():
+    """The benchmark's sync workload at its size: the 148 GPT-2-small fp32
+    parameter tensors of 8 ranks (views into one arena per rank, 64-element
+    aligned), two 250 MiB buckets, from rank 0. Every element of every rank
+    must equal rank 0's."""
+    p = 8
+    sizes = [W.numel(s) for _, s in W.gpt2_small_params()]
+    offs, off = [], 0
+    for n in sizes:
+        offs.append(off)
+        off += (n + 63) // 64 * 64
+    arenas = [W.normal_torch(off, 1e-3, 2, r, torch.device("cuda", 0)) for r in range(p)]
+    views = [[a[o:o + n] for o, n in zip(offs, sizes)] for a in arenas]
+    want = torch.cat([v for v in views[0]]).clone()
+    plan = ddp.ddp_coalesce_plan(sizes, 4, ddp.BROADCAST_BUCKET_BYTES).upload()
+    assert plan.num_buckets == 2
+    table = ddp.grad_pointer_table(views)
+    st = ddp.ddp_broadcast_coalesced(plan, table, p, 0)
+    torch.cuda.synchronize()
+    assert st.messages == 2 * (p - 1) and st.hbm_bytes == p * sum(sizes) * 4
+    for r in range(1, p):
+        got = torch.cat([v for v in views[r]])
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), r
