@@ -111,6 +111,9 @@ def parse():
                          "line for the record")
     ap.add_argument("--tokens", type=int, default=2048,
                     help="tokens per synthetic backward GEMM (overlap workload)")
+    ap.add_argument("--comm-workgroups", type=str, default="0,256,1024,4096",
+                    help="overlap workload: caps on the reducer's all-reduce workgroups "
+                         "to time (0 = one per tile)")
     return ap.parse_args()
 
 
@@ -583,8 +586,7 @@ def bench_overlap(torch, ddp, W, dev, args):
                 for b in range(plan.num_buckets):
                     ddp.ddp_allreduce_bucket(plan, b, wl.table, p, avg="world")
 
-    res = {}
-    for kind in ("backward_only", "sequential", "overlap"):
+    def timed_ms(kind):
         for _ in range(args.warmup):
             run(kind)
         torch.cuda.synchronize()
@@ -592,7 +594,17 @@ def bench_overlap(torch, ddp, W, dev, args):
         for _ in range(args.steps):
             run(kind)
         torch.cuda.synchronize()
-        res[kind] = (time.perf_counter() - t0) * 1e3 / args.steps
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    res = {}
+    for kind in ("backward_only", "sequential"):
+        res[kind] = timed_ms(kind)
+    capped = {}
+    for cap in [int(c) for c in args.comm_workgroups.split(",")]:
+        reducer.set_max_workgroups(cap)
+        capped[cap] = timed_ms("overlap")
+    best_cap = min(capped, key=capped.get)
+    res["overlap"] = capped[best_cap]
     gemm_flops = sum(2 * T * W.numel(params[i][1]) for i in gemms)
     exposed_seq = res["sequential"] - res["backward_only"]
     exposed_ovl = res["overlap"] - res["backward_only"]
@@ -605,6 +617,8 @@ def bench_overlap(torch, ddp, W, dev, args):
            "ms_per_step": {k: round(v, 3) for k, v in res.items()},
            "exposed_ms": {"sequential": round(exposed_seq, 3), "overlap": round(exposed_ovl, 3)},
            "hidden_fraction": round(1 - exposed_ovl / exposed_seq, 3) if exposed_seq > 0 else None,
+           "overlap_ms_by_workgroup_cap": {str(c): round(v, 3) for c, v in capped.items()},
+           "workgroup_cap": best_cap,
            "backward_gemm_tflop": round(gemm_flops / 1e12, 3),
            "runs_per_pass": len(reducer.launch_log())})
 

@@ -38,7 +38,7 @@ EXPORTS = [
     "ddp_allreduce_buckets",
     "ddp_reducer_create", "ddp_reducer_free", "ddp_reducer_prepare", "ddp_reducer_mark_ready",
     "ddp_reducer_finalize", "ddp_reducer_launch_log", "ddp_reducer_ready_order",
-    "ddp_bucket_plan_ordered", "ddp_coalesce_plan", "ddp_broadcast_coalesced",
+    "ddp_reducer_set_max_workgroups", "ddp_bucket_plan_ordered", "ddp_coalesce_plan", "ddp_broadcast_coalesced",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
     "allreduce_sim", "allreduce_sim_workspace", "ddp_schedule_time", "ddp_choose_schedule",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
@@ -116,6 +116,7 @@ def load_library(path: str = LIB_PATH):
         "ddp_reducer_finalize": ([vp, vp], st),
         "ddp_reducer_launch_log": ([vp, vp, vp, vp, i32], i32),
         "ddp_reducer_ready_order": ([vp, vp, i32], i32),
+        "ddp_reducer_set_max_workgroups": ([vp, i32], st),
         "ddp_bucket_plan_ordered": ([vp, i32, vp, i32, i64, i64, ctypes.POINTER(vp)], st),
         "ddp_coalesce_plan": ([vp, i32, i32, i64, ctypes.POINTER(vp)], st),
         "ddp_broadcast_coalesced": ([vp, i32, vp, i32, vp, vp], st),
@@ -489,6 +490,11 @@ class Reducer:
     def finalize(self, wait_stream=None) -> None:
         _check(load_library().ddp_reducer_finalize(self._h, _stream(wait_stream)),
                "ddp_reducer_finalize")
+
+    def set_max_workgroups(self, n: int) -> None:
+        """Cap each all-reduce launch at n workgroups (0: one per tile)."""
+        _check(load_library().ddp_reducer_set_max_workgroups(self._h, n),
+               "ddp_reducer_set_max_workgroups")
 
     def ready_order(self) -> List[int]:
         """Parameters in the order they were marked ready this (or the last)

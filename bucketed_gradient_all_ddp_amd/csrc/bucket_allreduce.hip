@@ -30,19 +30,16 @@ bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t 
 
 namespace {
 
-// Workgroup w handles tile tile_base + w of the plan's numbering; the tile
-// map names the piece (index into seg) each tile belongs to.
+// One tile of the plan's numbering; the tile map names the piece (index
+// into seg) each tile belongs to.
 template <typename Tr, int VPT, int RB, bool kNT>
-__global__ __launch_bounds__(kBucketThreads) void bucket_allreduce_kernel(
-    const SegDesc *__restrict__ seg, const int32_t *__restrict__ tile_seg,
-    int32_t tile_base, int32_t n_params, const void *const *__restrict__ grads,
-    int32_t p, Divide div) {
+__device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
+                                            const int32_t *__restrict__ tile_seg,
+                                            int32_t tile, int32_t n_params,
+                                            const void *const *__restrict__ grads, int32_t p,
+                                            const Divide &div) {
   constexpr int V = Tr::kVec;
   constexpr int64_t kElemBytes = sizeof(typename Tr::elem);
-  const int32_t tile =
-      tile_base + static_cast<int32_t>(DDPSIM_BUCKET_XCD
-                                           ? xcd_contiguous(blockIdx.x, gridDim.x)
-                                           : static_cast<int64_t>(blockIdx.x));
   const SegDesc d = seg[tile_seg[tile]];
   const int32_t t = tile - d.tile_begin;
   const int tid = static_cast<int>(threadIdx.x);
@@ -107,7 +104,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_allreduce_kernel(
     for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
     y[u] = Tr::narrow(acc[u]);
   }
-  const int32_t rot = store_rotation(p);
+  const int32_t rot = store_rotation(p, tile);
   for (int32_t k = 0; k < p; ++k) {
     void *dst = at(ring_rank(rot, k, p));
 #pragma unroll
@@ -117,16 +114,32 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_allreduce_kernel(
   }
 }
 
+// Workgroup w handles tiles tile_base + w, + gridDim.x, ... of the n_tiles
+// of a run of buckets: one tile each when the grid covers them all (the
+// default), several when the caller capped the number of workgroups so the
+// all-reduce leaves compute units to kernels running beside it.
+template <typename Tr, int VPT, int RB, bool kNT>
+__global__ __launch_bounds__(kBucketThreads) void bucket_allreduce_kernel(
+    const SegDesc *__restrict__ seg, const int32_t *__restrict__ tile_seg,
+    int32_t tile_base, int32_t n_tiles, int32_t n_params,
+    const void *const *__restrict__ grads, int32_t p, Divide div) {
+  for (int32_t w = static_cast<int32_t>(blockIdx.x); w < n_tiles;
+       w += static_cast<int32_t>(gridDim.x)) {
+    bucket_tile<Tr, VPT, RB, kNT>(seg, tile_seg, tile_base + w, n_params, grads, p, div);
+  }
+}
+
 }  // namespace
 }  // namespace ddpsim
 
 using namespace ddpsim;
 
-extern "C" ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_bucket,
-                                            int32_t n_buckets, int32_t p,
-                                            void *const *d_grad_ptrs, int32_t dtype,
-                                            int32_t avg_mode, const int64_t *tokens,
-                                            hipStream_t stream, ddp_comm_stats *stats) {
+namespace ddpsim {
+
+ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t n_buckets,
+                             int32_t p, void *const *d_grad_ptrs, int32_t dtype,
+                             int32_t avg_mode, const int64_t *tokens, hipStream_t stream,
+                             ddp_comm_stats *stats, int32_t max_workgroups) {
   clear_error();
   CallTimer timer = CallTimer::take();
   const char *what = "ddp_allreduce_buckets";
@@ -185,15 +198,27 @@ extern "C" ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_
   const SegDesc *seg = static_cast<const SegDesc *>(table);
   const int32_t *tile_seg = plan_tile_map(plan);
   const void *const *grads = d_grad_ptrs;
-  const dim3 grid(static_cast<uint32_t>(tiles));
+  const int32_t blocks = max_workgroups > 0 ? std::min(tiles, max_workgroups) : tiles;
+  const dim3 grid(static_cast<uint32_t>(blocks));
   if (dtype == DDP_F32) {
     return launch(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                   dim3(kBucketThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
-                  tile_seg, tile0, n_params, grads, p, div);
+                  tile_seg, tile0, tiles, n_params, grads, p, div);
   }
   return launch(bucket_allreduce_kernel<BF16Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                 dim3(kBucketThreads), stream, timer, true, "bucket_allreduce_kernel launch", seg,
-                tile_seg, tile0, n_params, grads, p, div);
+                tile_seg, tile0, tiles, n_params, grads, p, div);
+}
+
+}  // namespace ddpsim
+
+extern "C" ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_bucket,
+                                            int32_t n_buckets, int32_t p,
+                                            void *const *d_grad_ptrs, int32_t dtype,
+                                            int32_t avg_mode, const int64_t *tokens,
+                                            hipStream_t stream, ddp_comm_stats *stats) {
+  return allreduce_buckets(plan, first_bucket, n_buckets, p, d_grad_ptrs, dtype, avg_mode,
+                           tokens, stream, stats, 0);
 }
 
 extern "C" ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket, int32_t p,

@@ -68,9 +68,6 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #ifndef DDPSIM_BUCKET_VPT
 #define DDPSIM_BUCKET_VPT 1  // 16-byte vectors per thread per tile
 #endif
-#ifndef DDPSIM_BUCKET_XCD
-#define DDPSIM_BUCKET_XCD 0  // 1: give each XCD a contiguous range of tiles
-#endif
 #ifndef DDPSIM_BUCKET_THREADS
 #define DDPSIM_BUCKET_THREADS 64  // threads per workgroup (one wave)
 #endif
@@ -79,13 +76,6 @@ constexpr int kBucketThreads = DDPSIM_BUCKET_THREADS;
 constexpr int kBucketRb = 8;
 constexpr bool kBucketNt = DDPSIM_BUCKET_NT != 0;
 
-// Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD
-// b % 8). This bijection on [0, G) hands XCD x the contiguous block of
-// tiles [x q + min(x, r), ...), q = G / 8, r = G % 8.
-__host__ __device__ inline int64_t xcd_contiguous(int64_t b, int64_t G) {
-  const int64_t q = G / 8, r = G % 8, x = b % 8, k = b / 8;
-  return x * q + (x < r ? x : r) + k;
-}
 // elements per tile for a dtype whose 16-byte vector holds `vec` elements
 constexpr int64_t bucket_tile_elems(int vec) { return int64_t(kBucketThreads) * kBucketVpt * vec; }
 
@@ -119,6 +109,13 @@ ddp_status make_divide(int32_t avg_mode, int32_t p, const int64_t *tokens,
                        Divide *out);
 
 RankTable make_table(const void *const *bufs, int32_t p);
+
+// ddp_allreduce_buckets with an optional cap on its workgroups (0: one per
+// tile). Defined in bucket_allreduce.hip; the reducer uses the cap.
+ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t n_buckets,
+                             int32_t p, void *const *d_grad_ptrs, int32_t dtype,
+                             int32_t avg_mode, const int64_t *tokens, hipStream_t stream,
+                             ddp_comm_stats *stats, int32_t max_workgroups);
 
 // p, n, dtype, averaging and rank buffers of an in-place all-reduce.
 ddp_status validate_allreduce(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
@@ -280,8 +277,8 @@ __device__ __forceinline__ void store_vec(void *base, int64_t v, uint4 x) {
 // bucket all-reduce, whose chunks already start their folds at different
 // ranks; the order of the loads made no difference). Stores of one value to
 // several ranks commute, so the results are unchanged.
-__device__ __forceinline__ int32_t store_rotation(int32_t p) {
-  return DDPSIM_STORE_ROTATE ? static_cast<int32_t>(blockIdx.x % static_cast<uint32_t>(p)) : 0;
+__device__ __forceinline__ int32_t store_rotation(int32_t p, uint32_t unit = blockIdx.x) {
+  return DDPSIM_STORE_ROTATE ? static_cast<int32_t>(unit % static_cast<uint32_t>(p)) : 0;
 }
 
 // Rank (first + t) mod p without a division; first < p and t < p.

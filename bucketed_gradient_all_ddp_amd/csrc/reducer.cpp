@@ -48,6 +48,7 @@ struct ddp_reducer {
   std::vector<std::vector<hipEvent_t>> events;  // per bucket, this pass
   int32_t next = 0;
   int32_t marks = 0;
+  int32_t max_workgroups = 0;  // cap on each launch's workgroups (0: none)
   bool active = false;
   std::vector<int32_t> log_mark, log_first, log_count;
   std::vector<int32_t> ready_order;  // parameters in the order marked, this pass
@@ -107,6 +108,16 @@ extern "C" void ddp_reducer_free(ddp_reducer *r) {
   delete r;
 }
 
+extern "C" ddp_status ddp_reducer_set_max_workgroups(ddp_reducer *r, int32_t max_workgroups) {
+  clear_error();
+  if (r == nullptr) return fail(DDP_EINVAL, "ddp_reducer_set_max_workgroups: reducer is NULL");
+  if (max_workgroups < 0) {
+    return fail(DDP_EINVAL, "ddp_reducer_set_max_workgroups: %d is negative", max_workgroups);
+  }
+  r->max_workgroups = max_workgroups;
+  return DDP_OK;
+}
+
 extern "C" ddp_status ddp_reducer_prepare(ddp_reducer *r) {
   clear_error();
   if (r == nullptr) return fail(DDP_EINVAL, "ddp_reducer_prepare: reducer is NULL");
@@ -154,10 +165,9 @@ extern "C" ddp_status ddp_reducer_mark_ready(ddp_reducer *r, int32_t param,
       if (s != DDP_OK) return s;
     }
   }
-  ddp_status s = ddp_allreduce_buckets(r->plan, r->next, end - r->next, r->p, r->grads,
-                                       r->dtype, r->avg_mode,
-                                       r->tokens.empty() ? nullptr : r->tokens.data(),
-                                       r->comm, nullptr);
+  ddp_status s = allreduce_buckets(r->plan, r->next, end - r->next, r->p, r->grads, r->dtype,
+                                   r->avg_mode, r->tokens.empty() ? nullptr : r->tokens.data(),
+                                   r->comm, nullptr, r->max_workgroups);
   if (s != DDP_OK) return s;
   r->log_mark.push_back(mark);
   r->log_first.push_back(r->next);

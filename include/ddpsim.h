@@ -337,6 +337,15 @@ ddp_status ddp_reducer_finalize(ddp_reducer *reducer, hipStream_t wait_stream);
 int32_t ddp_reducer_launch_log(const ddp_reducer *reducer, int32_t *at_mark,
                                int32_t *first_bucket, int32_t *n_buckets,
                                int32_t capacity);
+/* Cap the number of workgroups of every all-reduce launch the reducer makes
+ * (0, the default: one workgroup per tile). On one device the bucket
+ * all-reduces share the compute units with the kernels producing the
+ * gradients; a capped launch walks its tiles with fewer workgroups and
+ * leaves the rest of the GPU to the backward, as a collective library gives
+ * a collective a fixed number of channels. Results are unchanged.
+ * Errors: DDP_EINVAL for a NULL reducer or a negative cap. */
+ddp_status ddp_reducer_set_max_workgroups(ddp_reducer *reducer,
+                                          int32_t max_workgroups);
 /* The parameters in the order they were marked ready in the current or last
  * pass (writes at most `capacity`; returns the count, -1 for NULL): the
  * order from which ddp_bucket_plan_ordered rebuilds the buckets. */
