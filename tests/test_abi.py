@@ -226,6 +226,9 @@ def test_reducer_errors_without_launching():
         assert L.ddp_reducer_ready_order(r, got, 8) == len(marked)
         assert list(got[:len(marked)]) == marked   # failed marks are not recorded
         assert L.ddp_reducer_ready_order(None, got, 8) == -1
+        assert L.ddp_reducer_set_max_workgroups(r, -1) == 1
+        assert L.ddp_reducer_set_max_workgroups(None, 4) == 1
+        assert L.ddp_reducer_set_max_workgroups(r, 64) == 0
         assert L.ddp_reducer_finalize(r, None) == 6
         assert b"never became ready" in L.ddp_last_error()
         assert L.ddp_reducer_finalize(r, None) == 1            # pass already ended

@@ -91,3 +91,25 @@ def test_reducer_second_pass_and_unready_bucket(oracle):
     red.finalize()
     torch.cuda.synchronize()
     assert len(red.launch_log()) == plan.num_buckets
+
+
+@pytest.mark.parametrize("cap", [1, 7, 300])
+def test_capped_workgroups_give_the_same_bits(oracle, cap):
+    """A reducer whose launches are capped at `cap` workgroups walks the
+    tiles grid-stride: same results as the oracle."""
+    p = 4
+    eb, cap_b, first = 4, 96 * 1024, 8 * 1024
+    plan = ddp.ddp_bucket_plan(SIZES, eb, cap_b, first).upload_segments(p)
+    host, grads = make_grads(p, SIZES, 1400 + cap, False, oracle, "mixed")
+    table = ddp.grad_pointer_table(grads)
+    red = ddp.Reducer(plan, p, table, avg="world")
+    red.set_max_workgroups(cap)
+    red.prepare()
+    for i in reversed(range(len(SIZES))):
+        red.mark_ready(i)
+    red.finalize()
+    torch.cuda.synchronize()
+    want, _ = _oracle_sync(oracle, host, SIZES, eb, cap_b, first, "world", None)
+    for r in range(p):
+        for i in range(len(SIZES)):
+            assert_bits_equal(to_host(grads[r][i]), want[r][i], f"cap {cap} rank {r} param {i}")
