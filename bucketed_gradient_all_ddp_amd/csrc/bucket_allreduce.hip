@@ -48,6 +48,18 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
 
   // The vector path needs every rank's copy of this parameter to sit at the
   // same offset from a 16-byte boundary.
+#if DDPSIM_BUCKET_LANEPTR
+  // lane r loads rank r's address (p <= 64 = the wave size)
+  const int my_lane = tid & 63;
+  const uint64_t mine =
+      my_lane < p
+          ? reinterpret_cast<uint64_t>(grads[static_cast<int64_t>(my_lane) * n_params + d.param])
+          : 0;
+  const uintptr_t phase =
+      __builtin_amdgcn_readlane(static_cast<uint32_t>(mine), 0) % static_cast<uint32_t>(kVecBytes);
+  const bool same =
+      phase % kElemBytes == 0 && __all(my_lane >= p || mine % kVecBytes == phase);
+#else
   const uintptr_t phase =
       reinterpret_cast<uintptr_t>(grads[d.param]) % static_cast<uintptr_t>(kVecBytes);
   bool same = phase % kElemBytes == 0;
@@ -55,6 +67,7 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
     same = same && reinterpret_cast<uintptr_t>(grads[static_cast<int64_t>(r) * n_params + d.param]) %
                        static_cast<uintptr_t>(kVecBytes) == phase;
   }
+#endif
 
   if (!same) {
     const GradPtrs at{grads, n_params, d.param, 0};
@@ -96,7 +109,12 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
     vi[u] = k.vs / V + jj;
   }
   float acc[VPT][V];
-  fold_vectors<Tr, VPT, RB, kNT>(at, p, d.chunk, vi, ok, acc);
+#if DDPSIM_BUCKET_LANEPTR
+  const LanePtrs lat{mine - static_cast<uint64_t>(m * kElemBytes)};
+#else
+  const GradPtrs &lat = at;
+#endif
+  fold_vectors<Tr, VPT, RB, kNT>(lat, p, d.chunk, vi, ok, acc);
   uint4 y[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -106,7 +124,7 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
   }
   const int32_t rot = store_rotation(p, tile);
   for (int32_t k = 0; k < p; ++k) {
-    void *dst = at(ring_rank(rot, k, p));
+    void *dst = lat(ring_rank(rot, k, p));
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);
@@ -218,7 +236,7 @@ extern "C" ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_
                                             int32_t avg_mode, const int64_t *tokens,
                                             hipStream_t stream, ddp_comm_stats *stats) {
   return allreduce_buckets(plan, first_bucket, n_buckets, p, d_grad_ptrs, dtype, avg_mode,
-                           tokens, stream, stats, 0);
+                           tokens, stream, stats, DDPSIM_BUCKET_MAX_WORKGROUPS);
 }
 
 extern "C" ddp_status ddp_allreduce_bucket(const ddp_plan *plan, int32_t bucket, int32_t p,

@@ -40,6 +40,20 @@ struct GradPtrs {
   }
 };
 
+// ...or one address per lane: lane r of the wave holds rank r's base
+// address (moved back by the same shift), and a wave-uniform rank index
+// reads it with readlane. The p addresses then cost one vector load per
+// workgroup instead of p scalar loads. Only for wave-uniform rank indices in
+// code every lane runs (the fold's and the stores' rank loops).
+struct LanePtrs {
+  uint64_t mine;
+  __device__ __forceinline__ void *operator()(int32_t r) const {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine), r);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine >> 32), r);
+    return reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+  }
+};
+
 // Fold VPT 16-byte vectors (vector indices vi[u], valid where ok[u]) over
 // the p ranks in ring order starting at `first`. RB rank loads are issued
 // before their additions; kNT makes them non-temporal.

@@ -68,6 +68,12 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #ifndef DDPSIM_BUCKET_VPT
 #define DDPSIM_BUCKET_VPT 1  // 16-byte vectors per thread per tile
 #endif
+#ifndef DDPSIM_BUCKET_MAX_WORKGROUPS
+#define DDPSIM_BUCKET_MAX_WORKGROUPS 0  // 0: one workgroup per tile
+#endif
+#ifndef DDPSIM_BUCKET_LANEPTR
+#define DDPSIM_BUCKET_LANEPTR 1  // rank addresses: one vector load + readlane
+#endif
 #ifndef DDPSIM_BUCKET_THREADS
 #define DDPSIM_BUCKET_THREADS 64  // threads per workgroup (one wave)
 #endif
