@@ -450,6 +450,10 @@ def bench_latency(torch, ddp, W, dev, args):
     for c in calls:
         c()
     wall, dms = _timed_calls(torch, ddp, calls, 5)
+    nb = plan.num_buckets
+    one = [lambda: ddp.ddp_allreduce_buckets(plan, 0, nb, table, p, avg="world")]
+    one[0]()
+    owall, odms = _timed_calls(torch, ddp, one, 5)
     _line("all-reduce step time, p=64, 20,000 tensors: bucketed vs per-tensor",
           graph_ms / wall, "x (per-tensor graph time / bucketed time)",
           "latency regime: 20,000 fp32 tensors of 64..65,536 elements (189,015,250 per rank), "
@@ -460,7 +464,10 @@ def bench_latency(torch, ddp, W, dev, args):
                           "hbm_GBps_graph": round(hbm / (graph_ms * 1e-3) / 1e9, 1)},
            "bucketed": {"buckets": plan.num_buckets, "ms_per_step": round(wall, 3),
                         "kernel_ms_per_step": round(dms, 3),
-                        "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1)},
+                        "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
+                        "one_launch_for_all_buckets": {
+                            "ms_per_step": round(owall, 3), "kernel_ms_per_step": round(odms, 3),
+                            "kernel_GBps": round(hbm / (odms * 1e-3) / 1e9, 1)}},
            **({} if args.no_cpu_baseline else {"cpu_baseline": _latency_cpu(W, cfg, sizes, p)})})
 
 
