@@ -54,8 +54,8 @@ MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
     # (all 13 buckets in one dispatch)
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7995590101,
-        "sources_sha256": "89358148f1f154fe49935f82b4a482d7b29923fd7ebd8c74ac1b0e85576f7bfd",
+        "bytes_per_launch": 7995505389,
+        "sources_sha256": "b815b28f68d0c26dea525fe165086d6e5860841f8bb527217a0708d3b2dbdcf6",
     },
 }
 
