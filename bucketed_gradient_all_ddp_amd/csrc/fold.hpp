@@ -1,5 +1,5 @@
-// fold.hpp -- the ring-order fold, shared by the fused all-reduce and the
-// fused reduce-scatter kernels.
+// fold.hpp -- the ring-order fold, shared by the fused all-reduce, the
+// in-place bucket all-reduce and the fused reduce-scatter kernels.
 //
 // The ring's reduce-scatter carries chunk c from rank c to rank c+1, c+2,
 // ... and each hop adds that rank's own, still untouched value ("Data
