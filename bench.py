@@ -54,8 +54,8 @@ MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
     # (all 13 buckets in one dispatch)
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7995505389,
-        "sources_sha256": "b815b28f68d0c26dea525fe165086d6e5860841f8bb527217a0708d3b2dbdcf6",
+        "bytes_per_launch": 7995593577,
+        "sources_sha256": "91db68c8b3b59f6aeade7de69bc6a62721e0e0073b73c5ca977e2be7ed510bff",
     },
 }
 
