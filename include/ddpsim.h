@@ -1,9 +1,12 @@
 /*
  * ddpsim.h -- C ABI of libddpsim.so: the data-parallel gradient
  * synchronisation hot path (bucket plan, flatten, ring all-reduce with
- * averaging, unflatten, and the standalone reduce-scatter / all-gather /
- * broadcast), with p simulated ranks whose buffers all live in the HBM of
- * one gfx950 GPU.
+ * averaging, unflatten, the in-place bucket all-reduce and the reducer that
+ * launches it as gradients become ready, the standalone reduce-scatter /
+ * all-gather / broadcast, the logarithmic-latency all-reduce schedules and
+ * their choice by size, and the coalesced broadcast of parameters and
+ * buffers), with p simulated ranks whose buffers all live in the HBM of one
+ * gfx950 GPU.
  *
  * Pages this interface follows, cited by title and section:
  *   [DDP] "PyTorch DDP Deep Dive -- Initialization, Buffer Broadcast, the
@@ -34,7 +37,8 @@
  *     x_c + x_{c+1} + ... + x_{c+p-1} (ranks mod p) accumulated left to
  *     right, exactly the order in which the ring's reduce-scatter adds the
  *     contributions ([COL] "Ring allreduce in two passes"; [DP] "Ring
- *     all-reduce, derived"). Both algorithms below produce these bits.
+ *     all-reduce, derived"). Both ring algorithms produce these bits; the
+ *     logarithmic schedules of allreduce_sim have their own fixed order.
  *
  * No C++ exception crosses this boundary.
  */

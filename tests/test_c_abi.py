@@ -1,0 +1,41 @@
+"""The library as a plain C program sees it: tests/c_abi/host_calls.c is
+compiled with gcc against include/ddpsim.h, linked to libddpsim.so and run
+(host-side entry points only, no GPU needed)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB_DIR = os.path.join(ROOT, "bucketed_gradient_all_ddp_amd")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+@pytest.fixture(scope="module")
+def program(tmp_path_factory):
+    if shutil.which("gcc") is None or not os.path.exists(os.path.join(LIB_DIR, "libddpsim.so")):
+        pytest.skip("needs gcc and the built library")
+    exe = str(tmp_path_factory.mktemp("cabi") / "host_calls")
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"),
+                    os.path.join(ROOT, "tests", "c_abi", "host_calls.c"), "-o", exe,
+                    "-L", LIB_DIR, "-lddpsim", f"-Wl,-rpath,{LIB_DIR}",
+                    "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+                    f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"], check=True)
+    return exe
+
+
+def test_c_caller_plans_prices_and_reports_errors(program, oracle):
+    out = subprocess.run([program], capture_output=True, text=True, timeout=60, check=True)
+    lines = out.stdout.splitlines()
+    assert lines[0] == "params 148 buckets 13"
+    from bucketed_gradient_all_ddp_amd import workloads as W
+    sizes = [W.numel(s) for _, s in W.gpt2_small_params()]
+    want = oracle.bucket_plan(sizes, 4, 25 << 20, 1 << 20)
+    for b in range(13):
+        assert lines[1 + b] == (f"bucket {b} size {len(want.bucket_params(b))} "
+                                f"numel {want.bucket_numel(b)}")
+    # 4.4 MB is the page's crossover: recursive doubling below, ring above
+    assert lines[14] == "choose 4.3MB 1 4.5MB 0"
+    assert lines[15] == "error 1 invalid argument"
