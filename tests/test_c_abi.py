@@ -39,3 +39,30 @@ def test_c_caller_plans_prices_and_reports_errors(program, oracle):
     # 4.4 MB is the page's crossover: recursive doubling below, ring above
     assert lines[14] == "choose 4.3MB 1 4.5MB 0"
     assert lines[15] == "error 1 invalid argument"
+
+
+@pytest.mark.gpu
+def test_c_caller_all_reduces_on_the_gpu_without_torch(oracle, tmp_path):
+    """tests/c_abi/device_allreduce.c allocates with hipMalloc, calls
+    ring_allreduce_sim on its own stream and dumps inputs and outputs; the
+    outputs must be the oracle's bits."""
+    import numpy as np
+
+    exe = str(tmp_path / "device_allreduce")
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"),
+                    os.path.join(ROOT, "tests", "c_abi", "device_allreduce.c"), "-o", exe,
+                    "-L", LIB_DIR, "-lddpsim", f"-Wl,-rpath,{LIB_DIR}",
+                    "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+                    f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"], check=True)
+    out = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    p, n = 4, 1000003
+    ins = np.fromfile(tmp_path / "inputs.bin", dtype=np.float32).reshape(p, n)
+    got = np.fromfile(tmp_path / "outputs.bin", dtype=np.float32).reshape(p, n)
+    want, log = oracle.ring_allreduce([ins[r] for r in range(p)], avg="world")
+    for r in range(p):
+        assert np.array_equal(got[r].view(np.uint32), want[r].view(np.uint32)), r
+    C = -(-n // p)
+    assert out.stdout.split() == ["steps", "6", "messages", str(len(log)),
+                                  "bytes_sent_per_rank", str(2 * (p - 1) * C * 4)]
