@@ -287,3 +287,38 @@ def test_cost_model_shape_p64_2gib(oracle):
         assert_bits_equal(got[:, r], src, f"broadcast rank {r}")
     del bufs, outs
     _free()
+
+
+def test_beyond_two_to_the_31_elements(oracle):
+    """Index arithmetic past 32 bits: p = 2 buffers of 2^31 + 7 fp32 elements
+    (8 GiB each) through the fused ring all-reduce, then the same elements as
+    one parameter of a bucket plan (a 9 GiB bucket) through the in-place
+    bucket all-reduce; sampled elements (random ones, every chunk's ends and
+    the last elements) against the oracle's fold."""
+    p, n = 2, (1 << 31) + 7
+    _need(p * n * 4 + 4 * GiB)
+    rng = np.random.default_rng(11)
+    bufs = [W.normal_torch(n, 1.0, 31, r, "cuda") for r in range(p)]
+    idx = np.unique(np.concatenate([_samples(n, p, 2048, rng),
+                                    np.arange(n - 40, n, dtype=np.int64)]))
+    vals = _gather(bufs, idx)
+    _say("2^31+7: fused ring all-reduce")
+    ddp.ring_allreduce_sim(bufs, avg="world")
+    torch.cuda.synchronize()
+    want = oracle.allreduce_at(vals, idx, n, avg="world")
+    got = _gather(bufs, idx)
+    for r in range(p):
+        assert_bits_equal(got[:, r], want, f"ring rank {r}")
+    # the results are the next inputs: one parameter, one bucket
+    vals2 = got.copy()
+    plan = ddp.ddp_bucket_plan([n], 4, 25 << 20, 1 << 20).upload_segments(p)
+    table = ddp.grad_pointer_table([[b] for b in bufs])
+    _say("2^31+7: in-place bucket all-reduce")
+    ddp.ddp_allreduce_buckets(plan, 0, 1, table, p, avg="none")
+    torch.cuda.synchronize()
+    want2 = oracle.allreduce_at(vals2, idx, n, avg="none")
+    got2 = _gather(bufs, idx)
+    for r in range(p):
+        assert_bits_equal(got2[:, r], want2, f"bucket rank {r}")
+    del bufs
+    _free()
