@@ -292,9 +292,10 @@ def test_cost_model_shape_p64_2gib(oracle):
 def test_beyond_two_to_the_31_elements(oracle):
     """Index arithmetic past 32 bits: p = 2 buffers of 2^31 + 7 fp32 elements
     (8 GiB each) through the fused ring all-reduce, then the same elements as
-    one parameter of a bucket plan (a 9 GiB bucket) through the in-place
-    bucket all-reduce; sampled elements (random ones, every chunk's ends and
-    the last elements) against the oracle's fold."""
+    one parameter of a bucket plan through the in-place bucket all-reduce,
+    the fused tree all-reduce and the coalesced broadcast; sampled elements
+    (random ones, every chunk's ends and the last elements) against the
+    oracle."""
     p, n = 2, (1 << 31) + 7
     _need(p * n * 4 + 4 * GiB)
     rng = np.random.default_rng(11)
@@ -320,5 +321,23 @@ def test_beyond_two_to_the_31_elements(oracle):
     got2 = _gather(bufs, idx)
     for r in range(p):
         assert_bits_equal(got2[:, r], want2, f"bucket rank {r}")
+    # the tree all-reduce (fused) and the coalesced broadcast on the same
+    # buffers
+    vals3 = got2.copy()
+    _say("2^31+7: tree all-reduce")
+    ddp.allreduce_sim(bufs, "tree", False, avg="world")
+    torch.cuda.synchronize()
+    want3 = oracle.tree_allreduce_at(vals3, "tree", avg="world")
+    got3 = _gather(bufs, idx)
+    for r in range(p):
+        assert_bits_equal(got3[:, r], want3, f"tree rank {r}")
+    bufs[1].add_(1.0)  # make the ranks differ again
+    _say("2^31+7: coalesced broadcast from rank 1")
+    bplan = ddp.ddp_coalesce_plan([n], 4, 1 << 40).upload()
+    ddp.ddp_broadcast_coalesced(bplan, table, p, 1)
+    torch.cuda.synchronize()
+    got4 = _gather(bufs, idx)
+    assert np.array_equal(got4[:, 0].view(np.uint32), got4[:, 1].view(np.uint32))
+    assert np.array_equal(got4[:, 1], (got3[:, 1] + np.float32(1.0)).astype(np.float32))
     del bufs
     _free()
