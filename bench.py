@@ -566,13 +566,17 @@ def bench_overlap(torch, ddp, W, dev, args):
     dsts = [[wl.grads[r][i] for r in range(p)] for i in range(len(sizes))]
     srcs = [[src_views[r][i] for r in range(p)] for i in range(len(sizes))]
 
-    def backward(mark):
+    def backward(mark, clock=None):
         with torch.cuda.stream(producer):
+            if clock is not None:
+                clock[0].record(producer)
             for i in order:
                 if i in gemms:
                     A, B, O = gemms[i]
                     torch.mm(A, B, out=O)
                 torch._foreach_copy_(dsts[i], srcs[i])
+                if clock is not None:
+                    clock[1][i].record(producer)
                 if mark:
                     events[i].record(producer)
                     reducer.mark_ready(i, events[i])
@@ -615,6 +619,7 @@ def bench_overlap(torch, ddp, W, dev, args):
     gemm_flops = sum(2 * T * W.numel(params[i][1]) for i in gemms)
     exposed_seq = res["sequential"] - res["backward_only"]
     exposed_ovl = res["overlap"] - res["backward_only"]
+    model = _overlap_model(torch, ddp, plan, p, wl.table, backward, len(sizes))
     _line("exposed all-reduce time per step, overlapped vs after backward",
           exposed_ovl, "ms", "gpt2-small gradients, p=8: synthetic backward (per parameter "
           f"in reverse order: a bf16 GEMM [a,{T}]x[{T},b] for each 2-D parameter, then its "
@@ -627,7 +632,54 @@ def bench_overlap(torch, ddp, W, dev, args):
            "overlap_ms_by_workgroup_cap": {str(c): round(v, 3) for c, v in capped.items()},
            "workgroup_cap": best_cap,
            "backward_gemm_tflop": round(gemm_flops / 1e12, 3),
-           "runs_per_pass": len(reducer.launch_log())})
+           "runs_per_pass": len(reducer.launch_log()),
+           "model": model})
+
+
+def _overlap_model(torch, ddp, plan, p, table, backward, n_params, reps=5):
+    """The overlapped step-time model (ddp_overlap_step_time) fed with this
+    device's own timings: each parameter's ready time from a backward-only
+    pass queued behind another (events after its gradients are written, from
+    an event at the pass's start), each bucket's all-reduce
+    time from its own launches. The model takes the all-reduces to run on a
+    resource of their own; on one GPU they share compute units and HBM with
+    the backward, which the measured exposed time includes. The same ready
+    times with the latency-bandwidth ring time of each bucket on the page's
+    example network (alpha 10 us, 50 GB/s) give what a real link would
+    expose."""
+    start = torch.cuda.Event(enable_timing=True)
+    after = [torch.cuda.Event(enable_timing=True) for _ in range(n_params)]
+    ready = [0.0] * n_params
+    for _ in range(reps):
+        # the timed pass queued behind an untimed one, as in back-to-back steps
+        torch.cuda.synchronize()
+        backward(False)
+        backward(False, (start, after))
+        torch.cuda.synchronize()
+        for i, e in enumerate(after):
+            ready[i] += start.elapsed_time(e) * 1e-3 / reps
+    nb = plan.num_buckets
+    timer = ddp.CallTimer(pairs=nb * reps)
+    ids = [[] for _ in range(nb)]
+    for _ in range(reps):
+        for b in range(nb):
+            ids[b].append(timer.arm())
+            ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
+    torch.cuda.synchronize()
+    btime = [sum(timer.elapsed_ms(k) for k in ids[b]) * 1e-3 / reps for b in range(nb)]
+    step, exposed = ddp.overlap_step_time(plan, ready, btime)
+    alpha, beta = 10e-6, 1 / 50e9
+    nbytes = [plan.bucket_numel(b) * plan.elem_bytes for b in range(nb)]
+    net = [ddp.schedule_time("ring", p, m, alpha, beta) for m in nbytes]
+    nstep, nexp = ddp.overlap_step_time(plan, ready, net)
+    return {"inputs": "ready times: backward-only pass on the device; bucket times: "
+                      "per-bucket all-reduce launches on the device",
+            "backward_ms": round(max(ready) * 1e3, 3),
+            "allreduce_ms_sum": round(sum(btime) * 1e3, 3),
+            "step_ms": round(step * 1e3, 3), "exposed_ms": round(exposed * 1e3, 3),
+            "network_alpha10us_50GBps": {"allreduce_ms_sum": round(sum(net) * 1e3, 3),
+                                         "step_ms": round(nstep * 1e3, 3),
+                                         "exposed_ms": round(nexp * 1e3, 3)}}
 
 
 def bench_crossover(torch, ddp, W, dev, args):

@@ -15,6 +15,6 @@ from .binding import (  # noqa: F401
     allgather_sim, allreduce_sim, allreduce_sim_workspace, broadcast_coalesced, broadcast_sim,
     choose_schedule, ddp_allreduce_bucket, ddp_allreduce_buckets, ddp_broadcast_coalesced,
     ddp_bucket_plan, ddp_coalesce_plan, ddp_flatten, ddp_unflatten, sync_module_states,
-    grad_pointer_table, load_library, reduce_scatter_sim, ring_allreduce_sim,
+    grad_pointer_table, load_library, overlap_step_time, reduce_scatter_sim, ring_allreduce_sim,
     ring_allreduce_sim_steps, ring_allreduce_sim_workspace, schedule_time,
 )

@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import List, Optional, Sequence
+from typing import List, Optional, Sequence, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libddpsim.so")
@@ -41,6 +41,7 @@ EXPORTS = [
     "ddp_reducer_set_max_workgroups", "ddp_bucket_plan_ordered", "ddp_coalesce_plan", "ddp_broadcast_coalesced",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
     "allreduce_sim", "allreduce_sim_workspace", "ddp_schedule_time", "ddp_choose_schedule",
+    "ddp_overlap_step_time",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
 ]
 
@@ -129,6 +130,7 @@ def load_library(path: str = LIB_PATH):
                               ctypes.c_double),
         "ddp_choose_schedule": ([i32, i64, ctypes.c_double, ctypes.c_double, ctypes.c_uint32],
                                 i32),
+        "ddp_overlap_step_time": ([vp, vp, vp, vp, vp], st),
         "reduce_scatter_sim": ([vp, vp, i32, i64, i32, i32, vp, vp, vp], st),
         "allgather_sim": ([vp, vp, i32, i64, i32, vp, vp], st),
         "broadcast_sim": ([vp, i32, i64, i32, i32, vp, vp], st),
@@ -587,6 +589,24 @@ def choose_schedule(p: int, nbytes: int, alpha: float, beta: float,
         raise DDPError(1, "ddp_choose_schedule",
                        load_library().ddp_last_error().decode(errors="replace"))
     return {v: k for k, v in SCHEDULES.items()}[s]
+
+
+def overlap_step_time(plan: "Plan", ready: Sequence[float],
+                      bucket_time: Sequence[float]) -> Tuple[float, float]:
+    """(step, exposed) seconds of a backward whose bucket all-reduces overlap
+    it: ready[i] is parameter i's ready time, bucket_time[b] bucket b's
+    all-reduce duration."""
+    if len(ready) != plan.num_params or len(bucket_time) != plan.num_buckets:
+        raise ValueError(f"overlap_step_time: {plan.num_params} ready times and "
+                         f"{plan.num_buckets} bucket times expected, got {len(ready)} "
+                         f"and {len(bucket_time)}")
+    rd = (ctypes.c_double * max(1, len(ready)))(*ready)
+    bt = (ctypes.c_double * max(1, len(bucket_time)))(*bucket_time)
+    step, exposed = ctypes.c_double(), ctypes.c_double()
+    _check(load_library().ddp_overlap_step_time(plan.handle, rd, bt, ctypes.byref(step),
+                                                ctypes.byref(exposed)),
+           "ddp_overlap_step_time")
+    return step.value, exposed.value
 
 
 def reduce_scatter_sim(inputs: Sequence, outputs: Sequence, avg: str = "none",

@@ -18,6 +18,7 @@
 // records each ready parameter while a rebuild is due, and the rebuild runs
 // before the next forward).
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -224,4 +225,44 @@ extern "C" int32_t ddp_reducer_ready_order(const ddp_reducer *r, int32_t *order,
   const int32_t n = static_cast<int32_t>(r->ready_order.size());
   for (int32_t k = 0; k < n && k < capacity && order != nullptr; ++k) order[k] = r->ready_order[k];
   return n;
+}
+
+// The reducer's schedule in the latency-bandwidth model: bucket b starts at
+// max(its last parameter's ready time, end of bucket b-1).
+extern "C" ddp_status ddp_overlap_step_time(const ddp_plan *plan, const double *ready,
+                                            const double *bucket_time, double *step,
+                                            double *exposed) {
+  clear_error();
+  const char *what = "ddp_overlap_step_time";
+  if (plan == nullptr || ready == nullptr || bucket_time == nullptr) {
+    return fail(DDP_EINVAL, "%s: plan, ready or bucket_time is NULL", what);
+  }
+  const int32_t n_params = ddp_plan_num_params(plan);
+  const int32_t n_buckets = ddp_plan_num_buckets(plan);
+  for (int32_t i = 0; i < n_params; ++i) {
+    if (!std::isfinite(ready[i]) || ready[i] < 0.0) {
+      return fail(DDP_EINVAL, "%s: ready[%d] = %g is not a finite time >= 0", what, i, ready[i]);
+    }
+  }
+  for (int32_t b = 0; b < n_buckets; ++b) {
+    if (!std::isfinite(bucket_time[b]) || bucket_time[b] < 0.0) {
+      return fail(DDP_EINVAL, "%s: bucket_time[%d] = %g is not a finite time >= 0", what, b,
+                  bucket_time[b]);
+    }
+  }
+  std::vector<double> bucket_ready(static_cast<size_t>(n_buckets), 0.0);
+  double end_bwd = 0.0;
+  for (int32_t i = 0; i < n_params; ++i) {
+    const int32_t b = ddp_plan_param_bucket(plan, i);
+    bucket_ready[static_cast<size_t>(b)] = std::max(bucket_ready[static_cast<size_t>(b)], ready[i]);
+    end_bwd = std::max(end_bwd, ready[i]);
+  }
+  double finish = 0.0;
+  for (int32_t b = 0; b < n_buckets; ++b) {
+    finish = std::max(bucket_ready[static_cast<size_t>(b)], finish) + bucket_time[b];
+  }
+  const double t = std::max(end_bwd, finish);
+  if (step != nullptr) *step = t;
+  if (exposed != nullptr) *exposed = t - end_bwd;
+  return DDP_OK;
 }

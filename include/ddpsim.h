@@ -4,9 +4,9 @@
  * averaging, unflatten, the in-place bucket all-reduce and the reducer that
  * launches it as gradients become ready, the standalone reduce-scatter /
  * all-gather / broadcast, the logarithmic-latency all-reduce schedules and
- * their choice by size, and the coalesced broadcast of parameters and
- * buffers), with p simulated ranks whose buffers all live in the HBM of one
- * gfx950 GPU.
+ * their choice by size, the overlapped step-time model, and the coalesced
+ * broadcast of parameters and buffers), with p simulated ranks whose
+ * buffers all live in the HBM of one gfx950 GPU.
  *
  * Pages this interface follows, cited by title and section:
  *   [DDP] "PyTorch DDP Deep Dive -- Initialization, Buffer Broadcast, the
@@ -482,6 +482,29 @@ double ddp_schedule_time(int32_t schedule, int32_t p, double bytes,
  * Returns -1 (with ddp_last_error) for bad arguments or no candidate. */
 int32_t ddp_choose_schedule(int32_t p, int64_t bytes, double alpha,
                             double beta, uint32_t candidates);
+
+/* Step time of a backward pass whose bucket all-reduces overlap it ([DP]
+ * "Overlapping communication with the backward pass": the step-time
+ * exercise there, whose printed stub has no overlap at all, taken with the
+ * overlap the section describes). Bucket b's all-reduce starts once the last
+ * of its parameters is ready and bucket b-1's all-reduce has finished
+ * (buckets run one at a time in index order, as the reducer launches them)
+ * and lasts bucket_time[b]. The backward ends at the latest ready time; the
+ * step ends when the backward and the last all-reduce have both finished;
+ * the exposed time is step minus the end of backward.
+ *   plan         bucket plan: the parameters of each bucket
+ *   ready        HOST array of ddp_plan_num_params(plan) times, in seconds
+ *                from the start of backward, at which each parameter's
+ *                gradient is ready (registration index order)
+ *   bucket_time  HOST array of ddp_plan_num_buckets(plan) all-reduce
+ *                durations in seconds: ddp_schedule_time of each bucket's
+ *                bytes for a network, or kernel times measured on a device
+ *   step, exposed  outputs (either may be NULL)
+ * Every time must be finite and >= 0. Errors: DDP_EINVAL (NULL plan or
+ * array, a negative, NaN or infinite time); outputs untouched then. */
+ddp_status ddp_overlap_step_time(const ddp_plan *plan, const double *ready,
+                                 const double *bucket_time, double *step,
+                                 double *exposed);
 
 /* ----------------------------------------------------------------------- */
 /* Standalone collectives                                                  */

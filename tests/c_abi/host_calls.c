@@ -34,6 +34,18 @@ int main(void) {
   ddp_plan_free(plan);
   /* the ring / recursive-doubling crossover at 10 us and 50 GB/s, p = 8 */
   const double alpha = 10e-6, beta = 1.0 / 50e9;
+  /* the overlapped step time on that network: 25 MiB buckets (the first one
+   * too), parameter i ready (n - i) ms into backward */
+  if (ddp_bucket_plan(numel, n, 4, 25LL << 20, 25LL << 20, &plan) != DDP_OK) return 1;
+  double ready[148], btime[148], step = 0.0, exposed = 0.0;
+  for (int i = 0; i < n; ++i) ready[i] = (n - i) * 1e-3;
+  for (int b = 0; b < ddp_plan_num_buckets(plan); ++b) {
+    btime[b] = ddp_schedule_time(DDP_SCHED_RING, 8, 4.0 * ddp_plan_bucket_numel(plan, b),
+                                 alpha, beta);
+  }
+  if (ddp_overlap_step_time(plan, ready, btime, &step, &exposed) != DDP_OK) return 1;
+  printf("overlap %.17g %.17g\n", step, exposed);
+  ddp_plan_free(plan);
   const uint32_t ring_rd = (1u << DDP_SCHED_RING) | (1u << DDP_SCHED_RECURSIVE_DOUBLING);
   printf("choose 4.3MB %d 4.5MB %d\n", ddp_choose_schedule(8, 4300000, alpha, beta, ring_rd),
          ddp_choose_schedule(8, 4500000, alpha, beta, ring_rd));

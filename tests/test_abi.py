@@ -297,6 +297,62 @@ def test_choose_schedule_matches_oracle_and_flips_at_crossover():
     assert L.ddp_schedule_time(9, 8, 1.0, a, b) < 0
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_overlap_step_time_matches_oracle(seed):
+    """The library's overlapped step-time model against the oracle's on
+    random plans, ready times and bucket durations. With the first-bucket
+    cap equal to the cap the oracle groups the gradients (given in backward
+    order, last registered first) into the plan's buckets; the model's
+    arithmetic is a max and a sum per bucket, so the values agree exactly."""
+    from oracle import costmodel as cm
+    rng = np.random.default_rng(seed)
+    P = int(rng.integers(1, 60))
+    numel = [int(x) for x in rng.integers(0, 5000, P)]
+    cap = int(rng.integers(4, 40000))
+    eb = 4
+    plan = ddp.ddp_bucket_plan(numel, eb, cap, cap)
+    # ready times: mostly in backward order, with some jitter and ties
+    ready = [float(x) for x in np.round((P - np.arange(P)) * 1e-3
+                                        + rng.uniform(0, 3e-3, P), 4)]
+    p, a, b = int(rng.integers(2, 65)), 10e-6, 1 / 50e9
+    bucket_bytes = [plan.bucket_numel(k) * eb for k in range(plan.num_buckets)]
+    btime = [cm.allreduce_time(m, p, a, b, "ring") for m in bucket_bytes]
+    got = ddp.overlap_step_time(plan, ready, btime)
+    grads = [(numel[i] * eb, ready[i]) for i in reversed(range(P))]
+    want = cm.ddp_step_time(grads, bucket_cap=cap, p=p, alpha=a, beta=b)
+    # the oracle's grouping is the plan's
+    assert got == want
+
+
+def test_overlap_step_time_cases_and_errors():
+    plan = ddp.ddp_bucket_plan([10, 20, 30], 4, 40, 40)  # one parameter per bucket
+    # buckets {2}, {1}, {0}: each starts at max(ready, previous finish)
+    assert ddp.overlap_step_time(plan, [3.0, 2.0, 1.0], [0.5, 0.25, 0.125]) == (3.125, 0.125)
+    # everything ready at once: the all-reduces run back to back after it
+    assert ddp.overlap_step_time(plan, [1.0, 1.0, 1.0], [0.5, 0.25, 0.125]) == (1.875, 0.875)
+    # all-reduces long enough to delay one another past the backward
+    assert ddp.overlap_step_time(plan, [0.75, 0.5, 0.25], [1.0, 1.0, 1.0]) == (3.25, 2.5)
+    L = load_library()
+    rd = (ctypes.c_double * 3)(1.0, 2.0, 3.0)
+    bt = (ctypes.c_double * 3)(1.0, 1.0, 1.0)
+    st = ctypes.c_double(-7.0)
+    assert L.ddp_overlap_step_time(None, rd, bt, ctypes.byref(st), None) != 0
+    assert L.ddp_overlap_step_time(plan.handle, None, bt, None, None) != 0
+    assert L.ddp_overlap_step_time(plan.handle, rd, None, None, None) != 0
+    for bad in (-1.0, float("nan"), float("inf")):
+        rd[1] = bad
+        assert L.ddp_overlap_step_time(plan.handle, rd, bt, ctypes.byref(st), None) != 0
+        assert b"ready[1]" in L.ddp_last_error()
+        rd[1] = 2.0
+        bt[2] = bad
+        assert L.ddp_overlap_step_time(plan.handle, rd, bt, ctypes.byref(st), None) != 0
+        assert b"bucket_time[2]" in L.ddp_last_error()
+        bt[2] = 1.0
+    assert st.value == -7.0
+    with pytest.raises(ValueError):
+        ddp.overlap_step_time(plan, [1.0, 2.0], [1.0, 1.0, 1.0])
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_ordered_and_coalesce_planners_match_oracle(oracle, seed):
     rng = np.random.default_rng(500 + seed)

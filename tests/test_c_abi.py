@@ -36,9 +36,19 @@ def test_c_caller_plans_prices_and_reports_errors(program, oracle):
     for b in range(13):
         assert lines[1 + b] == (f"bucket {b} size {len(want.bucket_params(b))} "
                                 f"numel {want.bucket_numel(b)}")
+    # the overlapped step time against the oracle's model (25 MiB buckets
+    # throughout, so the oracle's grouping is the plan's)
+    from oracle import costmodel as cm
+    n = len(sizes)
+    grads = [(sizes[i] * 4, (n - i) * 1e-3) for i in reversed(range(n))]
+    step, exposed = cm.ddp_step_time(grads, bucket_cap=25 << 20, p=8, alpha=10e-6,
+                                     beta=1 / 50e9)
+    word, got_step, got_exposed = lines[14].split()
+    assert word == "overlap"
+    assert (float(got_step), float(got_exposed)) == (step, exposed)
     # 4.4 MB is the page's crossover: recursive doubling below, ring above
-    assert lines[14] == "choose 4.3MB 1 4.5MB 0"
-    assert lines[15] == "error 1 invalid argument"
+    assert lines[15] == "choose 4.3MB 1 4.5MB 0"
+    assert lines[16] == "error 1 invalid argument"
 
 
 @pytest.mark.gpu
