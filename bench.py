@@ -454,6 +454,14 @@ def bench_latency(torch, ddp, W, dev, args):
     one = [lambda: ddp.ddp_allreduce_buckets(plan, 0, nb, table, p, avg="world")]
     one[0]()
     owall, odms = _timed_calls(torch, ddp, one, 5)
+    # the per-tensor arithmetic (every tensor padded and chunked on its own)
+    # in one launch: caps of 0 bytes give every tensor a bucket of its own
+    tplan = ddp.ddp_bucket_plan(sizes, 4, 0, 0)
+    tplan.upload_segments(p, dev)
+    tone = [lambda: ddp.ddp_allreduce_buckets(tplan, 0, tplan.num_buckets, table, p,
+                                              avg="world")]
+    tone[0]()
+    twall, tdms = _timed_calls(torch, ddp, tone, 5)
     _line("all-reduce step time, p=64, 20,000 tensors: bucketed vs per-tensor",
           graph_ms / wall, "x (per-tensor graph time / bucketed time)",
           "latency regime: 20,000 fp32 tensors of 64..65,536 elements (189,015,250 per rank), "
@@ -461,7 +469,11 @@ def bench_latency(torch, ddp, W, dev, args):
           {"per_tensor": {"launches": len(sizes), "host_loop_ms": round(host_ms, 2),
                           "graph_replay_ms": round(graph_ms, 2),
                           "graph_us_per_launch": round(graph_ms * 1e3 / len(sizes), 2),
-                          "hbm_GBps_graph": round(hbm / (graph_ms * 1e-3) / 1e9, 1)},
+                          "hbm_GBps_graph": round(hbm / (graph_ms * 1e-3) / 1e9, 1),
+                          "one_launch_for_all_tensors": {
+                              "ms_per_step": round(twall, 3),
+                              "kernel_ms_per_step": round(tdms, 3),
+                              "kernel_GBps": round(hbm / (tdms * 1e-3) / 1e9, 1)}},
            "bucketed": {"buckets": plan.num_buckets, "ms_per_step": round(wall, 3),
                         "kernel_ms_per_step": round(dms, 3),
                         "kernel_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),

@@ -1,6 +1,7 @@
 """GPU parity: the in-place bucket all-reduce (one pass over the gradients)
 must leave exactly the bits that the oracle's flatten -> ring all-reduce ->
 unflatten leaves, for every bucket of a plan."""
+import numpy as np
 import pytest
 import torch
 
@@ -122,3 +123,25 @@ def test_bucket_allreduce_at_max_ranks(oracle, bf16, layout):
     for r in range(p):
         for i in range(len(sizes)):
             assert_bits_equal(to_host(grads[r][i]), want[r][i], f"rank {r} param {i}")
+
+
+@pytest.mark.parametrize("p,layout", [(3, "odd"), (8, "aligned"), (64, "mixed")])
+def test_per_tensor_mode_in_one_launch(oracle, p, layout):
+    """Caps of 0 bytes put every tensor in a bucket of its own, so one
+    ddp_allreduce_buckets launch over all buckets does the per-tensor
+    all-reduce of every tensor (each with its own padding and chunks): the
+    bits of the oracle's ring all-reduce of each tensor alone."""
+    rng = np.random.default_rng(40 + p)
+    sizes = [int(v) for v in np.rint(np.exp(rng.uniform(0, np.log(6000), 60)))]
+    plan = ddp.ddp_bucket_plan(sizes, 4, 0, 0).upload_segments(p)
+    assert plan.num_buckets == len(sizes)
+    host, grads = make_grads(p, sizes, 1400 + p, False, oracle, layout)
+    table = ddp.grad_pointer_table(grads)
+    st = ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg="world")
+    assert st.hbm_bytes == 2 * p * sum(sizes) * 4
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        want, _ = oracle.ring_allreduce([host[r][i] for r in range(p)], avg="world",
+                                        want_log=False)
+        for r in range(p):
+            assert_bits_equal(to_host(grads[r][i]), want[r], f"rank {r} tensor {i}")
