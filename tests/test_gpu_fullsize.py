@@ -227,7 +227,28 @@ def test_latency_regime_per_tensor_and_bucketed(oracle):
         got = _gather(arenas, ai)
         for r in range(p):
             assert_bits_equal(got[:, r], want, f"bucket {b} rank {r}")
-    del arenas, grads
+    # the same 30 buckets as one launch, on the results as new inputs
+    picks = [(b, flat, ai, _gather(arenas, ai)) for b, flat, ai, _ in picks]
+    _say("latency: bucketed, one launch for all buckets")
+    ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg="world")
+    torch.cuda.synchronize()
+    for b, flat, ai, vals in picks:
+        want = oracle.allreduce_at(vals, flat, plan.bucket_numel(b), avg="world")
+        got = _gather(arenas, ai)
+        for r in range(p):
+            assert_bits_equal(got[:, r], want, f"one launch: bucket {b} rank {r}")
+    # the per-tensor arithmetic in one launch: caps of 0 bytes, every tensor
+    # its own bucket
+    _say("latency: per-tensor, one launch for all tensors")
+    tplan = ddp.ddp_bucket_plan(sizes, 4, 0, 0).upload_segments(p)
+    before = {i: [to_host(grads[r][i]) for r in range(p)] for i in check}
+    ddp.ddp_allreduce_buckets(tplan, 0, tplan.num_buckets, table, p, avg="world")
+    torch.cuda.synchronize()
+    for i in check:
+        want, _ = oracle.ring_allreduce(before[i], avg="world", want_log=False)
+        for r in range(p):
+            assert_bits_equal(to_host(grads[r][i]), want[r], f"one launch: tensor {i} rank {r}")
+    del arenas, grads, tplan
     _free()
 
 
@@ -285,6 +306,20 @@ def test_cost_model_shape_p64_2gib(oracle):
     got = _gather(bufs, idx)
     for r in range(p):
         assert_bits_equal(got[:, r], src, f"broadcast rank {r}")
+
+    # the token-weighted all-reduce under each logarithmic schedule, fused,
+    # each on fresh values
+    for k, schedule in enumerate(("recursive_doubling", "rabenseifner", "tree")):
+        for r in range(p):
+            W.normal_torch(n, 1.0, cfg["seed"] + 3 + k, r, "cuda", out=bufs[r])
+        vals = _gather(bufs, idx)
+        _say(f"cost-model shape: {schedule} all-reduce of 64 x 2 GiB")
+        ddp.allreduce_sim(bufs, schedule, False, avg="tokens", tokens=tokens)
+        torch.cuda.synchronize()
+        want = oracle.tree_allreduce_at(vals, schedule, avg="tokens", tokens=tokens)
+        got = _gather(bufs, idx)
+        for r in range(p):
+            assert_bits_equal(got[:, r], want, f"{schedule} rank {r}")
     del bufs, outs
     _free()
 
