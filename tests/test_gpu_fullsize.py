@@ -2,7 +2,9 @@
 
 - GPT-2 small (124M fp32 per rank, p=8): every element of every rank is
   compared with the oracle's flatten -> literal ring -> unflatten, for the
-  in-place bucket all-reduce, the three-kernel path and the ring-step path.
+  in-place bucket all-reduce (one launch for all buckets, one per bucket,
+  and the reducer's capped launches), the three-kernel path and the
+  ring-step path.
 - Llama-7B (6.7G bf16 per rank, p=8, 108 GB resident), the latency regime
   (20,000 tensors, p=64) and the 2 GiB x 64 cost-model shape: sampled
   elements (random ones plus every chunk's first and last element) are
@@ -117,7 +119,7 @@ def test_gpt2_small_full_compare(oracle):
             oracle.unflatten(red[r], oplan, b, want[r])
         del flats, red
     table = ddp.grad_pointer_table(grads)
-    for path in ("batched", "inplace", "copy-fused", "copy-ring"):
+    for path in ("batched", "inplace", "reducer-capped", "copy-fused", "copy-ring"):
         _say(f"gpt2: {path}")
         for r in range(p):
             for i, g in enumerate(grads[r]):
@@ -125,7 +127,18 @@ def test_gpt2_small_full_compare(oracle):
         if path == "batched":
             # the benchmark's headline launch: every bucket in one dispatch
             ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg="world")
-        for b in range(plan.num_buckets if path != "batched" else 0):
+        if path == "reducer-capped":
+            # the overlap workload's form: the reducer on its own stream, each
+            # launch capped at 1,024 workgroups, parameters marked in reverse
+            torch.cuda.synchronize()
+            comm = torch.cuda.Stream()
+            reducer = ddp.Reducer(plan, p, table, avg="world", comm_stream=comm)
+            reducer.set_max_workgroups(1024)
+            reducer.prepare()
+            for i in reversed(range(len(sizes))):
+                reducer.mark_ready(i)
+            reducer.finalize(torch.cuda.current_stream())
+        for b in range(plan.num_buckets if path in ("inplace", "copy-fused", "copy-ring") else 0):
             if path == "inplace":
                 ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
             else:
