@@ -9,7 +9,8 @@ straddle vectors or lie wholly in the padding, several tiles per job), the
 cancellation probes that pin each schedule's pairing, and the accounting
 against the oracle's message log. At a size the oracle does not simulate
 whole (64 ranks of 16 MiB), sampled elements are checked against the
-oracle's per-element form.
+oracle's per-element form; the crossover sweep's largest case (4 ranks of
+64 MB) is compared whole.
 """
 import itertools
 
@@ -147,3 +148,17 @@ def test_fused_hbm_bytes_and_step_traffic():
     assert fused.hbm_bytes == 2 * p * n * 4
     _, stepped = _run(host, "recursive_doubling", True)
     assert stepped.hbm_bytes == 3 * (p // 2) * 4 * n * 4  # 3 steps, p/2 pairs, 2 reads + 2 writes
+
+
+@pytest.mark.parametrize("schedule", ("ring",) + LOG_SCHEDULES)
+def test_crossover_sweep_largest_size_whole(oracle, schedule):
+    """The crossover sweep's largest case, 4 ranks of 64 MB averaged by p,
+    in both forms the sweep times (step by step and fused): every element
+    against the oracle's literal simulation."""
+    p, n = 4, 1 << 24
+    host = [W.normal_np(n, 1.0, 700, r) for r in range(p)]
+    want, _ = oracle.allreduce(host, schedule, avg="world", want_log=False)
+    for steps in (True, False):
+        got, _ = _run(host, schedule, steps, "world")
+        for r in range(p):
+            assert_bits_equal(got[r], want[r], f"{schedule} steps={steps} rank {r}")
