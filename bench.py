@@ -54,8 +54,8 @@ MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
     # (all 13 buckets in one dispatch)
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7995593577,
-        "sources_sha256": "91db68c8b3b59f6aeade7de69bc6a62721e0e0073b73c5ca977e2be7ed510bff",
+        "bytes_per_launch": 7995512085,
+        "sources_sha256": "d50a31af84321c3aa59b08208ca5760693d568f7d213c072349ab14e4605e202",
     },
 }
 

@@ -77,6 +77,9 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #ifndef DDPSIM_BUCKET_THREADS
 #define DDPSIM_BUCKET_THREADS 64  // threads per workgroup (one wave)
 #endif
+#ifndef DDPSIM_BUCKET_WGS_PER_CU
+#define DDPSIM_BUCKET_WGS_PER_CU 11  // workgroups resident per CU (0: no bound)
+#endif
 constexpr int kBucketVpt = DDPSIM_BUCKET_VPT;
 constexpr int kBucketThreads = DDPSIM_BUCKET_THREADS;
 constexpr int kBucketRb = 8;
@@ -152,13 +155,22 @@ struct CallTimer {
 };
 
 // Every kernel of the library is launched through here: a plain dispatch,
-// with the call's timing events attached when requested.
+// with the call's timing events attached when requested. lds_bytes of
+// dynamic LDS are reserved per workgroup (the kernels that take some use
+// it only to bound how many of their workgroups share a compute unit).
+template <typename Kernel, typename... Args>
+ddp_status launch_lds(Kernel kernel, dim3 grid, dim3 block, size_t lds_bytes,
+                      hipStream_t stream, CallTimer &timer, bool last, const char *what,
+                      Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, timer.start_event(),
+                        last ? timer.stop : nullptr, 0, args...);
+  return check_hip(hipGetLastError(), what);
+}
+
 template <typename Kernel, typename... Args>
 ddp_status launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream,
                   CallTimer &timer, bool last, const char *what, Args... args) {
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, timer.start_event(),
-                        last ? timer.stop : nullptr, 0, args...);
-  return check_hip(hipGetLastError(), what);
+  return launch_lds(kernel, grid, block, 0, stream, timer, last, what, args...);
 }
 
 // ---------------------------------------------------------------------------
