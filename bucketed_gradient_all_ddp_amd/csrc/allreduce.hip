@@ -214,20 +214,21 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
   }
   const dim3 grid(static_cast<uint32_t>(blocks));
   const dim3 block(kFusedThreads);
+  const size_t lds = residency_lds(DDPSIM_FUSED_WGS_PER_CU);
   if (dtype == DDP_F32) {
     if (nt) {
-      return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
-                    grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
+      return launch_lds(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
+                        grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
     }
-    return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
-                  grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
+    return launch_lds(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
+                      grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
   }
   if (nt) {
-    return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
-                  grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
+    return launch_lds(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
+                      grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
   }
-  return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
-                grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
+  return launch_lds(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
+                    grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
 }
 
 // Launch ring steps [first, first + count) on fp32 buffers.

@@ -147,37 +147,6 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_allreduce_kernel(
   }
 }
 
-// Dynamic LDS per workgroup that leaves room for only `wgs` of them on one
-// compute unit (0: none reserved); the kernel never touches it. Each
-// workgroup keeps 2p streams of 1 KiB in flight (p loads, p stores), and a
-// full CU (32 one-wave workgroups) puts more streams on every HBM channel
-// than the rows it can keep open: bounding residency at 11 per CU raised the
-// GPT-2 p=8 launch from 5.76 to 6.05 TB/s and the Llama bf16 buckets by
-// 3-4%, while 6 per CU starved the channels (5.2). Sizes follow the
-// device's LDS per CU, in the 512-byte allocation granule.
-size_t residency_lds(int32_t wgs) {
-  if (wgs <= 0) return 0;
-  constexpr int kMaxDevices = 64;
-  static int32_t per_cu_of[kMaxDevices];  // by device; 0 = not asked yet
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  const bool cached = dev >= 0 && dev < kMaxDevices;
-  int per_cu = cached ? __atomic_load_n(&per_cu_of[dev], __ATOMIC_RELAXED) : 0;
-  if (per_cu == 0) {
-    if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
-                              dev) != hipSuccess ||
-        per_cu <= 0) {
-      (void)hipGetLastError();
-      return 0;
-    }
-    if (cached) __atomic_store_n(&per_cu_of[dev], per_cu, __ATOMIC_RELAXED);
-  }
-  return static_cast<size_t>(per_cu / wgs) / 512 * 512;
-}
-
 }  // namespace
 }  // namespace ddpsim
 
@@ -249,6 +218,11 @@ ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t
   const void *const *grads = d_grad_ptrs;
   const int32_t blocks = max_workgroups > 0 ? std::min(tiles, max_workgroups) : tiles;
   const dim3 grid(static_cast<uint32_t>(blocks));
+  // Each workgroup keeps 2p streams of 1 KiB in flight (p loads, p
+  // stores); a CU full of them (32 one-wave workgroups) puts more streams on
+  // every HBM channel than it keeps rows open. Bounding residency at 11 per
+  // CU raised the GPT-2 p=8 launch from 5.76 to 6.05 TB/s and the Llama bf16
+  // buckets by 3-4%; 6 per CU starved the channels (5.2).
   const size_t lds = residency_lds(DDPSIM_BUCKET_WGS_PER_CU);
   if (dtype == DDP_F32) {
     return launch_lds(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,

@@ -116,9 +116,10 @@ ddp_status launch_bucket(const ParamDesc *desc, const int32_t *tile_map, int32_t
                          CallTimer &timer, bool last) {
   const int64_t blocks = int64_t(tiles) * (kFlattenTile * EB / (kBcastThreads * kVecBytes));
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ddp_broadcast_coalesced: bucket too large");
-  return launch(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(blocks)),
-                dim3(kBcastThreads), stream, timer, last, "coalesced_broadcast_kernel launch", desc,
-                tile_map, n_params, ptrs, p, root);
+  return launch_lds(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(blocks)),
+                    dim3(kBcastThreads), residency_lds(DDPSIM_BCAST_WGS_PER_CU), stream, timer,
+                    last, "coalesced_broadcast_kernel launch", desc, tile_map, n_params, ptrs, p,
+                    root);
 }
 
 }  // namespace

@@ -163,12 +163,13 @@ ddp_status launch_fanout(const RankTable &src, int32_t n_src, bool vec_ok,
   const int64_t tiles = std::max<int64_t>(1, ceil_div(bytes, per_tile));
   if (tiles > INT32_MAX) return fail(DDP_EINVAL, "%s: buffer too large", what);
   const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(n_src));
+  const size_t lds = residency_lds(DDPSIM_COPY_WGS_PER_CU);
   if (vec) {
-    return launch(fanout_copy_kernel<kCopyVpt, true>, grid, dim3(kCopyThreads), stream, timer, true,
-                  what, src, dst, p, bytes, dst_stride, skip);
+    return launch_lds(fanout_copy_kernel<kCopyVpt, true>, grid, dim3(kCopyThreads), lds, stream,
+                      timer, true, what, src, dst, p, bytes, dst_stride, skip);
   }
-  return launch(fanout_copy_kernel<kCopyVpt, false>, grid, dim3(kCopyThreads), stream, timer, true,
-                what, src, dst, p, bytes, dst_stride, skip);
+  return launch_lds(fanout_copy_kernel<kCopyVpt, false>, grid, dim3(kCopyThreads), lds, stream,
+                    timer, true, what, src, dst, p, bytes, dst_stride, skip);
 }
 
 void fill_stats(ddp_comm_stats *st, int64_t steps, int64_t messages, int64_t sent,
@@ -235,20 +236,22 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const dim3 grid(static_cast<uint32_t>(blocks));
   const int32_t tpc32 = static_cast<int32_t>(tpc);
   const char *kname = "reduce_scatter_kernel launch";
+  const size_t lds = residency_lds(DDPSIM_RS_WGS_PER_CU);
+  const dim3 block(kRsThreads);
   if (dtype == DDP_F32) {
     if (vec) {
-      return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true>, grid, dim3(kRsThreads),
-                    stream, timer, true, kname, tin, tout, p, C, tpc32, div);
+      return launch_lds(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true>, grid, block, lds,
+                        stream, timer, true, kname, tin, tout, p, C, tpc32, div);
     }
-    return launch(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false>, grid, dim3(kRsThreads),
-                  stream, timer, true, kname, tin, tout, p, C, tpc32, div);
+    return launch_lds(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false>, grid, block, lds,
+                      stream, timer, true, kname, tin, tout, p, C, tpc32, div);
   }
   if (vec) {
-    return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true>, grid, dim3(kRsThreads),
-                  stream, timer, true, kname, tin, tout, p, C, tpc32, div);
+    return launch_lds(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true>, grid, block, lds,
+                      stream, timer, true, kname, tin, tout, p, C, tpc32, div);
   }
-  return launch(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false>, grid, dim3(kRsThreads),
-                stream, timer, true, kname, tin, tout, p, C, tpc32, div);
+  return launch_lds(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false>, grid, block, lds,
+                    stream, timer, true, kname, tin, tout, p, C, tpc32, div);
 }
 
 extern "C" ddp_status allgather_sim(const void *const *in, void *const *out, int32_t p,

@@ -179,6 +179,29 @@ RankTable make_table(const void *const *bufs, int32_t p) {
   return t;
 }
 
+size_t residency_lds(int32_t wgs) {
+  if (wgs <= 0) return 0;
+  constexpr int kMaxDevices = 64;
+  static int32_t per_cu_of[kMaxDevices];  // by device; 0 = not asked yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  int per_cu = cached ? __atomic_load_n(&per_cu_of[dev], __ATOMIC_RELAXED) : 0;
+  if (per_cu == 0) {
+    if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              dev) != hipSuccess ||
+        per_cu <= 0) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    if (cached) __atomic_store_n(&per_cu_of[dev], per_cu, __ATOMIC_RELAXED);
+  }
+  return static_cast<size_t>(per_cu / wgs) / 512 * 512;
+}
+
 }  // namespace ddpsim
 
 using namespace ddpsim;

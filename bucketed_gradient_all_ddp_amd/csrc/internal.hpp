@@ -80,6 +80,22 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #ifndef DDPSIM_BUCKET_WGS_PER_CU
 #define DDPSIM_BUCKET_WGS_PER_CU 11  // workgroups resident per CU (0: no bound)
 #endif
+// The same bound for the other streaming kernels (0: none).
+#ifndef DDPSIM_FUSED_WGS_PER_CU
+#define DDPSIM_FUSED_WGS_PER_CU 0
+#endif
+#ifndef DDPSIM_RS_WGS_PER_CU
+#define DDPSIM_RS_WGS_PER_CU 0
+#endif
+#ifndef DDPSIM_COPY_WGS_PER_CU
+#define DDPSIM_COPY_WGS_PER_CU 0
+#endif
+#ifndef DDPSIM_TREE_WGS_PER_CU
+#define DDPSIM_TREE_WGS_PER_CU 0
+#endif
+#ifndef DDPSIM_BCAST_WGS_PER_CU
+#define DDPSIM_BCAST_WGS_PER_CU 0
+#endif
 constexpr int kBucketVpt = DDPSIM_BUCKET_VPT;
 constexpr int kBucketThreads = DDPSIM_BUCKET_THREADS;
 constexpr int kBucketRb = 8;
@@ -118,6 +134,14 @@ ddp_status make_divide(int32_t avg_mode, int32_t p, const int64_t *tokens,
                        Divide *out);
 
 RankTable make_table(const void *const *bufs, int32_t p);
+
+// Dynamic LDS per workgroup that leaves room for only `wgs` workgroups on
+// one compute unit (0 for wgs <= 0, or when the device cannot be asked):
+// the device's LDS per CU divided by wgs, in the 512-byte allocation
+// granule. Kernels launched with it never touch it; it only bounds how many
+// of their workgroups share a CU, so that fewer streams compete for each
+// memory channel's open rows.
+size_t residency_lds(int32_t wgs);
 
 // ddp_allreduce_buckets with an optional cap on its workgroups (0: one per
 // tile). Defined in bucket_allreduce.hip; the reducer uses the cap.
