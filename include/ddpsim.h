@@ -115,14 +115,17 @@ const char *ddp_last_error(void);
 /* Library version string. */
 const char *ddp_version(void);
 
-/* Instrumentation. The next entry-point call made on this thread attaches
+/* Instrumentation. The next call on this thread of an entry point that
+ * launches kernels (flatten / unflatten, the all-reduces and collectives,
+ * the coalesced broadcast, and a reducer mark that launches a run) attaches
  * `start` to the dispatch of its first kernel and `stop` to the dispatch of
  * its last kernel (hipExtLaunchKernel semantics), so
  * hipEventElapsedTime(start, stop) is exactly the device time of that
- * call's kernels, with nothing else on the stream in between. Events are
- * created and owned by the caller (hipEventCreate). The request is consumed
- * by the next call even if that call fails or launches nothing (n == 0);
- * then the events are not recorded. Pass NULL, NULL to cancel.
+ * call's kernels, with nothing else on the stream in between. Host-only
+ * calls (planning, uploads, the models, accessors) leave the request
+ * pending. Events are created and owned by the caller (hipEventCreate). The
+ * request is consumed by that call even if it fails or launches nothing
+ * (n == 0); then the events are not recorded. Pass NULL, NULL to cancel.
  * Errors: DDP_EINVAL if exactly one of the two is NULL. */
 ddp_status ddp_time_next_call(hipEvent_t start, hipEvent_t stop);
 
