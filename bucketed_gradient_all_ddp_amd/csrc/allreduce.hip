@@ -176,9 +176,17 @@ __global__ __launch_bounds__(kThreads) void ring_step_kernel(
 // ddp_flatten has just written, say), where ordinary accesses are faster.
 #define DDPSIM_FUSED_NT_BYTES (int64_t(256) << 20)
 #endif
+#ifndef DDPSIM_FUSED_NT_WGS_PER_CU
+// Buffers past the Infinity Cache take the in-place bucket kernel's shape:
+// one-wave workgroups of one vector per lane, at most this many resident per
+// CU (8 ranks of 1 GiB: 5.42 -> 6.06 TB/s against 256 threads x 2 vectors;
+// 64 ranks of 2 GiB: equal). Cache-resident buffers keep the shape above.
+#define DDPSIM_FUSED_NT_WGS_PER_CU 11
+#endif
 constexpr int kFusedVpt = DDPSIM_FUSED_VPT;
 constexpr int kFusedRb = DDPSIM_FUSED_RB;
 constexpr int kFusedThreads = DDPSIM_FUSED_THREADS;
+constexpr int kFusedNtThreads = 64;
 // Small problems (few workgroups) are latency-bound: the fold's load batches
 // run one after another, so there the kernel keeps 32 rank loads in flight
 // per thread (one vector each) instead of 8.
@@ -212,23 +220,29 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
     return launch(fused_allreduce_kernel<BF16Traits, 1, kSmallRb, false, kThreads>, grid1,
                   dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc1, div);
   }
+  if (nt) {
+    const int32_t tpcn = tiles_for(C, vec, 1, kFusedNtThreads);
+    const int64_t bn = int64_t(tpcn) * p;
+    if (bn > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
+    const dim3 gridn(static_cast<uint32_t>(bn));
+    const size_t lds = residency_lds(DDPSIM_FUSED_NT_WGS_PER_CU);
+    if (dtype == DDP_F32) {
+      return launch_lds(fused_allreduce_kernel<F32Traits, 1, kFusedRb, true, kFusedNtThreads>,
+                        gridn, dim3(kFusedNtThreads), lds, stream, timer, true, kname, tab, p, n,
+                        C, tpcn, div);
+    }
+    return launch_lds(fused_allreduce_kernel<BF16Traits, 1, kFusedRb, true, kFusedNtThreads>,
+                      gridn, dim3(kFusedNtThreads), lds, stream, timer, true, kname, tab, p, n, C,
+                      tpcn, div);
+  }
   const dim3 grid(static_cast<uint32_t>(blocks));
   const dim3 block(kFusedThreads);
-  const size_t lds = residency_lds(DDPSIM_FUSED_WGS_PER_CU);
   if (dtype == DDP_F32) {
-    if (nt) {
-      return launch_lds(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
-                        grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
-    }
-    return launch_lds(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
-                      grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
+    return launch(fused_allreduce_kernel<F32Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
+                  grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
   }
-  if (nt) {
-    return launch_lds(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, true, kFusedThreads>,
-                      grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
-  }
-  return launch_lds(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
-                    grid, block, lds, stream, timer, true, kname, tab, p, n, C, tpc, div);
+  return launch(fused_allreduce_kernel<BF16Traits, kFusedVpt, kFusedRb, false, kFusedThreads>,
+                grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
 }
 
 // Launch ring steps [first, first + count) on fp32 buffers.

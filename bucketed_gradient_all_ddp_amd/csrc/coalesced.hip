@@ -33,6 +33,9 @@ constexpr bool kBcastNtStore = (DDPSIM_BCAST_NT & 2) != 0;
 #ifndef DDPSIM_BCAST_THREADS
 #define DDPSIM_BCAST_THREADS 64  // threads per workgroup, one 16-byte vector each
 #endif
+#ifndef DDPSIM_BCAST_WGS_PER_CU
+#define DDPSIM_BCAST_WGS_PER_CU 0  // workgroups resident per CU (0: no bound)
+#endif
 constexpr int kBcastThreads = DDPSIM_BCAST_THREADS;
 
 template <int EB>

@@ -23,20 +23,38 @@
 namespace ddpsim {
 namespace {
 
+// Reduce-scatter shapes. Up to DDPSIM_RS_NARROW_MAX_RANKS ranks: one-wave
+// workgroups of one vector per lane, at most DDPSIM_RS_WGS_PER_CU of them
+// resident per CU (8 ranks of 1 GiB: 5.59 -> 6.36 TB/s). More ranks: the
+// wide shape below (at 64 ranks of 2 GiB the narrow one was 2% slower).
 #ifndef DDPSIM_RS_THREADS
-#define DDPSIM_RS_THREADS 256
+#define DDPSIM_RS_THREADS 256  // wide shape: threads per workgroup
 #endif
 #ifndef DDPSIM_RS_VPT
-#define DDPSIM_RS_VPT 2
+#define DDPSIM_RS_VPT 2  // wide shape: 16-byte vectors per thread
 #endif
+#ifndef DDPSIM_RS_NARROW_MAX_RANKS
+#define DDPSIM_RS_NARROW_MAX_RANKS 16
+#endif
+#ifndef DDPSIM_RS_WGS_PER_CU
+#define DDPSIM_RS_WGS_PER_CU 11
+#endif
+// Fan-out copy (all-gather, broadcast): one-wave workgroups of one vector per
+// lane (8 ranks of 1 GiB: all-gather 5.40 -> 5.83, broadcast 5.27 -> 5.77
+// TB/s against 256 threads x 4 vectors; at 64 ranks 1-4% better). A bound
+// on residency gained nothing here.
 #ifndef DDPSIM_COPY_THREADS
-#define DDPSIM_COPY_THREADS 256
+#define DDPSIM_COPY_THREADS 64
 #endif
 #ifndef DDPSIM_COPY_VPT
-#define DDPSIM_COPY_VPT 4
+#define DDPSIM_COPY_VPT 1
 #endif
-constexpr int kRsThreads = DDPSIM_RS_THREADS;  // reduce-scatter workgroup
-constexpr int kRsVpt = DDPSIM_RS_VPT;          // 16-byte vectors per thread
+#ifndef DDPSIM_COPY_WGS_PER_CU
+#define DDPSIM_COPY_WGS_PER_CU 0
+#endif
+constexpr int kRsThreads = DDPSIM_RS_THREADS;
+constexpr int kRsVpt = DDPSIM_RS_VPT;
+constexpr int kRsNarrowThreads = 64;
 constexpr int kRsRb = 8;
 constexpr int kCopyThreads = DDPSIM_COPY_THREADS;  // fan-out copy workgroup
 constexpr int kCopyVpt = DDPSIM_COPY_VPT;
@@ -44,8 +62,8 @@ constexpr int kCopyVpt = DDPSIM_COPY_VPT;
 // Reduce-scatter, C = n/p elements per shard. Workgroups of shard c:
 // blockIdx.x / tiles_per_chunk. kVector: C is a whole number of 16-byte
 // vectors, so input chunk c and output c are both vector aligned.
-template <typename Tr, int VPT, int RB, bool kVector>
-__global__ __launch_bounds__(kRsThreads) void reduce_scatter_kernel(
+template <typename Tr, int VPT, int RB, bool kVector, int THR>
+__global__ __launch_bounds__(THR) void reduce_scatter_kernel(
     RankTable in, RankTable out, int32_t p, int64_t C, int32_t tiles_per_chunk,
     Divide div) {
   constexpr int V = Tr::kVec;
@@ -56,13 +74,13 @@ __global__ __launch_bounds__(kRsThreads) void reduce_scatter_kernel(
   const int tid = static_cast<int>(threadIdx.x);
   if constexpr (kVector) {
     const int64_t nv = C / V;
-    const int64_t base = static_cast<int64_t>(t) * (kRsThreads * VPT);
+    const int64_t base = static_cast<int64_t>(t) * (THR * VPT);
     if (base >= nv) return;
     int64_t vi[VPT];
     bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int64_t j = base + u * kRsThreads + tid;
+      const int64_t j = base + u * THR + tid;
       ok[u] = j < nv;
       vi[u] = static_cast<int64_t>(c) * nv + j;
     }
@@ -77,9 +95,9 @@ __global__ __launch_bounds__(kRsThreads) void reduce_scatter_kernel(
     }
   } else {
     // Element-wise path for shards that are not a whole number of vectors.
-    const int64_t per_tile = int64_t(kRsThreads) * VPT * V;
+    const int64_t per_tile = int64_t(THR) * VPT * V;
     const int64_t lo = static_cast<int64_t>(t) * per_tile;
-    for (int64_t j = lo + tid; j < lo + per_tile && j < C; j += kRsThreads) {
+    for (int64_t j = lo + tid; j < lo + per_tile && j < C; j += THR) {
       const float y = apply_divide(fold_scalar<Tr>(TablePtrs{in}, p, first, c * C + j), div);
       Tr::store1(dst, j, y);
     }
@@ -158,7 +176,7 @@ ddp_status launch_fanout(const RankTable &src, int32_t n_src, bool vec_ok,
                          hipStream_t stream, CallTimer &timer, const char *what) {
   if (bytes == 0) return DDP_OK;
   const bool vec = vec_ok && dst_stride % 16 == 0;
-  // 16 KiB per workgroup in both paths
+  // kCopyThreads * kCopyVpt vectors per workgroup in both paths
   const int64_t per_tile = int64_t(kCopyThreads) * kCopyVpt * 16;
   const int64_t tiles = std::max<int64_t>(1, ceil_div(bytes, per_tile));
   if (tiles > INT32_MAX) return fail(DDP_EINVAL, "%s: buffer too large", what);
@@ -170,6 +188,35 @@ ddp_status launch_fanout(const RankTable &src, int32_t n_src, bool vec_ok,
   }
   return launch_lds(fanout_copy_kernel<kCopyVpt, false>, grid, dim3(kCopyThreads), lds, stream,
                     timer, true, what, src, dst, p, bytes, dst_stride, skip);
+}
+
+// Everything a reduce-scatter launch needs besides its shape.
+struct RsLaunch {
+  dim3 grid;
+  hipStream_t stream;
+  CallTimer *timer;
+  RankTable in, out;
+  int32_t p;
+  int64_t C;
+  int32_t tiles_per_chunk;
+  Divide div;
+};
+
+template <int VPT, int THR, typename Tr, bool kVector>
+ddp_status launch_rs_as(const RsLaunch &L, size_t lds) {
+  return launch_lds(reduce_scatter_kernel<Tr, VPT, kRsRb, kVector, THR>, L.grid, dim3(THR), lds,
+                    L.stream, *L.timer, true, "reduce_scatter_kernel launch", L.in, L.out, L.p,
+                    L.C, L.tiles_per_chunk, L.div);
+}
+
+template <int VPT, int THR>
+ddp_status launch_rs(const RsLaunch &L, int32_t dtype, bool vec, size_t lds) {
+  if (dtype == DDP_F32) {
+    return vec ? launch_rs_as<VPT, THR, F32Traits, true>(L, lds)
+               : launch_rs_as<VPT, THR, F32Traits, false>(L, lds);
+  }
+  return vec ? launch_rs_as<VPT, THR, BF16Traits, true>(L, lds)
+             : launch_rs_as<VPT, THR, BF16Traits, false>(L, lds);
 }
 
 void fill_stats(ddp_comm_stats *st, int64_t steps, int64_t messages, int64_t sent,
@@ -228,30 +275,19 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const RankTable tout = make_table(reinterpret_cast<const void *const *>(out), p);
   const int V = dtype == DDP_F32 ? 4 : 8;
   const bool vec = C % V == 0 && all_vec_aligned(reinterpret_cast<const void *const *>(out), p);
-  const int64_t per_tile = int64_t(kRsThreads) * kRsVpt * (vec ? 1 : V);
+  const bool narrow = p <= DDPSIM_RS_NARROW_MAX_RANKS;
+  const int64_t per_tile =
+      (narrow ? int64_t(kRsNarrowThreads) : int64_t(kRsThreads) * kRsVpt) * (vec ? 1 : V);
   const int64_t units = vec ? C / V : C;
   const int64_t tpc = std::max<int64_t>(1, ceil_div(units, per_tile));
   const int64_t blocks = tpc * p;
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "%s: n too large", what);
-  const dim3 grid(static_cast<uint32_t>(blocks));
-  const int32_t tpc32 = static_cast<int32_t>(tpc);
-  const char *kname = "reduce_scatter_kernel launch";
-  const size_t lds = residency_lds(DDPSIM_RS_WGS_PER_CU);
-  const dim3 block(kRsThreads);
-  if (dtype == DDP_F32) {
-    if (vec) {
-      return launch_lds(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, true>, grid, block, lds,
-                        stream, timer, true, kname, tin, tout, p, C, tpc32, div);
-    }
-    return launch_lds(reduce_scatter_kernel<F32Traits, kRsVpt, kRsRb, false>, grid, block, lds,
-                      stream, timer, true, kname, tin, tout, p, C, tpc32, div);
+  const RsLaunch L{dim3(static_cast<uint32_t>(blocks)), stream, &timer, tin, tout, p, C,
+                   static_cast<int32_t>(tpc), div};
+  if (narrow) {
+    return launch_rs<1, kRsNarrowThreads>(L, dtype, vec, residency_lds(DDPSIM_RS_WGS_PER_CU));
   }
-  if (vec) {
-    return launch_lds(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, true>, grid, block, lds,
-                      stream, timer, true, kname, tin, tout, p, C, tpc32, div);
-  }
-  return launch_lds(reduce_scatter_kernel<BF16Traits, kRsVpt, kRsRb, false>, grid, block, lds,
-                    stream, timer, true, kname, tin, tout, p, C, tpc32, div);
+  return launch_rs<kRsVpt, kRsThreads>(L, dtype, vec, 0);
 }
 
 extern "C" ddp_status allgather_sim(const void *const *in, void *const *out, int32_t p,

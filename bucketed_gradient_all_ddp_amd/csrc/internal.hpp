@@ -80,22 +80,6 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #ifndef DDPSIM_BUCKET_WGS_PER_CU
 #define DDPSIM_BUCKET_WGS_PER_CU 11  // workgroups resident per CU (0: no bound)
 #endif
-// The same bound for the other streaming kernels (0: none).
-#ifndef DDPSIM_FUSED_WGS_PER_CU
-#define DDPSIM_FUSED_WGS_PER_CU 0
-#endif
-#ifndef DDPSIM_RS_WGS_PER_CU
-#define DDPSIM_RS_WGS_PER_CU 0
-#endif
-#ifndef DDPSIM_COPY_WGS_PER_CU
-#define DDPSIM_COPY_WGS_PER_CU 0
-#endif
-#ifndef DDPSIM_TREE_WGS_PER_CU
-#define DDPSIM_TREE_WGS_PER_CU 0
-#endif
-#ifndef DDPSIM_BCAST_WGS_PER_CU
-#define DDPSIM_BCAST_WGS_PER_CU 0
-#endif
 constexpr int kBucketVpt = DDPSIM_BUCKET_VPT;
 constexpr int kBucketThreads = DDPSIM_BUCKET_THREADS;
 constexpr int kBucketRb = 8;

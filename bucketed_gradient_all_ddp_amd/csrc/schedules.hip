@@ -146,8 +146,15 @@ struct ElementLeaf {
 // One thread per 16-byte vector; thread nv (one past the last vector) folds
 // the fewer-than-V tail elements one by one. Ranks Q..p-1 (extra = p - Q of
 // them) are folded into ranks 0..extra-1 first.
+// One-wave workgroups, at most DDPSIM_TREE_WGS_PER_CU resident per CU
+// (Rabenseifner order, 8 ranks of 1 GiB: 5.61 -> 5.99 TB/s, 64 ranks of
+// 128 MiB: 4.71 -> 5.20, 64 ranks of 2 GiB: equal, against 256 threads and
+// full residency).
 #ifndef DDPSIM_TREE_THREADS
-#define DDPSIM_TREE_THREADS 256
+#define DDPSIM_TREE_THREADS 64
+#endif
+#ifndef DDPSIM_TREE_WGS_PER_CU
+#define DDPSIM_TREE_WGS_PER_CU 11
 #endif
 constexpr int kTreeThreads = DDPSIM_TREE_THREADS;
 
