@@ -54,8 +54,8 @@ MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
     # (all 13 buckets in one dispatch)
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7995535651,
-        "sources_sha256": "a9c5f3c68001101907e76f630cc688f627110c1bef51a57e9bf2a500772a991b",
+        "bytes_per_launch": 7995576146,
+        "sources_sha256": "15757e35291f72100803bfee926f7b699048373caccf1624d983fa7fa5590a37",
     },
 }
 
