@@ -151,3 +151,19 @@ def test_buffers_are_independent_allocations_at_offsets(oracle):
     g = big.cpu().numpy()
     for r in range(p):
         assert np.all(g[r * stride: r * stride + 4] == 0)
+
+
+@pytest.mark.parametrize("bf16,p,n", [(True, 8, 17_000_003), (False, 13, 6_000_001)])
+def test_fused_past_the_infinity_cache(oracle, bf16, p, n):
+    """Rank buffers totalling more than 256 MiB take the fused kernel's
+    streaming shape (one-wave workgroups, non-temporal accesses): every
+    element against the oracle, with a divisor that is not a power of two."""
+    host = [W.normal_np(n, 1.0, 900 + p, r) for r in range(p)]
+    if bf16:
+        host = [oracle.f32_to_bf16(h) for h in host]
+    assert p * n * (2 if bf16 else 4) > 256 << 20
+    tokens = tokens_for(p, 5)
+    got, _ = _run(host, "tokens", tokens, "fused")
+    want, _ = oracle.ring_allreduce(host, avg="tokens", tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(got[r], want[r], f"rank {r}")

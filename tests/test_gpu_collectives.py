@@ -19,7 +19,8 @@ def _vals(p, n, seed, bf16, oracle):
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("avg", ["none", "world", "tokens"])
-@pytest.mark.parametrize("p,C", [(1, 5), (2, 3), (3, 1001), (4, 4096), (8, 12_345), (8, 65_536), (64, 8), (64, 513)])
+@pytest.mark.parametrize("p,C", [(1, 5), (2, 3), (3, 1001), (4, 4096), (8, 12_345), (8, 65_536),
+                                 (16, 4099), (17, 4096), (64, 8), (64, 513)])
 def test_reduce_scatter(oracle, p, C, avg, in_place, bf16):
     n = p * C
     host = _vals(p, n, 400 + p, bf16, oracle)
