@@ -741,6 +741,7 @@ def bench_crossover(torch, ddp, W, dev, args):
             cross = float(np.exp(np.log(a) + f * (np.log(b) - np.log(a))))
             break
     pick = {m: min(scheds, key=lambda s: table[m][f"{s}_steps_us"]) for m in ms}
+    graph = _crossover_graphs(torch, ddp, arena, sizes, p, np)
     _line("ring vs recursive-doubling crossover, p=4, step-by-step schedules",
           cross if cross is not None else float("nan"), "bytes per rank",
           "crossover sweep: p=4, one fp32 tensor of 1 KB .. 64 MB per rank, average by p, "
@@ -750,7 +751,56 @@ def bench_crossover(torch, ddp, W, dev, args):
                      "predicted_crossover_bytes": round(float(mstar), 1)},
            "fastest_step_schedule": {str(m): pick[m] for m in ms},
            "the_three_sizes": {str(m): table[m] for m in (1 << 10, 1 << 20, 1 << 24)},
-           "sweep_us": {str(m): table[m] for m in ms}})
+           "sweep_us": {str(m): table[m] for m in ms},
+           "graph_replay": graph})
+
+
+def _crossover_graphs(torch, ddp, arena, sizes, p, np):
+    """The ring and recursive doubling step by step, each call captured once
+    in a HIP graph and replayed: the per-step cost without the host's launch
+    path. Fits alpha and beta to the replayed ring as above and finds where
+    the replayed schedules cross."""
+    times = {}
+    side = torch.cuda.Stream()
+    for n in sizes:
+        bufs = [a[:n] for a in arena]
+        reps = 200 if n * 4 <= (1 << 20) else (40 if n * 4 <= (1 << 24) else 10)
+        for sch in ("ring", "recursive_doubling"):
+            fn = lambda b=bufs, s=sch: ddp.allreduce_sim(b, s, True, avg="world")  # noqa: E731
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            g.replay()
+            torch.cuda.synchronize()
+            times[(n * 4, sch)] = _events_ms(torch, g.replay, reps) * 1e3
+            del g
+    ms = sorted({m for m, _ in times})
+    xs = np.array([float(m) for m in ms])
+    ts = np.array([times[(m, "ring")] * 1e-6 for m in ms])
+    A = np.stack([np.full_like(xs, 2.0 * (p - 1)), 2.0 * (p - 1) * xs / p], axis=1)
+    (alpha, beta), *_ = np.linalg.lstsq(A, ts, rcond=None)
+    lg = np.log2(p)
+    mstar = (alpha / beta) * (2 * (p - 1) - lg) / (lg - 2 * (p - 1) / p)
+    cross = None
+    for a, b in zip(ms, ms[1:]):
+        da = times[(a, "recursive_doubling")] - times[(a, "ring")]
+        db = times[(b, "recursive_doubling")] - times[(b, "ring")]
+        if da < 0 <= db:
+            f = -da / (db - da)
+            cross = float(np.exp(np.log(a) + f * (np.log(b) - np.log(a))))
+            break
+    return {"crossover_bytes": cross,
+            "model": {"alpha_us": round(alpha * 1e6, 3),
+                      "beta_ns_per_byte": round(beta * 1e9, 6),
+                      "predicted_crossover_bytes": round(float(mstar), 1)},
+            "us": {str(m): {"ring_steps_us": round(times[(m, "ring")], 2),
+                            "recursive_doubling_steps_us":
+                                round(times[(m, "recursive_doubling")], 2)} for m in ms}}
 
 
 def bench_sync(torch, ddp, W, dev, args):
