@@ -954,6 +954,18 @@ def main():
                 "bus_GBps": round(S * 2 * (p - 1) / p / (mms * 1e-3) / 1e9, 2),
                 "kernels": mk,
             }
+    # the practical roofline: the library's own copy (a broadcast between two
+    # ranks of 1 GiB reads one buffer and writes the other once)
+    cp = [torch.ones(1 << 28, device=dev), torch.empty(1 << 28, device=dev)]
+    ccall = [lambda: ddp.broadcast_sim(cp, src=0)]
+    ccall[0]()
+    _, cdms = _timed_calls(torch, ddp, ccall, 10)
+    copy_gbps = 2 * (1 << 30) / (cdms * 1e-3) / 1e9
+    result["practical_ceiling"] = {
+        "copy_GBps": round(copy_gbps, 1),
+        "kernel": "fanout_copy_kernel (broadcast_sim between 2 ranks of 1 GiB: 1 read, 1 write)",
+        "headline_frac_of_copy": round(d["GBps"] / copy_gbps, 4)}
+    del cp
     if args.calib_copy_mib:
         n = args.calib_copy_mib * 1024 * 1024 // 4
         a = torch.ones(n, device=dev)
