@@ -33,10 +33,14 @@ constexpr bool kBcastNtStore = (DDPSIM_BCAST_NT & 2) != 0;
 #ifndef DDPSIM_BCAST_THREADS
 #define DDPSIM_BCAST_THREADS 64  // threads per workgroup, one 16-byte vector each
 #endif
+#ifndef DDPSIM_BCAST_VPT
+#define DDPSIM_BCAST_VPT 1  // 16-byte vectors per lane (spans per workgroup)
+#endif
 #ifndef DDPSIM_BCAST_WGS_PER_CU
 #define DDPSIM_BCAST_WGS_PER_CU 0  // workgroups resident per CU (0: no bound)
 #endif
 constexpr int kBcastThreads = DDPSIM_BCAST_THREADS;
+constexpr int kBcastVpt = DDPSIM_BCAST_VPT;
 
 template <int EB>
 struct Unit;
@@ -60,7 +64,7 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
     const ParamDesc *__restrict__ desc, const int32_t *__restrict__ tile_map, int32_t n_params,
     const void *const *__restrict__ ptrs, int32_t p, int32_t root) {
   using U = typename Unit<EB>::type;
-  constexpr int kSpan = kBcastThreads * kVecBytes / EB;  // elements per workgroup
+  constexpr int kSpan = kBcastThreads * kBcastVpt * kVecBytes / EB;  // elements per workgroup
   constexpr int kSubs = kFlattenTile / kSpan;
   static_assert(kSubs >= 1 && kSubs * kSpan == kFlattenTile, "spans must tile a plan tile");
   const int32_t tile = static_cast<int32_t>(blockIdx.x) / kSubs;
@@ -93,14 +97,22 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
   int64_t done = 0;
   if (aligned) {
     const int64_t nv = cnt * EB / kVecBytes;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (tid < nv) x = load_vec<kBcastNtLoad>(src, tid);
+    uint4 x[kBcastVpt];
+#pragma unroll
+    for (int u = 0; u < kBcastVpt; ++u) {
+      const int64_t j = u * kBcastThreads + tid;
+      x[u] = j < nv ? load_vec<kBcastNtLoad>(src, j) : make_uint4(0, 0, 0, 0);
+    }
     const int32_t rot = store_rotation(p);
     for (int32_t k = 0; k < p; ++k) {
       const int32_t r = ring_rank(rot, k, p);
       if (r == root) continue;
       U *dst = slice(r);
-      if (tid < nv) store_vec<kBcastNtStore>(dst, tid, x);
+#pragma unroll
+      for (int u = 0; u < kBcastVpt; ++u) {
+        const int64_t j = u * kBcastThreads + tid;
+        if (j < nv) store_vec<kBcastNtStore>(dst, j, x[u]);
+      }
     }
     done = nv * kVecBytes / EB;
   }
@@ -117,7 +129,8 @@ ddp_status launch_bucket(const ParamDesc *desc, const int32_t *tile_map, int32_t
                          int32_t n_params,
                          const void *const *ptrs, int32_t p, int32_t root, hipStream_t stream,
                          CallTimer &timer, bool last) {
-  const int64_t blocks = int64_t(tiles) * (kFlattenTile * EB / (kBcastThreads * kVecBytes));
+  const int64_t blocks =
+      int64_t(tiles) * (kFlattenTile * EB / (kBcastThreads * kBcastVpt * kVecBytes));
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ddp_broadcast_coalesced: bucket too large");
   return launch_lds(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(blocks)),
                     dim3(kBcastThreads), residency_lds(DDPSIM_BCAST_WGS_PER_CU), stream, timer,
