@@ -309,8 +309,9 @@ ddp_status build_plan(const int64_t *numel, int32_t n_params, const int32_t *wal
   }
   const size_t desc_bytes = plan->desc.size() * sizeof(ParamDesc);
   plan->staged.resize(desc_bytes + tile_desc.size() * sizeof(int32_t));
-  if (!plan->staged.empty()) {
-    std::memcpy(plan->staged.data(), plan->desc.data(), desc_bytes);
+  // (zero-size parameters have descriptors but no tiles)
+  if (desc_bytes > 0) std::memcpy(plan->staged.data(), plan->desc.data(), desc_bytes);
+  if (!tile_desc.empty()) {
     std::memcpy(plan->staged.data() + desc_bytes, tile_desc.data(),
                 tile_desc.size() * sizeof(int32_t));
   }

@@ -234,11 +234,12 @@ extern "C" ddp_status ddp_overlap_step_time(const ddp_plan *plan, const double *
                                             double *exposed) {
   clear_error();
   const char *what = "ddp_overlap_step_time";
-  if (plan == nullptr || ready == nullptr || bucket_time == nullptr) {
-    return fail(DDP_EINVAL, "%s: plan, ready or bucket_time is NULL", what);
-  }
+  if (plan == nullptr) return fail(DDP_EINVAL, "%s: plan is NULL", what);
   const int32_t n_params = ddp_plan_num_params(plan);
   const int32_t n_buckets = ddp_plan_num_buckets(plan);
+  if ((n_params > 0 && ready == nullptr) || (n_buckets > 0 && bucket_time == nullptr)) {
+    return fail(DDP_EINVAL, "%s: ready or bucket_time is NULL", what);
+  }
   for (int32_t i = 0; i < n_params; ++i) {
     if (!std::isfinite(ready[i]) || ready[i] < 0.0) {
       return fail(DDP_EINVAL, "%s: ready[%d] = %g is not a finite time >= 0", what, i, ready[i]);

@@ -503,8 +503,9 @@ int32_t ddp_choose_schedule(int32_t p, int64_t bytes, double alpha,
  *                durations in seconds: ddp_schedule_time of each bucket's
  *                bytes for a network, or kernel times measured on a device
  *   step, exposed  outputs (either may be NULL)
- * Every time must be finite and >= 0. Errors: DDP_EINVAL (NULL plan or
- * array, a negative, NaN or infinite time); outputs untouched then. */
+ * Every time must be finite and >= 0; an array may be NULL when the plan
+ * has no parameters. Errors: DDP_EINVAL (NULL plan, a NULL array the plan
+ * needs, a negative, NaN or infinite time); outputs untouched then. */
 ddp_status ddp_overlap_step_time(const ddp_plan *plan, const double *ready,
                                  const double *bucket_time, double *step,
                                  double *exposed);

@@ -351,6 +351,12 @@ def test_overlap_step_time_cases_and_errors():
     assert st.value == -7.0
     with pytest.raises(ValueError):
         ddp.overlap_step_time(plan, [1.0, 2.0], [1.0, 1.0, 1.0])
+    # no parameters: the arrays may be NULL, and nothing is exposed
+    empty = ddp.ddp_bucket_plan([], 4)
+    st, ex = ctypes.c_double(-1.0), ctypes.c_double(-1.0)
+    assert L.ddp_overlap_step_time(empty.handle, None, None, ctypes.byref(st),
+                                   ctypes.byref(ex)) == 0
+    assert st.value == 0.0 and ex.value == 0.0
 
 
 @pytest.mark.parametrize("seed", range(40))
