@@ -167,8 +167,15 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
+def _device_ptr(t) -> int:
+    # the kernels dereference these addresses: host memory would fault the GPU
+    if not t.is_cuda:
+        raise TypeError("buffers must be device (cuda) tensors")
+    return t.data_ptr()
+
+
 def _ptrs(tensors: Sequence) -> ctypes.Array:
-    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return (ctypes.c_void_p * len(tensors))(*[_device_ptr(t) for t in tensors])
 
 
 def _tokens(tokens, p: int):
@@ -302,7 +309,7 @@ class Plan:
         nbytes = self.segment_bytes(p)
         self._segments = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         _check(load_library().ddp_plan_upload_segments(
-            self._h, p, self._segments.data_ptr(), nbytes, _stream(stream)),
+            self._h, p, _device_ptr(self._segments), nbytes, _stream(stream)),
             "ddp_plan_upload_segments")
         return self
 
@@ -311,7 +318,7 @@ class Plan:
 
         nbytes = self.device_bytes()
         self._table = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-        _check(load_library().ddp_plan_upload(self._h, self._table.data_ptr(), nbytes,
+        _check(load_library().ddp_plan_upload(self._h, _device_ptr(self._table), nbytes,
                                               _stream(stream)), "ddp_plan_upload")
         return self
 
@@ -360,7 +367,7 @@ def ddp_broadcast_coalesced(plan: Plan, tensor_table, p: int, root: int = 0,
     tensor_table is grad_pointer_table(tensors_per_rank)."""
     st = CommStats()
     _check(load_library().ddp_broadcast_coalesced(
-        plan.handle, p, tensor_table.data_ptr() if tensor_table is not None else None, root,
+        plan.handle, p, _device_ptr(tensor_table) if tensor_table is not None else None, root,
         _stream(stream), ctypes.byref(st)), "ddp_broadcast_coalesced")
     return st
 
@@ -402,17 +409,31 @@ def sync_module_states(params: Sequence[Sequence], buffers: Sequence[Sequence] =
 
 
 def grad_pointer_table(grads: Sequence[Sequence], device="cuda"):
-    """Device int64 tensor of p * n_params gradient addresses, rank-major."""
+    """Device int64 tensor of p * n_params gradient addresses, rank-major.
+    grads[r][i] is rank r's gradient of parameter i: contiguous device
+    tensors of one element size, and the same element count for a parameter
+    on every rank."""
     import torch
 
-    flat = [g.data_ptr() for rank in grads for g in rank]
+    if not grads:
+        raise ValueError("grad_pointer_table needs at least one rank")
+    first = grads[0]
+    for r, rank in enumerate(grads):
+        if len(rank) != len(first):
+            raise ValueError(f"rank {r} has {len(rank)} gradients, rank 0 {len(first)}")
+        for i, g in enumerate(rank):
+            if (not g.is_contiguous() or g.element_size() != first[0].element_size()
+                    or g.numel() != first[i].numel()):
+                raise ValueError(f"gradient {i} of rank {r}: contiguous tensors of one element "
+                                 "size and the same size on every rank are required")
+    flat = [_device_ptr(g) for rank in grads for g in rank]
     return torch.tensor(flat, dtype=torch.int64, device=device)
 
 
 def ddp_flatten(plan: Plan, bucket: int, grad_table, bucket_bufs: Sequence,
                 prescale_divisor: float = 1.0, stream=None) -> None:
     p = len(bucket_bufs)
-    _check(load_library().ddp_flatten(plan.handle, bucket, p, grad_table.data_ptr(),
+    _check(load_library().ddp_flatten(plan.handle, bucket, p, _device_ptr(grad_table),
                                       _ptrs(bucket_bufs), _dtype_code(bucket_bufs[0]),
                                       float(prescale_divisor), _stream(stream)),
            "ddp_flatten")
@@ -422,7 +443,7 @@ def ddp_unflatten(plan: Plan, bucket: int, bucket_bufs: Sequence, grad_table,
                   stream=None) -> None:
     p = len(bucket_bufs)
     _check(load_library().ddp_unflatten(plan.handle, bucket, p, _ptrs(bucket_bufs),
-                                        grad_table.data_ptr(), _dtype_code(bucket_bufs[0]),
+                                        _device_ptr(grad_table), _dtype_code(bucket_bufs[0]),
                                         _stream(stream)), "ddp_unflatten")
 
 
@@ -436,7 +457,7 @@ def ddp_allreduce_bucket(plan: Plan, bucket: int, grad_table, p: int, dtype=None
     code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
     st = CommStats()
     _check(load_library().ddp_allreduce_bucket(
-        plan.handle, bucket, p, grad_table.data_ptr(), code, AVG[avg], _tokens(tokens, p),
+        plan.handle, bucket, p, _device_ptr(grad_table), code, AVG[avg], _tokens(tokens, p),
         _stream(stream), ctypes.byref(st)), "ddp_allreduce_bucket")
     return st
 
@@ -451,7 +472,7 @@ def ddp_allreduce_buckets(plan: Plan, first_bucket: int, n_buckets: int, grad_ta
     code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
     st = CommStats()
     _check(load_library().ddp_allreduce_buckets(
-        plan.handle, first_bucket, n_buckets, p, grad_table.data_ptr(), code, AVG[avg],
+        plan.handle, first_bucket, n_buckets, p, _device_ptr(grad_table), code, AVG[avg],
         _tokens(tokens, p), _stream(stream), ctypes.byref(st)), "ddp_allreduce_buckets")
     return st
 
@@ -471,7 +492,7 @@ class Reducer:
         self._h = ctypes.c_void_p()
         self.comm_stream = comm_stream if comm_stream is not None else torch.cuda.current_stream()
         _check(load_library().ddp_reducer_create(
-            plan.handle, p, grad_table.data_ptr() if grad_table is not None else None, code,
+            plan.handle, p, _device_ptr(grad_table) if grad_table is not None else None, code,
             AVG[avg], _tokens(tokens, p), _stream(self.comm_stream), ctypes.byref(self._h)),
             "ddp_reducer_create")
 
@@ -530,7 +551,7 @@ def ring_allreduce_sim(bufs: Sequence, avg: str = "none", tokens=None,
     p = len(bufs)
     n = _numel_all(bufs)
     st = CommStats()
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_ptr = _device_ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().ring_allreduce_sim(
         _ptrs(bufs), p, n, _dtype_code(bufs[0]), AVG[avg], _tokens(tokens, p),
@@ -563,7 +584,7 @@ def allreduce_sim(bufs: Sequence, schedule: str = "ring", steps: bool = False,
     p = len(bufs)
     n = _numel_all(bufs)
     st = CommStats()
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_ptr = _device_ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().allreduce_sim(
         _ptrs(bufs), p, n, _dtype_code(bufs[0]), AVG[avg], _tokens(tokens, p),

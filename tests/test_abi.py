@@ -402,3 +402,29 @@ def test_coalesced_broadcast_argument_errors():
     st = ddp.CommStats()
     assert L.ddp_broadcast_coalesced(empty.handle, 3, None, 1, None, ctypes.byref(st)) == 0
     assert st.messages == 0 and st.hbm_bytes == 0
+
+
+def test_binding_rejects_host_tensors_and_ragged_tables():
+    """Addresses the kernels would dereference must be device memory: host
+    tensors are refused before anything reaches the library, and a gradient
+    table needs one element size, contiguous tensors and equal sizes across
+    ranks."""
+    import torch
+
+    host = [torch.zeros(16) for _ in range(2)]
+    with pytest.raises(TypeError, match="device"):
+        ddp.ring_allreduce_sim(host)
+    with pytest.raises(TypeError, match="device"):
+        ddp.grad_pointer_table([[host[0]], [host[1]]])
+    with pytest.raises(ValueError):
+        ddp.grad_pointer_table([[host[0]], [host[1], host[1]]])
+    with pytest.raises(ValueError):
+        ddp.grad_pointer_table([[host[0]], [torch.zeros(8)]])
+    with pytest.raises(ValueError):
+        ddp.grad_pointer_table([[host[0]], [torch.zeros(16, dtype=torch.bfloat16)]])
+    with pytest.raises(TypeError):  # same element size: only the device check is left
+        ddp.grad_pointer_table([[host[0]], [torch.zeros(16, dtype=torch.int32)]])
+    with pytest.raises(ValueError):
+        ddp.grad_pointer_table([[torch.zeros(4, 4).t()], [torch.zeros(4, 4).t()]])
+    with pytest.raises(ValueError):
+        ddp.grad_pointer_table([])
