@@ -106,7 +106,7 @@ def parse():
     ap.add_argument("--workload", default="gpt2-small-p8",
                     choices=["gpt2-small-p8", "ragged-ring-p4", "llama7b-bf16-p8",
                              "latency-p64", "cost-model-p64", "overlap-gpt2-p8",
-                             "crossover-p4", "sync-gpt2-p8"],
+                             "crossover-p4", "sync-gpt2-p8", "collectives-p8"],
                     help="the default is the headline; the others print their own "
                          "line for the record")
     ap.add_argument("--tokens", type=int, default=2048,
@@ -499,8 +499,12 @@ def _latency_cpu(W, cfg, sizes, p, k=1000):
                        f"{_host_cpu()}")}
 
 
-def bench_costmodel(torch, ddp, W, dev, args):
-    cfg = W.WORKLOADS["cost-model-p64"]
+def bench_collectives_p8(torch, ddp, W, dev, args):
+    bench_costmodel(torch, ddp, W, dev, args, "collectives-p8")
+
+
+def bench_costmodel(torch, ddp, W, dev, args, name="cost-model-p64"):
+    cfg = W.WORKLOADS[name]
     p, n = cfg["p"], cfg["n"]
     tokens = W.token_counts(p, cfg["seed"])
     bufs = [W.normal_torch(n, 1.0, cfg["seed"], r, dev) for r in range(p)]
@@ -528,18 +532,23 @@ def bench_costmodel(torch, ddp, W, dev, args):
                      "bus_GBps": round(S * busf / (dms * 1e-3) / 1e9, 1),
                      "hbm_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(hbm / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-    _line("all-reduce bus GB/s, p=64, 2 GiB fp32 per rank, token-weighted",
+    gib = n * 4 / (1 << 30)
+    what = ("cost-model shape: one 2^29-element fp32 tensor per rank (2 GiB), p=64"
+            if name == "cost-model-p64" else
+            f"flat collectives: one 2^{n.bit_length() - 1}-element fp32 tensor per rank "
+            f"({gib:g} GiB), p={p}")
+    _line(f"all-reduce bus GB/s, p={p}, {gib:g} GiB fp32 per rank, token-weighted",
           res["allreduce_tokens"]["bus_GBps"], "GB/s",
-          "cost-model shape: one 2^29-element fp32 tensor per rank (2 GiB), p=64, tokens "
-          "U{10..10000}; plus reduce-scatter, in-place all-gather, broadcast, and the "
-          "all-reduce under recursive doubling, Rabenseifner and the tree (fused)",
+          what + ", tokens U{10..10000}; plus reduce-scatter, in-place all-gather, "
+          "broadcast, and the all-reduce under recursive doubling, Rabenseifner and the "
+          "tree (fused)",
           {"ops": res, **({} if args.no_cpu_baseline else {"cpu_baseline": _costmodel_cpu(
               W, cfg, p, tokens)})})
 
 
 def _costmodel_cpu(W, cfg, p, tokens, window=1 << 21):
-    """Oracle on one window of 2^21 elements (8 MiB) of every rank's 2 GiB
-    tensor, token-weighted: the full tensors do not fit a host."""
+    """Oracle on one window of 2^21 elements (8 MiB) of every rank's tensor,
+    token-weighted: the full tensors do not fit a host comfortably."""
     bufs = [W.normal_np(window, 1.0, cfg["seed"], r) for r in range(p)]
     dt, text = cpu_oracle_ring(bufs, "tokens", tokens,
                                f"one 8 MiB window of each rank's tensor (p={p})")
@@ -874,6 +883,7 @@ def main():
     ddp.load_library()
     other = {"ragged-ring-p4": bench_ragged, "llama7b-bf16-p8": bench_llama,
              "latency-p64": bench_latency, "cost-model-p64": bench_costmodel,
+             "collectives-p8": bench_collectives_p8,
              "overlap-gpt2-p8": bench_overlap, "crossover-p4": bench_crossover,
              "sync-gpt2-p8": bench_sync}
     if args.workload in other:

@@ -164,4 +164,8 @@ WORKLOADS = {
                         sizes=latency_regime_sizes(), avg="world"),
     "cost-model-p64": dict(p=64, n=1 << 29, sigma=1.0, seed=5, dtype="f32",
                            avg="tokens"),
+    # the same operations on 8 ranks of 1 GiB (the headline's rank count with
+    # flat buffers well past the Infinity Cache)
+    "collectives-p8": dict(p=8, n=1 << 28, sigma=1.0, seed=6, dtype="f32",
+                           avg="tokens"),
 }
