@@ -145,3 +145,20 @@ def test_per_tensor_mode_in_one_launch(oracle, p, layout):
                                         want_log=False)
         for r in range(p):
             assert_bits_equal(to_host(grads[r][i]), want[r], f"rank {r} tensor {i}")
+
+
+def test_plan_of_zero_size_parameters_launches_nothing():
+    """A plan whose parameters all have zero elements has buckets but no
+    pieces and no tiles: the in-place all-reduce, flatten and unflatten return
+    without a launch and report no traffic."""
+    p, sizes = 4, [0, 0, 0]
+    plan = ddp.ddp_bucket_plan(sizes, 4, 1024, 256).upload().upload_segments(p)
+    assert plan.num_buckets == 1 and plan.bucket_numel(0) == 0
+    grads = [[torch.empty(0, device="cuda") for _ in sizes] for _ in range(p)]
+    table = ddp.grad_pointer_table(grads)
+    st = ddp.ddp_allreduce_buckets(plan, 0, 1, table, p, avg="world")
+    assert st.hbm_bytes == 0 and st.bytes_sent_per_rank == 0
+    flats = [torch.empty(0, device="cuda") for _ in range(p)]
+    ddp.ddp_flatten(plan, 0, table, flats)
+    ddp.ddp_unflatten(plan, 0, flats, table)
+    torch.cuda.synchronize()
