@@ -54,8 +54,8 @@ MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
     # (all 13 buckets in one dispatch)
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7995576146,
-        "sources_sha256": "15757e35291f72100803bfee926f7b699048373caccf1624d983fa7fa5590a37",
+        "bytes_per_launch": 7995560127,
+        "sources_sha256": "3f433f4134fd9cfeedca0660a1bbad7e15d2f6c17e232d42c7342905305281d7",
     },
 }
 

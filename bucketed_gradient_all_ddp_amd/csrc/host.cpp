@@ -182,7 +182,8 @@ RankTable make_table(const void *const *bufs, int32_t p) {
 size_t residency_lds(int32_t wgs) {
   if (wgs <= 0) return 0;
   constexpr int kMaxDevices = 64;
-  static int32_t per_cu_of[kMaxDevices];  // by device; 0 = not asked yet
+  // by device: LDS per CU and the most one workgroup may take (0 = not asked)
+  static int32_t per_cu_of[kMaxDevices], per_wg_of[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
@@ -190,16 +191,24 @@ size_t residency_lds(int32_t wgs) {
   }
   const bool cached = dev >= 0 && dev < kMaxDevices;
   int per_cu = cached ? __atomic_load_n(&per_cu_of[dev], __ATOMIC_RELAXED) : 0;
-  if (per_cu == 0) {
+  int per_wg = cached ? __atomic_load_n(&per_wg_of[dev], __ATOMIC_RELAXED) : 0;
+  if (per_cu == 0 || per_wg == 0) {
     if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
                               dev) != hipSuccess ||
-        per_cu <= 0) {
+        hipDeviceGetAttribute(&per_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        per_cu <= 0 || per_wg <= 0) {
       (void)hipGetLastError();
       return 0;
     }
-    if (cached) __atomic_store_n(&per_cu_of[dev], per_cu, __ATOMIC_RELAXED);
+    if (cached) {
+      __atomic_store_n(&per_wg_of[dev], per_wg, __ATOMIC_RELAXED);
+      __atomic_store_n(&per_cu_of[dev], per_cu, __ATOMIC_RELAXED);
+    }
   }
-  return static_cast<size_t>(per_cu / wgs) / 512 * 512;
+  // a bound below LDS-per-CU / max-per-workgroup cannot be reached this way
+  const size_t bytes = static_cast<size_t>(per_cu / wgs) / 512 * 512;
+  return bytes <= static_cast<size_t>(per_wg) ? bytes : static_cast<size_t>(per_wg) / 512 * 512;
 }
 
 }  // namespace ddpsim

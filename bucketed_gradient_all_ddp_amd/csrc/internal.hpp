@@ -122,9 +122,9 @@ RankTable make_table(const void *const *bufs, int32_t p);
 // Dynamic LDS per workgroup that leaves room for only `wgs` workgroups on
 // one compute unit (0 for wgs <= 0, or when the device cannot be asked):
 // the device's LDS per CU divided by wgs, in the 512-byte allocation
-// granule. Kernels launched with it never touch it; it only bounds how many
-// of their workgroups share a CU, so that fewer streams compete for each
-// memory channel's open rows.
+// granule, at most what one workgroup may take. Kernels launched with it
+// never touch it; it only bounds how many of their workgroups share a CU,
+// so that fewer streams compete for each memory channel's open rows.
 size_t residency_lds(int32_t wgs);
 
 // ddp_allreduce_buckets with an optional cap on its workgroups (0: one per
