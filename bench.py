@@ -47,8 +47,11 @@ METRIC = "all-reduce bus GB/s + % HBM peak, p=8 sim ranks, 124M fp32 grads"
 # the counters are taken again.
 CSRC = os.path.join(ROOT, "bucketed_gradient_all_ddp_amd", "csrc")
 KERNEL_SOURCES = {
-    "bucket_allreduce_kernel": ["bucket_allreduce.hip", "fold.hpp", "internal.hpp"],
-    "fused_allreduce_kernel": ["allreduce.hip", "fold.hpp", "internal.hpp"],
+    # the kernel, the headers it includes, and the host code that shapes its
+    # launch (residency bound) and builds the piece table and tile map it reads
+    "bucket_allreduce_kernel": ["bucket_allreduce.hip", "fold.hpp", "internal.hpp",
+                                "host.cpp", "plan.cpp"],
+    "fused_allreduce_kernel": ["allreduce.hip", "fold.hpp", "internal.hpp", "host.cpp"],
 }
 MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
@@ -141,7 +144,9 @@ class Workload:
             W.normal_torch(off, cfg["sigma"], cfg["seed"], r, dev, out=a)
             self.arenas.append(a)
             grads.append([a[o:o + n] for o, n in zip(offs, sizes)])
+        self.offs = offs
         self.grads = grads
+        self.host_arenas = None
         self.table = ddp.grad_pointer_table(grads, dev)
         self.buckets = None
 
@@ -224,6 +229,30 @@ def _host_cpu() -> str:
     return cpu
 
 
+def cpu_record(value, unit, sample, seconds=None):
+    """A cpu_baseline object: the oracle runs on one thread ("cores"); the
+    host's core count and model are stated beside it."""
+    rec = {"value": value, "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
+           "host_cores": os.cpu_count(), "host_cpu": _host_cpu()}
+    try:
+        rec["host_cores_usable"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    if seconds is not None:
+        rec["seconds"] = round(seconds, 3)
+    return rec
+
+
+def host_copy(t):
+    """A device tensor's values on the host (bf16 as uint16 bit patterns),
+    for the oracle."""
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view("uint16")
+    return t.cpu().numpy()
+
+
 def cpu_oracle_ring(bufs, avg="world", tokens=None, what=""):
     """The oracle's literal ring all-reduce on host arrays, one thread: the
     CPU-baseline leg of the non-headline workloads. Returns (seconds, the
@@ -238,17 +267,14 @@ def cpu_oracle_ring(bufs, avg="world", tokens=None, what=""):
 
 def cpu_baseline(W, wl, n_buckets_wanted):
     """The oracle (single thread): flatten, literal ring all-reduce averaged
-    by p, unflatten, over the first buckets of the same plan."""
+    by p, unflatten, over the first buckets of the same plan, on the values
+    the GPU started from (read back before any kernel ran)."""
     import oracle
 
-    cfg, p, sizes = wl.cfg, wl.p, wl.sizes
+    p, sizes = wl.p, wl.sizes
     oplan = oracle.bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
     nb = n_buckets_wanted or oplan.num_buckets
-    params = [i for b in range(nb) for i in oplan.bucket_params(b)]
-    host = [[None] * len(sizes) for _ in range(p)]
-    for r in range(p):
-        for i in params:
-            host[r][i] = W.normal_np(sizes[i], cfg["sigma"], cfg["seed"], r, stream=i)
+    host = [[a[o:o + n] for o, n in zip(wl.offs, sizes)] for a in wl.host_arenas]
     elems = sum(oplan.bucket_numel(b) for b in range(nb))
     t0 = time.perf_counter()
     for b in range(nb):
@@ -258,15 +284,11 @@ def cpu_baseline(W, wl, n_buckets_wanted):
             oracle.unflatten(red[r], oplan, b, host[r])
     dt = time.perf_counter() - t0
     S = elems * 4
-    cpu = _host_cpu()
-    return {
-        "value": round(S * 2 * (p - 1) / p / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{nb} of {oplan.num_buckets} buckets ({elems} fp32 elements per rank, "
-                   f"p={p}, numpy-drawn N(0,1e-3)): flatten + literal ring all-reduce "
-                   f"(avg by p) + unflatten, one thread, {dt:.2f} s on {cpu}"),
-        "seconds": round(dt, 3),
-    }
+    return cpu_record(
+        round(S * 2 * (p - 1) / p / dt / 1e9, 4), "GB/s",
+        f"{nb} of {oplan.num_buckets} buckets ({elems} fp32 elements per rank, p={p}, the "
+        f"GPU's own input values read back before its first kernel): flatten + literal ring "
+        f"all-reduce (avg by p) + unflatten, one thread, {dt:.2f} s", dt)
 
 
 # ---------------------------------------------------------------------------
@@ -312,6 +334,7 @@ def bench_ragged(torch, ddp, W, dev, args):
     cfg = W.WORKLOADS["ragged-ring-p4"]
     p, n = cfg["p"], cfg["n"]
     bufs = [W.normal_torch(n, 1.0, cfg["seed"], r, dev) for r in range(p)]
+    host = [host_copy(b) for b in bufs]
     out = {}
     for algo in ("fused", "ring"):
         for _ in range(args.warmup):
@@ -326,10 +349,10 @@ def bench_ragged(torch, ddp, W, dev, args):
                      "launches": 1 if algo == "fused" else 2 * (p - 1)}
     extra = {"algorithms": out}
     if not args.no_cpu_baseline:
-        host = [W.normal_np(n, 1.0, cfg["seed"], r) for r in range(p)]
-        dt, text = cpu_oracle_ring(host, "world", None, f"the whole workload (p={p}, n={n})")
-        extra["cpu_baseline"] = {"value": round(n * 4 * 2 * (p - 1) / p / dt / 1e9, 4),
-                                 "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": text}
+        dt, text = cpu_oracle_ring(host, "world", None,
+                                   f"the whole workload (p={p}, n={n}, the GPU's input values)")
+        extra["cpu_baseline"] = cpu_record(round(n * 4 * 2 * (p - 1) / p / dt / 1e9, 4),
+                                           "GB/s", text, dt)
     _line("all-reduce bus GB/s, p=4, 1,000,003 fp32 per rank", out["fused"]["bus_GBps"], "GB/s",
           "ragged ring: one 1,000,003-element fp32 tensor per rank, p=4, average by p", extra)
 
@@ -354,6 +377,10 @@ def bench_llama(torch, ddp, W, dev, args):
         arenas.append(a)
     grads = [[a[o:o + n] for o, n in zip(offs, sizes)] for a in arenas]
     table = ddp.grad_pointer_table(grads, dev)
+    # the oracle's sample: bucket 1's gradients as the GPU starts from them
+    cpu_in = None
+    if not args.no_cpu_baseline:
+        cpu_in = [{i: host_copy(grads[r][i]) for i in plan.bucket_params(1)} for r in range(p)]
     calls = [lambda b=b: ddp.ddp_allreduce_bucket(plan, b, table, p, avg="world")
              for b in range(plan.num_buckets)]
     for _ in range(max(1, args.warmup // 2)):
@@ -381,28 +408,31 @@ def bench_llama(torch, ddp, W, dev, args):
                "kernel_GBps": round(hbm / (bdms * 1e-3) / 1e9, 1),
                "kernel_frac_of_8TBps": round(hbm / (bdms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
            "dtype": "bf16 (fp32 accumulate)", "steps": reps,
-           **({} if args.no_cpu_baseline else {"cpu_baseline": _llama_cpu(W, cfg, sizes, p)})})
+           **({} if args.no_cpu_baseline else {"cpu_baseline": _llama_cpu(W, sizes, p, cpu_in)})})
 
 
-def _llama_cpu(W, cfg, sizes, p):
-    """Oracle on a streamed sample of the Llama-7B buckets (the whole set
-    does not fit a host comfortably): bucket 1 of the plan (one 4096 x 11008
-    tensor), drawn in fp32 and rounded to bf16 like the device inputs."""
+def _llama_cpu(W, sizes, p, cpu_in):
+    """Oracle on a sample of the Llama-7B buckets (the whole set does not fit
+    a host comfortably): bucket 1 of the plan (one 4096 x 11008 tensor), on
+    the GPU's own bf16 input values: flatten, ring all-reduce in fp32,
+    unflatten."""
     import oracle
 
     oplan = oracle.bucket_plan(sizes, 2, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
-    total, elems = 0.0, 0
-    for b in (1,):
-        n = oplan.bucket_numel(b)
-        flats = [oracle.f32_to_bf16(W.normal_np(n, cfg["sigma"], cfg["seed"], r, stream=b))
-                 for r in range(p)]
-        dt, _ = cpu_oracle_ring(flats, "world")
-        total += dt
-        elems += n
-    return {"value": round(elems * 2 * 2 * (p - 1) / p / total / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": (f"bucket 1 of 226 ({elems} bf16 elements per rank, p={p}): literal "
-                       f"ring all-reduce in fp32, one thread, {total:.2f} s on {_host_cpu()}")}
+    b = 1
+    n = oplan.bucket_numel(b)
+    host = [[cpu_in[r].get(i) for i in range(len(sizes))] for r in range(p)]
+    t0 = time.perf_counter()
+    flats = [oracle.flatten(host[r], oplan, b) for r in range(p)]
+    red, _ = oracle.ring_allreduce(flats, avg="world", want_log=False)
+    for r in range(p):
+        oracle.unflatten(red[r], oplan, b, host[r])
+    dt = time.perf_counter() - t0
+    return cpu_record(
+        round(n * 2 * 2 * (p - 1) / p / dt / 1e9, 4), "GB/s",
+        f"bucket 1 of {oplan.num_buckets} ({n} bf16 elements per rank, p={p}, the GPU's own "
+        f"input values): flatten + literal ring all-reduce in fp32 + unflatten, one thread, "
+        f"{dt:.2f} s", dt)
 
 
 def bench_latency(torch, ddp, W, dev, args):
@@ -417,6 +447,9 @@ def bench_latency(torch, ddp, W, dev, args):
     per_tensor = [[grads[r][i] for r in range(p)] for i in range(len(sizes))]
     S = sum(sizes) * 4
     hbm = 2 * p * S
+    # the oracle's sample: the first tensors as the GPU starts from them
+    cpu_in = None if args.no_cpu_baseline else [
+        [host_copy(t) for t in per_tensor[i]] for i in range(min(1000, len(sizes)))]
 
     def tensor_step():
         for bufs in per_tensor:
@@ -480,23 +513,23 @@ def bench_latency(torch, ddp, W, dev, args):
                         "one_launch_for_all_buckets": {
                             "ms_per_step": round(owall, 3), "kernel_ms_per_step": round(odms, 3),
                             "kernel_GBps": round(hbm / (odms * 1e-3) / 1e9, 1)}},
-           **({} if args.no_cpu_baseline else {"cpu_baseline": _latency_cpu(W, cfg, sizes, p)})})
+           **({} if args.no_cpu_baseline else {"cpu_baseline": _latency_cpu(sizes, p, cpu_in)})})
 
 
-def _latency_cpu(W, cfg, sizes, p, k=1000):
-    """Oracle on the first k of the 20,000 tensors, one ring all-reduce per
-    tensor (the per-tensor mode's arithmetic)."""
+def _latency_cpu(sizes, p, cpu_in):
+    """Oracle on the first of the 20,000 tensors (the GPU's own input
+    values), one ring all-reduce per tensor (the per-tensor mode's
+    arithmetic)."""
     total, elems = 0.0, 0
-    for i, n in enumerate(sizes[:k]):
-        bufs = [W.normal_np(n, 1.0, cfg["seed"] + i, r) for r in range(p)]
+    for bufs in cpu_in:
         dt, _ = cpu_oracle_ring(bufs, "world")
         total += dt
-        elems += n
-    return {"value": round(elems * 4 * 2 * (p - 1) / p / total / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": (f"the first {k} of {len(sizes)} tensors ({elems} fp32 elements per rank, "
-                       f"p={p}), one literal ring all-reduce each, one thread, {total:.2f} s on "
-                       f"{_host_cpu()}")}
+        elems += bufs[0].size
+    return cpu_record(
+        round(elems * 4 * 2 * (p - 1) / p / total / 1e9, 4), "GB/s",
+        f"the first {len(cpu_in)} of {len(sizes)} tensors ({elems} fp32 elements per rank, "
+        f"p={p}, the GPU's own input values), one literal ring all-reduce each, one thread, "
+        f"{total:.2f} s", total)
 
 
 def bench_collectives_p8(torch, ddp, W, dev, args):
@@ -508,6 +541,8 @@ def bench_costmodel(torch, ddp, W, dev, args, name="cost-model-p64"):
     p, n = cfg["p"], cfg["n"]
     tokens = W.token_counts(p, cfg["seed"])
     bufs = [W.normal_torch(n, 1.0, cfg["seed"], r, dev) for r in range(p)]
+    # the oracle's sample: one 8 MiB window of every rank, as the GPU starts
+    cpu_in = None if args.no_cpu_baseline else [host_copy(b[:1 << 21]) for b in bufs]
     S = n * 4
     C = n // p
     outs = [torch.empty(C, device=dev) for _ in range(p)]
@@ -543,17 +578,18 @@ def bench_costmodel(torch, ddp, W, dev, args, name="cost-model-p64"):
           "broadcast, and the all-reduce under recursive doubling, Rabenseifner and the "
           "tree (fused)",
           {"ops": res, **({} if args.no_cpu_baseline else {"cpu_baseline": _costmodel_cpu(
-              W, cfg, p, tokens)})})
+              p, tokens, cpu_in)})})
 
 
-def _costmodel_cpu(W, cfg, p, tokens, window=1 << 21):
-    """Oracle on one window of 2^21 elements (8 MiB) of every rank's tensor,
-    token-weighted: the full tensors do not fit a host comfortably."""
-    bufs = [W.normal_np(window, 1.0, cfg["seed"], r) for r in range(p)]
-    dt, text = cpu_oracle_ring(bufs, "tokens", tokens,
-                               f"one 8 MiB window of each rank's tensor (p={p})")
-    return {"value": round(window * 4 * 2 * (p - 1) / p / dt / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle", "sample": text}
+def _costmodel_cpu(p, tokens, cpu_in):
+    """Oracle on the first window of 2^21 elements (8 MiB) of every rank's
+    tensor (the GPU's own input values), token-weighted: the full tensors do
+    not fit a host comfortably."""
+    window = cpu_in[0].size
+    dt, text = cpu_oracle_ring(cpu_in, "tokens", tokens,
+                               f"the first 8 MiB window of each rank's tensor (p={p}, the "
+                               f"GPU's own input values)")
+    return cpu_record(round(window * 4 * 2 * (p - 1) / p / dt / 1e9, 4), "GB/s", text, dt)
 
 
 def bench_overlap(torch, ddp, W, dev, args):
@@ -893,6 +929,9 @@ def main():
     log("building workload")
     wl = Workload(torch, ddp, W, dev)
     p, S = wl.p, wl.S
+    if not args.no_cpu_baseline:
+        # the oracle's inputs: the values the GPU starts from
+        wl.host_arenas = [host_copy(a) for a in wl.arenas]
     ws = {}
     modes = [args.mode] + ([] if args.no_compare else
                            [m for m in ("batched", "inplace", "copy") if m != args.mode])
@@ -942,6 +981,9 @@ def main():
                 "copy": f"ddp_flatten + ring_allreduce_sim({args.algo}) + ddp_unflatten "
                         "per bucket"}[args.mode],
             "p": p, "buckets": wl.plan.num_buckets, "bytes_per_rank": S,
+            # where each rank's arena starts, modulo 2 MiB (the layout the
+            # kernel's speed was compared across)
+            "arena_base_mod_2MiB": [a.data_ptr() % (2 << 20) for a in wl.arenas],
         },
         "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels": kernels,

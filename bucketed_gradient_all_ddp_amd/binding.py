@@ -32,7 +32,8 @@ EXPORTS = [
     "ddp_strerror", "ddp_last_error", "ddp_version", "ddp_time_next_call",
     "ddp_bucket_plan", "ddp_plan_free", "ddp_plan_num_params", "ddp_plan_num_buckets",
     "ddp_plan_bucket_numel", "ddp_plan_bucket_size", "ddp_plan_bucket_params",
-    "ddp_plan_param_bucket", "ddp_plan_param_offset", "ddp_plan_device_bytes",
+    "ddp_plan_param_bucket", "ddp_plan_param_offset", "ddp_plan_param_numel",
+    "ddp_plan_elem_bytes", "ddp_plan_device_bytes",
     "ddp_plan_upload", "ddp_flatten", "ddp_unflatten",
     "ddp_plan_segment_bytes", "ddp_plan_upload_segments", "ddp_allreduce_bucket",
     "ddp_allreduce_buckets",
@@ -102,6 +103,8 @@ def load_library(path: str = LIB_PATH):
         "ddp_plan_bucket_params": ([vp, i32, vp], st),
         "ddp_plan_param_bucket": ([vp, i32], i32),
         "ddp_plan_param_offset": ([vp, i32], i64),
+        "ddp_plan_param_numel": ([vp, i32], i64),
+        "ddp_plan_elem_bytes": ([vp], i32),
         "ddp_plan_device_bytes": ([vp], sz),
         "ddp_plan_upload": ([vp, vp, sz, vp], st),
         "ddp_flatten": ([vp, i32, i32, vp, vp, i32, f32, vp], st),
@@ -257,6 +260,8 @@ class Plan:
         self._h = ctypes.c_void_p(handle)
         self.elem_bytes = elem_bytes
         self._table = None
+        self._segments = None
+        self._numels = None
 
     def __del__(self):
         if getattr(self, "_h", None) and self._h.value and _lib is not None:
@@ -296,30 +301,54 @@ class Plan:
     def param_offset(self, i: int) -> int:
         return load_library().ddp_plan_param_offset(self._h, i)
 
+    def param_numels(self) -> Tuple[int, ...]:
+        """Element count of every parameter, in registration order."""
+        if self._numels is None:
+            L = load_library()
+            self._numels = tuple(L.ddp_plan_param_numel(self._h, i)
+                                 for i in range(self.num_params))
+        return self._numels
+
     def device_bytes(self) -> int:
         return load_library().ddp_plan_device_bytes(self._h)
 
     def segment_bytes(self, p: int) -> int:
         return load_library().ddp_plan_segment_bytes(self._h, p)
 
+    # A re-upload replaces a device table that kernels already enqueued may
+    # still read, possibly on other streams (the reducer's communication
+    # stream): the old table is released only after the device has drained.
+    # The new table is kept only once the library has accepted it, so a
+    # refused upload leaves the plan's previous table in place and alive.
+    @staticmethod
+    def _retire(old) -> None:
+        if old is not None:
+            import torch
+
+            torch.cuda.synchronize(old.device)
+
     def upload_segments(self, p: int, device="cuda", stream=None) -> "Plan":
         """Upload the piece table ddp_allreduce_bucket needs for p ranks."""
         import torch
 
         nbytes = self.segment_bytes(p)
-        self._segments = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        fresh = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         _check(load_library().ddp_plan_upload_segments(
-            self._h, p, _device_ptr(self._segments), nbytes, _stream(stream)),
+            self._h, p, _device_ptr(fresh), nbytes, _stream(stream)),
             "ddp_plan_upload_segments")
+        self._retire(self._segments)
+        self._segments = fresh
         return self
 
     def upload(self, device="cuda", stream=None) -> "Plan":
         import torch
 
         nbytes = self.device_bytes()
-        self._table = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-        _check(load_library().ddp_plan_upload(self._h, _device_ptr(self._table), nbytes,
+        fresh = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _check(load_library().ddp_plan_upload(self._h, _device_ptr(fresh), nbytes,
                                               _stream(stream)), "ddp_plan_upload")
+        self._retire(self._table)
+        self._table = fresh
         return self
 
 
@@ -365,6 +394,7 @@ def ddp_broadcast_coalesced(plan: Plan, tensor_table, p: int, root: int = 0,
                             stream=None) -> CommStats:
     """Broadcast every tensor of an uploaded coalesce plan from `root`;
     tensor_table is grad_pointer_table(tensors_per_rank)."""
+    _check_grad_table(tensor_table, plan, p, "ddp_broadcast_coalesced")
     st = CommStats()
     _check(load_library().ddp_broadcast_coalesced(
         plan.handle, p, _device_ptr(tensor_table) if tensor_table is not None else None, root,
@@ -427,12 +457,87 @@ def grad_pointer_table(grads: Sequence[Sequence], device="cuda"):
                 raise ValueError(f"gradient {i} of rank {r}: contiguous tensors of one element "
                                  "size and the same size on every rank are required")
     flat = [_device_ptr(g) for rank in grads for g in rank]
-    return torch.tensor(flat, dtype=torch.int64, device=device)
+    _reject_overlaps(grads, flat)
+    table = torch.tensor(flat, dtype=torch.int64, device=device)
+    # what the table was built from, checked against the plan and the rank
+    # count of every call that takes it (the kernels trust the addresses)
+    table._ddp_ranks = len(grads)
+    table._ddp_numel = tuple(g.numel() for g in first)
+    table._ddp_elem_bytes = first[0].element_size() if first else 0
+    return table
+
+
+def _reject_overlaps(grads: Sequence[Sequence], addrs: Sequence[int]) -> None:
+    """Every gradient of every rank must own its bytes: the kernels write each
+    one, and two that share memory would race."""
+    import numpy as np
+
+    if not addrs:
+        return
+    nbytes = np.array([g.numel() * g.element_size() for rank in grads for g in rank],
+                      dtype=np.int64)
+    start = np.array(addrs, dtype=np.int64)
+    live = np.nonzero(nbytes > 0)[0]
+    if live.size < 2:
+        return
+    order = live[np.argsort(start[live], kind="stable")]
+    ends = start[order] + nbytes[order]
+    clash = np.nonzero(start[order][1:] < ends[:-1])[0]
+    if clash.size:
+        n_params = len(grads[0])
+        a, b = (int(order[clash[0]]), int(order[clash[0] + 1]))
+        raise ValueError(f"gradient {a % n_params} of rank {a // n_params} and gradient "
+                         f"{b % n_params} of rank {b // n_params} share memory")
+
+
+def _check_grad_table(table, plan: "Plan", p: int, what: str) -> None:
+    """The table must have been built by grad_pointer_table for p ranks of
+    tensors shaped as the plan's parameters: the kernels read p * n_params
+    addresses from it and write every element of every one."""
+    import torch
+
+    if table is None:
+        return  # the library refuses a NULL table wherever it would be read
+    if not isinstance(table, torch.Tensor) or getattr(table, "_ddp_numel", None) is None:
+        raise TypeError(f"{what}: build the gradient table with grad_pointer_table")
+    if table.dtype != torch.int64 or not table.is_contiguous():
+        raise TypeError(f"{what}: the gradient table must be a contiguous int64 tensor")
+    if table._ddp_ranks != p or table.numel() != p * plan.num_params:
+        raise ValueError(f"{what}: the gradient table holds {table._ddp_ranks} ranks of "
+                         f"{len(table._ddp_numel)} tensors; the call needs {p} ranks of "
+                         f"{plan.num_params}")
+    if table._ddp_elem_bytes != plan.elem_bytes and plan.num_params > 0:
+        raise ValueError(f"{what}: the gradients have {table._ddp_elem_bytes}-byte elements, "
+                         f"the plan {plan.elem_bytes}")
+    want = plan.param_numels()
+    if table._ddp_numel != want:
+        i = next(k for k, (a, b) in enumerate(zip(table._ddp_numel, want)) if a != b)
+        raise ValueError(f"{what}: tensor {i} has {table._ddp_numel[i]} elements, the plan "
+                         f"{want[i]}")
+    _device_ptr(table)
+
+
+def _check_bucket_bufs(plan: "Plan", bucket: int, bufs: Sequence, what: str) -> None:
+    """Flat bucket buffers: one per rank, each exactly the bucket's elements,
+    contiguous, of the plan's element size."""
+    if not bufs:
+        raise ValueError(f"{what}: needs one bucket buffer per rank")
+    n = plan.bucket_numel(bucket)
+    if n < 0:
+        return  # bucket out of range: the library reports it
+    for r, t in enumerate(bufs):
+        if (t.numel() != n or t.dtype != bufs[0].dtype or not t.is_contiguous()
+                or t.element_size() != plan.elem_bytes):
+            raise ValueError(f"{what}: bucket buffer of rank {r} must be a contiguous tensor of "
+                             f"{n} elements of {plan.elem_bytes} bytes (got {t.numel()} of "
+                             f"{t.element_size()})")
 
 
 def ddp_flatten(plan: Plan, bucket: int, grad_table, bucket_bufs: Sequence,
                 prescale_divisor: float = 1.0, stream=None) -> None:
     p = len(bucket_bufs)
+    _check_bucket_bufs(plan, bucket, bucket_bufs, "ddp_flatten")
+    _check_grad_table(grad_table, plan, p, "ddp_flatten")
     _check(load_library().ddp_flatten(plan.handle, bucket, p, _device_ptr(grad_table),
                                       _ptrs(bucket_bufs), _dtype_code(bucket_bufs[0]),
                                       float(prescale_divisor), _stream(stream)),
@@ -442,6 +547,8 @@ def ddp_flatten(plan: Plan, bucket: int, grad_table, bucket_bufs: Sequence,
 def ddp_unflatten(plan: Plan, bucket: int, bucket_bufs: Sequence, grad_table,
                   stream=None) -> None:
     p = len(bucket_bufs)
+    _check_bucket_bufs(plan, bucket, bucket_bufs, "ddp_unflatten")
+    _check_grad_table(grad_table, plan, p, "ddp_unflatten")
     _check(load_library().ddp_unflatten(plan.handle, bucket, p, _ptrs(bucket_bufs),
                                         _device_ptr(grad_table), _dtype_code(bucket_bufs[0]),
                                         _stream(stream)), "ddp_unflatten")
@@ -455,6 +562,7 @@ def ddp_allreduce_bucket(plan: Plan, bucket: int, grad_table, p: int, dtype=None
     if dtype is None:
         dtype = torch.float32 if plan.elem_bytes == 4 else torch.bfloat16
     code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
+    _check_grad_table(grad_table, plan, p, "ddp_allreduce_bucket")
     st = CommStats()
     _check(load_library().ddp_allreduce_bucket(
         plan.handle, bucket, p, _device_ptr(grad_table), code, AVG[avg], _tokens(tokens, p),
@@ -470,6 +578,7 @@ def ddp_allreduce_buckets(plan: Plan, first_bucket: int, n_buckets: int, grad_ta
     if dtype is None:
         dtype = torch.float32 if plan.elem_bytes == 4 else torch.bfloat16
     code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
+    _check_grad_table(grad_table, plan, p, "ddp_allreduce_buckets")
     st = CommStats()
     _check(load_library().ddp_allreduce_buckets(
         plan.handle, first_bucket, n_buckets, p, _device_ptr(grad_table), code, AVG[avg],
@@ -488,6 +597,7 @@ class Reducer:
         if dtype is None:
             dtype = torch.float32 if plan.elem_bytes == 4 else torch.bfloat16
         code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
+        _check_grad_table(grad_table, plan, p, "Reducer")
         self._plan, self._table = plan, grad_table  # kept alive
         self._h = ctypes.c_void_p()
         self.comm_stream = comm_stream if comm_stream is not None else torch.cuda.current_stream()

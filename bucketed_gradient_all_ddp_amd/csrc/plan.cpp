@@ -407,6 +407,15 @@ extern "C" int64_t ddp_plan_param_offset(const ddp_plan *plan, int32_t i) {
   return plan->offset[i];
 }
 
+extern "C" int64_t ddp_plan_param_numel(const ddp_plan *plan, int32_t i) {
+  if (plan == nullptr || i < 0 || i >= plan->n_params) return -1;
+  return plan->numel[i];
+}
+
+extern "C" int32_t ddp_plan_elem_bytes(const ddp_plan *plan) {
+  return plan ? plan->elem_bytes : -1;
+}
+
 extern "C" size_t ddp_plan_device_bytes(const ddp_plan *plan) {
   return plan ? plan->staged.size() : 0;
 }

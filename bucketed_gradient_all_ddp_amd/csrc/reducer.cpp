@@ -19,6 +19,7 @@
 // before the next forward).
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -54,6 +55,11 @@ struct ddp_reducer {
   std::vector<int32_t> log_mark, log_first, log_count;
   std::vector<int32_t> ready_order;  // parameters in the order marked, this pass
   hipEvent_t done = nullptr;
+  // A launch that failed during this pass: every later call of the pass
+  // (marks and finalize) reports it, so the cause is not hidden behind
+  // buckets that then look as if they never became ready.
+  ddp_status failed = DDP_OK;
+  char failed_detail[512] = "";
 };
 
 extern "C" ddp_status ddp_reducer_create(const ddp_plan *plan, int32_t p,
@@ -79,6 +85,9 @@ extern "C" ddp_status ddp_reducer_create(const ddp_plan *plan, int32_t p,
   if (eb == 0) return fail(DDP_EINVAL, "%s: unknown dtype %d", what, dtype);
   if (n_buckets > 0 && eb != eb_plan) {
     return fail(DDP_EINVAL, "%s: dtype has %d-byte elements, the plan %d", what, eb, eb_plan);
+  }
+  if (n_buckets > 0 && seg_p != p) {
+    return fail(DDP_ENOTREADY, "%s: call ddp_plan_upload_segments with p=%d first", what, p);
   }
   if (n_params > 0 && d_grad_ptrs == nullptr) {
     return fail(DDP_EINVAL, "%s: gradient pointer table is NULL", what);
@@ -131,9 +140,21 @@ extern "C" ddp_status ddp_reducer_prepare(ddp_reducer *r) {
   r->log_first.clear();
   r->log_count.clear();
   r->ready_order.clear();
+  r->failed = DDP_OK;
+  r->failed_detail[0] = '\0';
   r->active = true;
   return DDP_OK;
 }
+
+namespace {
+
+// The sticky launch failure of the pass, reported again by `what`.
+ddp_status report_failure(const ddp_reducer *r, const char *what) {
+  return fail(r->failed, "%s: an earlier launch of this pass failed: %s", what,
+              r->failed_detail);
+}
+
+}  // namespace
 
 extern "C" ddp_status ddp_reducer_mark_ready(ddp_reducer *r, int32_t param,
                                              hipEvent_t ready) {
@@ -141,6 +162,7 @@ extern "C" ddp_status ddp_reducer_mark_ready(ddp_reducer *r, int32_t param,
   const char *what = "ddp_reducer_mark_ready";
   if (r == nullptr) return fail(DDP_EINVAL, "%s: reducer is NULL", what);
   if (!r->active) return fail(DDP_EINVAL, "%s: call ddp_reducer_prepare first", what);
+  if (r->failed != DDP_OK) return report_failure(r, what);
   if (param < 0 || param >= static_cast<int32_t>(r->bucket_of.size())) {
     return fail(DDP_ERANGE, "%s: parameter %d out of range", what, param);
   }
@@ -160,16 +182,24 @@ extern "C" ddp_status ddp_reducer_mark_ready(ddp_reducer *r, int32_t param,
   if (r->pending[b] != 0 || b != r->next) return DDP_OK;
   int32_t end = r->next;
   while (end < n_buckets && r->pending[end] == 0) ++end;
-  for (int32_t k = r->next; k < end; ++k) {
+  ddp_status s = DDP_OK;
+  for (int32_t k = r->next; k < end && s == DDP_OK; ++k) {
     for (hipEvent_t ev : r->events[k]) {
-      ddp_status s = check_hip(hipStreamWaitEvent(r->comm, ev, 0), "hipStreamWaitEvent");
-      if (s != DDP_OK) return s;
+      s = check_hip(hipStreamWaitEvent(r->comm, ev, 0), "hipStreamWaitEvent");
+      if (s != DDP_OK) break;
     }
   }
-  ddp_status s = allreduce_buckets(r->plan, r->next, end - r->next, r->p, r->grads, r->dtype,
-                                   r->avg_mode, r->tokens.empty() ? nullptr : r->tokens.data(),
-                                   r->comm, nullptr, r->max_workgroups);
-  if (s != DDP_OK) return s;
+  if (s == DDP_OK) {
+    s = allreduce_buckets(r->plan, r->next, end - r->next, r->p, r->grads, r->dtype,
+                          r->avg_mode, r->tokens.empty() ? nullptr : r->tokens.data(), r->comm,
+                          nullptr, r->max_workgroups);
+  }
+  if (s != DDP_OK) {
+    r->failed = s;
+    std::snprintf(r->failed_detail, sizeof r->failed_detail, "buckets %d..%d: %s", r->next,
+                  end - 1, ddp_last_error());
+    return fail(s, "%s: %s", what, r->failed_detail);
+  }
   r->log_mark.push_back(mark);
   r->log_first.push_back(r->next);
   r->log_count.push_back(end - r->next);
@@ -183,6 +213,7 @@ extern "C" ddp_status ddp_reducer_finalize(ddp_reducer *r, hipStream_t wait_stre
   if (r == nullptr) return fail(DDP_EINVAL, "%s: reducer is NULL", what);
   if (!r->active) return fail(DDP_EINVAL, "%s: no backward pass in progress", what);
   r->active = false;
+  if (r->failed != DDP_OK) return report_failure(r, what);
   const int32_t n_buckets = static_cast<int32_t>(r->size.size());
   if (r->next < n_buckets) {
     int32_t missing = 0;

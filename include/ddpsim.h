@@ -199,6 +199,11 @@ ddp_status ddp_plan_bucket_params(const ddp_plan *plan, int32_t b,
  * (-1 if i is out of range). */
 int32_t ddp_plan_param_bucket(const ddp_plan *plan, int32_t i);
 int64_t ddp_plan_param_offset(const ddp_plan *plan, int32_t i);
+/* Element count of parameter i as the plan was built with it (-1 if i is
+ * out of range): what every rank's gradient of parameter i must hold. */
+int64_t ddp_plan_param_numel(const ddp_plan *plan, int32_t i);
+/* Bytes per element the plan was built for (-1 for a NULL plan). */
+int32_t ddp_plan_elem_bytes(const ddp_plan *plan);
 
 /* Size in bytes of the plan's device-side table: 32 bytes per parameter
  * descriptor, then 4 bytes per tile of 4096 elements naming the tile's
@@ -314,14 +319,17 @@ ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_bucket,
  *   create    plan (with ddp_plan_upload_segments done for p), p, the DEVICE
  *             gradient pointer table, dtype, averaging (tokens copied), and
  *             the stream the all-reduces run on. Plan and table must outlive
- *             the reducer. Errors: DDP_EINVAL, DDP_ERANGE.
+ *             the reducer. Errors: DDP_EINVAL, DDP_ERANGE; DDP_ENOTREADY
+ *             when the plan's piece table was not uploaded for this p.
  *   prepare   starts a backward pass (all counts reset).
  *   mark_ready  param in [0, n_params); `ready` is an event recorded after
  *             that parameter's gradients of all ranks were written (NULL if
  *             they already were when the call is made). DDP_EINVAL for a
  *             second mark of a parameter in one pass or a mark outside a
- *             pass, DDP_ERANGE for a bad index; a failed launch returns its
- *             error and leaves the pass unusable until the next prepare.
+ *             pass, DDP_ERANGE for a bad index. A failed launch returns its
+ *             error, and every later mark_ready and the finalize of that
+ *             pass return the same status with the same detail, until the
+ *             next prepare.
  *   finalize  ends the pass. DDP_ENOTREADY (with the bucket and counts in
  *             ddp_last_error) if some bucket never became ready -- what DDP
  *             would wait for forever without find_unused_parameters.

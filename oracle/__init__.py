@@ -123,7 +123,7 @@ def _load():
     lib.orc_allreduce.argtypes = [P, i32, i64, i32, i32, P, i32, P, i64, P]
     lib.orc_allreduce.restype = ctypes.c_int
     lib.orc_tree_fold_samples.argtypes = [P, i32, i64, i32, i32, f32, P]
-    lib.orc_tree_fold_samples.restype = None
+    lib.orc_tree_fold_samples.restype = i32
     _lib = lib
     return lib
 
@@ -548,9 +548,10 @@ def tree_allreduce_at(vals: np.ndarray, schedule: str, avg: str = "none",
                              dtype=np.float32)
     k = f.shape[0]
     out = np.empty(k, dtype=np.float32)
-    lib.orc_tree_fold_samples(_ptr(f), p, k, SCHEDULES[schedule],
-                              1 if avg != "none" else 0,
-                              avg_divisor(avg, p, tokens), _ptr(out))
+    _check(lib.orc_tree_fold_samples(_ptr(f), p, k, SCHEDULES[schedule],
+                                     1 if avg != "none" else 0,
+                                     avg_divisor(avg, p, tokens), _ptr(out)),
+           "orc_tree_fold_samples")
     return f32_to_bf16(out) if vals.dtype == np.uint16 else out
 
 

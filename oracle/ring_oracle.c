@@ -958,9 +958,11 @@ int orc_allreduce(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
  * Every rank of a pair computes a + b or b + a, the same number, so the
  * pairing alone fixes the result. Derived from the exchanges each schedule
  * performs; pinned to the literal simulations in tests. */
-void orc_tree_fold_samples(const float *vals, int32_t p, int64_t count,
-                           int32_t schedule, int32_t do_divide, float divisor,
-                           float *out) {
+int32_t orc_tree_fold_samples(const float *vals, int32_t p, int64_t count,
+                              int32_t schedule, int32_t do_divide, float divisor,
+                              float *out) {
+  /* the partial sums of one element live in t[]: at most 64 ranks */
+  if (p < 1 || p > 64 || count < 0) return ORC_EINVAL;
   int32_t q = pow2_floor(p);
   float t[64];
   for (int64_t s = 0; s < count; ++s) {
@@ -977,6 +979,7 @@ void orc_tree_fold_samples(const float *vals, int32_t p, int64_t count,
     }
     out[s] = do_divide ? t[0] / divisor : t[0];
   }
+  return ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */

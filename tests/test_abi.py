@@ -199,11 +199,20 @@ def test_reducer_errors_without_launching():
     """Bucket 0 never completes, so nothing is launched: every check here is
     host logic."""
     L = load_library()
-    sizes = [5, 7, 3, 9, 4]
-    plan = ddp.ddp_bucket_plan(sizes, 4, 32, 16)
-    assert plan.num_buckets >= 2
     fake = ctypes.c_void_p(0x100000000)
     out = ctypes.c_void_p()
+    # the piece table must have been uploaded for the reducer's p
+    real = ddp.ddp_bucket_plan([5, 7, 3, 9, 4], 4, 32, 16)
+    assert L.ddp_reducer_create(real.handle, 4, fake, 0, 1, None, None, ctypes.byref(out)) == 6
+    assert b"ddp_plan_upload_segments" in L.ddp_last_error()
+    # zero-size parameters with caps of 0 bytes: one bucket each and an empty
+    # piece table, which uploads without device memory
+    sizes = [0, 0, 0, 0, 0]
+    plan = ddp.ddp_bucket_plan(sizes, 4, 0, 0)
+    assert plan.num_buckets == len(sizes) and plan.segment_bytes(4) == 0
+    assert L.ddp_plan_upload_segments(plan.handle, 3, None, 0, None) == 0
+    assert L.ddp_reducer_create(plan.handle, 4, fake, 0, 1, None, None, ctypes.byref(out)) == 6
+    assert L.ddp_plan_upload_segments(plan.handle, 4, None, 0, None) == 0
     assert L.ddp_reducer_create(plan.handle, 0, fake, 0, 0, None, None, ctypes.byref(out)) == 2
     assert L.ddp_reducer_create(plan.handle, 4, None, 0, 0, None, None, ctypes.byref(out)) == 1
     assert L.ddp_reducer_create(plan.handle, 4, fake, 1, 0, None, None, ctypes.byref(out)) == 1
@@ -428,3 +437,125 @@ def test_binding_rejects_host_tensors_and_ragged_tables():
         ddp.grad_pointer_table([[torch.zeros(4, 4).t()], [torch.zeros(4, 4).t()]])
     with pytest.raises(ValueError):
         ddp.grad_pointer_table([])
+
+
+def _fake_table(p, numels, eb):
+    """A host stand-in for what grad_pointer_table returns (addresses are
+    never read: every call below is refused in the binding first)."""
+    import torch
+
+    t = torch.zeros(p * len(numels), dtype=torch.int64)
+    t._ddp_ranks, t._ddp_numel, t._ddp_elem_bytes = p, tuple(numels), eb
+    return t
+
+
+def test_binding_checks_grad_tables_against_plan_and_p():
+    """A table must come from grad_pointer_table, for the call's p, with the
+    plan's parameter sizes and element size; each mismatch is refused before
+    the library sees the call."""
+    import torch
+
+    from bucketed_gradient_all_ddp_amd.binding import _check_grad_table
+
+    plan = ddp.ddp_bucket_plan([10, 20, 30], 4, 1024, 256)
+    assert plan.param_numels() == (10, 20, 30)
+    assert load_library().ddp_plan_elem_bytes(plan.handle) == 4
+    assert load_library().ddp_plan_param_numel(plan.handle, 3) == -1
+    with pytest.raises(TypeError, match="grad_pointer_table"):
+        _check_grad_table(torch.zeros(6, dtype=torch.int64), plan, 2, "t")
+    bad = _fake_table(2, [10, 20, 30], 4).to(torch.int32)
+    bad._ddp_ranks, bad._ddp_numel, bad._ddp_elem_bytes = 2, (10, 20, 30), 4
+    with pytest.raises(TypeError, match="int64"):
+        _check_grad_table(bad, plan, 2, "t")
+    with pytest.raises(ValueError, match="ranks"):
+        _check_grad_table(_fake_table(2, [10, 20, 30], 4), plan, 3, "t")  # fewer ranks than p
+    with pytest.raises(ValueError, match="ranks"):
+        _check_grad_table(_fake_table(2, [10, 20], 4), plan, 2, "t")  # another model
+    with pytest.raises(ValueError, match="tensor 1 has 21"):
+        _check_grad_table(_fake_table(2, [10, 21, 30], 4), plan, 2, "t")
+    with pytest.raises(ValueError, match="2-byte"):
+        _check_grad_table(_fake_table(2, [10, 20, 30], 2), plan, 2, "t")
+    # everything matches: only the device check is left
+    with pytest.raises(TypeError, match="device"):
+        _check_grad_table(_fake_table(2, [10, 20, 30], 4), plan, 2, "t")
+    # the entry points run the same check
+    with pytest.raises(ValueError, match="ranks"):
+        ddp.ddp_allreduce_buckets(plan, 0, 1, _fake_table(2, [10, 20, 30], 4), 4)
+    with pytest.raises(ValueError, match="ranks"):
+        ddp.ddp_allreduce_bucket(plan, 0, _fake_table(1, [10, 20, 30], 4), 4)
+
+
+def test_binding_checks_bucket_buffers():
+    import torch
+
+    from bucketed_gradient_all_ddp_amd.binding import _check_bucket_bufs
+
+    plan = ddp.ddp_bucket_plan([10, 20, 30], 4, 1024, 256)
+    n = plan.bucket_numel(0)
+    _check_bucket_bufs(plan, 0, [torch.zeros(n), torch.zeros(n)], "t")
+    with pytest.raises(ValueError, match="rank 1"):
+        _check_bucket_bufs(plan, 0, [torch.zeros(n), torch.zeros(n - 1)], "t")
+    with pytest.raises(ValueError, match="rank 0"):
+        _check_bucket_bufs(plan, 0, [torch.zeros(n, dtype=torch.bfloat16)] * 2, "t")
+    with pytest.raises(ValueError, match="rank 0"):
+        _check_bucket_bufs(plan, 0, [torch.zeros(2 * n)[::2]] * 2, "t")
+    with pytest.raises(ValueError):
+        _check_bucket_bufs(plan, 0, [], "t")
+    # an out-of-range bucket is left to the library (DDP_ERANGE)
+    _check_bucket_bufs(plan, 7, [torch.zeros(1)], "t")
+
+
+def test_binding_rejects_overlapping_gradients():
+    import torch
+
+    from bucketed_gradient_all_ddp_amd.binding import _reject_overlaps
+
+    arena = torch.zeros(100)
+    ok = [[arena[0:10], arena[10:30]], [arena[30:40], arena[40:60]]]
+    _reject_overlaps(ok, [t.data_ptr() for r in ok for t in r])
+    # zero-size tensors own no bytes
+    empty = [[arena[0:10], arena[5:5]], [arena[10:20], arena[5:5]]]
+    _reject_overlaps(empty, [t.data_ptr() for r in empty for t in r])
+    same_rank = [[arena[0:10], arena[9:30]], [arena[30:40], arena[40:60]]]
+    with pytest.raises(ValueError, match="share memory"):
+        _reject_overlaps(same_rank, [t.data_ptr() for r in same_rank for t in r])
+    across = [[arena[0:10], arena[10:30]], [arena[0:10], arena[40:60]]]
+    with pytest.raises(ValueError, match="gradient 0 of rank 0 and gradient 0 of rank 1"):
+        _reject_overlaps(across, [t.data_ptr() for r in across for t in r])
+
+
+def test_reducer_failed_launch_is_sticky():
+    """A launch that fails inside mark_ready (here: the piece table was
+    re-uploaded for another p after the reducer was made, so the launch is
+    refused before anything is enqueued) is reported by every later mark and
+    by finalize of that pass, instead of finalize blaming a bucket that never
+    became ready; prepare starts clean."""
+    L = load_library()
+    fake = ctypes.c_void_p(0x100000000)
+    sizes = [0, 0, 0]
+    plan = ddp.ddp_bucket_plan(sizes, 4, 0, 0)
+    assert L.ddp_plan_upload_segments(plan.handle, 2, None, 0, None) == 0
+    out = ctypes.c_void_p()
+    assert L.ddp_reducer_create(plan.handle, 2, fake, 0, 1, None, None, ctypes.byref(out)) == 0
+    r = out
+    try:
+        assert L.ddp_reducer_prepare(r) == 0
+        assert L.ddp_plan_upload_segments(plan.handle, 3, None, 0, None) == 0
+        last = plan.num_buckets - 1
+        first_param = plan.bucket_params(0)[0]
+        assert L.ddp_reducer_mark_ready(r, first_param, None) == 6
+        assert b"upload_segments" in L.ddp_last_error()
+        other = plan.bucket_params(last)[0]
+        assert L.ddp_reducer_mark_ready(r, other, None) == 6
+        assert b"earlier launch" in L.ddp_last_error()
+        assert L.ddp_reducer_finalize(r, None) == 6
+        assert b"earlier launch" in L.ddp_last_error()
+        assert b"never became ready" not in L.ddp_last_error()
+        # with the right table again, a new pass launches every bucket
+        assert L.ddp_plan_upload_segments(plan.handle, 2, None, 0, None) == 0
+        assert L.ddp_reducer_prepare(r) == 0
+        for i in range(len(sizes)):
+            assert L.ddp_reducer_mark_ready(r, i, None) == 0
+        assert L.ddp_reducer_launch_log(r, None, None, None, 0) >= 1
+    finally:
+        L.ddp_reducer_free(r)

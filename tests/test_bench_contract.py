@@ -63,6 +63,8 @@ def test_headline_line_has_the_contract_fields():
     assert 0.3 < rf["frac"] < 1.0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
+    assert cb["host_cores"] == os.cpu_count() and "GPU's own input values" in cb["sample"]
+    assert len(d["config"]["arena_base_mod_2MiB"]) == d["config"]["p"]
     pc = d["practical_ceiling"]
     assert 1000 < pc["copy_GBps"] < 8000
     assert abs(pc["headline_frac_of_copy"] - rf["achieved"] / pc["copy_GBps"]) < 1e-3

@@ -65,14 +65,42 @@ def test_bucket_allreduce_gpt2_shaped(oracle):
 
 def test_bucket_allreduce_needs_segments_for_p():
     plan = ddp.ddp_bucket_plan([100, 200], 4, 1024, 256)
-    table = torch.zeros(8, dtype=torch.int64, device="cuda")
+    grads = [[torch.zeros(n, device="cuda") for n in (100, 200)] for _ in range(4)]
+    table4 = ddp.grad_pointer_table(grads)
+    table3 = ddp.grad_pointer_table(grads[:3])
     with pytest.raises(ddp.DDPError, match="ENOTREADY"):
-        ddp.ddp_allreduce_bucket(plan, 0, table, 4)
+        ddp.ddp_allreduce_bucket(plan, 0, table4, 4)
     plan.upload_segments(3)
     with pytest.raises(ddp.DDPError, match="ENOTREADY"):
-        ddp.ddp_allreduce_bucket(plan, 0, table, 4)
+        ddp.ddp_allreduce_bucket(plan, 0, table4, 4)
     with pytest.raises(ddp.DDPError, match="ERANGE"):
-        ddp.ddp_allreduce_bucket(plan, 9, table, 3)
+        ddp.ddp_allreduce_bucket(plan, 9, table3, 3)
+    # a table built for another rank count never reaches the library
+    with pytest.raises(ValueError, match="ranks"):
+        ddp.ddp_allreduce_bucket(plan, 0, table4, 3)
+
+
+def test_failed_segment_reupload_keeps_the_previous_table(oracle):
+    """A re-upload the library refuses (p = 65) must leave the p = 8 piece
+    table in place and alive: the all-reduce that follows still matches the
+    oracle, also after the allocator has handed out other memory."""
+    p = 8
+    cap, first = 64 * 1024, 8 * 1024
+    plan = ddp.ddp_bucket_plan(SIZES, 4, cap, first).upload_segments(p)
+    with pytest.raises(ddp.DDPError, match="ERANGE"):
+        plan.upload_segments(65)
+    # memory released to the caching allocator would be handed out here
+    scratch = [torch.full((plan.segment_bytes(p) // 4 + 64,), -1, dtype=torch.int32,
+                          device="cuda") for _ in range(4)]
+    host, grads = make_grads(p, SIZES, 1300, False, oracle, "aligned")
+    table = ddp.grad_pointer_table(grads)
+    ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg="world")
+    torch.cuda.synchronize()
+    del scratch
+    want = _oracle_sync(oracle, host, SIZES, 4, cap, first, "world", None)
+    for r in range(p):
+        for i in range(len(SIZES)):
+            assert_bits_equal(to_host(grads[r][i]), want[r][i], f"rank {r} param {i}")
 
 
 @pytest.mark.parametrize("p", [2, 8])

@@ -95,13 +95,24 @@ def test_bucketed_sync_end_to_end(oracle, p):
 
 
 def test_flatten_errors():
+    import ctypes
+
     plan = ddp.ddp_bucket_plan([10, 20], 4, 100, 40)
-    bufs = [torch.empty(30, device="cuda") for _ in range(2)]
-    table = torch.zeros(4, dtype=torch.int64, device="cuda")
+    assert plan.bucket_numel(0) == 20
+    bufs = [torch.empty(20, device="cuda") for _ in range(2)]
+    grads = [[torch.zeros(n, device="cuda") for n in (10, 20)] for _ in range(2)]
+    table = ddp.grad_pointer_table(grads)
     with pytest.raises(ddp.DDPError, match="ENOTREADY"):
         ddp.ddp_flatten(plan, 0, table, bufs)
     plan.upload()
     with pytest.raises(ddp.DDPError, match="ERANGE"):
         ddp.ddp_flatten(plan, 5, table, bufs)
-    with pytest.raises(ddp.DDPError, match="EINVAL"):
+    # the binding refuses buffers of the wrong element size or length ...
+    with pytest.raises(ValueError, match="rank 0"):
         ddp.ddp_flatten(plan, 0, table, [b.to(torch.bfloat16) for b in bufs])
+    with pytest.raises(ValueError, match="rank 1"):
+        ddp.ddp_unflatten(plan, 0, [bufs[0], bufs[1][:19]], table)
+    # ... and the library refuses a dtype the plan was not built for
+    L = ddp.load_library()
+    ptrs = (ctypes.c_void_p * 2)(*[b.data_ptr() for b in bufs])
+    assert L.ddp_flatten(plan.handle, 0, 2, table.data_ptr(), ptrs, 1, 1.0, None) == 1

@@ -300,3 +300,17 @@ def test_choice_flips_at_the_printed_crossover(p, mstar_mb):
     assert cm.choose_schedule(p, 0.99 * m, a, b) == "recursive_doubling"
     assert cm.choose_schedule(p, 1.01 * m, a, b) == "ring"
     assert cm.choose_schedule(1, 1e9, a, b) == "ring"  # tie: first candidate
+
+
+def test_tree_fold_samples_refuses_more_than_64_ranks(oracle):
+    """The per-element fold keeps one partial sum per core rank (at most 64):
+    a wider input is refused instead of overrunning that array; 64 is still
+    folded."""
+    import numpy as np
+
+    ok = oracle.tree_allreduce_at(np.ones((3, 64), dtype=np.float32), "tree")
+    assert ok.tolist() == [64.0, 64.0, 64.0]
+    with pytest.raises(oracle.OracleError):
+        oracle.tree_allreduce_at(np.ones((3, 128), dtype=np.float32), "tree")
+    with pytest.raises(oracle.OracleError):
+        oracle.tree_allreduce_at(np.ones((3, 65), dtype=np.float32), "recursive_doubling")
