@@ -41,6 +41,7 @@ EXPORTS = [
     "ddp_reducer_finalize", "ddp_reducer_launch_log", "ddp_reducer_ready_order",
     "ddp_reducer_set_max_workgroups", "ddp_bucket_plan_ordered", "ddp_coalesce_plan", "ddp_broadcast_coalesced",
     "ring_allreduce_sim", "ring_allreduce_sim_workspace", "ring_allreduce_sim_steps",
+    "ring_allreduce_sim_noalloc",
     "allreduce_sim", "allreduce_sim_workspace", "ddp_schedule_time", "ddp_choose_schedule",
     "ddp_overlap_step_time",
     "reduce_scatter_sim", "allgather_sim", "broadcast_sim",
@@ -126,6 +127,7 @@ def load_library(path: str = LIB_PATH):
         "ddp_broadcast_coalesced": ([vp, i32, vp, i32, vp, vp], st),
         "ring_allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, vp, sz, vp, vp], st),
         "ring_allreduce_sim_workspace": ([i32, i64, i32, i32], sz),
+        "ring_allreduce_sim_noalloc": ([vp, i32, i64, i32, i32, vp, i32, vp, vp], st),
         "ring_allreduce_sim_steps": ([vp, i32, i64, i32, vp, i32, i32, vp], st),
         "allreduce_sim": ([vp, i32, i64, i32, i32, vp, i32, i32, vp, sz, vp, vp], st),
         "allreduce_sim_workspace": ([i32, i64, i32, i32, i32], sz),
@@ -667,6 +669,23 @@ def ring_allreduce_sim(bufs: Sequence, avg: str = "none", tokens=None,
         _ptrs(bufs), p, n, _dtype_code(bufs[0]), AVG[avg], _tokens(tokens, p),
         ALGO[algo], ws_ptr, ws_bytes, _stream(stream), ctypes.byref(st)),
         "ring_allreduce_sim")
+    return st
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DDP_NOALLOC_SCRATCH_BYTES
+
+
+def ring_allreduce_sim_noalloc(bufs: Sequence, avg: str = "none", tokens=None,
+                               algo: str = "fused", stream=None) -> CommStats:
+    """ring_allreduce_sim without a workspace argument: the bf16 ring's
+    workspace is the library's per-GPU scratch array (at most
+    NOALLOC_SCRATCH_BYTES); nothing is allocated."""
+    p = len(bufs)
+    n = _numel_all(bufs)
+    st = CommStats()
+    _check(load_library().ring_allreduce_sim_noalloc(
+        _ptrs(bufs), p, n, _dtype_code(bufs[0]), AVG[avg], _tokens(tokens, p), ALGO[algo],
+        _stream(stream), ctypes.byref(st)), "ring_allreduce_sim_noalloc")
     return st
 
 

@@ -22,6 +22,8 @@
 // Padding to a multiple of p is virtual: chunks are [c C, (c+1) C) clipped
 // to n, and elements past n are never read or written.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "fold.hpp"
 #include "internal.hpp"
@@ -308,23 +310,23 @@ extern "C" size_t ring_allreduce_sim_workspace(int32_t p, int64_t n, int32_t dty
   return static_cast<size_t>(p) * workspace_stride_elems(n) * 4;
 }
 
-extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n,
-                                         int32_t dtype, int32_t avg_mode,
-                                         const int64_t *tokens, int32_t algo,
-                                         void *workspace, size_t workspace_bytes,
-                                         hipStream_t stream, ddp_comm_stats *stats) {
-  clear_error();
-  CallTimer timer = CallTimer::take();
+namespace ddpsim {
+namespace {
+
+// The whole of ring_allreduce_sim after its timing request was taken: the
+// workspace is the caller's, or the device's scratch array below.
+ddp_status run_allreduce(void *const *bufs, int32_t p, int64_t n, int32_t dtype,
+                         int32_t avg_mode, const int64_t *tokens, int32_t algo,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream,
+                         ddp_comm_stats *stats, CallTimer &timer, const char *what) {
   Divide div;
-  ddp_status s = validate_allreduce(bufs, p, n, dtype, avg_mode, tokens, &div,
-                                 "ring_allreduce_sim");
+  ddp_status s = validate_allreduce(bufs, p, n, dtype, avg_mode, tokens, &div, what);
   if (s != DDP_OK) return s;
   if (algo != DDP_ALGO_FUSED && algo != DDP_ALGO_RING) {
-    return fail(DDP_EINVAL, "ring_allreduce_sim: unknown algorithm %d", algo);
+    return fail(DDP_EINVAL, "%s: unknown algorithm %d", what, algo);
   }
   const size_t need = ring_allreduce_sim_workspace(p, n, dtype, algo);
-  s = check_workspace("ring_allreduce_sim", workspace, workspace_bytes, need, bufs, p,
-                      n * elem_bytes_of(dtype));
+  s = check_workspace(what, workspace, workspace_bytes, need, bufs, p, n * elem_bytes_of(dtype));
   if (s != DDP_OK) return s;
   fill_allreduce_stats(stats, p, n, dtype, algo);
   if (n == 0) return DDP_OK;
@@ -337,7 +339,7 @@ extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n
   float *ws = static_cast<float *>(workspace);
   const int32_t tpr = static_cast<int32_t>(ceil_div(ceil_div(n, 8), kThreads));
   const int64_t blocks = int64_t(tpr) * p;
-  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
+  if (blocks > INT32_MAX) return fail(DDP_EINVAL, "%s: n too large", what);
   const dim3 grid(static_cast<uint32_t>(blocks));
   s = launch(bf16_workspace_kernel<true>, grid, dim3(kThreads), stream, timer, false,
              "bf16_workspace_kernel launch", tab, ws, stride, n, tpr);
@@ -348,6 +350,83 @@ extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n
   if (s != DDP_OK) return s;
   return launch(bf16_workspace_kernel<false>, grid, dim3(kThreads), stream, timer, true,
                 "bf16_workspace_kernel launch", tab, ws, stride, n, tpr);
+}
+
+// Device memory that ring_allreduce_sim_noalloc uses as its workspace: the
+// fp32 rows of a bf16 ring. Each GPU holds its own copy from the moment the
+// library's code is loaded on it until the process ends. On the host the
+// name is only a stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress, once per device (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[DDP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_of[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (its device address, looked up
+// once per device and kept).
+ddp_status scratch_on_current_device(const char *what, void **out) {
+  int dev = -1;
+  ddp_status s = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (s != DDP_OK) return s;
+  if (dev < 0 || dev >= kScratchDevices) {
+    return fail(DDP_ERANGE, "%s: device %d beyond the %d this library keeps scratch for", what,
+                dev, kScratchDevices);
+  }
+  void *ptr = g_scratch_of[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_of[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      s = check_hip(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress");
+      if (s != DDP_OK) return s;
+      if (ptr == nullptr) {
+        return fail(DDP_EHIP, "%s: hipGetSymbolAddress gave no address for the scratch array",
+                    what);
+      }
+      g_scratch_of[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return DDP_OK;
+}
+
+}  // namespace
+}  // namespace ddpsim
+
+extern "C" ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n,
+                                         int32_t dtype, int32_t avg_mode,
+                                         const int64_t *tokens, int32_t algo,
+                                         void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream, ddp_comm_stats *stats) {
+  clear_error();
+  CallTimer timer = CallTimer::take();
+  return run_allreduce(bufs, p, n, dtype, avg_mode, tokens, algo, workspace, workspace_bytes,
+                       stream, stats, timer, "ring_allreduce_sim");
+}
+
+extern "C" ddp_status ring_allreduce_sim_noalloc(void *const *bufs, int32_t p, int64_t n,
+                                                 int32_t dtype, int32_t avg_mode,
+                                                 const int64_t *tokens, int32_t algo,
+                                                 hipStream_t stream, ddp_comm_stats *stats) {
+  clear_error();
+  CallTimer timer = CallTimer::take();
+  const char *what = "ring_allreduce_sim_noalloc";
+  const size_t need = ring_allreduce_sim_workspace(p, n, dtype, algo);
+  if (need > size_t(DDP_NOALLOC_SCRATCH_BYTES)) {
+    return fail(DDP_EWORKSPACE,
+                "%s: needs %zu bytes of workspace, more than the %lld of the device's scratch "
+                "array (p=%d, n=%lld); use ring_allreduce_sim with a workspace",
+                what, need, (long long)DDP_NOALLOC_SCRATCH_BYTES, p, (long long)n);
+  }
+  void *ws = nullptr;
+  if (need > 0) {
+    const ddp_status s = scratch_on_current_device(what, &ws);
+    if (s != DDP_OK) return s;
+  }
+  return run_allreduce(bufs, p, n, dtype, avg_mode, tokens, algo, ws,
+                       need > 0 ? size_t(DDP_NOALLOC_SCRATCH_BYTES) : 0, stream, stats, timer,
+                       what);
 }
 
 extern "C" ddp_status ring_allreduce_sim_steps(void *const *bufs, int32_t p, int64_t n,

@@ -399,6 +399,27 @@ ddp_status ring_allreduce_sim(void *const *bufs, int32_t p, int64_t n,
 size_t ring_allreduce_sim_workspace(int32_t p, int64_t n, int32_t dtype,
                                     int32_t algo);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * all-reduce as ring_allreduce_sim (same kernels, same bits), with the
+ * workspace of DDP_ALGO_RING on bf16 taken from a scratch array of
+ * DDP_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU, for the life of the process. Calls whose workspace would exceed
+ * it (ring_allreduce_sim_workspace(p, n, dtype, algo) bytes) fail with
+ * DDP_EWORKSPACE before anything is enqueued; the fused algorithm and fp32
+ * need no workspace and have no limit. The call allocates nothing and
+ * frees nothing. The array is overwritten before it is read, so what an
+ * earlier call left there does not matter; but every call on one GPU uses
+ * that GPU's single array, so calls whose bf16 rings can overlap in time on
+ * one GPU (other streams, other host threads) race and must be ordered by
+ * the caller. Errors: as ring_allreduce_sim, and DDP_EHIP if the array's
+ * device address cannot be obtained. */
+#define DDP_NOALLOC_SCRATCH_BYTES (64ll << 20)
+ddp_status ring_allreduce_sim_noalloc(void *const *bufs, int32_t p, int64_t n,
+                                      int32_t dtype, int32_t avg_mode,
+                                      const int64_t *tokens, int32_t algo,
+                                      hipStream_t stream, ddp_comm_stats *stats);
+
 /* Run only ring steps [first_step, first_step + n_steps) of the 2(p-1)
  * steps of the fp32 ring schedule, in place: steps 0..p-2 are the
  * reduce-scatter steps (step p-2 also applies the averaging to each

@@ -559,3 +559,16 @@ def test_reducer_failed_launch_is_sticky():
         assert L.ddp_reducer_launch_log(r, None, None, None, 0) >= 1
     finally:
         L.ddp_reducer_free(r)
+
+
+def test_noalloc_limit_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "ddpsim.h")).read()
+    m = re.search(r"#define DDP_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ddp.NOALLOC_SCRATCH_BYTES
+    L = load_library()
+    # refused before any device work: the workspace would pass the array
+    p = 8
+    n = ddp.NOALLOC_SCRATCH_BYTES // (4 * p) + 1
+    fake = (ctypes.c_void_p * p)(*[0x100000000 + k * 0x10000000 for k in range(p)])
+    assert L.ring_allreduce_sim_noalloc(fake, p, n, 1, 0, None, 1, None, None) == 7
+    assert b"scratch" in L.ddp_last_error()
