@@ -559,6 +559,13 @@ def bench_costmodel(torch, ddp, W, dev, args, name="cost-model-p64"):
         ops[f"allreduce_tokens_{sch}"] = (
             lambda s=sch: ddp.allreduce_sim(bufs, s, False, avg="tokens", tokens=tokens),
             2 * (p - 1) / p, 2 * p * S)
+    # the ring schedule step by step: 2(p-1) launches, each a ring step
+    # (reduce-scatter step: read sender and receiver, write receiver, 3n
+    # elements; all-gather step: read sender, write receiver, 2n), averaged
+    # by p so that repeated runs keep their magnitude
+    ops["allreduce_ring_steps"] = (lambda: ddp.ring_allreduce_sim(bufs, avg="world",
+                                                                  algo="ring"),
+                                   2 * (p - 1) / p, 5 * (p - 1) * S)
     res = {}
     for name, (fn, busf, hbm) in ops.items():
         fn()
@@ -567,6 +574,29 @@ def bench_costmodel(torch, ddp, W, dev, args, name="cost-model-p64"):
                      "bus_GBps": round(S * busf / (dms * 1e-3) / 1e9, 1),
                      "hbm_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(hbm / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log(f"{name}: {res[name]['device_ms']} ms, {res[name]['hbm_GBps']} GB/s")
+    # each ring step on its own (one launch per call, timed by its dispatch
+    # events): reduce-scatter steps move 3n elements, all-gather steps 2n
+    steps = [lambda k=k: ddp.ring_allreduce_sim_steps(bufs, k, 1, avg="world")
+             for k in range(2 * (p - 1))]
+    timer = ddp.CallTimer(pairs=len(steps) * 3)
+    ids = []
+    for _ in range(3):
+        for k, fn in enumerate(steps):
+            ids.append((k, timer.arm()))
+            fn()
+    torch.cuda.synchronize()
+    per = {"reduce_scatter": [], "allgather": []}
+    for k, i in ids:
+        per["reduce_scatter" if k < p - 1 else "allgather"].append(timer.elapsed_ms(i))
+    res["ring_step_kernel"] = {}
+    for kind, elems in (("reduce_scatter", 3), ("allgather", 2)):
+        us = 1e3 * sum(per[kind]) / len(per[kind])
+        res["ring_step_kernel"][kind] = {
+            "launches": len(per[kind]), "avg_us": round(us, 2),
+            "bytes_per_launch": elems * S,
+            "hbm_GBps": round(elems * S / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(elems * S / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     gib = n * 4 / (1 << 30)
     what = ("cost-model shape: one 2^29-element fp32 tensor per rank (2 GiB), p=64"
             if name == "cost-model-p64" else
@@ -575,8 +605,8 @@ def bench_costmodel(torch, ddp, W, dev, args, name="cost-model-p64"):
     _line(f"all-reduce bus GB/s, p={p}, {gib:g} GiB fp32 per rank, token-weighted",
           res["allreduce_tokens"]["bus_GBps"], "GB/s",
           what + ", tokens U{10..10000}; plus reduce-scatter, in-place all-gather, "
-          "broadcast, and the all-reduce under recursive doubling, Rabenseifner and the "
-          "tree (fused)",
+          "broadcast, the all-reduce under recursive doubling, Rabenseifner and the "
+          "tree (fused), and the ring step by step (2(p-1) launches, averaged by p)",
           {"ops": res, **({} if args.no_cpu_baseline else {"cpu_baseline": _costmodel_cpu(
               p, tokens, cpu_in)})})
 
@@ -870,6 +900,12 @@ def bench_sync(torch, ddp, W, dev, args):
     S = sum(sizes) * 4
     hbm = p * S
     st = fn()
+    # the same ranks' whole arenas through broadcast_sim (one flat buffer per
+    # rank, the fan-out copy): the same access pattern without the plan
+    flat = [lambda: ddp.broadcast_sim(arenas, src=0)]
+    flat[0]()
+    _, fdms = _timed_calls(torch, ddp, flat, args.steps)
+    fbytes = p * arenas[0].numel() * 4
     # per-forward buffer broadcast: 12 layers x (running mean, running var)
     # of 3072 fp32 each, plus an int64 counter per layer
     bn = [[torch.randn(3072, device=dev) for _ in range(24)] +
@@ -896,6 +932,10 @@ def bench_sync(torch, ddp, W, dev, args):
            "kernel_hbm_GBps": round(hbm / (dms * 1e-3) / 1e9, 1),
            "kernel_frac_of_8TBps": round(hbm / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
            "tree_messages": st.messages, "tree_rounds": st.steps,
+           "broadcast_sim_of_the_arenas": {
+               "kernel_ms": round(fdms, 3),
+               "kernel_hbm_GBps": round(fbytes / (fdms * 1e-3) / 1e9, 1),
+               "kernel_frac_of_8TBps": round(fbytes / (fdms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
            "buffer_broadcast": {"tensors": 36, "groups": len(calls),
                                 "us_per_forward": round(bwall * 1e3, 2),
                                 "kernel_us_per_forward": round(bdms * 1e3, 2)}})

@@ -101,8 +101,10 @@ __global__ __launch_bounds__(THR) void fused_allreduce_kernel(
 // sends chunk (r + chunk_shift) mod p to rank r+1.
 //   kReduce  receiver = receiver + sender (then divide, on the last
 //            reduce-scatter step); otherwise receiver = sender.
-template <bool kReduce, int VPT>
-__global__ __launch_bounds__(kThreads) void ring_step_kernel(
+// THR threads of VPT 16-byte vectors per workgroup; kNT makes the loads and
+// stores non-temporal (buffers past the Infinity Cache).
+template <bool kReduce, int VPT, int THR, bool kNT>
+__global__ __launch_bounds__(THR) void ring_step_kernel(
     RankTable bufs, int32_t p, int32_t chunk_shift, int64_t n, int64_t C,
     int32_t tiles_per_chunk, Divide div) {
   constexpr int V = 4;
@@ -116,8 +118,8 @@ __global__ __launch_bounds__(kThreads) void ring_step_kernel(
   float *out = static_cast<float *>(bufs.ptr[dst]);
   const int tid = static_cast<int>(threadIdx.x);
 
-  if (t == 0 && tid >= kThreads - 2 * (V - 1)) {
-    const int lane = tid - (kThreads - 2 * (V - 1));
+  if (t == 0 && tid >= THR - 2 * (V - 1)) {
+    const int lane = tid - (THR - 2 * (V - 1));
     const bool head = lane < V - 1;
     const int64_t i = head ? k.s + lane : k.tail_begin + (lane - (V - 1));
     if (i < (head ? k.head_end : k.e)) {
@@ -126,19 +128,19 @@ __global__ __launch_bounds__(kThreads) void ring_step_kernel(
   }
 
   const int64_t nv = (k.ve - k.vs) / V;
-  const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
+  const int64_t base = static_cast<int64_t>(t) * (THR * VPT);
   if (base >= nv) return;
   uint4 a[VPT], b[VPT];
   int64_t vi[VPT];
   bool ok[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    const int64_t jj = base + u * kThreads + tid;
+    const int64_t jj = base + u * THR + tid;
     ok[u] = jj < nv;
     vi[u] = k.vs / V + jj;
     if (ok[u]) {
-      b[u] = load_vec(src, vi[u]);
-      if (kReduce) a[u] = load_vec(out, vi[u]);
+      b[u] = load_vec<kNT>(src, vi[u]);
+      if (kReduce) a[u] = load_vec<kNT>(out, vi[u]);
     }
   }
 #pragma unroll
@@ -150,9 +152,9 @@ __global__ __launch_bounds__(kThreads) void ring_step_kernel(
       F32Traits::widen(b[u], fb);
 #pragma unroll
       for (int e = 0; e < 4; ++e) fa[e] = apply_divide(fa[e] + fb[e], div);
-      store_vec<false>(out, vi[u], F32Traits::narrow(fa));
+      store_vec<kNT>(out, vi[u], F32Traits::narrow(fa));
     } else {
-      store_vec<false>(out, vi[u], b[u]);
+      store_vec<kNT>(out, vi[u], b[u]);
     }
   }
 }
@@ -194,7 +196,43 @@ constexpr int kFusedNtThreads = 64;
 // per thread (one vector each) instead of 8.
 constexpr int kSmallRb = 32;
 constexpr int64_t kSmallBlocks = 512;
-constexpr int kStepVpt = 4;
+// Ring steps, each a copy or an add of one chunk per rank pair: one-wave
+// workgroups of one 16-byte vector per lane in both shapes. At 8 ranks of
+// 1 GiB, non-temporal accesses lifted a reduce-scatter step from 5.60 to
+// 6.59 TB/s and an all-gather step from 5.76 to 6.56 (256 threads x 4
+// vectors with ordinary accesses before; 256 x 1 and 64 x 2 both ~6.4); a
+// residency bound cost 13-45% (16 and 11 workgroups per CU). On the GPT-2
+// buckets (cache-resident) the one-wave shape with ordinary accesses gained
+// 2% over 256 x 4; non-temporal accesses there lost 5%.
+#ifndef DDPSIM_STEP_THREADS
+#define DDPSIM_STEP_THREADS 64  // ring steps on cache-resident buffers
+#endif
+#ifndef DDPSIM_STEP_VPT
+#define DDPSIM_STEP_VPT 1
+#endif
+constexpr int kStepVpt = DDPSIM_STEP_VPT;
+constexpr int kStepThreads = DDPSIM_STEP_THREADS;
+#ifndef DDPSIM_STEP_NT_BYTES
+// Ring steps over rank buffers larger than this in total take the one-wave
+// shape with non-temporal accesses (buffers past the Infinity Cache);
+// smaller ones keep 256 threads x 4 vectors and ordinary accesses.
+#define DDPSIM_STEP_NT_BYTES (int64_t(256) << 20)
+#endif
+#ifndef DDPSIM_STEP_NT_THREADS
+#define DDPSIM_STEP_NT_THREADS 64
+#endif
+#ifndef DDPSIM_STEP_NT_VPT
+#define DDPSIM_STEP_NT_VPT 1
+#endif
+#ifndef DDPSIM_STEP_NT_WGS_PER_CU
+#define DDPSIM_STEP_NT_WGS_PER_CU 0  // workgroups resident per CU (0: no bound)
+#endif
+#ifndef DDPSIM_STEP_NT
+#define DDPSIM_STEP_NT 1  // the large shape's accesses are non-temporal
+#endif
+constexpr int kStepNtThreads = DDPSIM_STEP_NT_THREADS;
+constexpr int kStepNtVpt = DDPSIM_STEP_NT_VPT;
+constexpr bool kStepNt = DDPSIM_STEP_NT != 0;
 
 
 int32_t tiles_for(int64_t C, int vec, int vpt, int threads = kThreads) {
@@ -247,12 +285,14 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
                 grid, block, stream, timer, true, kname, tab, p, n, C, tpc, div);
 }
 
-// Launch ring steps [first, first + count) on fp32 buffers.
-ddp_status launch_steps(const RankTable &tab, int32_t p, int64_t n, const Divide &div,
-                        int32_t first, int32_t count, hipStream_t stream, CallTimer &timer,
-                        bool ends_call) {
+// Launch ring steps [first, first + count) on fp32 buffers, in one of two
+// shapes (the same arithmetic).
+template <int VPT, int THR, bool kNT>
+ddp_status launch_steps_as(const RankTable &tab, int32_t p, int64_t n, const Divide &div,
+                           int32_t first, int32_t count, hipStream_t stream, CallTimer &timer,
+                           bool ends_call, size_t lds) {
   const int64_t C = ceil_div(n, p);
-  const int32_t tpc = tiles_for(C, 4, kStepVpt);
+  const int32_t tpc = tiles_for(C, 4, VPT, THR);
   const int64_t blocks = int64_t(tpc) * p;
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring step: n too large");
   const Divide none{kNone, 1.0f, 1.0f};
@@ -264,17 +304,29 @@ ddp_status launch_steps(const RankTable &tab, int32_t p, int64_t n, const Divide
       const int32_t k = s;  // reduce-scatter step k: rank r sends chunk r - k
       const int32_t shift = ((-k) % p + p) % p;
       const Divide &d = (k == p - 2) ? div : none;
-      st = launch(ring_step_kernel<true, kStepVpt>, grid, dim3(kThreads), stream, timer, last,
-                  "ring_step_kernel launch", tab, p, shift, n, C, tpc, d);
+      st = launch_lds(ring_step_kernel<true, VPT, THR, kNT>, grid, dim3(THR), lds, stream, timer,
+                      last, "ring_step_kernel launch", tab, p, shift, n, C, tpc, d);
     } else {
       const int32_t k = s - (p - 1);  // all-gather step k: chunk r + 1 - k
       const int32_t shift = ((1 - k) % p + p) % p;
-      st = launch(ring_step_kernel<false, kStepVpt>, grid, dim3(kThreads), stream, timer, last,
-                  "ring_step_kernel launch", tab, p, shift, n, C, tpc, none);
+      st = launch_lds(ring_step_kernel<false, VPT, THR, kNT>, grid, dim3(THR), lds, stream,
+                      timer, last, "ring_step_kernel launch", tab, p, shift, n, C, tpc, none);
     }
     if (st != DDP_OK) return st;
   }
   return DDP_OK;
+}
+
+ddp_status launch_steps(const RankTable &tab, int32_t p, int64_t n, const Divide &div,
+                        int32_t first, int32_t count, hipStream_t stream, CallTimer &timer,
+                        bool ends_call) {
+  if (int64_t(p) * n * 4 > DDPSIM_STEP_NT_BYTES) {
+    return launch_steps_as<kStepNtVpt, kStepNtThreads, kStepNt>(
+        tab, p, n, div, first, count, stream, timer, ends_call,
+        residency_lds(DDPSIM_STEP_NT_WGS_PER_CU));
+  }
+  return launch_steps_as<kStepVpt, kStepThreads, false>(tab, p, n, div, first, count, stream,
+                                                        timer, ends_call, 0);
 }
 
 

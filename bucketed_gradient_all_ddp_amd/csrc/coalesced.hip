@@ -26,10 +26,16 @@ int32_t plan_num_buckets(const ddp_plan *plan);
 namespace {
 
 #ifndef DDPSIM_BCAST_NT
-#define DDPSIM_BCAST_NT 0  // bit 0: non-temporal loads; bit 1: non-temporal stores
+#define DDPSIM_BCAST_NT 0  // non-temporal loads of the root's tensors
 #endif
-constexpr bool kBcastNtLoad = (DDPSIM_BCAST_NT & 1) != 0;
-constexpr bool kBcastNtStore = (DDPSIM_BCAST_NT & 2) != 0;
+constexpr bool kBcastNtLoad = DDPSIM_BCAST_NT != 0;
+#ifndef DDPSIM_BCAST_NT_STORE_BYTES
+// Buckets whose copies total more than this take non-temporal stores (the
+// GPT-2 parameter sync, two buckets of 250 MiB to 7 ranks: +1%); smaller
+// ones stay eligible for the Infinity Cache. Non-temporal loads as well
+// lost 4%.
+#define DDPSIM_BCAST_NT_STORE_BYTES (int64_t(256) << 20)
+#endif
 #ifndef DDPSIM_BCAST_THREADS
 #define DDPSIM_BCAST_THREADS 64  // threads per workgroup, one 16-byte vector each
 #endif
@@ -53,31 +59,50 @@ struct Unit<4> { using type = uint32_t; };
 template <>
 struct Unit<8> { using type = uint64_t; };
 
+#ifndef DDPSIM_BCAST_SPANS
+// Consecutive spans per workgroup, each span's stores overlapping the next
+// span's load. One is best: 2, 4 and 16 lost 5%, 5% and 12% on the GPT-2
+// parameter sync (fewer, longer workgroups keep fewer loads in flight).
+#define DDPSIM_BCAST_SPANS 1
+#endif
+constexpr int kBcastSpans = DDPSIM_BCAST_SPANS;
+
 // Each plan tile of kFlattenTile elements of one tensor (named by the plan's
 // tile map, as in flatten_kernel) is split into spans of one 16-byte vector
-// per lane, one span per workgroup. The root's span is loaded once and
-// stored to every other rank. 16-byte vectors when every rank's copy of the
-// tensor is 16-byte aligned (spans start at multiples of 16 bytes from the
-// tensor's base, so the base decides), elements of EB bytes otherwise.
+// per lane; a workgroup takes kBcastSpans consecutive spans of one tile. The
+// root's span is loaded once and stored to every other rank; the next span's
+// load is issued before this span's stores. 16-byte vectors when every
+// rank's copy of the tensor is 16-byte aligned (spans start at multiples of
+// 16 bytes from the tensor's base, so the base decides), elements of EB
+// bytes otherwise.
+// Spans per workgroup for EB-byte elements: at most the spans of one tile.
 template <int EB>
+constexpr int bcast_spans() {
+  constexpr int per_tile = kFlattenTile * EB / (kBcastThreads * kBcastVpt * kVecBytes);
+  return kBcastSpans < per_tile ? kBcastSpans : per_tile;
+}
+
+template <int EB, bool kNtStore>
 __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
     const ParamDesc *__restrict__ desc, const int32_t *__restrict__ tile_map, int32_t n_params,
     const void *const *__restrict__ ptrs, int32_t p, int32_t root) {
   using U = typename Unit<EB>::type;
-  constexpr int kSpan = kBcastThreads * kBcastVpt * kVecBytes / EB;  // elements per workgroup
-  constexpr int kSubs = kFlattenTile / kSpan;
-  static_assert(kSubs >= 1 && kSubs * kSpan == kFlattenTile, "spans must tile a plan tile");
+  constexpr int kSpans = bcast_spans<EB>();
+  constexpr int kSpan = kBcastThreads * kBcastVpt * kVecBytes / EB;  // elements per span
+  constexpr int kSubs = kFlattenTile / (kSpan * kSpans);             // workgroups per tile
+  static_assert(kSubs >= 1 && kSubs * kSpan * kSpans == kFlattenTile,
+                "spans must tile a plan tile");
   const int32_t tile = static_cast<int32_t>(blockIdx.x) / kSubs;
   const int32_t sub = static_cast<int32_t>(blockIdx.x) - tile * kSubs;
   const ParamDesc d = desc[tile_map[tile]];
   const int64_t start = static_cast<int64_t>(tile - d.tile_begin) * kFlattenTile +
-                        static_cast<int64_t>(sub) * kSpan;
+                        static_cast<int64_t>(sub) * kSpan * kSpans;
   const int64_t left = d.numel - start;
   if (left <= 0) return;
-  const int64_t cnt = left < kSpan ? left : kSpan;
+  const int64_t cnt = left < int64_t(kSpan) * kSpans ? left : int64_t(kSpan) * kSpans;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & 63;
-  // rank r's span, read from the device table (uniform: scalar loads)
+  // rank r's part, read from the device table (uniform: scalar loads)
   auto slice_mem = [&](int32_t r) {
     return static_cast<U *>(const_cast<void *>(ptrs[static_cast<int64_t>(r) * n_params +
                                                     d.param])) + start;
@@ -96,22 +121,37 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
   const U *src = slice(root);
   int64_t done = 0;
   if (aligned) {
+    constexpr int64_t kPerSpan = int64_t(kBcastThreads) * kBcastVpt;  // vectors
     const int64_t nv = cnt * EB / kVecBytes;
-    uint4 x[kBcastVpt];
+    const int32_t rot = store_rotation(p);
+    uint4 nxt[kBcastVpt];
 #pragma unroll
     for (int u = 0; u < kBcastVpt; ++u) {
       const int64_t j = u * kBcastThreads + tid;
-      x[u] = j < nv ? load_vec<kBcastNtLoad>(src, j) : make_uint4(0, 0, 0, 0);
+      nxt[u] = j < nv ? load_vec<kBcastNtLoad>(src, j) : make_uint4(0, 0, 0, 0);
     }
-    const int32_t rot = store_rotation(p);
-    for (int32_t k = 0; k < p; ++k) {
-      const int32_t r = ring_rank(rot, k, p);
-      if (r == root) continue;
-      U *dst = slice(r);
+    for (int sp = 0; sp < kSpans; ++sp) {
+      const int64_t j0 = sp * kPerSpan;
+      if (j0 >= nv) break;
+      uint4 x[kBcastVpt];
 #pragma unroll
-      for (int u = 0; u < kBcastVpt; ++u) {
-        const int64_t j = u * kBcastThreads + tid;
-        if (j < nv) store_vec<kBcastNtStore>(dst, j, x[u]);
+      for (int u = 0; u < kBcastVpt; ++u) x[u] = nxt[u];
+      if (sp + 1 < kSpans) {
+#pragma unroll
+        for (int u = 0; u < kBcastVpt; ++u) {
+          const int64_t j = j0 + kPerSpan + u * kBcastThreads + tid;
+          nxt[u] = j < nv ? load_vec<kBcastNtLoad>(src, j) : make_uint4(0, 0, 0, 0);
+        }
+      }
+      for (int32_t k = 0; k < p; ++k) {
+        const int32_t r = ring_rank(rot, k, p);
+        if (r == root) continue;
+        U *dst = slice(r);
+#pragma unroll
+        for (int u = 0; u < kBcastVpt; ++u) {
+          const int64_t j = j0 + u * kBcastThreads + tid;
+          if (j < nv) store_vec<kNtStore>(dst, j, x[u]);
+        }
       }
     }
     done = nv * kVecBytes / EB;
@@ -126,16 +166,20 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
 
 template <int EB>
 ddp_status launch_bucket(const ParamDesc *desc, const int32_t *tile_map, int32_t tiles,
-                         int32_t n_params,
-                         const void *const *ptrs, int32_t p, int32_t root, hipStream_t stream,
-                         CallTimer &timer, bool last) {
-  const int64_t blocks =
-      int64_t(tiles) * (kFlattenTile * EB / (kBcastThreads * kBcastVpt * kVecBytes));
+                         int64_t elems, int32_t n_params, const void *const *ptrs, int32_t p,
+                         int32_t root, hipStream_t stream, CallTimer &timer, bool last) {
+  const int64_t blocks = int64_t(tiles) * (kFlattenTile * EB / (kBcastThreads * kBcastVpt *
+                                                                 kVecBytes * bcast_spans<EB>()));
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ddp_broadcast_coalesced: bucket too large");
-  return launch_lds(coalesced_broadcast_kernel<EB>, dim3(static_cast<uint32_t>(blocks)),
-                    dim3(kBcastThreads), residency_lds(DDPSIM_BCAST_WGS_PER_CU), stream, timer,
-                    last, "coalesced_broadcast_kernel launch", desc, tile_map, n_params, ptrs, p,
-                    root);
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  const size_t lds = residency_lds(DDPSIM_BCAST_WGS_PER_CU);
+  const char *what = "coalesced_broadcast_kernel launch";
+  if (int64_t(p - 1) * elems * EB > DDPSIM_BCAST_NT_STORE_BYTES) {
+    return launch_lds(coalesced_broadcast_kernel<EB, true>, grid, dim3(kBcastThreads), lds,
+                      stream, timer, last, what, desc, tile_map, n_params, ptrs, p, root);
+  }
+  return launch_lds(coalesced_broadcast_kernel<EB, false>, grid, dim3(kBcastThreads), lds, stream,
+                    timer, last, what, desc, tile_map, n_params, ptrs, p, root);
 }
 
 }  // namespace
@@ -198,10 +242,10 @@ extern "C" ddp_status ddp_broadcast_coalesced(const ddp_plan *plan, int32_t p,
     const ParamDesc *desc = static_cast<const ParamDesc *>(table) + first;
     const bool fin = b == last;
     switch (eb) {
-      case 1: s = launch_bucket<1>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
-      case 2: s = launch_bucket<2>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
-      case 4: s = launch_bucket<4>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
-      default: s = launch_bucket<8>(desc, tile_map, tiles, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 1: s = launch_bucket<1>(desc, tile_map, tiles, elems, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 2: s = launch_bucket<2>(desc, tile_map, tiles, elems, n_params, ptrs, p, root, stream, timer, fin); break;
+      case 4: s = launch_bucket<4>(desc, tile_map, tiles, elems, n_params, ptrs, p, root, stream, timer, fin); break;
+      default: s = launch_bucket<8>(desc, tile_map, tiles, elems, n_params, ptrs, p, root, stream, timer, fin); break;
     }
     if (s != DDP_OK) return s;
   }

@@ -167,3 +167,33 @@ def test_fused_past_the_infinity_cache(oracle, bf16, p, n):
     want, _ = oracle.ring_allreduce(host, avg="tokens", tokens=tokens, want_log=False)
     for r in range(p):
         assert_bits_equal(got[r], want[r], f"rank {r}")
+
+
+def test_ring_steps_past_the_infinity_cache(oracle):
+    """Rank buffers totalling more than 256 MiB take the ring step's
+    streaming shape (one-wave workgroups, non-temporal accesses): every
+    intermediate state of a ragged n against the oracle's, every element,
+    with a divisor that is not a power of two."""
+    p, n = 5, 14_000_003
+    assert p * n * 4 > 256 << 20
+    host = [W.normal_np(n, 1.0, 950, r) for r in range(p)]
+    bufs = [to_dev(h) for h in host]
+    tokens = tokens_for(p, 6)
+    for s in range(2 * (p - 1)):
+        ddp.ring_allreduce_sim_steps(bufs, s, 1, avg="tokens", tokens=tokens)
+        torch.cuda.synchronize()
+        want, _ = oracle.ring_allreduce(host, avg="tokens", tokens=tokens, max_steps=s + 1,
+                                        want_log=False)
+        for r in range(p):
+            assert_bits_equal(to_host(bufs[r]), want[r], f"step {s} rank {r}")
+
+
+def test_bf16_ring_past_the_infinity_cache(oracle):
+    """The bf16 ring's fp32 workspace rows past 256 MiB: the whole call."""
+    p, n = 8, 9_000_001
+    host = [oracle.f32_to_bf16(W.normal_np(n, 1.0, 960, r)) for r in range(p)]
+    assert p * n * 4 > 256 << 20
+    got, _ = _run(host, "world", None, "ring")
+    want, _ = oracle.ring_allreduce(host, avg="world", want_log=False)
+    for r in range(p):
+        assert_bits_equal(got[r], want[r], f"rank {r}")
