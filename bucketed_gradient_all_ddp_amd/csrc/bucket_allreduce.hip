@@ -9,12 +9,19 @@
 // finalize_backward"). The ring's chunk geometry lives in the bucket's flat
 // index space ("Collective Ops From Scratch", "Ring allreduce in two
 // passes"). Nothing in that arithmetic needs the flat copy to exist: element
-// i of the bucket is element i - offset of some parameter, and its ring
-// chunk is i / C. So the plan cuts each bucket into pieces that lie in one
-// parameter and one chunk (SegDesc), and a workgroup folds a tile of one
-// piece across the p ranks' gradients of that parameter, in ring order
-// starting at the piece's chunk, and writes the result back to all p ranks.
-// HBM traffic 2 p n eb per bucket instead of 6 p n eb.
+// j of parameter i is element offset_i + j of the bucket, and its ring chunk
+// is (offset_i + j) / C. So a workgroup takes a tile of one parameter, folds
+// every element across the p ranks' gradients of that parameter in ring
+// order starting at the element's chunk, and writes the result back to all
+// p ranks. HBM traffic 2 p n eb per bucket instead of 6 p n eb.
+//
+// A tile inside one chunk folds with one rank order for the whole wave. A
+// tile that crosses chunk boundaries (small parameters, small chunks) folds
+// per lane: each lane loads the ranks in the order of the chunk of its
+// vector's first element, and an element whose chunk starts d ranks later
+// skips the first d loads and adds them at the end, which is its own ring
+// order. Tiles are therefore whole parameters cut into 64-vector runs, with
+// no lanes left idle at chunk ends.
 #include <algorithm>
 
 #include "fold.hpp"
@@ -30,8 +37,82 @@ bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t 
 
 namespace {
 
-// One tile of the plan's numbering; the tile map names the piece (index
-// into seg) each tile belongs to.
+// Element j of a parameter at bucket offset `off` is in ring chunk
+// (off + j) / C; j may run past the parameter by a few elements (a clamped
+// lane), which only moves the chunk of results that are never stored.
+__device__ __forceinline__ int32_t chunk_of(int64_t off, int64_t j, int64_t C) {
+  return static_cast<int32_t>((off + j) / C);
+}
+
+// The fold of one lane's vectors when the ranks' order differs between
+// lanes: lane-held rank addresses (lane r holds rank r's, moved back by the
+// alignment shift) are fetched per lane with a cross-lane read. For vector
+// u, c0 is the chunk of its first element and dist[e] how many chunks later
+// element e's chunk starts (0..V-1; it is below p because every chunk index
+// is). Loads run in the order c0, c0+1, ...; element e adds load t only from
+// t = dist[e] on, then loads 0..dist[e]-1 after the last one, so it sums
+// ranks c0+dist[e], ..., c0+dist[e]+p-1 (mod p) left to right: its own
+// ring order.
+template <typename Tr, int RB, bool kNT>
+__device__ __forceinline__ void fold_vector_per_lane(uint64_t mine, int32_t p, int32_t c0,
+                                                     const int32_t (&dist)[Tr::kVec],
+                                                     int64_t vi, bool ok,
+                                                     float (&acc)[Tr::kVec]) {
+  constexpr int V = Tr::kVec;
+  static_assert(RB >= V - 1, "the first batch must hold the loads added last");
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = -0.0f;
+  uint4 keep[V > 1 ? V - 1 : 1];
+  const uint32_t lo = static_cast<uint32_t>(mine);
+  const uint32_t hi = static_cast<uint32_t>(mine >> 32);
+  for (int32_t s0 = 0; s0 < p; s0 += RB) {
+    uint4 x[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const bool live = s0 + j < p;  // wave-uniform
+      x[j] = make_uint4(0, 0, 0, 0);
+      if (live) {
+        const int32_t r = ring_rank(c0, s0 + j, p);
+        // every lane takes part in the cross-lane reads (no divergence here)
+        const uint32_t alo = static_cast<uint32_t>(__shfl(static_cast<int>(lo), r, 64));
+        const uint32_t ahi = static_cast<uint32_t>(__shfl(static_cast<int>(hi), r, 64));
+        const void *src =
+            reinterpret_cast<const void *>((static_cast<uint64_t>(ahi) << 32) | alo);
+        if (ok) x[j] = load_vec<kNT>(src, vi);
+      }
+    }
+    if (s0 == 0) {
+#pragma unroll
+      for (int j = 0; j < V - 1; ++j) keep[j] = x[j];
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int32_t t = s0 + j;
+      if (t < p) {
+        float w[V];
+        Tr::widen(x[j], w);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          if (t >= dist[e]) acc[e] = acc[e] + w[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V - 1; ++j) {
+    if (j < p) {
+      float w[V];
+      Tr::widen(keep[j], w);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (j < dist[e]) acc[e] = acc[e] + w[e];
+      }
+    }
+  }
+}
+
+// One tile of the plan's numbering; the tile map names the parameter
+// descriptor (index into seg) each tile belongs to.
 template <typename Tr, int VPT, int RB, bool kNT>
 __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
                                             const int32_t *__restrict__ tile_seg,
@@ -48,7 +129,6 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
 
   // The vector path needs every rank's copy of this parameter to sit at the
   // same offset from a 16-byte boundary.
-#if DDPSIM_BUCKET_LANEPTR
   // lane r loads rank r's address (p <= 64 = the wave size)
   const int my_lane = tid & 63;
   const uint64_t mine =
@@ -59,22 +139,13 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
       __builtin_amdgcn_readlane(static_cast<uint32_t>(mine), 0) % static_cast<uint32_t>(kVecBytes);
   const bool same =
       phase % kElemBytes == 0 && __all(my_lane >= p || mine % kVecBytes == phase);
-#else
-  const uintptr_t phase =
-      reinterpret_cast<uintptr_t>(grads[d.param]) % static_cast<uintptr_t>(kVecBytes);
-  bool same = phase % kElemBytes == 0;
-  for (int32_t r = 1; r < p; ++r) {
-    same = same && reinterpret_cast<uintptr_t>(grads[static_cast<int64_t>(r) * n_params + d.param]) %
-                       static_cast<uintptr_t>(kVecBytes) == phase;
-  }
-#endif
 
   if (!same) {
     const GradPtrs at{grads, n_params, d.param, 0};
-    const int64_t j0 = d.param_begin + static_cast<int64_t>(t) * kTile;
-    const int64_t j1 = std::min(j0 + kTile, d.param_begin + d.len);
+    const int64_t j0 = static_cast<int64_t>(t) * kTile;
+    const int64_t j1 = std::min(j0 + kTile, d.len);
     for (int64_t j = j0 + tid; j < j1; j += kThr) {
-      const float y = apply_divide(fold_scalar<Tr>(at, p, d.chunk, j), div);
+      const float y = apply_divide(fold_scalar<Tr>(at, p, chunk_of(d.offset, j, d.chunk), j), div);
       for (int32_t r = 0; r < p; ++r) Tr::store1(at(r), j, y);
     }
     return;
@@ -85,14 +156,15 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
   // aligned for every rank.
   const int64_t m = static_cast<int64_t>(phase) / kElemBytes;
   const GradPtrs at{grads, n_params, d.param, m * kElemBytes};
-  const ChunkSpan k = make_span(d.param_begin + m, d.param_begin + d.len + m, V);
+  const ChunkSpan k = make_span(m, d.len + m, V);
 
   if (t == 0 && tid >= kThr - 2 * (V - 1)) {
     const int lane = tid - (kThr - 2 * (V - 1));
     const bool head = lane < V - 1;
     const int64_t J = head ? k.s + lane : k.tail_begin + (lane - (V - 1));
     if (J < (head ? k.head_end : k.e)) {
-      const float y = apply_divide(fold_scalar<Tr>(at, p, d.chunk, J), div);
+      const float y =
+          apply_divide(fold_scalar<Tr>(at, p, chunk_of(d.offset, J - m, d.chunk), J), div);
       for (int32_t r = 0; r < p; ++r) Tr::store1(at(r), J, y);
     }
   }
@@ -108,13 +180,36 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
     ok[u] = jj < nv;
     vi[u] = k.vs / V + jj;
   }
+  const uint64_t shifted = mine - static_cast<uint64_t>(m * kElemBytes);
+  const LanePtrs lat{shifted};
+  // chunks of the tile's first and last element (wave-uniform)
+  const int64_t last_v = k.vs / V + std::min(base + int64_t(kThr) * VPT, nv) - 1;
+  const int32_t c_first = chunk_of(d.offset, k.vs + base * V - m, d.chunk);
+  const int32_t c_last = chunk_of(d.offset, last_v * V + V - 1 - m, d.chunk);
   float acc[VPT][V];
-#if DDPSIM_BUCKET_LANEPTR
-  const LanePtrs lat{mine - static_cast<uint64_t>(m * kElemBytes)};
-#else
-  const GradPtrs &lat = at;
-#endif
-  fold_vectors<Tr, VPT, RB, kNT>(lat, p, d.chunk, vi, ok, acc);
+  if (c_first == c_last) {
+    fold_vectors<Tr, VPT, RB, kNT>(lat, p, c_first, vi, ok, acc);
+  } else {
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      // a lane past the body computes with the last vector (never stored)
+      const int64_t v = ok[u] ? vi[u] : last_v;
+      const int64_t j0 = v * V - m;
+      const int32_t c0 = chunk_of(d.offset, j0, d.chunk);
+      int32_t dist[V];
+      int64_t next = (static_cast<int64_t>(c0) + 1) * d.chunk - d.offset;  // next chunk's first j
+      int32_t dd = 0;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        while (j0 + e >= next) {
+          ++dd;
+          next += d.chunk;
+        }
+        dist[e] = dd;
+      }
+      fold_vector_per_lane<Tr, RB, kNT>(shifted, p, c0, dist, vi[u], ok[u], acc[u]);
+    }
+  }
   uint4 y[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -123,8 +218,8 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
     y[u] = Tr::narrow(acc[u]);
   }
   const int32_t rot = store_rotation(p, tile);
-  for (int32_t k = 0; k < p; ++k) {
-    void *dst = lat(ring_rank(rot, k, p));
+  for (int32_t r = 0; r < p; ++r) {
+    void *dst = lat(ring_rank(rot, r, p));
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);

@@ -50,15 +50,16 @@ static_assert(sizeof(ParamDesc) == 32, "ParamDesc layout");
 
 constexpr int kFlattenTile = 4096;  // elements per flatten workgroup
 
-// One piece of a bucket for the in-place bucket all-reduce: the part of one
-// parameter that falls in one ring chunk of the bucket (32 bytes).
+// One parameter of a bucket as the in-place bucket all-reduce reads it
+// (32 bytes): where the parameter sits in the bucket's flat index space and
+// the ring chunk size of that bucket, so that element j of the parameter is
+// in ring chunk (offset + j) / chunk.
 struct SegDesc {
-  int64_t param_begin;  // first element of the piece inside the parameter
-  int64_t len;          // elements
-  int32_t param;        // registration index
-  int32_t chunk;        // ring chunk of the bucket holding every element
-  int32_t tile_begin;   // first tile of the piece within its bucket
-  int32_t reserved;
+  int64_t offset;      // element offset of the parameter in its bucket
+  int64_t len;         // elements of the parameter
+  int64_t chunk;       // ring chunk size C = ceil(n_b / p) of the bucket
+  int32_t param;       // registration index
+  int32_t tile_begin;  // first tile of the parameter (plan-wide numbering)
 };
 static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 
@@ -71,9 +72,6 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #ifndef DDPSIM_BUCKET_MAX_WORKGROUPS
 #define DDPSIM_BUCKET_MAX_WORKGROUPS 0  // 0: one workgroup per tile
 #endif
-#ifndef DDPSIM_BUCKET_LANEPTR
-#define DDPSIM_BUCKET_LANEPTR 1  // rank addresses: one vector load + readlane
-#endif
 #ifndef DDPSIM_BUCKET_THREADS
 #define DDPSIM_BUCKET_THREADS 64  // threads per workgroup (one wave)
 #endif
@@ -82,7 +80,10 @@ static_assert(sizeof(SegDesc) == 32, "SegDesc layout");
 #endif
 constexpr int kBucketVpt = DDPSIM_BUCKET_VPT;
 constexpr int kBucketThreads = DDPSIM_BUCKET_THREADS;
-constexpr int kBucketRb = 8;
+#ifndef DDPSIM_BUCKET_RB
+#define DDPSIM_BUCKET_RB 8  // rank loads issued before their additions
+#endif
+constexpr int kBucketRb = DDPSIM_BUCKET_RB;
 constexpr bool kBucketNt = DDPSIM_BUCKET_NT != 0;
 
 // elements per tile for a dtype whose 16-byte vector holds `vec` elements

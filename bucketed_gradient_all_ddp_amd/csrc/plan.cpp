@@ -38,8 +38,8 @@ struct ddp_plan {
   std::vector<unsigned char> staged;
   void *d_table = nullptr;
   bool uploaded = false;
-  // in-place bucket all-reduce: pieces of (parameter x ring chunk), for
-  // seg_p ranks
+  // in-place bucket all-reduce: one descriptor per parameter with elements
+  // and the chunk size of its bucket for seg_p ranks
   int32_t seg_p = 0;
   std::vector<SegDesc> seg;
   std::vector<int32_t> seg_first, seg_count, seg_tiles, seg_tile_first;
@@ -108,10 +108,12 @@ bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t 
   return true;
 }
 
-// Cut every bucket into pieces that lie in one parameter and one ring chunk
-// (chunks of ceil(n_b / p) elements of the bucket's flat index space). Tiles
-// are numbered across the whole plan, bucket after bucket, so one launch can
-// cover a run of consecutive buckets.
+// One descriptor per parameter with elements, bucket after bucket, carrying
+// its offset in the bucket's flat index space and the bucket's ring chunk
+// size ceil(n_b / p); each parameter is cut into tiles of bucket_tile_elems
+// elements (a tile may cross ring chunks: every lane finds the chunk of its
+// own elements). Tiles are numbered across the whole plan, bucket after
+// bucket, so one launch can cover a run of consecutive buckets.
 static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc> *seg,
                            std::vector<int32_t> *first, std::vector<int32_t> *count,
                            std::vector<int32_t> *tiles, std::vector<int32_t> *tile_first,
@@ -125,28 +127,21 @@ static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc>
     const int64_t nb = plan->bucket_elems[b];
     const int64_t C = nb > 0 ? ceil_div(nb, p) : 1;
     for (int32_t i : plan->members[b]) {
-      const int64_t o = plan->offset[i];
-      const int64_t end = o + plan->numel[i];
-      for (int64_t pos = o; pos < end;) {
-        const int64_t c = pos / C;
-        const int64_t piece_end = std::min(end, (c + 1) * C);
-        SegDesc d;
-        std::memset(&d, 0, sizeof d);
-        d.param_begin = pos - o;
-        d.len = piece_end - pos;
-        d.param = i;
-        d.chunk = static_cast<int32_t>(c);
-        d.tile_begin = static_cast<int32_t>(t);
-        const int64_t nt = std::max<int64_t>(1, ceil_div(d.len, tile_elems));
-        t += nt;
-        if (t > INT32_MAX) return false;
-        tile_seg->insert(tile_seg->end(), static_cast<size_t>(nt),
-                         static_cast<int32_t>(seg->size()));
-        seg->push_back(d);
-        pos = piece_end;
-      }
+      if (plan->numel[i] == 0) continue;
+      SegDesc d;
+      std::memset(&d, 0, sizeof d);
+      d.offset = plan->offset[i];
+      d.len = plan->numel[i];
+      d.chunk = C;
+      d.param = i;
+      d.tile_begin = static_cast<int32_t>(t);
+      const int64_t nt = ceil_div(d.len, tile_elems);
+      t += nt;
+      if (t > INT32_MAX) return false;
+      tile_seg->insert(tile_seg->end(), static_cast<size_t>(nt),
+                       static_cast<int32_t>(seg->size()));
+      seg->push_back(d);
     }
-    if (t > INT32_MAX) return false;
     count->push_back(static_cast<int32_t>(seg->size()) - first->back());
     tiles->push_back(static_cast<int32_t>(t - t0));
   }

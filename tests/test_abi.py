@@ -166,19 +166,18 @@ def test_collective_argument_errors():
 
 
 def test_segment_table_sizes():
-    """The piece table holds 32 bytes per piece of (parameter x ring chunk) --
-    at least one per non-empty parameter, at most that plus p - 1 per
-    bucket -- and 4 bytes per tile (at least one tile per piece)."""
+    """The in-place all-reduce's table holds 32 bytes per parameter with
+    elements, then 4 bytes per tile of 256 fp32 (512 bf16) elements of each
+    such parameter; its size does not depend on p (only the chunk size
+    inside each descriptor does)."""
     sizes = [5000, 0, 7, 4096, 4097, 1, 33_333, 12, 0, 65_545]
-    plan = ddp.ddp_bucket_plan(sizes, 4, 96 * 1024, 8 * 1024)
     nonzero = sum(1 for s in sizes if s)
-    for p in (1, 2, 3, 8, 64):
-        nbytes = plan.segment_bytes(p)
-        assert nbytes % 4 == 0
-        assert 36 * nonzero <= nbytes
-        assert nbytes <= 36 * (nonzero + plan.num_buckets * (p - 1)) + 4 * sum(sizes)
-    assert plan.segment_bytes(2) >= plan.segment_bytes(1)
-    assert plan.segment_bytes(0) == 0 and plan.segment_bytes(65) == 0
+    for eb, tile in ((4, 256), (2, 512)):
+        plan = ddp.ddp_bucket_plan(sizes, eb, 96 * 1024, 8 * 1024)
+        want = 32 * nonzero + 4 * sum(-(-s // tile) for s in sizes)
+        for p in (1, 2, 3, 8, 64):
+            assert plan.segment_bytes(p) == want
+        assert plan.segment_bytes(0) == 0 and plan.segment_bytes(65) == 0
 
 
 def test_bucket_allreduce_argument_errors():

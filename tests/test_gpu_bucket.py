@@ -190,3 +190,71 @@ def test_plan_of_zero_size_parameters_launches_nothing():
     ddp.ddp_flatten(plan, 0, table, flats)
     ddp.ddp_unflatten(plan, 0, flats, table)
     torch.cuda.synchronize()
+
+
+TINY = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 64, 65, 127, 200, 255, 256, 257, 300, 513,
+        1000, 1023, 4097]
+
+
+@pytest.mark.parametrize("layout", ["aligned", "odd", "mixed"])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("p", [3, 7, 64])
+def test_tiles_across_chunks_per_tensor_plan(oracle, p, bf16, layout):
+    """Every tensor its own bucket (caps of 0 bytes), tensors of 1..4097
+    elements: ring chunks of 1..65 elements, so one 16-byte vector spans up
+    to 4 (fp32) or 8 (bf16) chunks and one tile many; each element must
+    still be folded from its own chunk's first rank."""
+    eb = 2 if bf16 else 4
+    plan = ddp.ddp_bucket_plan(TINY, eb, 0, 0).upload_segments(p)
+    assert plan.num_buckets == len(TINY)
+    host, grads = make_grads(p, TINY, 1400 + p, bf16, oracle, layout)
+    table = ddp.grad_pointer_table(grads)
+    tokens = tokens_for(p, 9)
+    ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg="tokens", tokens=tokens)
+    torch.cuda.synchronize()
+    want = _oracle_sync(oracle, host, TINY, eb, 0, 0, "tokens", tokens)
+    for r in range(p):
+        for i in range(len(TINY)):
+            assert_bits_equal(to_host(grads[r][i]), want[r][i], f"rank {r} tensor {i}")
+
+
+@pytest.mark.parametrize("pattern", ["late", "early"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_tiles_across_chunks_order_probe(oracle, bf16, pattern):
+    """Cancellation probes inside tiles that cross chunk ends. Element j of
+    chunk c gets 2^24, 1 and -2^24 on ranks c, c+1, c+2 ("late"): folded from
+    rank c, 2^24 + 1 ties to 2^24 and the sum is 0; from rank c+1 or c+2 it
+    is 1. Or 1, 2^24 and -2^24 on ranks c-1, c, c+1 ("early"): from rank c
+    the sum is 1; from rank c-1 it is 0. All values are exact in bf16, and
+    0 and 1 survive the final rounding."""
+    p = 5
+    sizes = [23, 41, 7]  # chunks of 5, 9 and 2 elements: vectors cross chunk ends
+    eb = 2 if bf16 else 4
+    plan = ddp.ddp_bucket_plan(sizes, eb, 0, 0).upload_segments(p)
+    big = np.float32(2.0 ** 24)
+    put = ({0: big, 1: np.float32(1.0), 2: -big} if pattern == "late"
+           else {p - 1: np.float32(1.0), 0: big, 1: -big})
+    expect = np.float32(0.0 if pattern == "late" else 1.0)
+    host = []
+    for r in range(p):
+        rank = []
+        for n in sizes:
+            C = -(-n // p)
+            a = np.zeros(n, dtype=np.float32)
+            for j in range(n):
+                a[j] = put.get((r - j // C) % p, np.float32(0.0))
+            rank.append(oracle.f32_to_bf16(a) if bf16 else a)
+        host.append(rank)
+    from helpers import to_dev
+    grads = [[to_dev(h) for h in rank] for rank in host]
+    table = ddp.grad_pointer_table(grads)
+    ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg="none")
+    torch.cuda.synchronize()
+    want = _oracle_sync(oracle, host, sizes, eb, 0, 0, "none", None)
+    for r in range(p):
+        for i, n in enumerate(sizes):
+            got = to_host(grads[r][i])
+            assert_bits_equal(got, want[r][i], f"rank {r} tensor {i}")
+            ref = np.full(n, expect, dtype=np.float32)
+            assert_bits_equal(got, oracle.f32_to_bf16(ref) if bf16 else ref,
+                              f"probe rank {r} tensor {i}")
