@@ -40,25 +40,27 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "all-reduce bus GB/s + % HBM peak, p=8 sim ranks, 124M fp32 grads"
 
-# Device-memory traffic per launch of a kernel, from the two rocprofv3 --pmc
-# passes (FETCH_SIZE, WRITE_SIZE; scaled by a 1 GiB copy) summarised in
-# profiles/. A figure is used only while the kernel's sources hash to the
-# value it was measured with; after any change it is reported as null until
-# the counters are taken again.
+# Device-memory traffic per launch of a kernel: the DRAM-side request counters
+# of a rocprofv3 --pmc pass (TCC_EA0_RDREQ_DRAM_32B_sum and
+# TCC_EA0_WRREQ_WRITE_DRAM_32B_sum, 32-byte units, read + write), which read
+# back a plain 1 GiB copy exactly (no scale factor), summarised in profiles/.
+# A figure is used only while the kernel's sources hash to the value it was
+# measured with; after any change it is reported as null until the counters
+# are taken again.
 CSRC = os.path.join(ROOT, "bucketed_gradient_all_ddp_amd", "csrc")
 KERNEL_SOURCES = {
     # the kernel, the headers it includes, and the host code that shapes its
-    # launch (residency bound) and builds the piece table and tile map it reads
+    # launch (residency bound) and builds the descriptor table and tile map it reads
     "bucket_allreduce_kernel": ["bucket_allreduce.hip", "fold.hpp", "internal.hpp",
                                 "host.cpp", "plan.cpp"],
     "fused_allreduce_kernel": ["allreduce.hip", "fold.hpp", "internal.hpp", "host.cpp"],
 }
 MEASURED_TRAFFIC = {
-    # profiles/bucket_allreduce_gpt2_p8_pmc_traffic.md: the headline launch
-    # (all 13 buckets in one dispatch)
+    # profiles/bucket_allreduce_gpt2_p8.md: the headline launch (all 13
+    # buckets in one dispatch), 3,997,874,283 read + 3,982,212,651 written
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7995560127,
-        "sources_sha256": "3f433f4134fd9cfeedca0660a1bbad7e15d2f6c17e232d42c7342905305281d7",
+        "bytes_per_launch": 7980086934,
+        "sources_sha256": "c3ab31572d7806fc3e4ee6106ec504386d295339da41f370c651589ddee25342",
     },
 }
 
@@ -114,6 +116,9 @@ def parse():
                          "line for the record")
     ap.add_argument("--tokens", type=int, default=2048,
                     help="tokens per synthetic backward GEMM (overlap workload)")
+    ap.add_argument("--no-per-tensor-loop", action="store_true",
+                    help="latency workload: skip the 20,000 per-tensor launches (loop and "
+                         "graph replay), e.g. under a counter profiler")
     ap.add_argument("--comm-workgroups", type=str, default="0,256,1024,4096",
                     help="overlap workload: caps on the reducer's all-reduce workgroups "
                          "to time (0 = one per tile)")
@@ -455,26 +460,28 @@ def bench_latency(torch, ddp, W, dev, args):
         for bufs in per_tensor:
             ddp.ring_allreduce_sim(bufs, avg="world")
 
-    tensor_step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    tensor_step()
-    torch.cuda.synchronize()
-    host_ms = (time.perf_counter() - t0) * 1e3
-    # the same 20,000 launches replayed from a captured HIP graph
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    host_ms = graph_ms = float("nan")
+    if not args.no_per_tensor_loop:
         tensor_step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         tensor_step()
-    g.replay()
-    torch.cuda.synchronize()
-    graph_ms = _events_ms(torch, g.replay, 3)
-    del g
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        # the same 20,000 launches replayed from a captured HIP graph
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            tensor_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            tensor_step()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_ms = _events_ms(torch, g.replay, 3)
+        del g
     plan = ddp.ddp_bucket_plan(sizes, 4, W.BUCKET_CAP_BYTES, W.FIRST_BUCKET_CAP_BYTES)
     plan.upload_segments(p, dev)
     table = ddp.grad_pointer_table(grads, dev)
