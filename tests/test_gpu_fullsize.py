@@ -175,7 +175,18 @@ def test_llama7b_bf16_sampled(oracle):
         flat = _samples(plan.bucket_numel(b), p, 256, rng)
         ai = index.arena_index(b, flat)
         picks.append((b, flat, ai, _gather(arenas, ai)))
-    _say("llama7b: samples taken; all-reducing 226 buckets")
+    # whole buckets, every element: both 262 MB buckets (the head, filled
+    # first, and the embedding, filled last), the 90 MB bucket of four
+    # parameters that mixes the RMSNorm weights with a projection, and a
+    # 33.5 MB attention bucket
+    whole_buckets = (0, 1, 4, plan.num_buckets - 1)
+    assert [plan.bucket_numel(b) * 2 for b in (0, 1, 4)] == [262_144_000, 90_202_112, 33_554_432]
+    whole = {}
+    for b in whole_buckets:
+        whole[b] = [oracle.flatten(_host_params(grads[r], oplan.bucket_params(b)), oplan, b)
+                    for r in range(p)]
+    _say("llama7b: samples and %d whole buckets taken; all-reducing 226 buckets"
+         % len(whole_buckets))
     # the first half as one launch (the batched form the benchmark also
     # times), the rest one launch per bucket
     half = plan.num_buckets // 2
@@ -193,8 +204,33 @@ def test_llama7b_bf16_sampled(oracle):
         y = oracle.bf16_to_f32(want).astype(np.float64)
         scale = np.abs(oracle.bf16_to_f32(vals)).astype(np.float64).sum(1) / p
         assert np.all(np.abs(y - s) <= 1e-2 * np.abs(s) + (p - 1) * 2.0 ** -24 * scale + 1e-45)
+    for b in whole_buckets:
+        want, _ = oracle.ring_allreduce(whole[b], avg="world", want_log=False)
+        for r in range(p):
+            got = oracle.flatten(_host_params(grads[r], oplan.bucket_params(b)), oplan, b)
+            assert_bits_equal(got, want[r], f"whole bucket {b} rank {r}")
+        # the stated bound against an fp64 sum, norm-wise per bucket
+        s = np.zeros(want[0].size, dtype=np.float64)
+        for r in range(p):
+            s += oracle.bf16_to_f32(whole[b][r])
+        s /= p
+        y = oracle.bf16_to_f32(want[0]).astype(np.float64)
+        assert np.linalg.norm(y - s) <= 1e-2 * np.linalg.norm(s)
+        _say("llama7b: whole bucket %d (%d elements x %d ranks) matches" % (b, want[0].size, p))
+        del want, s, y
+        whole[b] = None
     del arenas, grads
     _free()
+
+
+def _host_params(rank_grads, params):
+    """One rank's gradients of `params` on the host (bf16 as uint16 bit
+    patterns), indexed by parameter, None elsewhere: the oracle's flatten
+    input."""
+    out = [None] * len(rank_grads)
+    for i in params:
+        out[i] = to_host(rank_grads[i])
+    return out
 
 
 def test_latency_regime_per_tensor_and_bucketed(oracle):
