@@ -312,6 +312,12 @@ def test_cost_model_shape_p64_2gib(oracle):
     idx = _samples(n, p, 4096, rng)
     vals = _gather(bufs, idx)
 
+    # a whole window across the end of chunk 31 and the start of chunk 32,
+    # every element
+    lo = 32 * C - (1 << 19)
+    window = np.arange(lo, lo + (1 << 20), dtype=np.int64)
+    wvals = np.stack([to_host(b[lo:lo + (1 << 20)]) for b in bufs], axis=1)
+
     # token-weighted all-reduce, fused
     _say("cost-model shape: all-reduce of 64 x 2 GiB")
     ddp.ring_allreduce_sim(bufs, avg="tokens", tokens=tokens)
@@ -320,6 +326,13 @@ def test_cost_model_shape_p64_2gib(oracle):
     got = _gather(bufs, idx)
     for r in range(p):
         assert_bits_equal(got[:, r], want, f"all-reduce rank {r}")
+    want = oracle.allreduce_at(wvals, window, n, avg="tokens", tokens=tokens)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r][lo:lo + (1 << 20)]), want, f"window rank {r}")
+    # every element of every rank: all ranks hold the same bits afterwards
+    for r in range(1, p):
+        assert torch.equal(bufs[r].view(torch.int32), bufs[0].view(torch.int32)), f"rank {r}"
+    del wvals
 
     # standalone reduce-scatter (pre-rotated), on fresh values
     for r in range(p):
