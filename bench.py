@@ -111,7 +111,7 @@ def parse():
     ap.add_argument("--workload", default="gpt2-small-p8",
                     choices=["gpt2-small-p8", "ragged-ring-p4", "llama7b-bf16-p8",
                              "latency-p64", "cost-model-p64", "overlap-gpt2-p8",
-                             "crossover-p4", "sync-gpt2-p8", "collectives-p8"],
+                             "crossover-p4", "sync-gpt2-p8", "collectives-p8", "ceilings"],
                     help="the default is the headline; the others print their own "
                          "line for the record")
     ap.add_argument("--tokens", type=int, default=2048,
@@ -948,6 +948,61 @@ def bench_sync(torch, ddp, W, dev, args):
                                 "kernel_us_per_forward": round(bdms * 1e3, 2)}})
 
 
+def bench_ceilings(torch, ddp, W, dev, args):
+    """Device-memory ceilings by access pattern, measured with the library's
+    own kernels (and torch's fill for a single write stream): how much a
+    kernel's speed depends on how many buffers each wave reads and writes at
+    the same offset. A copy is broadcast_sim between 2 ranks; 1 read to p-1
+    writes is broadcast_sim at p; p reads to 1 write is reduce_scatter_sim;
+    2 reads to 1 write and 1 to 1 are the ring's steps; p to p is the fused
+    all-reduce."""
+    rows = {}
+
+    def timed_ms(fn, reps):
+        fn()
+        _, dms = _timed_calls(torch, ddp, [fn], reps)
+        return dms
+
+    for p, mib in ((2, 1024), (8, 1024), (64, 128)):
+        n = mib * (1 << 20) // 4
+        bufs = [torch.full((n,), float(r), device=dev) for r in range(p)]
+        S = n * 4
+        ms = timed_ms(lambda: ddp.broadcast_sim(bufs, src=0), args.steps)
+        rows[f"broadcast_sim p={p}, {mib} MiB per rank: 1 read, {p - 1} writes"] = p * S / ms / 1e6
+        outs = [torch.empty(n // p, device=dev) for _ in range(p)]
+        ms = timed_ms(lambda: ddp.reduce_scatter_sim(bufs, outs), args.steps)
+        rows[f"reduce_scatter_sim p={p}: {p} reads, 1 write"] = (p + 1) * S / ms / 1e6
+        ms = timed_ms(lambda: ddp.ring_allreduce_sim(bufs, avg="world"), args.steps)
+        rows[f"ring_allreduce_sim fused p={p}: {p} reads, {p} writes"] = 2 * p * S / ms / 1e6
+        if p == 8:
+            rs = [lambda: ddp.ring_allreduce_sim_steps(bufs, 0, 1, avg="world")]
+            ms = timed_ms(rs[0], args.steps)
+            rows["ring reduce-scatter step p=8: 2 reads, 1 write"] = 3 * S / ms / 1e6
+            ag = [lambda: ddp.ring_allreduce_sim_steps(bufs, p - 1, 1, avg="world")]
+            ms = timed_ms(ag[0], args.steps)
+            rows["ring all-gather step p=8: 1 read, 1 write"] = 2 * S / ms / 1e6
+        del bufs, outs
+        torch.cuda.empty_cache()
+    a = torch.empty(1 << 28, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        a.fill_(2.0)
+    e1.record()
+    torch.cuda.synchronize()
+    rows["torch fill_ of 1 GiB: 1 write"] = (1 << 30) / (e0.elapsed_time(e1) / args.steps) / 1e6
+    del a
+    _line("device-memory GB/s by access pattern (library kernels)",
+          rows["broadcast_sim p=2, 1024 MiB per rank: 1 read, 1 writes"], "GB/s",
+          "ceilings: the library's copy, fan-out, fan-in, ring-step and fused kernels on 2, 8 "
+          "and 64 ranks of 1 GiB / 1 GiB / 128 MiB, and a single-stream fill",
+          {"GBps": {k: round(v, 1) for k, v in rows.items()},
+           "frac_of_8TBps": {k: round(v / HBM_PEAK_GBPS, 4) for k, v in rows.items()}})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -968,7 +1023,7 @@ def main():
              "latency-p64": bench_latency, "cost-model-p64": bench_costmodel,
              "collectives-p8": bench_collectives_p8,
              "overlap-gpt2-p8": bench_overlap, "crossover-p4": bench_crossover,
-             "sync-gpt2-p8": bench_sync}
+             "sync-gpt2-p8": bench_sync, "ceilings": bench_ceilings}
     if args.workload in other:
         log(f"workload {args.workload}")
         other[args.workload](torch, ddp, W, dev, args)

@@ -265,7 +265,7 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
     const int64_t bn = int64_t(tpcn) * p;
     if (bn > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
     const dim3 gridn(static_cast<uint32_t>(bn));
-    const size_t lds = residency_lds(DDPSIM_FUSED_NT_WGS_PER_CU);
+    const size_t lds = residency_lds(fold_residency(DDPSIM_FUSED_NT_WGS_PER_CU, p));
     if (dtype == DDP_F32) {
       return launch_lds(fused_allreduce_kernel<F32Traits, 1, kFusedRb, true, kFusedNtThreads>,
                         gridn, dim3(kFusedNtThreads), lds, stream, timer, true, kname, tab, p, n,

@@ -318,7 +318,7 @@ ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t
   // every HBM channel than it keeps rows open. Bounding residency at 11 per
   // CU raised the GPT-2 p=8 launch from 5.76 to 6.05 TB/s and the Llama bf16
   // buckets by 3-4%; 6 per CU starved the channels (5.2).
-  const size_t lds = residency_lds(DDPSIM_BUCKET_WGS_PER_CU);
+  const size_t lds = residency_lds(fold_residency(DDPSIM_BUCKET_WGS_PER_CU, p));
   if (dtype == DDP_F32) {
     return launch_lds(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                       dim3(kBucketThreads), lds, stream, timer, true,

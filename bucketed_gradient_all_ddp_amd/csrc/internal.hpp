@@ -128,6 +128,12 @@ RankTable make_table(const void *const *bufs, int32_t p);
 // so that fewer streams compete for each memory channel's open rows.
 size_t residency_lds(int32_t wgs);
 
+// The residency bound of a fold kernel whose waves each read p ranks: `wgs`
+// workgroups per CU (tuned at 8 ranks and more), scaled up for fewer ranks
+// so that each CU keeps as many bytes in flight (one 1 KiB load per rank
+// per wave): wgs * 8 / p, rounded up.
+int32_t fold_residency(int32_t wgs, int32_t p);
+
 // ddp_allreduce_buckets with an optional cap on its workgroups (0: one per
 // tile). Defined in bucket_allreduce.hip; the reducer uses the cap.
 ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t n_buckets,

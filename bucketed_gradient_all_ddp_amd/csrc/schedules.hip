@@ -438,7 +438,7 @@ ddp_status launch_tree_q(const RankTable &tab, int32_t p, int64_t n, const Divid
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "allreduce_sim: n too large");
   const dim3 grid(static_cast<uint32_t>(blocks));
   const char *what = "tree_allreduce_kernel launch";
-  const size_t lds = residency_lds(DDPSIM_TREE_WGS_PER_CU);
+  const size_t lds = residency_lds(fold_residency(DDPSIM_TREE_WGS_PER_CU, p));
   if (nt) {
     return launch_lds(tree_allreduce_kernel<Tr, Q, kHalvingFirst, true>, grid, dim3(kTreeThreads),
                       lds, stream, timer, true, what, tab, p, n, div);

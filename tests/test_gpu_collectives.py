@@ -88,3 +88,49 @@ def test_rs_then_ag_equals_allreduce_on_integers(oracle):
     torch.cuda.synchronize()
     for r in range(p):
         assert_bits_equal(to_host(outs[r]), to_host(ar[r]))
+
+
+@pytest.mark.parametrize("op", ["broadcast", "allgather_in_place"])
+def test_two_rank_copies_past_the_infinity_cache(oracle, op):
+    """Two ranks of 150 Mi elements (600 MB each): the copy whose every
+    source byte goes to one destination, which streams both its loads and its
+    stores, against the oracle (the broadcast with a tail of 8 bytes past the
+    last 16-byte vector; the all-gather's shards whole vectors)."""
+    p, n = 2, 150 * (1 << 20) + (6 if op == "broadcast" else 8)
+    host = _vals(p, n, 650, False, oracle)
+    if op == "broadcast":
+        bufs = [to_dev(h) for h in host]
+        ddp.broadcast_sim(bufs, src=1)
+        torch.cuda.synchronize()
+        want, _ = oracle.broadcast(host, 1)
+    else:
+        C = n // p
+        shards = [h[r * C:(r + 1) * C] for r, h in enumerate(host)]
+        bufs = [to_dev(h) for h in host]
+        ddp.allgather_sim([bufs[r][r * C:(r + 1) * C] for r in range(p)], bufs)
+        torch.cuda.synchronize()
+        want, _ = oracle.allgather(shards)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r]), want[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("p", [2, 3, 5])
+def test_few_ranks_past_the_infinity_cache(oracle, p):
+    """Fewer than 8 ranks of large buffers: the fused all-reduce and the
+    reduce-scatter take a residency bound scaled by the rank count; every
+    element against the oracle."""
+    C = (300 << 20) // (4 * p) // 4 * 4 + 4
+    n = p * C
+    host = _vals(p, n, 660 + p, False, oracle)
+    tokens = tokens_for(p, 2)
+    ins = [to_dev(h) for h in host]
+    outs = [torch.empty(C, device="cuda") for _ in range(p)]
+    ddp.reduce_scatter_sim(ins, outs, avg="tokens", tokens=tokens)
+    ddp.ring_allreduce_sim(ins, avg="tokens", tokens=tokens)
+    torch.cuda.synchronize()
+    want, _ = oracle.reduce_scatter(host, avg="tokens", tokens=tokens)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"reduce-scatter rank {r}")
+    want, _ = oracle.ring_allreduce(host, avg="tokens", tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(to_host(ins[r]), want[r], f"all-reduce rank {r}")
