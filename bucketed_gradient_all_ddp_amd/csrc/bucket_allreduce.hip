@@ -29,7 +29,7 @@
 
 namespace ddpsim {
 int32_t plan_num_buckets(const ddp_plan *plan);
-const int32_t *plan_tile_map(const ddp_plan *plan);
+const int32_t *plan_tile_map(const ddp_plan *plan, int64_t *stride);
 bool plan_segment_info(const ddp_plan *plan, int32_t b, int32_t *first, int32_t *count,
                        int32_t *tiles, int32_t *tile_first, int64_t *elems,
                        const void **table, int32_t *seg_p, int32_t *n_params,
@@ -116,12 +116,12 @@ __device__ __forceinline__ void fold_vector_per_lane(uint64_t mine, int32_t p, i
 template <typename Tr, int VPT, int RB, bool kNT>
 __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
                                             const int32_t *__restrict__ tile_seg,
-                                            int32_t tile, int32_t n_params,
+                                            int64_t map_stride, int32_t tile, int32_t n_params,
                                             const void *const *__restrict__ grads, int32_t p,
                                             const Divide &div) {
   constexpr int V = Tr::kVec;
   constexpr int64_t kElemBytes = sizeof(typename Tr::elem);
-  const SegDesc d = seg[tile_seg[tile]];
+  const SegDesc d = seg[tile_seg[tile_map_index(tile, map_stride)]];
   const int32_t t = tile - d.tile_begin;
   const int tid = static_cast<int>(threadIdx.x);
   constexpr int kThr = kBucketThreads;
@@ -233,12 +233,13 @@ __device__ __forceinline__ void bucket_tile(const SegDesc *__restrict__ seg,
 // all-reduce leaves compute units to kernels running beside it.
 template <typename Tr, int VPT, int RB, bool kNT>
 __global__ __launch_bounds__(kBucketThreads) void bucket_allreduce_kernel(
-    const SegDesc *__restrict__ seg, const int32_t *__restrict__ tile_seg,
+    const SegDesc *__restrict__ seg, const int32_t *__restrict__ tile_seg, int64_t map_stride,
     int32_t tile_base, int32_t n_tiles, int32_t n_params,
     const void *const *__restrict__ grads, int32_t p, Divide div) {
   for (int32_t w = static_cast<int32_t>(blockIdx.x); w < n_tiles;
        w += static_cast<int32_t>(gridDim.x)) {
-    bucket_tile<Tr, VPT, RB, kNT>(seg, tile_seg, tile_base + w, n_params, grads, p, div);
+    bucket_tile<Tr, VPT, RB, kNT>(seg, tile_seg, map_stride, tile_base + w, n_params, grads, p,
+                                  div);
   }
 }
 
@@ -309,7 +310,8 @@ ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t
   (void)seg0;
   (void)nseg;
   const SegDesc *seg = static_cast<const SegDesc *>(table);
-  const int32_t *tile_seg = plan_tile_map(plan);
+  int64_t map_stride = 0;
+  const int32_t *tile_seg = plan_tile_map(plan, &map_stride);
   const void *const *grads = d_grad_ptrs;
   const int32_t blocks = max_workgroups > 0 ? std::min(tiles, max_workgroups) : tiles;
   const dim3 grid(static_cast<uint32_t>(blocks));
@@ -322,12 +324,12 @@ ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t
   if (dtype == DDP_F32) {
     return launch_lds(bucket_allreduce_kernel<F32Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                       dim3(kBucketThreads), lds, stream, timer, true,
-                      "bucket_allreduce_kernel launch", seg, tile_seg, tile0, tiles, n_params,
+                      "bucket_allreduce_kernel launch", seg, tile_seg, map_stride, tile0, tiles, n_params,
                       grads, p, div);
   }
   return launch_lds(bucket_allreduce_kernel<BF16Traits, kBucketVpt, kBucketRb, kBucketNt>, grid,
                     dim3(kBucketThreads), lds, stream, timer, true,
-                    "bucket_allreduce_kernel launch", seg, tile_seg, tile0, tiles, n_params, grads,
+                    "bucket_allreduce_kernel launch", seg, tile_seg, map_stride, tile0, tiles, n_params, grads,
                     p, div);
 }
 

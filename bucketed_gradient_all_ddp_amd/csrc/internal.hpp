@@ -86,6 +86,16 @@ constexpr int kBucketThreads = DDPSIM_BUCKET_THREADS;
 constexpr int kBucketRb = DDPSIM_BUCKET_RB;
 constexpr bool kBucketNt = DDPSIM_BUCKET_NT != 0;
 
+// The in-place kernel's tile -> descriptor map is stored grouped by tile
+// mod kXcds: entry for tile t at (t % kXcds) * stride + t / kXcds, stride =
+// ceil(tiles / kXcds). Consecutive workgroups of a launch run on
+// consecutive XCDs, so each XCD reads one contiguous eighth of the map
+// instead of every cache line of it.
+constexpr int32_t kXcds = 8;
+__host__ __device__ constexpr int64_t tile_map_index(int64_t t, int64_t stride) {
+  return (t % kXcds) * stride + t / kXcds;
+}
+
 // elements per tile for a dtype whose 16-byte vector holds `vec` elements
 constexpr int64_t bucket_tile_elems(int vec) { return int64_t(kBucketThreads) * kBucketVpt * vec; }
 

@@ -45,6 +45,7 @@ struct ddp_plan {
   std::vector<int32_t> seg_first, seg_count, seg_tiles, seg_tile_first;
   std::vector<unsigned char> seg_staged;  // host copy of the device table
   size_t seg_bytes = 0;                   // the tile map starts here
+  int64_t seg_map_stride = 0;             // entries per XCD group of the tile map
   void *d_seg = nullptr;
 };
 
@@ -79,8 +80,9 @@ int32_t plan_num_buckets(const ddp_plan *plan) {
   return plan ? static_cast<int32_t>(plan->members.size()) : 0;
 }
 
-const int32_t *plan_tile_map(const ddp_plan *plan) {
+const int32_t *plan_tile_map(const ddp_plan *plan, int64_t *stride) {
   if (plan == nullptr || plan->d_seg == nullptr) return nullptr;
+  *stride = plan->seg_map_stride;
   return reinterpret_cast<const int32_t *>(static_cast<const char *>(plan->d_seg) +
                                            plan->seg_bytes);
 }
@@ -150,12 +152,16 @@ static bool build_segments(const ddp_plan *plan, int32_t p, std::vector<SegDesc>
 
 }  // namespace ddpsim
 
+// Entries of the tile map as stored (grouped by tile mod kXcds, each group
+// padded to the same length).
+static int64_t map_stride(size_t tiles) { return ceil_div(static_cast<int64_t>(tiles), kXcds); }
+
 extern "C" size_t ddp_plan_segment_bytes(const ddp_plan *plan, int32_t p) {
   if (plan == nullptr || p < 1 || p > kMaxRanks) return 0;
   std::vector<SegDesc> seg;
   std::vector<int32_t> f, c, t, tf, ts;
   if (!build_segments(plan, p, &seg, &f, &c, &t, &tf, &ts)) return 0;
-  return seg.size() * sizeof(SegDesc) + ts.size() * sizeof(int32_t);
+  return seg.size() * sizeof(SegDesc) + map_stride(ts.size()) * kXcds * sizeof(int32_t);
 }
 
 extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *d_table,
@@ -169,10 +175,12 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
   if (!build_segments(plan, p, &seg, &first, &count, &tiles, &tile_first, &tile_seg)) {
     return fail(DDP_EINVAL, "ddp_plan_upload_segments: a bucket is too large");
   }
-  // Device layout: the pieces, then one int32 per tile naming its piece.
-  // Both parts are staged in one host buffer that the plan keeps alive.
+  // Device layout: the descriptors, then one int32 per tile naming its
+  // descriptor, grouped by tile mod kXcds (tile_map_index). Both parts are
+  // staged in one host buffer that the plan keeps alive.
   const size_t seg_bytes = seg.size() * sizeof(SegDesc);
-  const size_t need = seg_bytes + tile_seg.size() * sizeof(int32_t);
+  const int64_t stride = map_stride(tile_seg.size());
+  const size_t need = seg_bytes + static_cast<size_t>(stride) * kXcds * sizeof(int32_t);
   if (need > 0) {
     if (d_table == nullptr || bytes < need) {
       return fail(DDP_EINVAL, "ddp_plan_upload_segments: needs %zu bytes of device memory",
@@ -182,10 +190,13 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
       return fail(DDP_EALIGN, "ddp_plan_upload_segments: table is not 16-byte aligned");
     }
   }
-  std::vector<unsigned char> staged(need);
+  std::vector<unsigned char> staged(need, 0);
   if (need > 0) {
     std::memcpy(staged.data(), seg.data(), seg_bytes);
-    std::memcpy(staged.data() + seg_bytes, tile_seg.data(), need - seg_bytes);
+    int32_t *map = reinterpret_cast<int32_t *>(staged.data() + seg_bytes);
+    for (size_t t = 0; t < tile_seg.size(); ++t) {
+      map[tile_map_index(static_cast<int64_t>(t), stride)] = tile_seg[t];
+    }
   }
   plan->seg.swap(seg);
   plan->seg_first.swap(first);
@@ -194,6 +205,7 @@ extern "C" ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *
   plan->seg_tile_first.swap(tile_first);
   plan->seg_staged.swap(staged);
   plan->seg_bytes = seg_bytes;
+  plan->seg_map_stride = stride;
   if (need > 0) {
     s = check_hip(hipMemcpyAsync(d_table, plan->seg_staged.data(), need,
                                  hipMemcpyHostToDevice, stream),

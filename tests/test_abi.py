@@ -168,13 +168,15 @@ def test_collective_argument_errors():
 def test_segment_table_sizes():
     """The in-place all-reduce's table holds 32 bytes per parameter with
     elements, then 4 bytes per tile of 256 fp32 (512 bf16) elements of each
-    such parameter; its size does not depend on p (only the chunk size
-    inside each descriptor does)."""
+    such parameter, the tiles grouped by tile mod 8 in groups of equal
+    length; its size does not depend on p (only the chunk size inside each
+    descriptor does)."""
     sizes = [5000, 0, 7, 4096, 4097, 1, 33_333, 12, 0, 65_545]
     nonzero = sum(1 for s in sizes if s)
     for eb, tile in ((4, 256), (2, 512)):
         plan = ddp.ddp_bucket_plan(sizes, eb, 96 * 1024, 8 * 1024)
-        want = 32 * nonzero + 4 * sum(-(-s // tile) for s in sizes)
+        tiles = sum(-(-s // tile) for s in sizes)
+        want = 32 * nonzero + 4 * 8 * -(-tiles // 8)
         for p in (1, 2, 3, 8, 64):
             assert plan.segment_bytes(p) == want
         assert plan.segment_bytes(0) == 0 and plan.segment_bytes(65) == 0
