@@ -55,7 +55,8 @@ def test_c_caller_plans_prices_and_reports_errors(program, oracle):
 def test_c_caller_all_reduces_on_the_gpu_without_torch(oracle, tmp_path):
     """tests/c_abi/device_allreduce.c allocates with hipMalloc, calls
     ring_allreduce_sim on its own stream and dumps inputs and outputs; the
-    outputs must be the oracle's bits."""
+    outputs must be the oracle's bits. It then runs the bf16 ring through
+    ring_allreduce_sim_noalloc eagerly and from a captured HIP graph."""
     import numpy as np
 
     exe = str(tmp_path / "device_allreduce")
@@ -76,3 +77,18 @@ def test_c_caller_all_reduces_on_the_gpu_without_torch(oracle, tmp_path):
     C = -(-n // p)
     assert out.stdout.split() == ["steps", "6", "messages", str(len(log)),
                                   "bytes_sent_per_rank", str(2 * (p - 1) * C * 4)]
+    # the no-allocation entry point on bf16 with the step-by-step ring:
+    # eager, captured in a HIP graph, and that graph replayed on its own
+    # results
+    nb = 100003
+    bins = {k: np.fromfile(tmp_path / f"bf16_{k}.bin", dtype=np.uint16).reshape(p, nb)
+            for k in ("inputs", "eager", "graph1", "graph2")}
+    want, _ = oracle.ring_allreduce([bins["inputs"][r] for r in range(p)], avg="world",
+                                    want_log=False)
+    for r in range(p):
+        assert np.array_equal(bins["eager"][r], want[r]), f"eager rank {r}"
+        assert np.array_equal(bins["graph1"][r], want[r]), f"replay 1 rank {r}"
+    again, _ = oracle.ring_allreduce([bins["graph1"][r] for r in range(p)], avg="world",
+                                     want_log=False)
+    for r in range(p):
+        assert np.array_equal(bins["graph2"][r], again[r]), f"replay 2 rank {r}"
