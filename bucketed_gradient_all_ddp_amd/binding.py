@@ -330,7 +330,7 @@ class Plan:
             torch.cuda.synchronize(old.device)
 
     def upload_segments(self, p: int, device="cuda", stream=None) -> "Plan":
-        """Upload the piece table ddp_allreduce_bucket needs for p ranks."""
+        """Upload the descriptor table ddp_allreduce_bucket needs for p ranks."""
         import torch
 
         nbytes = self.segment_bytes(p)

@@ -264,10 +264,14 @@ ddp_status ddp_unflatten(const ddp_plan *plan, int32_t bucket, int32_t p,
  * backward" item 1 and "Step 3: finalize_backward" describe the copies this
  * replaces). Device-memory traffic is 2 p n_b bytes-per-element.
  *
- * Before the first call for a given p, upload the plan's piece table for p:
+ * Before the first call for a given p, upload the plan's descriptor table
+ * for p (each parameter's offset in its bucket and the bucket's ring chunk
+ * size for p, then a map from 256-element tiles to descriptors):
  * ddp_plan_segment_bytes(plan, p) bytes of caller-owned device memory
  * (16-byte aligned), filled by ddp_plan_upload_segments on `stream`. The
- * plan keeps the host copy alive; uploading for another p replaces it.
+ * plan keeps the host copy alive; uploading for another p replaces it, and
+ * a refused upload leaves the previous table in use. The caller keeps the
+ * device memory alive while launches may read it, on any stream.
  *
  *   d_grad_ptrs  DEVICE array of p * n_params gradient addresses, rank-major
  *                (as for ddp_flatten); each gradient must be aligned to its
@@ -275,9 +279,10 @@ ddp_status ddp_unflatten(const ddp_plan *plan, int32_t bucket, int32_t p,
  *                same offset from a 16-byte boundary the kernel moves 16-byte
  *                vectors, otherwise elements.
  *   avg_mode, tokens, stats   as ring_allreduce_sim.
- * Errors: DDP_ENOTREADY (no piece table for this p), DDP_ERANGE, DDP_EINVAL.
- * Gradients of different ranks or parameters must not overlap (not checked:
- * the addresses are device-resident). */
+ * Errors: DDP_ENOTREADY (no descriptor table for this p), DDP_ERANGE,
+ * DDP_EINVAL. Gradients of different ranks or parameters must not overlap
+ * (not checked here: the addresses are device-resident; the Python
+ * binding's grad_pointer_table refuses overlapping gradients). */
 size_t ddp_plan_segment_bytes(const ddp_plan *plan, int32_t p);
 ddp_status ddp_plan_upload_segments(ddp_plan *plan, int32_t p, void *d_table,
                                     size_t bytes, hipStream_t stream);
@@ -320,7 +325,7 @@ ddp_status ddp_allreduce_buckets(const ddp_plan *plan, int32_t first_bucket,
  *             gradient pointer table, dtype, averaging (tokens copied), and
  *             the stream the all-reduces run on. Plan and table must outlive
  *             the reducer. Errors: DDP_EINVAL, DDP_ERANGE; DDP_ENOTREADY
- *             when the plan's piece table was not uploaded for this p.
+ *             when the plan's descriptor table was not uploaded for this p.
  *   prepare   starts a backward pass (all counts reset).
  *   mark_ready  param in [0, n_params); `ready` is an event recorded after
  *             that parameter's gradients of all ranks were written (NULL if

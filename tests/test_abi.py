@@ -186,7 +186,7 @@ def test_bucket_allreduce_argument_errors():
     L = load_library()
     plan = ddp.ddp_bucket_plan([100, 200], 4, 1024, 256)
     fake = ctypes.c_void_p(0x100000000)
-    # no piece table yet
+    # no descriptor table yet
     assert L.ddp_allreduce_bucket(plan.handle, 0, 4, fake, 0, 0, None, None, None) == 6
     assert L.ddp_allreduce_bucket(plan.handle, 5, 4, fake, 0, 0, None, None, None) == 2
     assert L.ddp_allreduce_bucket(plan.handle, 0, 0, fake, 0, 0, None, None, None) == 2
@@ -202,12 +202,12 @@ def test_reducer_errors_without_launching():
     L = load_library()
     fake = ctypes.c_void_p(0x100000000)
     out = ctypes.c_void_p()
-    # the piece table must have been uploaded for the reducer's p
+    # the descriptor table must have been uploaded for the reducer's p
     real = ddp.ddp_bucket_plan([5, 7, 3, 9, 4], 4, 32, 16)
     assert L.ddp_reducer_create(real.handle, 4, fake, 0, 1, None, None, ctypes.byref(out)) == 6
     assert b"ddp_plan_upload_segments" in L.ddp_last_error()
     # zero-size parameters with caps of 0 bytes: one bucket each and an empty
-    # piece table, which uploads without device memory
+    # descriptor table, which uploads without device memory
     sizes = [0, 0, 0, 0, 0]
     plan = ddp.ddp_bucket_plan(sizes, 4, 0, 0)
     assert plan.num_buckets == len(sizes) and plan.segment_bytes(4) == 0
@@ -526,7 +526,7 @@ def test_binding_rejects_overlapping_gradients():
 
 
 def test_reducer_failed_launch_is_sticky():
-    """A launch that fails inside mark_ready (here: the piece table was
+    """A launch that fails inside mark_ready (here: the descriptor table was
     re-uploaded for another p after the reducer was made, so the launch is
     refused before anything is enqueued) is reported by every later mark and
     by finalize of that pass, instead of finalize blaming a bucket that never

@@ -81,7 +81,7 @@ def test_bucket_allreduce_needs_segments_for_p():
 
 
 def test_failed_segment_reupload_keeps_the_previous_table(oracle):
-    """A re-upload the library refuses (p = 65) must leave the p = 8 piece
+    """A re-upload the library refuses (p = 65) must leave the p = 8 descriptor
     table in place and alive: the all-reduce that follows still matches the
     oracle, also after the allocator has handed out other memory."""
     p = 8
@@ -134,8 +134,8 @@ def test_bucket_run_in_one_launch_equals_per_bucket(oracle, p):
 
 @pytest.mark.parametrize("bf16,layout", [(False, "mixed"), (True, "odd"), (False, "aligned")])
 def test_bucket_allreduce_at_max_ranks(oracle, bf16, layout):
-    """p = 64 (the library's maximum), small parameters so that many pieces
-    are shorter than a vector and most chunks have unaligned ends."""
+    """p = 64 (the library's maximum), small parameters so that many ring
+    chunks are shorter than a vector and most chunk ends are unaligned."""
     p = 64
     sizes = [129, 0, 1, 4096 + 3, 640, 7, 2049]
     eb = 2 if bf16 else 4
@@ -177,7 +177,7 @@ def test_per_tensor_mode_in_one_launch(oracle, p, layout):
 
 def test_plan_of_zero_size_parameters_launches_nothing():
     """A plan whose parameters all have zero elements has buckets but no
-    pieces and no tiles: the in-place all-reduce, flatten and unflatten return
+    descriptors and no tiles: the in-place all-reduce, flatten and unflatten return
     without a launch and report no traffic."""
     p, sizes = 4, [0, 0, 0]
     plan = ddp.ddp_bucket_plan(sizes, 4, 1024, 256).upload().upload_segments(p)
