@@ -83,7 +83,7 @@ constexpr int bcast_spans() {
 }
 
 template <int EB, bool kNtStore>
-__global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
+__global__ __launch_bounds__(kBcastThreads * kMaxFanoutWaves) void coalesced_broadcast_kernel(
     const ParamDesc *__restrict__ desc, const int32_t *__restrict__ tile_map, int32_t n_params,
     const void *const *__restrict__ ptrs, int32_t p, int32_t root) {
   using U = typename Unit<EB>::type;
@@ -100,31 +100,47 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
   const int64_t left = d.numel - start;
   if (left <= 0) return;
   const int64_t cnt = left < int64_t(kSpan) * kSpans ? left : int64_t(kSpan) * kSpans;
-  const int tid = static_cast<int>(threadIdx.x);
-  const int lane = tid & 63;
+  // blockDim.x / kBcastThreads groups copy the same span, each to its share
+  // of the ranks: ring positions [g*p/G, (g+1)*p/G) in the rotated order.
+  const int tid = static_cast<int>(threadIdx.x) % kBcastThreads;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  static_assert(kBcastThreads % 64 == 0, "a group is whole waves");
+  const int32_t groups = static_cast<int32_t>(blockDim.x) / kBcastThreads;
+  // The group index is the same in every lane of a wave; saying so keeps
+  // the store loop and its readlane rank indices in scalar registers (left
+  // to the compiler, the loop ran under an exec mask with the lane index
+  // re-read per store: 0.745 against 0.770 of peak on the GPT-2 sync).
+  const int32_t g =
+      __builtin_amdgcn_readfirstlane(static_cast<int32_t>(threadIdx.x) / kBcastThreads);
+  const int32_t k0 = g * p / groups, k1 = (g + 1) * p / groups;
+  const int32_t rot = store_rotation(p);
   // rank r's part, read from the device table (uniform: scalar loads)
   auto slice_mem = [&](int32_t r) {
     return static_cast<U *>(const_cast<void *>(ptrs[static_cast<int64_t>(r) * n_params +
                                                     d.param])) + start;
   };
+  constexpr int64_t kPerSpan = int64_t(kBcastThreads) * kBcastVpt;  // vectors
+  const int64_t nv = cnt * EB / kVecBytes;
+  uint4 nxt[kBcastVpt];
   // Lane r of every wave loads rank r's address once; the vector path takes
   // it from that lane (readlane, in wave-uniform code only), so the p
   // addresses cost one vector load instead of p scalar loads.
   uintptr_t mine = 0;
-  if (lane < p) mine = reinterpret_cast<uintptr_t>(slice_mem(lane));
+  if (lane < p) {
+    mine = reinterpret_cast<uintptr_t>(ptrs[static_cast<int64_t>(lane) * n_params + d.param]);
+  }
   auto slice = [&](int32_t r) {
     const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine), r);
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine >> 32), r);
-    return reinterpret_cast<U *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return reinterpret_cast<U *>((static_cast<uint64_t>(hi) << 32) | lo) + start;
   };
-  const bool aligned = __all(lane >= p || mine % kVecBytes == 0);
+  const bool aligned = __all(lane >= p || (mine + start * EB) % kVecBytes == 0);
   const U *src = slice(root);
   int64_t done = 0;
   if (aligned) {
-    constexpr int64_t kPerSpan = int64_t(kBcastThreads) * kBcastVpt;  // vectors
-    const int64_t nv = cnt * EB / kVecBytes;
-    const int32_t rot = store_rotation(p);
-    uint4 nxt[kBcastVpt];
+    // (Loading the root's address separately with a scalar load, so that
+    // this load could be issued before the p addresses arrive, was slower:
+    // 0.68 against 0.77.)
 #pragma unroll
     for (int u = 0; u < kBcastVpt; ++u) {
       const int64_t j = u * kBcastThreads + tid;
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
           nxt[u] = j < nv ? load_vec<kBcastNtLoad>(src, j) : make_uint4(0, 0, 0, 0);
         }
       }
-      for (int32_t k = 0; k < p; ++k) {
+      for (int32_t k = k0; k < k1; ++k) {
         const int32_t r = ring_rank(rot, k, p);
         if (r == root) continue;
         U *dst = slice(r);
@@ -157,9 +173,10 @@ __global__ __launch_bounds__(kBcastThreads) void coalesced_broadcast_kernel(
     done = nv * kVecBytes / EB;
   }
   for (int64_t i = done + tid; i < cnt; i += kBcastThreads) {
-    const U v = src[i];
-    for (int32_t r = 0; r < p; ++r) {
-      if (r != root) slice_mem(r)[i] = v;
+    const U v = global_ptr<U>(src)[i];
+    for (int32_t k = k0; k < k1; ++k) {
+      const int32_t r = ring_rank(rot, k, p);
+      if (r != root) global_ptr<U>(slice_mem(r))[i] = v;
     }
   }
 }
@@ -172,13 +189,20 @@ ddp_status launch_bucket(const ParamDesc *desc, const int32_t *tile_map, int32_t
                                                                  kVecBytes * bcast_spans<EB>()));
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ddp_broadcast_coalesced: bucket too large");
   const dim3 grid(static_cast<uint32_t>(blocks));
+  // A launch holds at most 2^32 - 1 work-items along x.
+  int32_t waves = fanout_waves(p - 1);
+  while (waves > 1 && blocks * kBcastThreads * waves > int64_t(UINT32_MAX)) waves /= 2;
+  if (blocks * kBcastThreads > int64_t(UINT32_MAX)) {
+    return fail(DDP_EINVAL, "ddp_broadcast_coalesced: bucket too large");
+  }
+  const dim3 block(static_cast<uint32_t>(kBcastThreads * waves));
   const size_t lds = residency_lds(DDPSIM_BCAST_WGS_PER_CU);
   const char *what = "coalesced_broadcast_kernel launch";
   if (int64_t(p - 1) * elems * EB > DDPSIM_BCAST_NT_STORE_BYTES) {
-    return launch_lds(coalesced_broadcast_kernel<EB, true>, grid, dim3(kBcastThreads), lds,
+    return launch_lds(coalesced_broadcast_kernel<EB, true>, grid, block, lds,
                       stream, timer, last, what, desc, tile_map, n_params, ptrs, p, root);
   }
-  return launch_lds(coalesced_broadcast_kernel<EB, false>, grid, dim3(kBcastThreads), lds, stream,
+  return launch_lds(coalesced_broadcast_kernel<EB, false>, grid, block, lds, stream,
                     timer, last, what, desc, tile_map, n_params, ptrs, p, root);
 }
 

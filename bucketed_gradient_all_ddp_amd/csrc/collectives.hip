@@ -118,15 +118,23 @@ struct SkipTable {
   int32_t rank[kMaxRanks];
 };
 
+// The workgroup is blockDim.x / kCopyThreads groups of kCopyThreads threads
+// (one wave each at the default shape). Every group copies the same tile and
+// stores it to its share of the destinations: ring positions [g*p/G,
+// (g+1)*p/G) of the workgroup's rotated rank order (fanout_waves).
 template <int VPT, bool kVector, bool kNtStore, bool kNtLoad>
-__global__ __launch_bounds__(kCopyThreads) void fanout_copy_kernel(
+__global__ __launch_bounds__(kCopyThreads * kMaxFanoutWaves) void fanout_copy_kernel(
     RankTable src, RankTable dst, int32_t p, int64_t bytes, int64_t dst_stride,
     SkipTable skip) {
   const int32_t s = static_cast<int32_t>(blockIdx.y);
   const int32_t no = skip.rank[s];
   const char *from = static_cast<const char *>(src.ptr[s]);
   const int64_t off = static_cast<int64_t>(s) * dst_stride;
-  const int tid = static_cast<int>(threadIdx.x);
+  const int tid = static_cast<int>(threadIdx.x) % kCopyThreads;
+  const int32_t groups = static_cast<int32_t>(blockDim.x) / kCopyThreads;
+  const int32_t g = static_cast<int32_t>(threadIdx.x) / kCopyThreads;
+  const int32_t k0 = g * p / groups, k1 = (g + 1) * p / groups;
+  const int32_t rot = store_rotation(p);
   if constexpr (kVector) {
     const int64_t nv = bytes / 16;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * (kCopyThreads * VPT);
@@ -138,8 +146,7 @@ __global__ __launch_bounds__(kCopyThreads) void fanout_copy_kernel(
       ok[u] = j < nv;
       if (ok[u]) x[u] = load_vec<kNtLoad>(from, j);
     }
-    const int32_t rot = store_rotation(p);
-    for (int32_t k = 0; k < p; ++k) {
+    for (int32_t k = k0; k < k1; ++k) {
       const int32_t r = ring_rank(rot, k, p);
       if (r == no) continue;
       char *to = static_cast<char *>(dst.ptr[r]) + off;
@@ -155,7 +162,8 @@ __global__ __launch_bounds__(kCopyThreads) void fanout_copy_kernel(
       if (tid < units) {
         const int64_t b = nv * 16 + 2 * tid;
         const uint16_t v = *reinterpret_cast<const uint16_t *>(from + b);
-        for (int32_t r = 0; r < p; ++r) {
+        for (int32_t k = k0; k < k1; ++k) {
+          const int32_t r = ring_rank(rot, k, p);
           if (r == no) continue;
           *reinterpret_cast<uint16_t *>(static_cast<char *>(dst.ptr[r]) + off + b) = v;
         }
@@ -167,7 +175,8 @@ __global__ __launch_bounds__(kCopyThreads) void fanout_copy_kernel(
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * per_tile;
     for (int64_t j = lo + tid; j < lo + per_tile && j < units; j += kCopyThreads) {
       const uint16_t v = reinterpret_cast<const uint16_t *>(from)[j];
-      for (int32_t r = 0; r < p; ++r) {
+      for (int32_t k = k0; k < k1; ++k) {
+        const int32_t r = ring_rank(rot, k, p);
         if (r == no) continue;
         *reinterpret_cast<uint16_t *>(static_cast<char *>(dst.ptr[r]) + off + 2 * j) = v;
       }
@@ -185,30 +194,39 @@ ddp_status launch_fanout(const RankTable &src, int32_t n_src, bool vec_ok,
   // kCopyThreads * kCopyVpt vectors per workgroup in both paths
   const int64_t per_tile = int64_t(kCopyThreads) * kCopyVpt * 16;
   const int64_t tiles = std::max<int64_t>(1, ceil_div(bytes, per_tile));
-  if (tiles > INT32_MAX) return fail(DDP_EINVAL, "%s: buffer too large", what);
   const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(n_src));
   const size_t lds = residency_lds(DDPSIM_COPY_WGS_PER_CU);
   const bool nt = int64_t(p) * n_src * bytes > DDPSIM_COPY_NT_BYTES;
+  // Destinations per source vector: p, less one where a source's own rank
+  // is skipped.
+  int32_t dests = 0;
+  for (int32_t s = 0; s < n_src; ++s) {
+    dests = std::max(dests, p - (skip.rank[s] >= 0 ? 1 : 0));
+  }
+  // A launch holds at most 2^32 - 1 work-items along x.
+  int32_t waves = fanout_waves(dests);
+  while (waves > 1 && tiles * kCopyThreads * waves > int64_t(UINT32_MAX)) waves /= 2;
+  if (tiles * kCopyThreads > int64_t(UINT32_MAX)) {
+    return fail(DDP_EINVAL, "%s: buffer too large", what);
+  }
+  const dim3 block(static_cast<uint32_t>(kCopyThreads * waves));
   // A plain copy (every source byte written to one destination) also
   // streams its loads: 2 ranks of 1 GiB, 6.44 -> 6.66 TB/s. With more
-  // destinations per read non-temporal loads lost 4% (8 ranks) and 6% (64).
-  bool one_dest = true;
-  for (int32_t s = 0; s < n_src; ++s) {
-    if (p - (skip.rank[s] >= 0 ? 1 : 0) != 1) one_dest = false;
-  }
-  if (vec && nt && one_dest) {
-    return launch_lds(fanout_copy_kernel<kCopyVpt, true, true, true>, grid, dim3(kCopyThreads),
+  // destinations per read non-temporal loads lost 4% (8 ranks) and 6% (64),
+  // and the waves of a workgroup would no longer find the source in cache.
+  if (vec && nt && dests == 1) {
+    return launch_lds(fanout_copy_kernel<kCopyVpt, true, true, true>, grid, block,
                       lds, stream, timer, true, what, src, dst, p, bytes, dst_stride, skip);
   }
   if (vec && nt) {
-    return launch_lds(fanout_copy_kernel<kCopyVpt, true, true, false>, grid, dim3(kCopyThreads),
+    return launch_lds(fanout_copy_kernel<kCopyVpt, true, true, false>, grid, block,
                       lds, stream, timer, true, what, src, dst, p, bytes, dst_stride, skip);
   }
   if (vec) {
-    return launch_lds(fanout_copy_kernel<kCopyVpt, true, false, false>, grid, dim3(kCopyThreads),
+    return launch_lds(fanout_copy_kernel<kCopyVpt, true, false, false>, grid, block,
                       lds, stream, timer, true, what, src, dst, p, bytes, dst_stride, skip);
   }
-  return launch_lds(fanout_copy_kernel<kCopyVpt, false, false, false>, grid, dim3(kCopyThreads),
+  return launch_lds(fanout_copy_kernel<kCopyVpt, false, false, false>, grid, block,
                     lds, stream, timer, true, what, src, dst, p, bytes, dst_stride, skip);
 }
 

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(
     if (scale) {
       Tr::store1(dst, i, apply_divide(Tr::load1(src, i), div));
     } else {
-      dst[i] = src[i];
+      global_ptr<E>(dst)[i] = global_ptr<E>(src)[i];
     }
   }
 }

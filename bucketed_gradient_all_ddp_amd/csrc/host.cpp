@@ -222,6 +222,12 @@ int32_t fold_residency(int32_t wgs, int32_t p) {
   return (wgs * 8 + p - 1) / p;
 }
 
+int32_t fanout_waves(int32_t dests) {
+  int32_t w = 1;
+  while (w < kMaxFanoutWaves && w * DDPSIM_FANOUT_DESTS_PER_WAVE < dests) w *= 2;
+  return w;
+}
+
 }  // namespace ddpsim
 
 using namespace ddpsim;

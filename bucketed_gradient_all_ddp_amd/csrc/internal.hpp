@@ -144,6 +144,28 @@ size_t residency_lds(int32_t wgs);
 // per wave): wgs * 8 / p, rounded up.
 int32_t fold_residency(int32_t wgs, int32_t p);
 
+// Kernels that write one loaded vector to many ranks (the fan-out copy, the
+// coalesced broadcast) split the destinations of a tile over the waves of
+// one workgroup: every wave loads the same source vectors (the later loads
+// hit the cache; the DRAM read counters stay at one read of the source) and
+// stores to its own share of the ranks, about DDPSIM_FANOUT_DESTS_PER_WAVE
+// of them. Measured on one box against one wave per tile: a broadcast to 8
+// ranks of 1 GiB 0.73 -> 0.80 of peak, to 64 ranks of 128 MiB 0.68 -> 0.73,
+// the in-place all-gather of 8 x 1 GiB 0.73 -> 0.81, the GPT-2 parameter
+// sync 0.72 -> 0.74 (0.77 with the group index made wave-uniform). Probes
+// of the same pattern: 2 destinations per wave lose at 8 ranks, 16 waves
+// lose at 64; separate one-wave workgroups per destination group, or one
+// loading wave that shares the vectors through LDS, were slower. Group w of
+// W stores ring positions [w*p/W, (w+1)*p/W) of the workgroup's rotated
+// rank order.
+#ifndef DDPSIM_FANOUT_DESTS_PER_WAVE
+#define DDPSIM_FANOUT_DESTS_PER_WAVE 4
+#endif
+constexpr int32_t kMaxFanoutWaves = 8;
+// Waves per workgroup for `dests` destinations per source vector: the
+// smallest power of two W (at most kMaxFanoutWaves) with W * 4 >= dests.
+int32_t fanout_waves(int32_t dests);
+
 // ddp_allreduce_buckets with an optional cap on its workgroups (0: one per
 // tile). Defined in bucket_allreduce.hip; the reducer uses the cap.
 ddp_status allreduce_buckets(const ddp_plan *plan, int32_t first_bucket, int32_t n_buckets,
@@ -231,6 +253,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Rank buffers are device memory, but their addresses come from tables in
+// memory or from other lanes, so the compiler cannot infer the address space
+// and would emit flat accesses. A flat load counts against both the vector
+// memory and the LDS/scalar counters and can only be waited on with a count
+// of zero, so a wait for a scalar or LDS result also drains the rank loads in
+// flight (the fold's eight loads were issued as four, a drain, and four).
+// Every access to rank data goes through these global-space casts instead.
+// The measured throughput of the fold kernels did not change (GPT-2, Llama-7B
+// and p = 64 bucket launches within 0.3%), but no wait now couples the two.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *global_ptr(const void *p) {
+  return (const __attribute__((address_space(1))) T *)p;
+}
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *global_ptr(void *p) {
+  return (__attribute__((address_space(1))) T *)p;
+}
+
 // Element traits: how a 16-byte vector of the storage type widens to fp32
 // lanes and narrows back.
 struct F32Traits {
@@ -247,10 +287,10 @@ struct F32Traits {
                       __float_as_uint(f[2]), __float_as_uint(f[3]));
   }
   __device__ static __forceinline__ float load1(const void *base, int64_t i) {
-    return static_cast<const float *>(base)[i];
+    return global_ptr<float>(base)[i];
   }
   __device__ static __forceinline__ void store1(void *base, int64_t i, float v) {
-    static_cast<float *>(base)[i] = v;
+    global_ptr<float>(base)[i] = v;
   }
 };
 
@@ -273,11 +313,10 @@ struct BF16Traits {
   }
   __device__ static __forceinline__ float load1(const void *base, int64_t i) {
     return __uint_as_float(
-        static_cast<uint32_t>(static_cast<const uint16_t *>(base)[i]) << 16);
+        static_cast<uint32_t>(global_ptr<uint16_t>(base)[i]) << 16);
   }
   __device__ static __forceinline__ void store1(void *base, int64_t i, float v) {
-    static_cast<uint16_t *>(base)[i] =
-        static_cast<uint16_t>(f32_to_bf16_bits(v));
+    global_ptr<uint16_t>(base)[i] = static_cast<uint16_t>(f32_to_bf16_bits(v));
   }
 };
 
@@ -288,7 +327,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool kNonTemporal = false>
 __device__ __forceinline__ uint4 load_vec(const void *base, int64_t v) {
-  const u32x4 *p = static_cast<const u32x4 *>(base) + v;
+  const __attribute__((address_space(1))) u32x4 *p = global_ptr<u32x4>(base) + v;
   u32x4 x;
   if constexpr (kNonTemporal) {
     x = __builtin_nontemporal_load(p);
@@ -300,7 +339,7 @@ __device__ __forceinline__ uint4 load_vec(const void *base, int64_t v) {
 
 template <bool kNonTemporal>
 __device__ __forceinline__ void store_vec(void *base, int64_t v, uint4 x) {
-  u32x4 *p = static_cast<u32x4 *>(base) + v;
+  __attribute__((address_space(1))) u32x4 *p = global_ptr<u32x4>(base) + v;
   const u32x4 y = {x.x, x.y, x.z, x.w};
   if constexpr (kNonTemporal) {
     __builtin_nontemporal_store(y, p);
