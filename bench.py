@@ -57,10 +57,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8.md: the headline launch (all 13
-    # buckets in one dispatch), 3,984,262,998 read + 3,982,252,330 written
+    # buckets in one dispatch), 3,984,253,504 read + 3,982,195,328 written
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7966515328,
-        "sources_sha256": "c0cd1b2e97b322a459cb6a746f0d88c00429278ae7d65bb193abdd40997830aa",
+        "bytes_per_launch": 7966448832,
+        "sources_sha256": "886c884c1c65e0f87e5cef649b20d69a49e7870f4bcffd47ae9498e8c025d724",
     },
 }
 
