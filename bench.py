@@ -198,8 +198,19 @@ def run_steps(ddp, wl, mode, algo, steps, timer, ws):
 
 
 def timed(torch, ddp, wl, mode, algo, steps, warmup, ws):
+    """(ms per step, per-kernel figures, ms per step with the kernel events).
+
+    The step time comes from a pass with no per-call events: recording a
+    start and a stop event on every dispatch costs about 5 us of GPU time per
+    launch (13 launches per step in the per-bucket form). A second pass of
+    the same steps times every kernel by events on its own dispatch."""
     run_steps(ddp, wl, mode, algo, warmup, None, ws)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(ddp, wl, mode, algo, steps, None, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
     per_step_calls = {"batched": 1, "inplace": wl.plan.num_buckets,
                       "copy": 3 * wl.plan.num_buckets}[mode]
     timer = ddp.CallTimer(pairs=per_step_calls * steps)
@@ -207,7 +218,7 @@ def timed(torch, ddp, wl, mode, algo, steps, warmup, ws):
     rec = run_steps(ddp, wl, mode, algo, steps, timer, ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
+    ms_events = (t1 - t0) * 1e3 / steps
     kernels = {}
     for kind, nbytes, k in rec:
         e = kernels.setdefault(kind, {"launches": 0, "bytes": 0, "ms": 0.0})
@@ -219,7 +230,7 @@ def timed(torch, ddp, wl, mode, algo, steps, warmup, ws):
         e["GBps"] = round(e["bytes"] / (e["ms"] * 1e-3) / 1e9, 1)
         e["ms_per_step"] = round(e["ms"] / steps, 4)
         e["ms"] = round(e["ms"], 4)
-    return ms, kernels
+    return ms, kernels, ms_events
 
 
 def _host_cpu() -> str:
@@ -311,21 +322,31 @@ def _events_ms(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def _timed_calls(torch, ddp, calls, reps):
-    """Each call once per rep, every call's kernels timed by dispatch events.
-    Returns (host wall ms per rep, device ms per rep)."""
+def _timed_calls(torch, ddp, calls, reps, wall=True):
+    """Each call once per rep. Returns (host wall ms per rep, device ms per
+    rep). The wall time comes from a pass without events (an event pair on
+    every dispatch costs about 5 us of GPU time per launch); a second pass
+    times every call's kernels by events on their own dispatches. wall=False
+    skips the first pass (and returns None for it)."""
+    wall_ms = None
+    if wall:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / reps
     timer = ddp.CallTimer(pairs=len(calls) * reps)
     ids = []
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for _ in range(reps):
         for c in calls:
             ids.append(timer.arm())
             c()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / reps
     dev = sum(timer.elapsed_ms(k) for k in ids) / reps
-    return wall, dev
+    return wall_ms, dev
 
 
 def _line(metric, value, unit, workload, extra):
@@ -801,7 +822,7 @@ def bench_crossover(torch, ddp, W, dev, args):
                       ddp.allreduce_sim(b, s, st, avg="world"))
                 for _ in range(3):
                     fn()
-                _, dms = _timed_calls(torch, ddp, [fn], reps)
+                _, dms = _timed_calls(torch, ddp, [fn], reps, wall=False)
                 row[f"{sch}{'_steps' if steps else '_fused'}_us"] = round(dms * 1e3, 2)
         table[n * 4] = row
         log(f"crossover: {n * 4} bytes done")
@@ -911,7 +932,7 @@ def bench_sync(torch, ddp, W, dev, args):
     # rank, the fan-out copy): the same access pattern without the plan
     flat = [lambda: ddp.broadcast_sim(arenas, src=0)]
     flat[0]()
-    _, fdms = _timed_calls(torch, ddp, flat, args.steps)
+    _, fdms = _timed_calls(torch, ddp, flat, args.steps, wall=False)
     fbytes = p * arenas[0].numel() * 4
     # per-forward buffer broadcast: 12 layers x (running mean, running var)
     # of 3072 fp32 each, plus an int64 counter per layer
@@ -960,7 +981,7 @@ def bench_ceilings(torch, ddp, W, dev, args):
 
     def timed_ms(fn, reps):
         fn()
-        _, dms = _timed_calls(torch, ddp, [fn], reps)
+        _, dms = _timed_calls(torch, ddp, [fn], reps, wall=False)
         return dms
 
     for p, mib in ((2, 1024), (8, 1024), (64, 128)):
@@ -1048,12 +1069,12 @@ def main():
     results = {}
     for mode in modes:
         log(f"{mode}: warmup {args.warmup}, timing {args.steps} steps")
-        ms, kernels = timed(torch, ddp, wl, mode, args.algo, args.steps, args.warmup, ws)
-        results[mode] = (ms, kernels)
-        log(f"{mode}: {ms:.3f} ms/step; " + "; ".join(
+        ms, kernels, ms_ev = timed(torch, ddp, wl, mode, args.algo, args.steps, args.warmup, ws)
+        results[mode] = (ms, kernels, ms_ev)
+        log(f"{mode}: {ms:.3f} ms/step ({ms_ev:.3f} with kernel events); " + "; ".join(
             f"{k} {v['avg_us']} us avg, {v['GBps']} GB/s" for k, v in kernels.items()))
 
-    ms, kernels = results[args.mode]
+    ms, kernels, ms_ev = results[args.mode]
     dominant = max(kernels.items(), key=lambda kv: kv[1]["ms"])
     dname, d = dominant
     bus = S * 2 * (p - 1) / p / (ms * 1e-3) / 1e9
@@ -1066,6 +1087,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_with_kernel_events": round(ms_ev, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1101,11 +1123,14 @@ def main():
             "bytes_per_launch": d["bytes"] // d["launches"],
         },
     }
-    for mode, (mms, mk) in results.items():
+    for mode, (mms, mk, mev) in results.items():
         if mode != args.mode:
+            sb = 6 * p * S if mode == "copy" else 2 * p * S
             result[f"{mode}_step"] = {
                 "ms_per_step": round(mms, 4),
+                "ms_per_step_with_kernel_events": round(mev, 4),
                 "bus_GBps": round(S * 2 * (p - 1) / p / (mms * 1e-3) / 1e9, 2),
+                "hbm_frac_step": round(sb / (mms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 "kernels": mk,
             }
     # the practical roofline: the library's own copy (a broadcast between two
@@ -1113,7 +1138,7 @@ def main():
     cp = [torch.ones(1 << 28, device=dev), torch.empty(1 << 28, device=dev)]
     ccall = [lambda: ddp.broadcast_sim(cp, src=0)]
     ccall[0]()
-    _, cdms = _timed_calls(torch, ddp, ccall, 10)
+    _, cdms = _timed_calls(torch, ddp, ccall, 10, wall=False)
     copy_gbps = 2 * (1 << 30) / (cdms * 1e-3) / 1e9
     result["practical_ceiling"] = {
         "copy_GBps": round(copy_gbps, 1),
