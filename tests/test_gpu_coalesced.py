@@ -53,7 +53,8 @@ def _arena_views(p, sizes, dtype, layout, seed):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.int64, torch.uint8])
 @pytest.mark.parametrize("layout", ["aligned", "odd", "mixed"])
-@pytest.mark.parametrize("p,root", [(1, 0), (2, 1), (3, 0), (8, 5), (64, 63)])
+@pytest.mark.parametrize("p,root", [(1, 0), (2, 1), (3, 0), (5, 4), (8, 5), (13, 7), (17, 16),
+                                    (64, 63)])
 def test_broadcast_coalesced_bit_exact(oracle, dtype, layout, p, root):
     arenas, views, before = _arena_views(p, SIZES, dtype, layout, 31 * p + root)
     eb = torch.tensor([], dtype=dtype).element_size()

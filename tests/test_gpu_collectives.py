@@ -41,7 +41,8 @@ def test_reduce_scatter(oracle, p, C, avg, in_place, bf16):
 
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("p,C", [(1, 7), (2, 3), (3, 1001), (4, 4096), (8, 12_345), (64, 9), (64, 1024)])
+@pytest.mark.parametrize("p,C", [(1, 7), (2, 3), (3, 1001), (4, 4096), (5, 333), (8, 12_345),
+                                 (13, 777), (16, 100), (17, 55), (64, 9), (64, 1024)])
 def test_allgather(oracle, p, C, bf16, in_place):
     host = _vals(p, C, 500 + p, bf16, oracle)
     dt = torch.bfloat16 if bf16 else torch.float32
