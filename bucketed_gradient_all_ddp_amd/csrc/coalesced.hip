@@ -69,9 +69,10 @@ constexpr int kBcastSpans = DDPSIM_BCAST_SPANS;
 
 // Each plan tile of kFlattenTile elements of one tensor (named by the plan's
 // tile map, as in flatten_kernel) is split into spans of one 16-byte vector
-// per lane; a workgroup takes kBcastSpans consecutive spans of one tile. The
-// root's span is loaded once and stored to every other rank; the next span's
-// load is issued before this span's stores. 16-byte vectors when every
+// per lane; a workgroup takes kBcastSpans consecutive spans of one tile. Its
+// waves (fanout_waves of the p - 1 destinations) each load the root's span
+// and store it to their own share of the other ranks; the next span's load
+// is issued before this span's stores. 16-byte vectors when every
 // rank's copy of the tensor is 16-byte aligned (spans start at multiples of
 // 16 bytes from the tensor's base, so the base decides), elements of EB
 // bytes otherwise.

@@ -39,10 +39,11 @@ namespace {
 #ifndef DDPSIM_RS_WGS_PER_CU
 #define DDPSIM_RS_WGS_PER_CU 11
 #endif
-// Fan-out copy (all-gather, broadcast): one-wave workgroups of one vector per
-// lane (8 ranks of 1 GiB: all-gather 5.40 -> 5.83, broadcast 5.27 -> 5.77
-// TB/s against 256 threads x 4 vectors; at 64 ranks 1-4% better). A bound
-// on residency gained nothing here.
+// Fan-out copy (all-gather, broadcast): tiles of one vector per lane across
+// one wave (8 ranks of 1 GiB: all-gather 5.40 -> 5.83, broadcast 5.27 ->
+// 5.77 TB/s against 256 threads x 4 vectors; at 64 ranks 1-4% better), each
+// tile's destinations shared by the waves of its workgroup (fanout_waves). A
+// bound on residency gained nothing here.
 #ifndef DDPSIM_COPY_THREADS
 #define DDPSIM_COPY_THREADS 64
 #endif
