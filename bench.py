@@ -57,10 +57,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # profiles/bucket_allreduce_gpt2_p8.md: the headline launch (all 13
-    # buckets in one dispatch), 3,984,253,504 read + 3,982,195,328 written
+    # buckets in one dispatch), 3,984,249,536 read + 3,982,158,746 written
     "bucket_allreduce_kernel": {
-        "bytes_per_launch": 7966448832,
-        "sources_sha256": "886c884c1c65e0f87e5cef649b20d69a49e7870f4bcffd47ae9498e8c025d724",
+        "bytes_per_launch": 7966408282,
+        "sources_sha256": "76ddd334aeba600aefb1aa94f7f9a85a567df5f46f89a254e6932a37598151b8",
     },
 }
 

@@ -66,16 +66,15 @@ __global__ __launch_bounds__(THR) void fused_allreduce_kernel(
       }
     }
 
-    const int64_t nv = (k.ve - k.vs) / V;
-    const int64_t base = static_cast<int64_t>(t) * (THR * VPT);
-    if (base >= nv) continue;
+    const int64_t v0 = k.vs / V, v1 = k.ve / V;
+    const int64_t base = aligned_tile_base(v0, t, int64_t(THR) * VPT);
+    if (base >= v1) continue;
     int64_t vi[VPT];
     bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int64_t j = base + u * THR + tid;
-      ok[u] = j < nv;
-      vi[u] = k.vs / V + j;
+      vi[u] = base + u * THR + tid;
+      ok[u] = vi[u] >= v0 && vi[u] < v1;
     }
     float acc[VPT][V];
     fold_vectors<Tr, VPT, RB, kNT>(TablePtrs{bufs}, p, c, vi, ok, acc);
@@ -94,6 +93,81 @@ __global__ __launch_bounds__(THR) void fused_allreduce_kernel(
         if (ok[u]) store_vec<kNT>(dst, vi[u], y[u]);
       }
     }
+  }
+}
+
+// The streaming form with the ranks of a tile split over the W waves of a
+// workgroup: wave w loads ring positions [w*p/W, (w+1)*p/W) of the tile
+// (counted from rank c), adds them, in order, to the sum of the waves before
+// it, passed on through LDS, and stores the result to its share of the
+// ranks. The sum is the same left-to-right fold as above. lds holds two
+// slots of 64 * V floats, alternated between tiles so that a slot is
+// rewritten only after every wave has passed the barriers of the tile that
+// used the other one.
+template <typename Tr, int W, int S>
+__global__ __launch_bounds__(64 * W) void fused_allreduce_waves_kernel(
+    RankTable bufs, int32_t p, int64_t n, int64_t C, int32_t tiles_per_chunk, Divide div) {
+  extern __shared__ float lds[];
+  constexpr int V = Tr::kVec;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(threadIdx.x) >> 6);
+  const int32_t lo = wave * p / W, hi = (wave + 1) * p / W;
+  const int64_t total = int64_t(tiles_per_chunk) * p;
+  int32_t uses = 0;
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int32_t c = static_cast<int32_t>(tile / tiles_per_chunk);
+    const int32_t t = static_cast<int32_t>(tile - int64_t(c) * tiles_per_chunk);
+    const ChunkSpan k = chunk_span(c, C, n, V);
+    if (k.s >= k.e) continue;
+    if (t == 0 && wave == 0 && lane >= 64 - 2 * (V - 1)) {
+      const int e = lane - (64 - 2 * (V - 1));
+      const bool head = e < V - 1;
+      const int64_t i = head ? k.s + e : k.tail_begin + (e - (V - 1));
+      if (i < (head ? k.head_end : k.e)) {
+        const float y = apply_divide(fold_scalar<Tr>(TablePtrs{bufs}, p, c, i), div);
+        for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
+      }
+    }
+    const int64_t v0 = k.vs / V, v1 = k.ve / V;
+    const int64_t base = aligned_tile_base(v0, t, 64);
+    if (base >= v1) continue;
+    const int64_t vi = base + lane;
+    const bool ok = vi >= v0 && vi < v1;
+    // this wave's positions, every load in flight before the first add
+    uint4 x[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const bool live = lo + j < hi;  // wave-uniform
+      const void *src = bufs.ptr[live ? ring_rank(c, lo + j, p) : 0];
+      x[j] = (live && ok) ? load_vec<true>(src, vi) : make_uint4(0, 0, 0, 0);
+    }
+    float *slot = lds + (uses & 1) * (64 * V);
+    ++uses;
+    float acc[V];
+    for (int32_t w = 0; w < W; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = w == 0 ? -0.0f : slot[e * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+          if (lo + j < hi) {
+            float f[V];
+            Tr::widen(x[j], f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[e] = acc[e] + f[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) slot[e * 64 + lane] = acc[e];
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = apply_divide(slot[e * 64 + lane], div);
+    const uint4 y = Tr::narrow(acc);
+    if (!ok) continue;
+    const int32_t rot = store_rotation(p);
+    for (int32_t r = lo; r < hi; ++r) store_vec<true>(bufs.ptr[ring_rank(rot, r, p)], vi, y);
   }
 }
 
@@ -127,17 +201,16 @@ __global__ __launch_bounds__(THR) void ring_step_kernel(
     }
   }
 
-  const int64_t nv = (k.ve - k.vs) / V;
-  const int64_t base = static_cast<int64_t>(t) * (THR * VPT);
-  if (base >= nv) return;
+  const int64_t v0 = k.vs / V, v1 = k.ve / V;
+  const int64_t base = aligned_tile_base(v0, t, int64_t(THR) * VPT);
+  if (base >= v1) return;
   uint4 a[VPT], b[VPT];
   int64_t vi[VPT];
   bool ok[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    const int64_t jj = base + u * THR + tid;
-    ok[u] = jj < nv;
-    vi[u] = k.vs / V + jj;
+    vi[u] = base + u * THR + tid;
+    ok[u] = vi[u] >= v0 && vi[u] < v1;
     if (ok[u]) {
       b[u] = load_vec<kNT>(src, vi[u]);
       if (kReduce) a[u] = load_vec<kNT>(out, vi[u]);
@@ -191,6 +264,17 @@ constexpr int kFusedVpt = DDPSIM_FUSED_VPT;
 constexpr int kFusedRb = DDPSIM_FUSED_RB;
 constexpr int kFusedThreads = DDPSIM_FUSED_THREADS;
 constexpr int kFusedNtThreads = 64;
+#ifndef DDPSIM_FUSED_WAVE_RULE
+#define DDPSIM_FUSED_WAVE_RULE 1  // 0: one wave per tile at every p
+#endif
+// Waves per tile of the streaming form for p ranks, measured on identical
+// buffers against one wave: 1 up to 8 ranks (2 waves: -1% to +1.5% at 4-9
+// ranks), 2 up to 27 (+4-7% at 12-24 ranks; 8 waves lost 3-18% there), 8
+// from 28 (+6-11% at 28-64 ranks of 128-256 MiB, equal at 64 of 2 GiB).
+int32_t fused_waves(int32_t p) {
+  if (!DDPSIM_FUSED_WAVE_RULE || p <= 8) return 1;
+  return p < 28 ? 2 : 8;
+}
 // Small problems (few workgroups) are latency-bound: the fold's load batches
 // run one after another, so there the kernel keeps 32 rank loads in flight
 // per thread (one vector each) instead of 8.
@@ -235,9 +319,44 @@ constexpr int kStepNtVpt = DDPSIM_STEP_NT_VPT;
 constexpr bool kStepNt = DDPSIM_STEP_NT != 0;
 
 
+// Tiles per chunk of C elements: tiles of threads * vpt vectors on the grid
+// of aligned_tile_base, one more when chunks do not start on that grid.
 int32_t tiles_for(int64_t C, int vec, int vpt, int threads = kThreads) {
+  const int64_t tw = int64_t(threads) * vpt;
   const int64_t vectors = C / vec;
-  return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(vectors, int64_t(threads) * vpt)));
+  const bool aligned = C % (tw * vec) == 0;
+  return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(vectors, tw) + (aligned ? 0 : 1)));
+}
+
+template <int W>
+ddp_status launch_fused_waves(const RankTable &tab, int32_t p, int64_t n, int64_t C, int32_t tpc,
+                              int32_t dtype, const Divide &div, dim3 grid, hipStream_t stream,
+                              CallTimer &timer) {
+  const char *kname = "fused_allreduce_waves_kernel launch";
+  // the residency bound counts waves: ceil(bound / W) workgroups per CU
+  // (counted in workgroups it lost 3% at 8 ranks and 2% at 64)
+  const int32_t bound = fold_residency(DDPSIM_FUSED_NT_WGS_PER_CU, p);
+  const size_t lds_bound = residency_lds(bound > 0 ? (bound + W - 1) / W : 0);
+  const int vec = dtype == DDP_F32 ? F32Traits::kVec : BF16Traits::kVec;
+  const size_t lds = std::max(lds_bound, size_t(2) * 64 * vec * sizeof(float));
+  constexpr int kLarge = W > 1 ? (kMaxRanks + W - 1) / W : 1;
+  constexpr int kSmall = kLarge < 8 ? kLarge : 8;
+  const bool few = (p + W - 1) / W <= kSmall;
+  const dim3 block(64 * W);
+  if (dtype == DDP_F32) {
+    if (few) {
+      return launch_lds(fused_allreduce_waves_kernel<F32Traits, W, kSmall>, grid, block, lds,
+                        stream, timer, true, kname, tab, p, n, C, tpc, div);
+    }
+    return launch_lds(fused_allreduce_waves_kernel<F32Traits, W, kLarge>, grid, block, lds, stream,
+                      timer, true, kname, tab, p, n, C, tpc, div);
+  }
+  if (few) {
+    return launch_lds(fused_allreduce_waves_kernel<BF16Traits, W, kSmall>, grid, block, lds,
+                      stream, timer, true, kname, tab, p, n, C, tpc, div);
+  }
+  return launch_lds(fused_allreduce_waves_kernel<BF16Traits, W, kLarge>, grid, block, lds, stream,
+                    timer, true, kname, tab, p, n, C, tpc, div);
 }
 
 ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtype,
@@ -259,6 +378,18 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
     }
     return launch(fused_allreduce_kernel<BF16Traits, 1, kSmallRb, false, kThreads>, grid1,
                   dim3(kThreads), stream, timer, true, kname, tab, p, n, C, tpc1, div);
+  }
+  const int32_t waves = fused_waves(p);
+  if (nt && waves > 1) {
+    const int32_t tpcn = tiles_for(C, vec, 1, kFusedNtThreads);
+    const int64_t bn = int64_t(tpcn) * p;
+    // a launch holds at most 2^32 - 1 threads; past that the one-wave form runs
+    if (bn * kFusedNtThreads * waves <= int64_t(UINT32_MAX)) {
+      const dim3 gridn(static_cast<uint32_t>(bn));
+      return waves == 2
+                 ? launch_fused_waves<2>(tab, p, n, C, tpcn, dtype, div, gridn, stream, timer)
+                 : launch_fused_waves<8>(tab, p, n, C, tpcn, dtype, div, gridn, stream, timer);
+    }
   }
   if (nt) {
     const int32_t tpcn = tiles_for(C, vec, 1, kFusedNtThreads);

@@ -80,16 +80,17 @@ __global__ __launch_bounds__(THR) void reduce_scatter_kernel(
   void *dst = out.ptr[c];
   const int tid = static_cast<int>(threadIdx.x);
   if constexpr (kVector) {
+    // tiles on the inputs' grid (p streams), the one output stream follows
     const int64_t nv = C / V;
-    const int64_t base = static_cast<int64_t>(t) * (THR * VPT);
-    if (base >= nv) return;
+    const int64_t v0 = static_cast<int64_t>(c) * nv, v1 = v0 + nv;
+    const int64_t base = aligned_tile_base(v0, t, int64_t(THR) * VPT);
+    if (base >= v1) return;
     int64_t vi[VPT];
     bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int64_t j = base + u * THR + tid;
-      ok[u] = j < nv;
-      vi[u] = static_cast<int64_t>(c) * nv + j;
+      vi[u] = base + u * THR + tid;
+      ok[u] = vi[u] >= v0 && vi[u] < v1;
     }
     float acc[VPT][V];
     fold_vectors<Tr, VPT, RB, true>(TablePtrs{in}, p, first, vi, ok, acc);
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(THR) void reduce_scatter_kernel(
       if (!ok[u]) continue;
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[u][e] = apply_divide(acc[u][e], div);
-      store_vec<true>(dst, vi[u] - static_cast<int64_t>(c) * nv, Tr::narrow(acc[u]));
+      store_vec<true>(dst, vi[u] - v0, Tr::narrow(acc[u]));
     }
   } else {
     // Element-wise path for shards that are not a whole number of vectors.
@@ -142,14 +143,19 @@ __global__ __launch_bounds__(kCopyThreads * kMaxFanoutWaves) void fanout_copy_ke
   const int32_t k0 = g * p / groups, k1 = (g + 1) * p / groups;
   const int32_t rot = store_rotation(p);
   if constexpr (kVector) {
+    // tiles on the destinations' grid (they are the many streams): source
+    // s lands at s * dst_stride, so its tiles start `shift` vectors early
     const int64_t nv = bytes / 16;
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kCopyThreads * VPT);
+    constexpr int64_t kTw = int64_t(kCopyThreads) * VPT;
+    static_assert((kTw & (kTw - 1)) == 0, "tile width must be a power of two");
+    const int64_t shift = (off / 16) & (kTw - 1);
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTw - shift;
     uint4 x[VPT];
     bool ok[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       const int64_t j = base + u * kCopyThreads + tid;
-      ok[u] = j < nv;
+      ok[u] = j >= 0 && j < nv;
       if (ok[u]) x[u] = load_vec<kNtLoad>(from, j);
     }
     for (int32_t k = k0; k < k1; ++k) {
@@ -199,7 +205,9 @@ ddp_status launch_fanout(const RankTable &src, int32_t n_src, bool vec_ok,
   const bool vec = vec_ok && dst_stride % 16 == 0;
   // kCopyThreads * kCopyVpt vectors per workgroup in both paths
   const int64_t per_tile = int64_t(kCopyThreads) * kCopyVpt * 16;
-  const int64_t tiles = std::max<int64_t>(1, ceil_div(bytes, per_tile));
+  // one more tile when a source lands off the destinations' tile grid
+  const int64_t tiles = std::max<int64_t>(
+      1, ceil_div(bytes, per_tile) + (n_src > 1 && dst_stride % per_tile != 0 ? 1 : 0));
   const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(n_src));
   const size_t lds = residency_lds(DDPSIM_COPY_WGS_PER_CU);
   const bool nt = int64_t(p) * n_src * bytes > DDPSIM_COPY_NT_BYTES;
@@ -325,7 +333,9 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const int64_t per_tile =
       (narrow ? int64_t(kRsNarrowThreads) : int64_t(kRsThreads) * kRsVpt) * (vec ? 1 : V);
   const int64_t units = vec ? C / V : C;
-  const int64_t tpc = std::max<int64_t>(1, ceil_div(units, per_tile));
+  // one more tile when the chunks do not start on the vector path's tile grid
+  const int64_t tpc =
+      std::max<int64_t>(1, ceil_div(units, per_tile) + (vec && units % per_tile != 0 ? 1 : 0));
   const int64_t blocks = tpc * p;
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "%s: n too large", what);
   const RsLaunch L{dim3(static_cast<uint32_t>(blocks)), stream, &timer, tin, tout, p, C,

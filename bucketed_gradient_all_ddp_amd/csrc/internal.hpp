@@ -392,6 +392,19 @@ __device__ __forceinline__ ChunkSpan make_span(int64_t s, int64_t e, int vec) {
   return k;
 }
 
+// First vector of tile t of a chunk whose vector body starts at vector v0:
+// tiles of tw vectors (a power of two) on a grid counted from the buffer's
+// base rather than from the chunk's start, so that a tile covers whole
+// 128-byte lines of a line-aligned buffer. A chunk that starts off the grid
+// has a partial first tile (lanes below v0 idle) and perhaps one more tile
+// than its length needs; a chunk boundary that splits a line leaves that
+// line to the two chunks' tiles. (With tiles counted from each chunk's
+// start, every line straddled by a tile was written in two parts by two
+// workgroups: chunks 16 bytes off the grid cost the fused all-reduce 20%.)
+__device__ __forceinline__ int64_t aligned_tile_base(int64_t v0, int32_t t, int64_t tw) {
+  return (v0 & ~(tw - 1)) + static_cast<int64_t>(t) * tw;  // tw: a power of two
+}
+
 __device__ __forceinline__ ChunkSpan chunk_span(int64_t c, int64_t C,
                                                 int64_t n, int vec) {
   const int64_t s = c * C;

@@ -234,17 +234,16 @@ __global__ __launch_bounds__(kThreads) void schedule_step_kernel(RankTable rows,
     }
   }
 
-  const int64_t nv = (k.ve - k.vs) / V;
-  const int64_t base = static_cast<int64_t>(t) * (kThreads * VPT);
-  if (base >= nv) return;
+  const int64_t v0 = k.vs / V, v1 = k.ve / V;
+  const int64_t base = aligned_tile_base(v0, t, int64_t(kThreads) * VPT);
+  if (base >= v1) return;
   uint4 xa[VPT], xb[VPT];
   int64_t vi[VPT];
   bool ok[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    const int64_t jj = base + u * kThreads + tid;
-    ok[u] = jj < nv;
-    vi[u] = k.vs / V + jj;
+    vi[u] = base + u * kThreads + tid;
+    ok[u] = vi[u] >= v0 && vi[u] < v1;
     if (ok[u]) {
       xb[u] = load_vec(b, vi[u]);
       if (op != kOpCopy) xa[u] = load_vec(a, vi[u]);
@@ -489,10 +488,11 @@ ddp_status launch_schedule_steps(const RankTable &rows, const std::vector<Step> 
       jobs.src[j] = static_cast<int8_t>(s.jobs[j].src);
       longest = std::max(longest, s.jobs[j].end - s.jobs[j].begin);
     }
-    // vectors of the longest job, plus one for a range that straddles
+    // vectors of the longest job, plus one for a range that straddles, and
+    // one more tile for a job that starts off the tile grid
     const int64_t vectors = longest / 4 + 1;
     const int32_t tpj = static_cast<int32_t>(
-        std::max<int64_t>(1, ceil_div(vectors, int64_t(kThreads) * kStepVpt)));
+        std::max<int64_t>(1, ceil_div(vectors, int64_t(kThreads) * kStepVpt) + 1));
     const int64_t blocks = int64_t(tpj) * static_cast<int64_t>(s.jobs.size());
     if (blocks > INT32_MAX) return fail(DDP_EINVAL, "allreduce_sim: n too large");
     const bool last = ends_call && k + 1 == steps.size();

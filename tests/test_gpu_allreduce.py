@@ -153,11 +153,15 @@ def test_buffers_are_independent_allocations_at_offsets(oracle):
         assert np.all(g[r * stride: r * stride + 4] == 0)
 
 
-@pytest.mark.parametrize("bf16,p,n", [(True, 8, 17_000_003), (False, 13, 6_000_001)])
+@pytest.mark.parametrize("bf16,p,n", [(True, 8, 17_000_003), (False, 13, 6_000_001),
+                                       (True, 20, 7_000_003), (False, 29, 2_400_001),
+                                       (True, 64, 2_200_001), (False, 64, 1_100_000)])
 def test_fused_past_the_infinity_cache(oracle, bf16, p, n):
     """Rank buffers totalling more than 256 MiB take the fused kernel's
-    streaming shape (one-wave workgroups, non-temporal accesses): every
-    element against the oracle, with a divisor that is not a power of two."""
+    streaming shape (non-temporal accesses; beyond 8 ranks the ranks of a
+    tile are split over 2 or 8 waves whose running sum passes through LDS):
+    every element against the oracle, with a divisor that is not a power of
+    two."""
     host = [W.normal_np(n, 1.0, 900 + p, r) for r in range(p)]
     if bf16:
         host = [oracle.f32_to_bf16(h) for h in host]
