@@ -26,6 +26,7 @@
 #include <mutex>
 
 #include "fold.hpp"
+#include "fold_waves.hpp"
 #include "internal.hpp"
 #include "workspace.hpp"
 
@@ -97,13 +98,10 @@ __global__ __launch_bounds__(THR) void fused_allreduce_kernel(
 }
 
 // The streaming form with the ranks of a tile split over the W waves of a
-// workgroup: wave w loads ring positions [w*p/W, (w+1)*p/W) of the tile
-// (counted from rank c), adds them, in order, to the sum of the waves before
-// it, passed on through LDS, and stores the result to its share of the
-// ranks. The sum is the same left-to-right fold as above. lds holds two
-// slots of 64 * V floats, alternated between tiles so that a slot is
-// rewritten only after every wave has passed the barriers of the tile that
-// used the other one.
+// workgroup (fold_tile_waves): wave w folds ring positions [w*p/W,
+// (w+1)*p/W) of the tile (counted from rank c) after the waves before it,
+// and stores the result to its share of the ranks. lds holds the two slots
+// the fold alternates between from tile to tile.
 template <typename Tr, int W, int S>
 __global__ __launch_bounds__(64 * W) void fused_allreduce_waves_kernel(
     RankTable bufs, int32_t p, int64_t n, int64_t C, int32_t tiles_per_chunk, Divide div) {
@@ -133,37 +131,12 @@ __global__ __launch_bounds__(64 * W) void fused_allreduce_waves_kernel(
     if (base >= v1) continue;
     const int64_t vi = base + lane;
     const bool ok = vi >= v0 && vi < v1;
-    // this wave's positions, every load in flight before the first add
-    uint4 x[S];
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const bool live = lo + j < hi;  // wave-uniform
-      const void *src = bufs.ptr[live ? ring_rank(c, lo + j, p) : 0];
-      x[j] = (live && ok) ? load_vec<true>(src, vi) : make_uint4(0, 0, 0, 0);
-    }
-    float *slot = lds + (uses & 1) * (64 * V);
-    ++uses;
     float acc[V];
-    for (int32_t w = 0; w < W; ++w) {
-      if (wave == w) {
+    fold_tile_waves<Tr, W, S>(TablePtrs{bufs}, p, c, wave, lo, hi, vi, ok,
+                              lds + (uses & 1) * (64 * V), acc);
+    ++uses;
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc[e] = w == 0 ? -0.0f : slot[e * 64 + lane];
-#pragma unroll
-        for (int j = 0; j < S; ++j) {
-          if (lo + j < hi) {
-            float f[V];
-            Tr::widen(x[j], f);
-#pragma unroll
-            for (int e = 0; e < V; ++e) acc[e] = acc[e] + f[e];
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < V; ++e) slot[e * 64 + lane] = acc[e];
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] = apply_divide(slot[e * 64 + lane], div);
+    for (int e = 0; e < V; ++e) acc[e] = apply_divide(acc[e], div);
     const uint4 y = Tr::narrow(acc);
     if (!ok) continue;
     const int32_t rot = store_rotation(p);
@@ -270,9 +243,11 @@ constexpr int kFusedNtThreads = 64;
 // Waves per tile of the streaming form for p ranks, measured on identical
 // buffers against one wave: 1 up to 8 ranks (2 waves: -1% to +1.5% at 4-9
 // ranks), 2 up to 27 (+4-7% at 12-24 ranks; 8 waves lost 3-18% there), 8
-// from 28 (+6-11% at 28-64 ranks of 128-256 MiB, equal at 64 of 2 GiB).
+// from 28 (+6-11% at 28-64 ranks of 128-256 MiB, level at 64 of 2 GiB; 4
+// waves trailed 2 or 8 at every count from 20 to 64).
 int32_t fused_waves(int32_t p) {
   if (!DDPSIM_FUSED_WAVE_RULE || p <= 8) return 1;
+  if (DDPSIM_FUSED_WAVE_RULE == 2 || DDPSIM_FUSED_WAVE_RULE == 8) return DDPSIM_FUSED_WAVE_RULE;
   return p < 28 ? 2 : 8;
 }
 // Small problems (few workgroups) are latency-bound: the fold's load batches

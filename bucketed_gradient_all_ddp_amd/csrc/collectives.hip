@@ -18,6 +18,7 @@
 #include <cstring>
 
 #include "fold.hpp"
+#include "fold_waves.hpp"
 #include "internal.hpp"
 
 namespace ddpsim {
@@ -58,6 +59,12 @@ namespace {
 #endif
 #ifndef DDPSIM_COPY_WGS_PER_CU
 #define DDPSIM_COPY_WGS_PER_CU 0
+#endif
+#ifndef DDPSIM_RS_WAVE_RULE
+#define DDPSIM_RS_WAVE_RULE 1  // 0: never split a tile's ranks over waves; 2, 8: always W
+#endif
+#ifndef DDPSIM_RS_WAVES_BYTES
+#define DDPSIM_RS_WAVES_BYTES (int64_t(256) << 20)  // inputs past the Infinity Cache
 #endif
 constexpr int kRsThreads = DDPSIM_RS_THREADS;
 constexpr int kRsVpt = DDPSIM_RS_VPT;
@@ -110,6 +117,34 @@ __global__ __launch_bounds__(THR) void reduce_scatter_kernel(
       Tr::store1(dst, j, y);
     }
   }
+}
+
+// The same reduce-scatter on the vector path with the ranks of a 64-vector
+// tile split over the W waves of a workgroup (fold_tile_waves): one tile per
+// workgroup, and the first wave stores the finished sum.
+template <typename Tr, int W, int S>
+__global__ __launch_bounds__(64 * W) void reduce_scatter_waves_kernel(
+    RankTable in, RankTable out, int32_t p, int64_t C, int32_t tiles_per_chunk, Divide div) {
+  extern __shared__ float lds[];
+  constexpr int V = Tr::kVec;
+  const int32_t c = static_cast<int32_t>(blockIdx.x) / tiles_per_chunk;
+  const int32_t t = static_cast<int32_t>(blockIdx.x) - c * tiles_per_chunk;
+  const int32_t first = c + 1 == p ? 0 : c + 1;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(threadIdx.x) >> 6);
+  const int32_t lo = wave * p / W, hi = (wave + 1) * p / W;
+  const int64_t nv = C / V;
+  const int64_t v0 = static_cast<int64_t>(c) * nv, v1 = v0 + nv;
+  const int64_t base = aligned_tile_base(v0, t, 64);
+  if (base >= v1) return;  // workgroup-uniform
+  const int64_t vi = base + lane;
+  const bool ok = vi >= v0 && vi < v1;
+  float acc[V];
+  fold_tile_waves<Tr, W, S>(TablePtrs{in}, p, first, wave, lo, hi, vi, ok, lds, acc);
+  if (wave != 0 || !ok) return;
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = apply_divide(acc[e], div);
+  store_vec<true>(out.ptr[c], vi - v0, Tr::narrow(acc));
 }
 
 // Copy `bytes` from each source s (blockIdx.y) to every destination r at
@@ -263,6 +298,50 @@ ddp_status launch_rs_as(const RsLaunch &L, size_t lds) {
                     L.C, L.tiles_per_chunk, L.div);
 }
 
+// Waves per tile of the reduce-scatter's split form for p ranks (1: the
+// shapes above). Measured on identical buffers past the Infinity Cache
+// against those shapes: 2 waves lost at 12 ranks (0.83 -> 0.75 of peak),
+// were level at 16 and 17, and gained from 20 up (20-28 ranks 0.72-0.73 ->
+// 0.80-0.82, 40 ranks 0.74 -> 0.79, 64 ranks 0.745 -> 0.79); 4 and 8 waves
+// lost everywhere below 64 ranks and trailed 2 waves at 64.
+int32_t rs_waves(int32_t p) {
+  if (!DDPSIM_RS_WAVE_RULE || p <= 8) return 1;
+  if (DDPSIM_RS_WAVE_RULE == 2 || DDPSIM_RS_WAVE_RULE == 8) return DDPSIM_RS_WAVE_RULE;
+  return p <= 16 ? 1 : 2;
+}
+
+template <int W>
+ddp_status launch_rs_waves(const RsLaunch &L, int32_t dtype) {
+  // the residency bound counts waves: ceil(bound / W) workgroups per CU
+  const int32_t bound = fold_residency(DDPSIM_RS_WGS_PER_CU, L.p);
+  const int vec = dtype == DDP_F32 ? F32Traits::kVec : BF16Traits::kVec;
+  const size_t lds = std::max(residency_lds(bound > 0 ? (bound + W - 1) / W : 0),
+                              size_t(64) * vec * sizeof(float));
+  constexpr int kLarge = (kMaxRanks + W - 1) / W;
+  constexpr int kSmall = kLarge < 8 ? kLarge : 8;
+  const bool few = (L.p + W - 1) / W <= kSmall;
+  const char *kname = "reduce_scatter_waves_kernel launch";
+  const dim3 block(64 * W);
+  if (dtype == DDP_F32) {
+    if (few) {
+      return launch_lds(reduce_scatter_waves_kernel<F32Traits, W, kSmall>, L.grid, block, lds,
+                        L.stream, *L.timer, true, kname, L.in, L.out, L.p, L.C,
+                        L.tiles_per_chunk, L.div);
+    }
+    return launch_lds(reduce_scatter_waves_kernel<F32Traits, W, kLarge>, L.grid, block, lds,
+                      L.stream, *L.timer, true, kname, L.in, L.out, L.p, L.C, L.tiles_per_chunk,
+                      L.div);
+  }
+  if (few) {
+    return launch_lds(reduce_scatter_waves_kernel<BF16Traits, W, kSmall>, L.grid, block, lds,
+                      L.stream, *L.timer, true, kname, L.in, L.out, L.p, L.C, L.tiles_per_chunk,
+                      L.div);
+  }
+  return launch_lds(reduce_scatter_waves_kernel<BF16Traits, W, kLarge>, L.grid, block, lds,
+                    L.stream, *L.timer, true, kname, L.in, L.out, L.p, L.C, L.tiles_per_chunk,
+                    L.div);
+}
+
 template <int VPT, int THR>
 ddp_status launch_rs(const RsLaunch &L, int32_t dtype, bool vec, size_t lds) {
   if (dtype == DDP_F32) {
@@ -329,10 +408,22 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const RankTable tout = make_table(reinterpret_cast<const void *const *>(out), p);
   const int V = dtype == DDP_F32 ? 4 : 8;
   const bool vec = C % V == 0 && all_vec_aligned(reinterpret_cast<const void *const *>(out), p);
+  const int64_t units = vec ? C / V : C;
+  const int32_t waves = rs_waves(p);
+  if (vec && waves > 1 && int64_t(p) * n * eb > DDPSIM_RS_WAVES_BYTES) {
+    // tiles of 64 vectors on the inputs' grid, one more when chunks are off it
+    const int64_t tpcw = std::max<int64_t>(1, ceil_div(units, 64) + (units % 64 != 0 ? 1 : 0));
+    const int64_t bw = tpcw * p;
+    // a launch holds at most 2^32 - 1 threads; past that the shapes below run
+    if (bw * 64 * waves <= int64_t(UINT32_MAX)) {
+      const RsLaunch Lw{dim3(static_cast<uint32_t>(bw)), stream, &timer, tin, tout, p, C,
+                        static_cast<int32_t>(tpcw), div};
+      return waves == 2 ? launch_rs_waves<2>(Lw, dtype) : launch_rs_waves<8>(Lw, dtype);
+    }
+  }
   const bool narrow = p <= DDPSIM_RS_NARROW_MAX_RANKS;
   const int64_t per_tile =
       (narrow ? int64_t(kRsNarrowThreads) : int64_t(kRsThreads) * kRsVpt) * (vec ? 1 : V);
-  const int64_t units = vec ? C / V : C;
   // one more tile when the chunks do not start on the vector path's tile grid
   const int64_t tpc =
       std::max<int64_t>(1, ceil_div(units, per_tile) + (vec && units % per_tile != 0 ? 1 : 0));

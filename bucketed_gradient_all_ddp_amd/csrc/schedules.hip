@@ -53,50 +53,61 @@ constexpr int bit_reverse(int t, int k) {
 // subtree, and the batch sum joins the earlier batches like a binary
 // counter (pending sums of 1, 2 and 4 batches in c[0..2]). The batch loop is
 // not unrolled, so a thread holds one batch of vectors at a time.
+
+// The complete subtree of visit-order batch m (leaves m*RB .. m*RB+RB-1 in
+// visit order, each with its extra rank folded in first).
 template <int Q, bool kHalvingFirst, int W, typename LeafLoad>
-__device__ __forceinline__ void tree_fold(const LeafLoad &leaf, int32_t extra,
-                                          float (&out)[W]) {
+__device__ __forceinline__ void tree_batch(const LeafLoad &leaf, int32_t extra, int m,
+                                           float (&s)[W]) {
   constexpr int K = ilog2(Q);
   constexpr int RB = Q < 8 ? Q : 8;
   constexpr int KB = ilog2(RB);
   constexpr int B = Q / RB;
   // p < 2Q, so with Q at the rank limit there are no extra ranks
   constexpr bool kExtras = Q < kMaxRanks;
+  int low = 0;  // the visit-order batch number's contribution to the leaf index
+  if constexpr (B > 1) {
+    low = kHalvingFirst ? static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(m)) >>
+                                           (32 - (K - KB)))
+                        : m * RB;
+  }
+  float x[RB][W], y[RB][W];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int u = kHalvingFirst ? (bit_reverse(j, KB) << (K - KB)) + low : low + j;
+    leaf(u, x[j]);
+    if (kExtras && u < extra) leaf(u + Q, y[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int u = kHalvingFirst ? (bit_reverse(j, KB) << (K - KB)) + low : low + j;
+    if (kExtras && u < extra) {
+#pragma unroll
+      for (int e = 0; e < W; ++e) x[j][e] = x[j][e] + y[j][e];
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < RB; d *= 2) {
+#pragma unroll
+    for (int j = 0; j < RB; j += 2 * d) {
+#pragma unroll
+      for (int e = 0; e < W; ++e) x[j][e] = x[j][e] + x[j + d][e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < W; ++e) s[e] = x[0][e];
+}
+
+template <int Q, bool kHalvingFirst, int W, typename LeafLoad>
+__device__ __forceinline__ void tree_fold(const LeafLoad &leaf, int32_t extra,
+                                          float (&out)[W]) {
+  constexpr int RB = Q < 8 ? Q : 8;
+  constexpr int B = Q / RB;
   float c[3][W];
 #pragma unroll 1
   for (int m = 0; m < B; ++m) {
-    int low = 0;  // the visit-order batch number's contribution to the leaf index
-    if constexpr (B > 1) {
-      low = kHalvingFirst ? static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(m)) >>
-                                             (32 - (K - KB)))
-                          : m * RB;
-    }
-    float x[RB][W], y[RB][W];
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int u = kHalvingFirst ? (bit_reverse(j, KB) << (K - KB)) + low : low + j;
-      leaf(u, x[j]);
-      if (kExtras && u < extra) leaf(u + Q, y[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int u = kHalvingFirst ? (bit_reverse(j, KB) << (K - KB)) + low : low + j;
-      if (kExtras && u < extra) {
-#pragma unroll
-        for (int e = 0; e < W; ++e) x[j][e] = x[j][e] + y[j][e];
-      }
-    }
-#pragma unroll
-    for (int d = 1; d < RB; d *= 2) {
-#pragma unroll
-      for (int j = 0; j < RB; j += 2 * d) {
-#pragma unroll
-        for (int e = 0; e < W; ++e) x[j][e] = x[j][e] + x[j + d][e];
-      }
-    }
     float s[W];
-#pragma unroll
-    for (int e = 0; e < W; ++e) s[e] = x[0][e];
+    tree_batch<Q, kHalvingFirst>(leaf, extra, m, s);
     if (m & 1) {
 #pragma unroll
       for (int e = 0; e < W; ++e) s[e] = c[0][e] + s[e];
@@ -143,6 +154,18 @@ struct ElementLeaf {
   }
 };
 
+// A vector leaf for lanes that may lie past the last vector (those load
+// nothing and fold zeros that are never stored).
+template <typename Tr, bool kNT>
+struct MaskedVectorLeaf {
+  const RankTable &bufs;
+  int64_t v;
+  bool ok;
+  __device__ __forceinline__ void operator()(int u, float (&w)[Tr::kVec]) const {
+    Tr::widen(ok ? load_vec<kNT>(bufs.ptr[u], v) : make_uint4(0, 0, 0, 0), w);
+  }
+};
+
 // One thread per 16-byte vector; thread nv (one past the last vector) folds
 // the fewer-than-V tail elements one by one. Ranks Q..p-1 (extra = p - Q of
 // them) are folded into ranks 0..extra-1 first.
@@ -174,6 +197,62 @@ __global__ __launch_bounds__(kTreeThreads) void tree_allreduce_kernel(RankTable 
     const int32_t rot = store_rotation(p);
     for (int32_t k = 0; k < p; ++k) store_vec<kNT>(bufs.ptr[ring_rank(rot, k, p)], g, y);
   } else if (g == nv) {
+    for (int64_t i = nv * V; i < n; ++i) {
+      float acc[1];
+      tree_fold<Q, kHalvingFirst>(ElementLeaf<Tr>{bufs, i}, extra, acc);
+      const float y = apply_divide(acc[0], div);
+      for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
+    }
+  }
+}
+
+// The streaming form for Q >= 16 with the batches of a tile split over the
+// Q / 8 waves of a workgroup: wave m sums batch m (a complete subtree of 8
+// visit-order leaves), the batch sums meet in LDS, and every wave joins them
+// the way the binary counter above does (earlier + later at every level of
+// a balanced tree over the batches), then stores the result to its share of
+// the ranks. Same bits as tree_allreduce_kernel. lds holds Q / 8 * 64 * V
+// floats.
+template <typename Tr, int Q, bool kHalvingFirst>
+__global__ __launch_bounds__(8 * Q) void tree_allreduce_waves_kernel(RankTable bufs, int32_t p,
+                                                                    int64_t n, Divide div) {
+  extern __shared__ float lds[];
+  constexpr int V = Tr::kVec;
+  constexpr int W = Q / 8;
+  static_assert(Q >= 16 && W * 8 == Q, "one batch of 8 leaves per wave");
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(threadIdx.x) >> 6);
+  const int32_t extra = p - Q;
+  const int64_t nv = n / V;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool ok = g < nv;
+  float s[V];
+  tree_batch<Q, kHalvingFirst>(MaskedVectorLeaf<Tr, true>{bufs, g, ok}, extra, wave, s);
+#pragma unroll
+  for (int e = 0; e < V; ++e) lds[(wave * V + e) * 64 + lane] = s[e];
+  __syncthreads();
+  float t[W][V];
+#pragma unroll
+  for (int m = 0; m < W; ++m) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) t[m][e] = lds[(m * V + e) * 64 + lane];
+  }
+#pragma unroll
+  for (int d = 1; d < W; d *= 2) {
+#pragma unroll
+    for (int m = 0; m < W; m += 2 * d) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) t[m][e] = t[m][e] + t[m + d][e];
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) t[0][e] = apply_divide(t[0][e], div);
+    const uint4 y = Tr::narrow(t[0]);
+    const int32_t rot = store_rotation(p);
+    const int32_t lo = wave * p / W, hi = (wave + 1) * p / W;
+    for (int32_t k = lo; k < hi; ++k) store_vec<true>(bufs.ptr[ring_rank(rot, k, p)], g, y);
+  } else if (g == nv && wave == 0) {
     for (int64_t i = nv * V; i < n; ++i) {
       float acc[1];
       tree_fold<Q, kHalvingFirst>(ElementLeaf<Tr>{bufs, i}, extra, acc);
@@ -425,6 +504,9 @@ void fill_stats(ddp_comm_stats *st, const std::vector<Step> &steps, int32_t p, i
 // Host: launches
 // ---------------------------------------------------------------------------
 
+#ifndef DDPSIM_TREE_WAVES
+#define DDPSIM_TREE_WAVES 1  // 16 ranks and more past the Infinity Cache: a batch per wave
+#endif
 #ifndef DDPSIM_TREE_NT_BYTES
 #define DDPSIM_TREE_NT_BYTES (int64_t(256) << 20)  // as the ring's fused kernel
 #endif
@@ -437,7 +519,20 @@ ddp_status launch_tree_q(const RankTable &tab, int32_t p, int64_t n, const Divid
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "allreduce_sim: n too large");
   const dim3 grid(static_cast<uint32_t>(blocks));
   const char *what = "tree_allreduce_kernel launch";
-  const size_t lds = residency_lds(fold_residency(DDPSIM_TREE_WGS_PER_CU, p));
+  const int32_t bound = fold_residency(DDPSIM_TREE_WGS_PER_CU, p);
+  if constexpr (Q >= 16) {
+    constexpr int W = Q / 8;
+    // a launch holds at most 2^32 - 1 threads; past that the one-wave form runs
+    if (nt && DDPSIM_TREE_WAVES && blocks * 64 * W <= int64_t(UINT32_MAX)) {
+      // the residency bound counts waves: ceil(bound / W) workgroups per CU
+      const size_t lds = std::max(residency_lds(bound > 0 ? (bound + W - 1) / W : 0),
+                                  size_t(W) * 64 * Tr::kVec * sizeof(float));
+      return launch_lds(tree_allreduce_waves_kernel<Tr, Q, kHalvingFirst>, grid, dim3(64 * W),
+                        lds, stream, timer, true, "tree_allreduce_waves_kernel launch", tab, p,
+                        n, div);
+    }
+  }
+  const size_t lds = residency_lds(bound);
   if (nt) {
     return launch_lds(tree_allreduce_kernel<Tr, Q, kHalvingFirst, true>, grid, dim3(kTreeThreads),
                       lds, stream, timer, true, what, tab, p, n, div);

@@ -135,3 +135,30 @@ def test_few_ranks_past_the_infinity_cache(oracle, p):
     want, _ = oracle.ring_allreduce(host, avg="tokens", tokens=tokens, want_log=False)
     for r in range(p):
         assert_bits_equal(to_host(ins[r]), want[r], f"all-reduce rank {r}")
+
+
+@pytest.mark.parametrize("p,C,bf16,in_place,avg", [
+    (17, 240_004, False, False, "world"),   # chunks off the 64-vector tile grid
+    (20, 336_008, True, True, "tokens"),
+    (40, 83_896, True, False, "none"),
+    (64, 16_388, False, True, "tokens"),
+    (64, 16_390, False, False, "world"),    # shards not whole vectors: element path
+])
+def test_reduce_scatter_many_ranks_past_the_infinity_cache(oracle, p, C, bf16, in_place, avg):
+    """Beyond 16 ranks of inputs past the Infinity Cache the reduce-scatter
+    splits a tile's ranks over two waves whose running sum passes through
+    LDS: every element of every shard against the oracle."""
+    n = p * C
+    assert p * n * (2 if bf16 else 4) > 256 << 20
+    host = _vals(p, n, 670 + p, bf16, oracle)
+    tokens = tokens_for(p, 3) if avg == "tokens" else None
+    ins = [to_dev(h) for h in host]
+    if in_place:
+        outs = [ins[r][r * C:(r + 1) * C] for r in range(p)]
+    else:
+        outs = [torch.empty(C, dtype=ins[0].dtype, device="cuda") for _ in range(p)]
+    ddp.reduce_scatter_sim(ins, outs, avg=avg, tokens=tokens)
+    torch.cuda.synchronize()
+    want, _ = oracle.reduce_scatter(host, avg=avg, tokens=tokens)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"rank {r}")

@@ -162,3 +162,26 @@ def test_crossover_sweep_largest_size_whole(oracle, schedule):
         got, _ = _run(host, schedule, steps, "world")
         for r in range(p):
             assert_bits_equal(got[r], want[r], f"{schedule} steps={steps} rank {r}")
+
+
+@pytest.mark.parametrize("schedule", LOG_SCHEDULES)
+@pytest.mark.parametrize("p,n,bf16,avg", [
+    (16, 4_194_305, False, "world"),   # a tail shorter than a vector
+    (24, 5_592_408, True, "tokens"),
+    (40, 1_677_723, False, "none"),
+    (64, 1_048_579, False, "tokens"),
+])
+def test_fused_many_ranks_past_the_infinity_cache(oracle, schedule, p, n, bf16, avg):
+    """From 16 ranks of buffers past the Infinity Cache the fused kernel
+    gives each wave of a workgroup one batch of eight leaves and joins the
+    batch sums through LDS: every element of every rank against the
+    oracle's literal schedule."""
+    assert p * n * (2 if bf16 else 4) > 256 << 20
+    host = [W.normal_np(n, 1.0, 800 + p, r) for r in range(p)]
+    if bf16:
+        host = [oracle.f32_to_bf16(h) for h in host]
+    tokens = tokens_for(p, 4) if avg == "tokens" else None
+    got, _ = _run(host, schedule, False, avg, tokens)
+    want, _ = oracle.allreduce(host, schedule, avg=avg, tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(got[r], want[r], f"{schedule} rank {r}")
