@@ -98,50 +98,43 @@ __global__ __launch_bounds__(THR) void fused_allreduce_kernel(
 }
 
 // The streaming form with the ranks of a tile split over the W waves of a
-// workgroup (fold_tile_waves): wave w folds ring positions [w*p/W,
-// (w+1)*p/W) of the tile (counted from rank c) after the waves before it,
-// and stores the result to its share of the ranks. lds holds the two slots
-// the fold alternates between from tile to tile.
+// workgroup (fold_tile_waves): workgroup = tile, wave w folds ring positions
+// [w*p/W, (w+1)*p/W) of the tile (counted from rank c) after the waves
+// before it, and stores the result to its share of the ranks.
 template <typename Tr, int W, int S>
 __global__ __launch_bounds__(64 * W) void fused_allreduce_waves_kernel(
     RankTable bufs, int32_t p, int64_t n, int64_t C, int32_t tiles_per_chunk, Divide div) {
-  extern __shared__ float lds[];
+  extern __shared__ float lds[];  // 64 * V floats (more when it bounds residency)
   constexpr int V = Tr::kVec;
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(threadIdx.x) >> 6);
-  const int32_t lo = wave * p / W, hi = (wave + 1) * p / W;
-  const int64_t total = int64_t(tiles_per_chunk) * p;
-  int32_t uses = 0;
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int32_t c = static_cast<int32_t>(tile / tiles_per_chunk);
-    const int32_t t = static_cast<int32_t>(tile - int64_t(c) * tiles_per_chunk);
-    const ChunkSpan k = chunk_span(c, C, n, V);
-    if (k.s >= k.e) continue;
-    if (t == 0 && wave == 0 && lane >= 64 - 2 * (V - 1)) {
-      const int e = lane - (64 - 2 * (V - 1));
-      const bool head = e < V - 1;
-      const int64_t i = head ? k.s + e : k.tail_begin + (e - (V - 1));
-      if (i < (head ? k.head_end : k.e)) {
-        const float y = apply_divide(fold_scalar<Tr>(TablePtrs{bufs}, p, c, i), div);
-        for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
-      }
+  const int32_t c = static_cast<int32_t>(blockIdx.x) / tiles_per_chunk;
+  const int32_t t = static_cast<int32_t>(blockIdx.x) - c * tiles_per_chunk;
+  const ChunkSpan k = chunk_span(c, C, n, V);
+  if (k.s >= k.e) return;  // workgroup-uniform
+  if (t == 0 && wave == 0 && lane >= 64 - 2 * (V - 1)) {
+    const int e = lane - (64 - 2 * (V - 1));
+    const bool head = e < V - 1;
+    const int64_t i = head ? k.s + e : k.tail_begin + (e - (V - 1));
+    if (i < (head ? k.head_end : k.e)) {
+      const float y = apply_divide(fold_scalar<Tr>(TablePtrs{bufs}, p, c, i), div);
+      for (int32_t r = 0; r < p; ++r) Tr::store1(bufs.ptr[r], i, y);
     }
-    const int64_t v0 = k.vs / V, v1 = k.ve / V;
-    const int64_t base = aligned_tile_base(v0, t, 64);
-    if (base >= v1) continue;
-    const int64_t vi = base + lane;
-    const bool ok = vi >= v0 && vi < v1;
-    float acc[V];
-    fold_tile_waves<Tr, W, S>(TablePtrs{bufs}, p, c, wave, lo, hi, vi, ok,
-                              lds + (uses & 1) * (64 * V), acc);
-    ++uses;
-#pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] = apply_divide(acc[e], div);
-    const uint4 y = Tr::narrow(acc);
-    if (!ok) continue;
-    const int32_t rot = store_rotation(p);
-    for (int32_t r = lo; r < hi; ++r) store_vec<true>(bufs.ptr[ring_rank(rot, r, p)], vi, y);
   }
+  const int64_t v0 = k.vs / V, v1 = k.ve / V;
+  const int64_t base = aligned_tile_base(v0, t, 64);
+  if (base >= v1) return;  // workgroup-uniform
+  const int64_t vi = base + lane;
+  const bool ok = vi >= v0 && vi < v1;
+  const int32_t lo = wave * p / W, hi = (wave + 1) * p / W;
+  float acc[V];
+  fold_tile_waves<Tr, W, S>(TablePtrs{bufs}, p, c, wave, lo, hi, vi, ok, lds, acc);
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = apply_divide(acc[e], div);
+  const uint4 y = Tr::narrow(acc);
+  if (!ok) return;
+  const int32_t rot = store_rotation(p);
+  for (int32_t r = lo; r < hi; ++r) store_vec<true>(bufs.ptr[ring_rank(rot, r, p)], vi, y);
 }
 
 // One ring step on p fp32 buffers. Sender r = blockIdx.x / tiles_per_chunk
@@ -313,7 +306,7 @@ ddp_status launch_fused_waves(const RankTable &tab, int32_t p, int64_t n, int64_
   const int32_t bound = fold_residency(DDPSIM_FUSED_NT_WGS_PER_CU, p);
   const size_t lds_bound = residency_lds(bound > 0 ? (bound + W - 1) / W : 0);
   const int vec = dtype == DDP_F32 ? F32Traits::kVec : BF16Traits::kVec;
-  const size_t lds = std::max(lds_bound, size_t(2) * 64 * vec * sizeof(float));
+  const size_t lds = std::max(lds_bound, size_t(64) * vec * sizeof(float));
   constexpr int kLarge = W > 1 ? (kMaxRanks + W - 1) / W : 1;
   constexpr int kSmall = kLarge < 8 ? kLarge : 8;
   const bool few = (p + W - 1) / W <= kSmall;

@@ -20,9 +20,8 @@ namespace ddpsim {
 // [lo, hi) = [wave*p/W, (wave+1)*p/W), at most S of them; every wave of the
 // workgroup must call this with the same tile (it contains W barriers), and
 // every wave returns the finished sum in acc. slot is 64 * Tr::kVec floats
-// of LDS. A workgroup that folds several tiles alternates between two slots:
-// a slot is then rewritten only after every wave has passed the barriers of
-// the tile that used the other one, i.e. after every wave has read the sum.
+// of LDS that hold the sum after the call, so the kernels take one tile per
+// workgroup.
 template <typename Tr, int W, int S, typename Ptrs>
 __device__ __forceinline__ void fold_tile_waves(const Ptrs &ptr_of, int32_t p, int32_t first,
                                                 int32_t wave, int32_t lo, int32_t hi,
