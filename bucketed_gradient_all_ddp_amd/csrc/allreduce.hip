@@ -231,7 +231,7 @@ constexpr int kFusedRb = DDPSIM_FUSED_RB;
 constexpr int kFusedThreads = DDPSIM_FUSED_THREADS;
 constexpr int kFusedNtThreads = 64;
 #ifndef DDPSIM_FUSED_WAVE_RULE
-#define DDPSIM_FUSED_WAVE_RULE 1  // 0: one wave per tile at every p
+#define DDPSIM_FUSED_WAVE_RULE 1  // 0: one wave per tile at every p; 2, 8: always W beyond 8 ranks
 #endif
 // Waves per tile of the streaming form for p ranks, measured on identical
 // buffers against one wave: 1 up to 8 ranks (2 waves: -1% to +1.5% at 4-9
