@@ -230,6 +230,13 @@ constexpr int kFusedVpt = DDPSIM_FUSED_VPT;
 constexpr int kFusedRb = DDPSIM_FUSED_RB;
 constexpr int kFusedThreads = DDPSIM_FUSED_THREADS;
 constexpr int kFusedNtThreads = 64;
+#ifndef DDPSIM_FUSED_SMALL_WAVES
+// Small problems beyond 32 ranks take the 8-wave form: at 64 ranks a call on
+// a tensor of 1,000 to 65,528 elements went from 12-14 us to 6-7 us (dispatch
+// events included), the latency workload's 20,000 per-tensor calls replayed
+// from a HIP graph from 336 to 270 ms.
+#define DDPSIM_FUSED_SMALL_WAVES 1
+#endif
 #ifndef DDPSIM_FUSED_WAVE_RULE
 #define DDPSIM_FUSED_WAVE_RULE 1  // 0: one wave per tile at every p; 2, 8: always W beyond 8 ranks
 #endif
@@ -336,6 +343,19 @@ ddp_status launch_fused(const RankTable &tab, int32_t p, int64_t n, int32_t dtyp
   const int32_t tpc = tiles_for(C, vec, kFusedVpt, kFusedThreads);
   const int64_t blocks = int64_t(tpc) * p;
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "ring_allreduce_sim: n too large");
+  if (DDPSIM_FUSED_SMALL_WAVES && p > kSmallRb && blocks * 2 <= kSmallBlocks) {
+    // latency-bound with more ranks than one batch: every rank load of a
+    // tile at once, split over 8 waves (64 ranks: one memory latency, not two)
+    const int32_t tpcn = tiles_for(C, vec, 1, kFusedNtThreads);
+    const dim3 gridn(static_cast<uint32_t>(int64_t(tpcn) * p));
+    const size_t lds = size_t(64) * vec * sizeof(float);
+    if (dtype == DDP_F32) {
+      return launch_lds(fused_allreduce_waves_kernel<F32Traits, 8, 8>, gridn, dim3(512), lds,
+                        stream, timer, true, kname, tab, p, n, C, tpcn, div);
+    }
+    return launch_lds(fused_allreduce_waves_kernel<BF16Traits, 8, 8>, gridn, dim3(512), lds,
+                      stream, timer, true, kname, tab, p, n, C, tpcn, div);
+  }
   if (p > kFusedRb && blocks * 2 <= kSmallBlocks) {
     // latency-bound: one vector per thread, 32 loads in flight
     const int32_t tpc1 = tiles_for(C, vec, 1);

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 CASES = [(1, 0), (1, 7), (2, 1), (2, 9), (3, 10), (4, 10), (4, 1_000_003), (5, 3),
          (5, 4099), (7, 50), (8, 8), (8, 61), (8, 8 * 65536 + 5), (13, 100_003),
-         (16, 257), (64, 200), (64, 100_000)]
+         (16, 257), (33, 137), (40, 40_003), (48, 1_000), (64, 200), (64, 100_000)]
 
 
 def _run(host, avg, tokens, algo):
@@ -51,7 +51,7 @@ def test_allreduce_f32_bit_exact(oracle, p, n, avg, algo):
 
 @pytest.mark.parametrize("algo", ["fused", "ring"])
 @pytest.mark.parametrize("p,n", [(2, 1), (3, 10), (4, 1_000_003), (8, 4097), (8, 1 << 20),
-                                 (16, 100_000), (64, 65_536 + 3)])
+                                 (16, 100_000), (33, 5_003), (64, 1_031), (64, 65_536 + 3)])
 def test_allreduce_bf16_bit_exact(oracle, p, n, algo):
     host = [oracle.f32_to_bf16(W.normal_np(n, 1e-2, 200 + p, r)) for r in range(p)]
     got, _ = _run(host, "world", None, algo)
