@@ -66,6 +66,9 @@ namespace {
 #ifndef DDPSIM_RS_WAVES_BYTES
 #define DDPSIM_RS_WAVES_BYTES (int64_t(256) << 20)  // inputs past the Infinity Cache
 #endif
+#ifndef DDPSIM_RS_WAVES_SMALL_TILES
+#define DDPSIM_RS_WAVES_SMALL_TILES 512  // calls of at most this many tiles are latency-bound
+#endif
 constexpr int kRsThreads = DDPSIM_RS_THREADS;
 constexpr int kRsVpt = DDPSIM_RS_VPT;
 constexpr int kRsNarrowThreads = 64;
@@ -304,10 +307,16 @@ ddp_status launch_rs_as(const RsLaunch &L, size_t lds) {
 // were level at 16 and 17, and gained from 20 up (20-28 ranks 0.72-0.73 ->
 // 0.80-0.82, 40 ranks 0.74 -> 0.79, 64 ranks 0.745 -> 0.79); 4 and 8 waves
 // lost everywhere below 64 ranks and trailed 2 waves at 64.
-int32_t rs_waves(int32_t p) {
-  if (!DDPSIM_RS_WAVE_RULE || p <= 8) return 1;
+// A small call (at most DDPSIM_RS_WAVES_SMALL_TILES tiles) is latency-bound
+// and takes 8 waves from 17 ranks on: 64 ranks, shards of 64 and 1,024
+// elements, 10.0 -> 4.6 and 15.6 -> 4.8 us per call (2 waves: 5.5, 5.8);
+// 32 ranks 7.0 -> 4.1 us. Between the two regimes (inputs in the Infinity
+// Cache, more tiles) the split gained nothing (2 waves) or lost (8 waves).
+int32_t rs_waves(int32_t p, bool small) {
+  if (!DDPSIM_RS_WAVE_RULE || p <= 16) return 1;
+  if (small) return 8;
   if (DDPSIM_RS_WAVE_RULE == 2 || DDPSIM_RS_WAVE_RULE == 8) return DDPSIM_RS_WAVE_RULE;
-  return p <= 16 ? 1 : 2;
+  return 2;
 }
 
 template <int W>
@@ -409,13 +418,16 @@ extern "C" ddp_status reduce_scatter_sim(const void *const *in, void *const *out
   const int V = dtype == DDP_F32 ? 4 : 8;
   const bool vec = C % V == 0 && all_vec_aligned(reinterpret_cast<const void *const *>(out), p);
   const int64_t units = vec ? C / V : C;
-  const int32_t waves = rs_waves(p);
-  if (vec && waves > 1 && int64_t(p) * n * eb > DDPSIM_RS_WAVES_BYTES) {
+  if (vec) {
     // tiles of 64 vectors on the inputs' grid, one more when chunks are off it
     const int64_t tpcw = std::max<int64_t>(1, ceil_div(units, 64) + (units % 64 != 0 ? 1 : 0));
     const int64_t bw = tpcw * p;
-    // a launch holds at most 2^32 - 1 threads; past that the shapes below run
-    if (bw * 64 * waves <= int64_t(UINT32_MAX)) {
+    const bool small = bw <= DDPSIM_RS_WAVES_SMALL_TILES;
+    const int32_t waves = rs_waves(p, small);
+    // past the Infinity Cache or latency-bound; a launch holds at most
+    // 2^32 - 1 threads, and past that the shapes below run
+    if (waves > 1 && (small || int64_t(p) * n * eb > DDPSIM_RS_WAVES_BYTES) &&
+        bw * 64 * waves <= int64_t(UINT32_MAX)) {
       const RsLaunch Lw{dim3(static_cast<uint32_t>(bw)), stream, &timer, tin, tout, p, C,
                         static_cast<int32_t>(tpcw), div};
       return waves == 2 ? launch_rs_waves<2>(Lw, dtype) : launch_rs_waves<8>(Lw, dtype);

@@ -510,10 +510,20 @@ void fill_stats(ddp_comm_stats *st, const std::vector<Step> &steps, int32_t p, i
 #ifndef DDPSIM_TREE_NT_BYTES
 #define DDPSIM_TREE_NT_BYTES (int64_t(256) << 20)  // as the ring's fused kernel
 #endif
+#ifndef DDPSIM_TREE_WAVES_BYTES
+#define DDPSIM_TREE_WAVES_BYTES DDPSIM_TREE_NT_BYTES  // the split form above this many bytes
+#endif
+#ifndef DDPSIM_TREE_WAVES_SMALL_TILES
+// ... and at or below this many 64-vector tiles. Against one wave per tile:
+// 64 ranks of 4,096 or 65,536 elements 9.4 -> 4.1 and 11.3 -> 5.5 us per
+// call; between the two regimes (64 ranks of 1 Mi elements, in the
+// Infinity Cache) the split lost 20% (79 -> 95 us), 32 and 24 ranks 10-28%.
+#define DDPSIM_TREE_WAVES_SMALL_TILES 512
+#endif
 
 template <typename Tr, int Q, bool kHalvingFirst>
 ddp_status launch_tree_q(const RankTable &tab, int32_t p, int64_t n, const Divide &div,
-                         bool nt, hipStream_t stream, CallTimer &timer) {
+                         bool nt, bool waves, hipStream_t stream, CallTimer &timer) {
   const int64_t nv = n / Tr::kVec;
   const int64_t blocks = ceil_div(nv + 1, kTreeThreads);
   if (blocks > INT32_MAX) return fail(DDP_EINVAL, "allreduce_sim: n too large");
@@ -523,7 +533,9 @@ ddp_status launch_tree_q(const RankTable &tab, int32_t p, int64_t n, const Divid
   if constexpr (Q >= 16) {
     constexpr int W = Q / 8;
     // a launch holds at most 2^32 - 1 threads; past that the one-wave form runs
-    if (nt && DDPSIM_TREE_WAVES && blocks * 64 * W <= int64_t(UINT32_MAX)) {
+    // past the Infinity Cache, or few enough tiles that a call is latency-bound
+    const bool split = waves || blocks <= DDPSIM_TREE_WAVES_SMALL_TILES;
+    if (split && DDPSIM_TREE_WAVES && blocks * 64 * W <= int64_t(UINT32_MAX)) {
       // the residency bound counts waves: ceil(bound / W) workgroups per CU
       const size_t lds = std::max(residency_lds(bound > 0 ? (bound + W - 1) / W : 0),
                                   size_t(W) * 64 * Tr::kVec * sizeof(float));
@@ -543,29 +555,32 @@ ddp_status launch_tree_q(const RankTable &tab, int32_t p, int64_t n, const Divid
 
 template <typename Tr, bool kHalvingFirst>
 ddp_status launch_tree(const RankTable &tab, int32_t p, int64_t n, const Divide &div, bool nt,
-                       hipStream_t stream, CallTimer &timer) {
+                       bool waves, hipStream_t stream, CallTimer &timer) {
   switch (pow2_floor(p)) {
-    case 1: return launch_tree_q<Tr, 1, kHalvingFirst>(tab, p, n, div, nt, stream, timer);
-    case 2: return launch_tree_q<Tr, 2, kHalvingFirst>(tab, p, n, div, nt, stream, timer);
-    case 4: return launch_tree_q<Tr, 4, kHalvingFirst>(tab, p, n, div, nt, stream, timer);
-    case 8: return launch_tree_q<Tr, 8, kHalvingFirst>(tab, p, n, div, nt, stream, timer);
-    case 16: return launch_tree_q<Tr, 16, kHalvingFirst>(tab, p, n, div, nt, stream, timer);
-    case 32: return launch_tree_q<Tr, 32, kHalvingFirst>(tab, p, n, div, nt, stream, timer);
-    default: return launch_tree_q<Tr, 64, kHalvingFirst>(tab, p, n, div, nt, stream, timer);
+    case 1: return launch_tree_q<Tr, 1, kHalvingFirst>(tab, p, n, div, nt, waves, stream, timer);
+    case 2: return launch_tree_q<Tr, 2, kHalvingFirst>(tab, p, n, div, nt, waves, stream, timer);
+    case 4: return launch_tree_q<Tr, 4, kHalvingFirst>(tab, p, n, div, nt, waves, stream, timer);
+    case 8: return launch_tree_q<Tr, 8, kHalvingFirst>(tab, p, n, div, nt, waves, stream, timer);
+    case 16: return launch_tree_q<Tr, 16, kHalvingFirst>(tab, p, n, div, nt, waves, stream, timer);
+    case 32: return launch_tree_q<Tr, 32, kHalvingFirst>(tab, p, n, div, nt, waves, stream, timer);
+    default: return launch_tree_q<Tr, 64, kHalvingFirst>(tab, p, n, div, nt, waves, stream, timer);
   }
 }
 
 ddp_status launch_fused_tree(const RankTable &tab, int32_t p, int64_t n, int32_t dtype,
                              int32_t schedule, const Divide &div, hipStream_t stream,
                              CallTimer &timer) {
-  const bool nt = int64_t(p) * n * elem_bytes_of(dtype) > DDPSIM_TREE_NT_BYTES;
+  const int64_t bytes = int64_t(p) * n * elem_bytes_of(dtype);
+  const bool nt = bytes > DDPSIM_TREE_NT_BYTES;
+  const bool waves = bytes > DDPSIM_TREE_WAVES_BYTES;
   const bool halving_first = schedule != DDP_SCHED_RECURSIVE_DOUBLING;
   if (dtype == DDP_F32) {
-    return halving_first ? launch_tree<F32Traits, true>(tab, p, n, div, nt, stream, timer)
-                         : launch_tree<F32Traits, false>(tab, p, n, div, nt, stream, timer);
+    return halving_first
+               ? launch_tree<F32Traits, true>(tab, p, n, div, nt, waves, stream, timer)
+               : launch_tree<F32Traits, false>(tab, p, n, div, nt, waves, stream, timer);
   }
-  return halving_first ? launch_tree<BF16Traits, true>(tab, p, n, div, nt, stream, timer)
-                       : launch_tree<BF16Traits, false>(tab, p, n, div, nt, stream, timer);
+  return halving_first ? launch_tree<BF16Traits, true>(tab, p, n, div, nt, waves, stream, timer)
+                       : launch_tree<BF16Traits, false>(tab, p, n, div, nt, waves, stream, timer);
 }
 
 ddp_status launch_schedule_steps(const RankTable &rows, const std::vector<Step> &steps,
