@@ -438,3 +438,56 @@ def test_beyond_two_to_the_31_elements(oracle):
     assert np.array_equal(got4[:, 1], (got3[:, 1] + np.float32(1.0)).astype(np.float32))
     del bufs
     _free()
+
+
+def test_beyond_two_to_the_31_elements_many_ranks(oracle):
+    """Index arithmetic past 32 bits in the kernels that split a tile's ranks
+    over waves: p = 17 bf16 buffers of 17 * 126,322,576 elements (just over
+    2^31, 4 GiB each) through the fused ring all-reduce, the reduce-scatter
+    and the fused tree all-reduce, each on fresh values; sampled elements
+    (random ones, every chunk's ends and the last elements) against the
+    oracle."""
+    p, C = 17, 126_322_576
+    n = p * C
+    assert n > 1 << 31
+    _need(p * n * 2 + p * C * 2 + 8 * GiB)
+    rng = np.random.default_rng(12)
+    bufs = [W.normal_torch(n, 1.0, 41, r, "cuda", dtype=torch.bfloat16) for r in range(p)]
+    idx = np.unique(np.concatenate([_samples(n, p, 2048, rng),
+                                    np.arange(n - 40, n, dtype=np.int64)]))
+    vals = _gather(bufs, idx)
+    assert vals.dtype == np.uint16
+    _say("17 x (2^31+): fused ring all-reduce, bf16")
+    ddp.ring_allreduce_sim(bufs, avg="world")
+    torch.cuda.synchronize()
+    want = oracle.allreduce_at(vals, idx, n, avg="world")
+    got = _gather(bufs, idx)
+    for r in range(p):
+        assert_bits_equal(got[:, r], want, f"ring rank {r}")
+
+    for r in range(p):
+        W.normal_torch(n, 1.0, 42, r, "cuda", dtype=torch.bfloat16, out=bufs[r])
+    vals = _gather(bufs, idx)
+    outs = [torch.empty(C, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    _say("17 x (2^31+): reduce-scatter, bf16")
+    ddp.reduce_scatter_sim(bufs, outs, avg="world")
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter_at(vals, idx, n, avg="world")
+    owner, pos = idx // C, idx % C
+    got = np.array([to_host(outs[int(o)][int(j):int(j) + 1])[0] for o, j in zip(owner, pos)],
+                   dtype=np.uint16)
+    assert_bits_equal(got, want, "reduce-scatter")
+    del outs
+
+    for r in range(p):
+        W.normal_torch(n, 1.0, 43, r, "cuda", dtype=torch.bfloat16, out=bufs[r])
+    vals = _gather(bufs, idx)
+    _say("17 x (2^31+): tree all-reduce, bf16")
+    ddp.allreduce_sim(bufs, "tree", False, avg="world")
+    torch.cuda.synchronize()
+    want = oracle.tree_allreduce_at(vals, "tree", avg="world")
+    got = _gather(bufs, idx)
+    for r in range(p):
+        assert_bits_equal(got[:, r], want, f"tree rank {r}")
+    del bufs
+    _free()
