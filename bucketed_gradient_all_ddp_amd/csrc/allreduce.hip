@@ -38,9 +38,8 @@ namespace {
 // ---------------------------------------------------------------------------
 
 // Workgroup w handles tiles w, w + gridDim.x, ... (a grid-stride loop; the
-// launches below give every tile a workgroup of its own, since a grid sized
-// to the GPU measured slower); tile -> (chunk c, tile t within the chunk) =
-// (tile / tiles_per_chunk, tile % tiles_per_chunk).
+// launches below give every tile a workgroup of its own); tile -> (chunk c,
+// tile t within the chunk) = (tile / tiles_per_chunk, tile % tiles_per_chunk).
 template <typename Tr, int VPT, int RB, bool kNT, int THR>
 __global__ __launch_bounds__(THR) void fused_allreduce_kernel(
     RankTable bufs, int32_t p, int64_t n, int64_t C, int32_t tiles_per_chunk,
