@@ -1,0 +1,154 @@
+"""GPU parity on randomly drawn cases: rank counts, sizes, element types and
+averaging modes picked by a seeded generator (for the in-place bucket
+all-reduce also the parameter sizes, the bucket caps and the gradients'
+layout), every element of every rank against the oracle, bit for bit.
+
+The hand-picked cases elsewhere aim at known boundaries (chunk ends inside a
+vector, empty chunks, the switches between launch shapes); these draw the
+shape freely, so that a boundary nobody thought of is likely to be crossed
+somewhere. Each operation gets its own stream of cases; a few of them are
+sized past 256 MiB of rank buffers, where the streaming and wave-split
+kernels run. The draw is fixed by the seed, so a failure names a case that
+runs again the same way.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bucketed_gradient_all_ddp_amd as ddp
+from bucketed_gradient_all_ddp_amd import workloads as W
+from helpers import assert_bits_equal, make_grads, to_dev, to_host, tokens_for
+
+pytestmark = pytest.mark.gpu
+
+N_SMALL = 60  # cases per operation with rank buffers in the Infinity Cache
+N_LARGE = 6   # cases per operation past 256 MiB of rank buffers
+AVGS = ("none", "world", "tokens")
+SCHEDULES = ("recursive_doubling", "rabenseifner", "tree")
+
+
+def _draw(op, k):
+    """Case k of operation op: (p, n, bf16, avg, extra)."""
+    rng = np.random.default_rng([hash_op(op), k])
+    large = k >= N_SMALL
+    p = int(rng.integers(1, 65))
+    bf16 = bool(rng.integers(0, 2))
+    eb = 2 if bf16 else 4
+    if large:
+        p = int(rng.integers(9, 65))
+        lo = (256 << 20) // (p * eb) + 1
+        n = int(rng.integers(lo, lo + lo // 4))
+    else:
+        # log-uniform from 1 element to 2^20
+        n = int(np.exp(rng.uniform(0.0, np.log(1 << 20))))
+    if op == "reduce_scatter":
+        n = max(p, n // p * p)
+        if rng.integers(0, 2):
+            n = (n // (p * 8)) * p * 8 or p * 8  # whole vectors per shard
+    avg = AVGS[int(rng.integers(0, 3))]
+    extra = SCHEDULES[int(rng.integers(0, 3))] if op == "schedule" else None
+    return p, n, bf16, avg, extra
+
+
+def hash_op(op):
+    return sum(ord(c) * (i + 1) for i, c in enumerate(op))
+
+
+def _values(p, n, bf16, seed, oracle):
+    host = [W.normal_np(n, 1.0, seed, r) for r in range(p)]
+    return [oracle.f32_to_bf16(h) for h in host] if bf16 else host
+
+
+CASES = range(N_SMALL + N_LARGE)
+
+
+@pytest.mark.parametrize("k", CASES)
+def test_fused_allreduce_random(oracle, k):
+    p, n, bf16, avg, _ = _draw("fused", k)
+    host = _values(p, n, bf16, 5000 + k, oracle)
+    tokens = tokens_for(p, k) if avg == "tokens" else None
+    bufs = [to_dev(h) for h in host]
+    ddp.ring_allreduce_sim(bufs, avg=avg, tokens=tokens, algo="fused")
+    torch.cuda.synchronize()
+    want, _ = oracle.ring_allreduce(host, avg=avg, tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r]), want[r], f"case {k} p={p} n={n} bf16={bf16} "
+                                                      f"{avg} rank {r}")
+
+
+@pytest.mark.parametrize("k", CASES)
+def test_reduce_scatter_random(oracle, k):
+    p, n, bf16, avg, _ = _draw("reduce_scatter", k)
+    host = _values(p, n, bf16, 6000 + k, oracle)
+    tokens = tokens_for(p, k) if avg == "tokens" else None
+    C = n // p
+    ins = [to_dev(h) for h in host]
+    in_place = k % 2 == 1
+    if in_place:
+        outs = [ins[r][r * C:(r + 1) * C] for r in range(p)]
+    else:
+        outs = [torch.empty(C, dtype=ins[0].dtype, device="cuda") for _ in range(p)]
+    ddp.reduce_scatter_sim(ins, outs, avg=avg, tokens=tokens)
+    torch.cuda.synchronize()
+    want, _ = oracle.reduce_scatter(host, avg=avg, tokens=tokens)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"case {k} p={p} n={n} bf16={bf16} "
+                                                     f"{avg} in_place={in_place} rank {r}")
+
+
+@pytest.mark.parametrize("k", CASES)
+def test_schedule_allreduce_random(oracle, k):
+    p, n, bf16, avg, schedule = _draw("schedule", k)
+    host = _values(p, n, bf16, 7000 + k, oracle)
+    tokens = tokens_for(p, k) if avg == "tokens" else None
+    bufs = [to_dev(h) for h in host]
+    ddp.allreduce_sim(bufs, schedule, False, avg=avg, tokens=tokens)
+    torch.cuda.synchronize()
+    want, _ = oracle.allreduce(host, schedule, avg=avg, tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r]), want[r], f"case {k} p={p} n={n} bf16={bf16} "
+                                                     f"{avg} {schedule} rank {r}")
+
+
+BUCKET_CASES = range(N_SMALL)
+
+
+@pytest.mark.parametrize("k", BUCKET_CASES)
+def test_bucket_allreduce_random(oracle, k):
+    """The in-place bucket all-reduce of a random gradient set: 1 to 40
+    parameters of 1 to 2^18 elements, random caps, one launch for all
+    buckets (even k) or one launch per bucket (odd k)."""
+    rng = np.random.default_rng([hash_op("bucket"), k])
+    p = int(rng.integers(1, 65))
+    bf16 = bool(rng.integers(0, 2))
+    eb = 2 if bf16 else 4
+    count = int(rng.integers(1, 41))
+    sizes = [int(np.exp(rng.uniform(0.0, np.log(1 << 18)))) for _ in range(count)]
+    if rng.integers(0, 4) == 0:
+        sizes[int(rng.integers(0, len(sizes)))] = 0
+    cap = int(rng.integers(1, 1 << 20)) * eb
+    first = int(rng.integers(0, cap // eb + 1)) * eb
+    layout = ("aligned", "odd", "mixed")[int(rng.integers(0, 3))]
+    avg = AVGS[int(rng.integers(0, 3))]
+    tokens = tokens_for(p, k) if avg == "tokens" else None
+    host, grads = make_grads(p, sizes, 8000 + k, bf16, oracle, layout)
+    plan = ddp.ddp_bucket_plan(sizes, eb, cap, first).upload_segments(p)
+    table = ddp.grad_pointer_table(grads)
+    if k % 2 == 0:
+        ddp.ddp_allreduce_buckets(plan, 0, plan.num_buckets, table, p, avg=avg, tokens=tokens)
+    else:
+        for b in range(plan.num_buckets):
+            ddp.ddp_allreduce_bucket(plan, b, table, p, avg=avg, tokens=tokens)
+    torch.cuda.synchronize()
+    oplan = oracle.bucket_plan(sizes, eb, cap, first)
+    assert plan.buckets() == oplan.buckets()
+    want = [[g.copy() for g in rank] for rank in host]
+    for b in range(oplan.num_buckets):
+        flats = [oracle.flatten(want[r], oplan, b) for r in range(p)]
+        red, _ = oracle.ring_allreduce(flats, avg=avg, tokens=tokens, want_log=False)
+        for r in range(p):
+            oracle.unflatten(red[r], oplan, b, want[r])
+    what = f"case {k} p={p} bf16={bf16} {layout} {avg} sizes={sizes} cap={cap} first={first}"
+    for r in range(p):
+        for i in range(len(sizes)):
+            assert_bits_equal(to_host(grads[r][i]), want[r][i], f"{what} rank {r} param {i}")
