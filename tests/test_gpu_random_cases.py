@@ -152,3 +152,55 @@ def test_bucket_allreduce_random(oracle, k):
     for r in range(p):
         for i in range(len(sizes)):
             assert_bits_equal(to_host(grads[r][i]), want[r][i], f"{what} rank {r} param {i}")
+
+
+@pytest.mark.parametrize("k", range(N_SMALL))
+def test_ring_allreduce_random(oracle, k):
+    """The step-by-step ring (2(p-1) launches; bf16 on its fp32 workspace)."""
+    p, n, bf16, avg, _ = _draw("ring", k)
+    host = _values(p, n, bf16, 9000 + k, oracle)
+    tokens = tokens_for(p, k) if avg == "tokens" else None
+    bufs = [to_dev(h) for h in host]
+    need = ddp.ring_allreduce_sim_workspace(p, n, 1 if bf16 else 0, "ring")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    ddp.ring_allreduce_sim(bufs, avg=avg, tokens=tokens, algo="ring", workspace=ws)
+    torch.cuda.synchronize()
+    want, _ = oracle.ring_allreduce(host, avg=avg, tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r]), want[r], f"case {k} p={p} n={n} bf16={bf16} "
+                                                      f"{avg} rank {r}")
+
+
+@pytest.mark.parametrize("k", CASES)
+def test_allgather_and_broadcast_random(oracle, k):
+    """All-gather (in place for odd k) of shards drawn like the other cases,
+    then a broadcast of the gathered buffers from a random rank."""
+    p, n, bf16, _, _ = _draw("allgather", k)
+    C = max(1, n // p)
+    shards = _values(p, C, bf16, 10000 + k, oracle)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    outs = [torch.full((p * C,), 3.0, dtype=dt, device="cuda") for _ in range(p)]
+    if k % 2 == 1:
+        ins = [outs[r][r * C:(r + 1) * C] for r in range(p)]
+        for r in range(p):
+            ins[r].copy_(to_dev(shards[r]))
+    else:
+        ins = [to_dev(h) for h in shards]
+    ddp.allgather_sim(ins, outs)
+    torch.cuda.synchronize()
+    want, _ = oracle.allgather(shards)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"all-gather case {k} p={p} C={C} rank {r}")
+    # make the ranks differ, then broadcast from a random source
+    host = [to_host(o) for o in outs]
+    for r in range(p):
+        host[r] = host[r].copy()
+        host[r][r % host[r].size] = host[r][(r + 1) % host[r].size]
+        outs[r].copy_(to_dev(host[r]))
+    src = int(np.random.default_rng([hash_op("broadcast"), k]).integers(0, p))
+    ddp.broadcast_sim(outs, src=src)
+    torch.cuda.synchronize()
+    want, _ = oracle.broadcast(host, src)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"broadcast case {k} p={p} src={src} "
+                                                     f"rank {r}")
