@@ -204,3 +204,75 @@ def test_allgather_and_broadcast_random(oracle, k):
     for r in range(p):
         assert_bits_equal(to_host(outs[r]), want[r], f"broadcast case {k} p={p} src={src} "
                                                      f"rank {r}")
+
+
+def _random_set(rng, max_count, max_size):
+    count = int(rng.integers(1, max_count + 1))
+    sizes = [int(np.exp(rng.uniform(0.0, np.log(max_size)))) for _ in range(count)]
+    if rng.integers(0, 4) == 0:
+        sizes[int(rng.integers(0, count))] = 0
+    return sizes
+
+
+@pytest.mark.parametrize("k", range(N_SMALL // 2))
+def test_flatten_unflatten_random(oracle, k):
+    """ddp_flatten (with a random pre-divide for odd k) and ddp_unflatten of
+    every bucket of a random gradient set."""
+    rng = np.random.default_rng([hash_op("flatten"), k])
+    p = int(rng.integers(1, 65))
+    bf16 = bool(rng.integers(0, 2))
+    eb = 2 if bf16 else 4
+    sizes = _random_set(rng, 30, 1 << 17)
+    cap = int(rng.integers(1, 1 << 19)) * eb
+    first = int(rng.integers(0, cap // eb + 1)) * eb
+    layout = ("aligned", "odd", "mixed")[int(rng.integers(0, 3))]
+    divisor = float(rng.integers(2, 9)) if k % 2 else 1.0
+    host, grads = make_grads(p, sizes, 11000 + k, bf16, oracle, layout)
+    plan = ddp.ddp_bucket_plan(sizes, eb, cap, first).upload()
+    table = ddp.grad_pointer_table(grads)
+    oplan = oracle.bucket_plan(sizes, eb, cap, first)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    what = f"case {k} p={p} bf16={bf16} {layout} divisor={divisor} sizes={sizes}"
+    for b in range(plan.num_buckets):
+        bufs = [torch.empty(plan.bucket_numel(b), dtype=dt, device="cuda") for _ in range(p)]
+        ddp.ddp_flatten(plan, b, table, bufs, prescale_divisor=divisor)
+        torch.cuda.synchronize()
+        for r in range(p):
+            assert_bits_equal(to_host(bufs[r]), oracle.flatten(host[r], oplan, b, divisor),
+                              f"{what} flatten bucket {b} rank {r}")
+        # write back values the gradients do not hold yet: the flat buffers
+        # of the next rank
+        back = [to_host(bufs[(r + 1) % p]) for r in range(p)]
+        for r in range(p):
+            bufs[r].copy_(to_dev(back[r]))
+        ddp.ddp_unflatten(plan, b, bufs, table)
+        torch.cuda.synchronize()
+        for r in range(p):
+            oracle.unflatten(back[r], oplan, b, host[r])
+            for i in oplan.bucket_params(b):
+                assert_bits_equal(to_host(grads[r][i]), host[r][i],
+                                  f"{what} unflatten bucket {b} rank {r} param {i}")
+
+
+@pytest.mark.parametrize("k", range(N_SMALL // 2))
+def test_coalesced_broadcast_random(oracle, k):
+    """ddp_broadcast_coalesced of a random tensor set from a random root."""
+    rng = np.random.default_rng([hash_op("coalesced"), k])
+    p = int(rng.integers(1, 65))
+    bf16 = bool(rng.integers(0, 2))
+    eb = 2 if bf16 else 4
+    sizes = _random_set(rng, 30, 1 << 17)
+    cap = int(rng.integers(1, 1 << 20)) * eb
+    layout = ("aligned", "odd", "mixed")[int(rng.integers(0, 3))]
+    root = int(rng.integers(0, p))
+    host, views = make_grads(p, sizes, 12000 + k, bf16, oracle, layout)
+    plan = ddp.ddp_coalesce_plan(sizes, eb, cap).upload()
+    table = ddp.grad_pointer_table(views)
+    ddp.ddp_broadcast_coalesced(plan, table, p, root)
+    torch.cuda.synchronize()
+    want, _, _ = oracle.broadcast_coalesced(host, root=root, cap_bytes=cap)
+    for r in range(p):
+        for i in range(len(sizes)):
+            assert_bits_equal(to_host(views[r][i]), want[r][i],
+                              f"case {k} p={p} bf16={bf16} {layout} root={root} rank {r} "
+                              f"tensor {i}")
