@@ -110,7 +110,7 @@ def test_schedule_allreduce_random(oracle, k):
                                                      f"{avg} {schedule} rank {r}")
 
 
-BUCKET_CASES = range(N_SMALL)
+BUCKET_CASES = range(2 * N_SMALL)
 
 
 @pytest.mark.parametrize("k", BUCKET_CASES)
