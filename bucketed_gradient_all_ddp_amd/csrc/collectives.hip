@@ -61,7 +61,7 @@ namespace {
 #define DDPSIM_COPY_WGS_PER_CU 0
 #endif
 #ifndef DDPSIM_RS_WAVE_RULE
-#define DDPSIM_RS_WAVE_RULE 1  // 0: never split a tile's ranks over waves; 2, 8: always W beyond 8 ranks
+#define DDPSIM_RS_WAVE_RULE 1  // 0: never split a tile's ranks over waves; 2, 8: W beyond 16 ranks
 #endif
 #ifndef DDPSIM_RS_WAVES_BYTES
 #define DDPSIM_RS_WAVES_BYTES (int64_t(256) << 20)  // inputs past the Infinity Cache
