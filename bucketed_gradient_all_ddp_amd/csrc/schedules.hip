@@ -45,15 +45,6 @@ constexpr int bit_reverse(int t, int k) {
 // Fused form
 // ---------------------------------------------------------------------------
 
-// Leaves are visited in order t = 0..Q-1: leaf index t (recursive doubling,
-// nearest neighbours first) or the bit reversal of t over log2 Q bits (q/2
-// apart first). The balanced pairwise tree over that visit order is built
-// in batches of RB = min(Q, 8) consecutive visits: the batch's RB loads are
-// all issued before its additions, its leaves are summed as a complete
-// subtree, and the batch sum joins the earlier batches like a binary
-// counter (pending sums of 1, 2 and 4 batches in c[0..2]). The batch loop is
-// not unrolled, so a thread holds one batch of vectors at a time.
-
 // The complete subtree of visit-order batch m (leaves m*RB .. m*RB+RB-1 in
 // visit order, each with its extra rank folded in first).
 template <int Q, bool kHalvingFirst, int W, typename LeafLoad>
@@ -98,6 +89,14 @@ __device__ __forceinline__ void tree_batch(const LeafLoad &leaf, int32_t extra, 
   for (int e = 0; e < W; ++e) s[e] = x[0][e];
 }
 
+// Leaves are visited in order t = 0..Q-1: leaf index t (recursive doubling,
+// nearest neighbours first) or the bit reversal of t over log2 Q bits (q/2
+// apart first). The balanced pairwise tree over that visit order is built
+// in batches of RB = min(Q, 8) consecutive visits: the batch's RB loads are
+// all issued before its additions, its leaves are summed as a complete
+// subtree, and the batch sum joins the earlier batches like a binary
+// counter (pending sums of 1, 2 and 4 batches in c[0..2]). The batch loop is
+// not unrolled, so a thread holds one batch of vectors at a time.
 template <int Q, bool kHalvingFirst, int W, typename LeafLoad>
 __device__ __forceinline__ void tree_fold(const LeafLoad &leaf, int32_t extra,
                                           float (&out)[W]) {
