@@ -11,6 +11,8 @@ sized past 256 MiB of rank buffers, where the streaming and wave-split
 kernels run. The draw is fixed by the seed, so a failure names a case that
 runs again the same way.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +23,9 @@ from helpers import assert_bits_equal, make_grads, to_dev, to_host, tokens_for
 
 pytestmark = pytest.mark.gpu
 
+# Another draw of the same sizes: DDPSIM_TEST_SEED=k (0, the default, is the
+# committed draw).
+SEED = int(os.environ.get("DDPSIM_TEST_SEED", "0"))
 N_SMALL = 60  # cases per operation with rank buffers in the Infinity Cache
 N_LARGE = 6   # cases per operation past 256 MiB of rank buffers
 AVGS = ("none", "world", "tokens")
@@ -51,7 +56,7 @@ def _draw(op, k):
 
 
 def hash_op(op):
-    return sum(ord(c) * (i + 1) for i, c in enumerate(op))
+    return sum(ord(c) * (i + 1) for i, c in enumerate(op)) + 1000003 * SEED
 
 
 def _values(p, n, bf16, seed, oracle):
@@ -65,7 +70,7 @@ CASES = range(N_SMALL + N_LARGE)
 @pytest.mark.parametrize("k", CASES)
 def test_fused_allreduce_random(oracle, k):
     p, n, bf16, avg, _ = _draw("fused", k)
-    host = _values(p, n, bf16, 5000 + k, oracle)
+    host = _values(p, n, bf16, 5000 + k + 100000 * SEED, oracle)
     tokens = tokens_for(p, k) if avg == "tokens" else None
     bufs = [to_dev(h) for h in host]
     ddp.ring_allreduce_sim(bufs, avg=avg, tokens=tokens, algo="fused")
@@ -79,7 +84,7 @@ def test_fused_allreduce_random(oracle, k):
 @pytest.mark.parametrize("k", CASES)
 def test_reduce_scatter_random(oracle, k):
     p, n, bf16, avg, _ = _draw("reduce_scatter", k)
-    host = _values(p, n, bf16, 6000 + k, oracle)
+    host = _values(p, n, bf16, 6000 + k + 100000 * SEED, oracle)
     tokens = tokens_for(p, k) if avg == "tokens" else None
     C = n // p
     ins = [to_dev(h) for h in host]
@@ -99,7 +104,7 @@ def test_reduce_scatter_random(oracle, k):
 @pytest.mark.parametrize("k", CASES)
 def test_schedule_allreduce_random(oracle, k):
     p, n, bf16, avg, schedule = _draw("schedule", k)
-    host = _values(p, n, bf16, 7000 + k, oracle)
+    host = _values(p, n, bf16, 7000 + k + 100000 * SEED, oracle)
     tokens = tokens_for(p, k) if avg == "tokens" else None
     bufs = [to_dev(h) for h in host]
     ddp.allreduce_sim(bufs, schedule, False, avg=avg, tokens=tokens)
@@ -131,7 +136,7 @@ def test_bucket_allreduce_random(oracle, k):
     layout = ("aligned", "odd", "mixed")[int(rng.integers(0, 3))]
     avg = AVGS[int(rng.integers(0, 3))]
     tokens = tokens_for(p, k) if avg == "tokens" else None
-    host, grads = make_grads(p, sizes, 8000 + k, bf16, oracle, layout)
+    host, grads = make_grads(p, sizes, 8000 + k + 100000 * SEED, bf16, oracle, layout)
     plan = ddp.ddp_bucket_plan(sizes, eb, cap, first).upload_segments(p)
     table = ddp.grad_pointer_table(grads)
     if k % 2 == 0:
@@ -158,7 +163,7 @@ def test_bucket_allreduce_random(oracle, k):
 def test_ring_allreduce_random(oracle, k):
     """The step-by-step ring (2(p-1) launches; bf16 on its fp32 workspace)."""
     p, n, bf16, avg, _ = _draw("ring", k)
-    host = _values(p, n, bf16, 9000 + k, oracle)
+    host = _values(p, n, bf16, 9000 + k + 100000 * SEED, oracle)
     tokens = tokens_for(p, k) if avg == "tokens" else None
     bufs = [to_dev(h) for h in host]
     need = ddp.ring_allreduce_sim_workspace(p, n, 1 if bf16 else 0, "ring")
@@ -177,7 +182,7 @@ def test_allgather_and_broadcast_random(oracle, k):
     then a broadcast of the gathered buffers from a random rank."""
     p, n, bf16, _, _ = _draw("allgather", k)
     C = max(1, n // p)
-    shards = _values(p, C, bf16, 10000 + k, oracle)
+    shards = _values(p, C, bf16, 10000 + k + 100000 * SEED, oracle)
     dt = torch.bfloat16 if bf16 else torch.float32
     outs = [torch.full((p * C,), 3.0, dtype=dt, device="cuda") for _ in range(p)]
     if k % 2 == 1:
@@ -227,7 +232,7 @@ def test_flatten_unflatten_random(oracle, k):
     first = int(rng.integers(0, cap // eb + 1)) * eb
     layout = ("aligned", "odd", "mixed")[int(rng.integers(0, 3))]
     divisor = float(rng.integers(2, 9)) if k % 2 else 1.0
-    host, grads = make_grads(p, sizes, 11000 + k, bf16, oracle, layout)
+    host, grads = make_grads(p, sizes, 11000 + k + 100000 * SEED, bf16, oracle, layout)
     plan = ddp.ddp_bucket_plan(sizes, eb, cap, first).upload()
     table = ddp.grad_pointer_table(grads)
     oplan = oracle.bucket_plan(sizes, eb, cap, first)
@@ -265,7 +270,7 @@ def test_coalesced_broadcast_random(oracle, k):
     cap = int(rng.integers(1, 1 << 20)) * eb
     layout = ("aligned", "odd", "mixed")[int(rng.integers(0, 3))]
     root = int(rng.integers(0, p))
-    host, views = make_grads(p, sizes, 12000 + k, bf16, oracle, layout)
+    host, views = make_grads(p, sizes, 12000 + k + 100000 * SEED, bf16, oracle, layout)
     plan = ddp.ddp_coalesce_plan(sizes, eb, cap).upload()
     table = ddp.grad_pointer_table(views)
     ddp.ddp_broadcast_coalesced(plan, table, p, root)
