@@ -51,7 +51,7 @@ def _draw(op, k):
         if rng.integers(0, 2):
             n = (n // (p * 8)) * p * 8 or p * 8  # whole vectors per shard
     avg = AVGS[int(rng.integers(0, 3))]
-    extra = SCHEDULES[int(rng.integers(0, 3))] if op == "schedule" else None
+    extra = SCHEDULES[int(rng.integers(0, 3))] if op.startswith("schedule") else None
     return p, n, bf16, avg, extra
 
 
@@ -281,3 +281,21 @@ def test_coalesced_broadcast_random(oracle, k):
             assert_bits_equal(to_host(views[r][i]), want[r][i],
                               f"case {k} p={p} bf16={bf16} {layout} root={root} rank {r} "
                               f"tensor {i}")
+
+
+@pytest.mark.parametrize("k", range(N_SMALL))
+def test_schedule_steps_random(oracle, k):
+    """The logarithmic schedules step by step (one launch per message round;
+    bf16 on the fp32 workspace)."""
+    p, n, bf16, avg, schedule = _draw("schedule_steps", k)
+    host = _values(p, n, bf16, 13000 + k + 100000 * SEED, oracle)
+    tokens = tokens_for(p, k) if avg == "tokens" else None
+    bufs = [to_dev(h) for h in host]
+    need = ddp.allreduce_sim_workspace(p, n, 1 if bf16 else 0, schedule, True)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    ddp.allreduce_sim(bufs, schedule, True, avg=avg, tokens=tokens, workspace=ws)
+    torch.cuda.synchronize()
+    want, _ = oracle.allreduce(host, schedule, avg=avg, tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r]), want[r], f"case {k} p={p} n={n} bf16={bf16} "
+                                                     f"{avg} {schedule} steps rank {r}")
