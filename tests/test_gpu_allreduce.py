@@ -173,6 +173,41 @@ def test_fused_past_the_infinity_cache(oracle, bf16, p, n):
         assert_bits_equal(got[r], want[r], f"rank {r}")
 
 
+# Sizes on both sides of each rule that picks the fused kernel's form: the
+# small-call bound (at most 256 workgroups of 256 threads x 2 vectors), which
+# takes the 8-wave form beyond 32 ranks and the 32-load one-vector form at
+# 9-32 ranks, and the 256 MiB streaming bound, past which 8 ranks keep one
+# wave per tile, 9-27 ranks take 2 waves and 28 or more take 8.
+FORM_EDGES = [
+    (False, 64, 524_288), (False, 64, 524_289),      # 256 | 320 workgroups
+    (False, 33, 473_088), (False, 33, 473_089),      # 231 | 264
+    (False, 32, 524_288), (False, 32, 524_289),      # 256 | 288
+    (True, 64, 1_048_576), (True, 64, 1_048_577),    # bf16: 256 | 320
+    (False, 8, 8_388_609),                           # streaming, one wave
+    (False, 9, 7_456_541),                           # streaming, 2 waves
+    (False, 27, 2_485_513), (False, 27, 2_485_514),  # cached | streaming, 2 waves
+    (False, 28, 2_396_746),                          # streaming, 8 waves
+]
+
+
+@pytest.mark.parametrize("bf16,p,n", FORM_EDGES)
+def test_fused_launch_form_edges(oracle, bf16, p, n):
+    """Every element against the oracle on either side of each launch-form
+    rule of the fused all-reduce, token-weighted (a divisor that is not a
+    power of two)."""
+    eb = 2 if bf16 else 4
+    if p == 27:
+        assert (p * n * eb > 256 << 20) == (n % 2 == 0)
+    host = [W.normal_np(n, 1.0, 970 + p, r) for r in range(p)]
+    if bf16:
+        host = [oracle.f32_to_bf16(h) for h in host]
+    tokens = tokens_for(p, 7)
+    got, _ = _run(host, "tokens", tokens, "fused")
+    want, _ = oracle.ring_allreduce(host, avg="tokens", tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(got[r], want[r], f"rank {r}")
+
+
 def test_ring_steps_past_the_infinity_cache(oracle):
     """Rank buffers totalling more than 256 MiB take the ring step's
     streaming shape (one-wave workgroups, non-temporal accesses): every

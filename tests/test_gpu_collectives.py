@@ -162,3 +162,34 @@ def test_reduce_scatter_many_ranks_past_the_infinity_cache(oracle, p, C, bf16, i
     want, _ = oracle.reduce_scatter(host, avg=avg, tokens=tokens)
     for r in range(p):
         assert_bits_equal(to_host(outs[r]), want[r], f"rank {r}")
+
+
+# Shard sizes on both sides of each rule that picks the reduce-scatter's
+# form beyond 16 ranks (whole-vector shards): at most 512 tiles of 64 vectors
+# take 8 waves per tile, inputs past 256 MiB take 2, the rest 256 threads x
+# 2 vectors; 16 ranks keep one wave per tile.
+@pytest.mark.parametrize("p,C", [
+    (17, 7_680), (17, 7_684),        # 510 tiles | 544
+    (64, 2_048), (64, 2_052),        # 512 | 640
+    (17, 232_208), (17, 232_212),    # cached | past 256 MiB
+    (16, 7_680),                     # 480 tiles, one wave
+])
+def test_reduce_scatter_launch_form_edges(oracle, p, C):
+    """Every element of every shard against the oracle, token-weighted, in
+    place for even C / 4 and out of place otherwise."""
+    n = p * C
+    if (p, C) in ((17, 232_208), (17, 232_212)):
+        assert (p * n * 4 > 256 << 20) == (C == 232_212)
+    in_place = (C // 4) % 2 == 0
+    host = _vals(p, n, 690 + p, False, oracle)
+    tokens = tokens_for(p, 8)
+    ins = [to_dev(h) for h in host]
+    if in_place:
+        outs = [ins[r][r * C:(r + 1) * C] for r in range(p)]
+    else:
+        outs = [torch.empty(C, dtype=ins[0].dtype, device="cuda") for _ in range(p)]
+    ddp.reduce_scatter_sim(ins, outs, avg="tokens", tokens=tokens)
+    torch.cuda.synchronize()
+    want, _ = oracle.reduce_scatter(host, avg="tokens", tokens=tokens)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"rank {r}")

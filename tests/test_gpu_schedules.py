@@ -185,3 +185,25 @@ def test_fused_many_ranks_past_the_infinity_cache(oracle, schedule, p, n, bf16, 
     want, _ = oracle.allreduce(host, schedule, avg=avg, tokens=tokens, want_log=False)
     for r in range(p):
         assert_bits_equal(got[r], want[r], f"{schedule} rank {r}")
+
+
+# Sizes on both sides of each rule that picks the fused schedules' form from
+# 16 ranks: at most 512 one-wave tiles, or buffers past 256 MiB, take one
+# batch of eight leaves per wave; 16 ranks of exactly 256 MiB, and 15 ranks
+# past it (eight core ranks), keep one wave per tile.
+@pytest.mark.parametrize("schedule", LOG_SCHEDULES)
+@pytest.mark.parametrize("p,n", [
+    (16, 131_071), (16, 131_072),    # 512 tiles | 513
+    (64, 131_071), (64, 131_072),
+    (16, 4_194_304),                 # 256 MiB exactly: one wave
+    (15, 4_473_925),                 # past 256 MiB, Q = 8: one wave
+])
+def test_fused_launch_form_edges(oracle, schedule, p, n):
+    """Every element of every rank against the oracle's literal schedule,
+    token-weighted."""
+    host = [W.normal_np(n, 1.0, 820 + p, r) for r in range(p)]
+    tokens = tokens_for(p, 9)
+    got, _ = _run(host, schedule, False, "tokens", tokens)
+    want, _ = oracle.allreduce(host, schedule, avg="tokens", tokens=tokens, want_log=False)
+    for r in range(p):
+        assert_bits_equal(got[r], want[r], f"{schedule} rank {r}")
