@@ -193,3 +193,45 @@ def test_reduce_scatter_launch_form_edges(oracle, p, C):
     want, _ = oracle.reduce_scatter(host, avg="tokens", tokens=tokens)
     for r in range(p):
         assert_bits_equal(to_host(outs[r]), want[r], f"rank {r}")
+
+
+# The fan-out copy splits a tile's destinations over W waves, W the smallest
+# power of two with 4 W >= destinations (at most 8): rank counts on both
+# sides of each step, and the 256 MiB bound past which its stores stream.
+@pytest.mark.parametrize("p,n,src", [
+    (5, 100_003, 4), (6, 100_003, 0),    # 4 destinations: 1 wave | 5: 2 waves
+    (9, 100_003, 8), (10, 100_003, 3),   # 8: 2 | 9: 4
+    (17, 30_001, 16), (18, 30_001, 1),   # 16: 4 | 17: 8
+    (9, 7_456_540, 2), (9, 7_456_541, 5),  # cached | streaming stores
+])
+def test_broadcast_launch_form_edges(oracle, p, n, src):
+    if n > 7_000_000:
+        assert (p * n * 4 > 256 << 20) == (n % 2 == 1)
+    host = _vals(p, n, 610 + p, False, oracle)
+    bufs = [to_dev(h) for h in host]
+    ddp.broadcast_sim(bufs, src=src)
+    torch.cuda.synchronize()
+    want, _ = oracle.broadcast(host, src)
+    for r in range(p):
+        assert_bits_equal(to_host(bufs[r]), want[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("p,C", [(5, 10_007), (9, 10_007), (17, 3_001)])
+def test_allgather_launch_form_edges(oracle, p, C, in_place):
+    """In place a source skips its own rank (p - 1 destinations), out of
+    place it does not (p): at 5, 9 and 17 ranks the two take different
+    wave counts."""
+    host = _vals(p, C, 520 + p, False, oracle)
+    outs = [torch.full((p * C,), 7.0, dtype=torch.float32, device="cuda") for _ in range(p)]
+    if in_place:
+        ins = [outs[r][r * C:(r + 1) * C] for r in range(p)]
+        for r in range(p):
+            ins[r].copy_(to_dev(host[r]))
+    else:
+        ins = [to_dev(h) for h in host]
+    ddp.allgather_sim(ins, outs)
+    torch.cuda.synchronize()
+    want, _ = oracle.allgather(host)
+    for r in range(p):
+        assert_bits_equal(to_host(outs[r]), want[r], f"rank {r}")
